@@ -132,11 +132,16 @@ def backup(layout: Layout, alloc: np.ndarray, ids: Sequence[int], l0: int, l1: i
 
 
 def restore(layout: Layout, alloc: np.ndarray, host: np.ndarray, ids: Sequence[int], l0: int,
-            l1: int) -> np.ndarray:
+            l1: int, out: np.ndarray = None) -> np.ndarray:
     """RESTORE of the packed `host` buffer into pages `ids`, layers [l0, l1).
-    Returns a new allocation; `alloc` itself is not modified."""
+    Returns a new allocation and leaves `alloc` as it was, unless `out` is
+    given (it may be `alloc` itself), which is then written in place."""
     ids = _ids(ids)
-    out = np.array(alloc, dtype=np.uint8, copy=True)
+    if out is None:
+        out = np.array(alloc, dtype=np.uint8, copy=True)
+    elif out is not alloc:
+        out[...] = alloc
+    assert out.dtype == np.uint8 and out.flags.c_contiguous
     assert host.dtype == np.uint8 and host.flags.c_contiguous
     assert host.size >= layout.host_bytes(len(ids))
     c = layout.c()

@@ -1,0 +1,933 @@
+// api.cpp - the C ABI of kvx: handles and their lifecycle, the order of
+// validation (everything is checked before anything is enqueued), the path
+// executor (staged DMA through a device ring on a side stream, zero-copy
+// kernels on pinned host memory, or device-to-device), ready objects and
+// small utilities.
+//
+// Ownership follows the RFC's split ([RFC] "Ownership"): the caller owns the
+// pool allocation, page IDs and the decision that pages are safe to read or
+// write; the library owns its side streams, staging rings, events and
+// completion counters. Lifecycle follows [RFC] "Failure and lifecycle
+// handling" (generation-tagged handles, fail closed) and the RawCudaIPCWrapper
+// article's lifecycle section (teardown logs, never raises).
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <set>
+
+#include "kvx_internal.h"
+
+namespace kvx {
+
+// ---------------------------------------------------------------------------
+// errors and logging
+// ---------------------------------------------------------------------------
+namespace {
+thread_local std::string t_error;
+
+int log_level()
+{
+    static const int lvl = [] {
+        const char* e = std::getenv("KVX_LOG");
+        return e ? std::atoi(e) : 1;
+    }();
+    return lvl;
+}
+}  // namespace
+
+int fail(int code, const std::string& msg)
+{
+    t_error = msg;
+    if (log_level() >= 2) std::fprintf(stderr, "kvx: error %d: %s\n", code, msg.c_str());
+    return code;
+}
+
+void clear_error() { t_error.clear(); }
+
+void log_warn(const std::string& msg)
+{
+    if (log_level() >= 1) std::fprintf(stderr, "kvx: warning: %s\n", msg.c_str());
+}
+
+void log_info(const std::string& msg)
+{
+    if (log_level() >= 2) std::fprintf(stderr, "kvx: %s\n", msg.c_str());
+}
+
+int hip_fail(hipError_t e, const char* what)
+{
+    return fail(KVX_E_HIP, std::string(what) + " failed: " + hipGetErrorName(e) + " (" +
+                               hipGetErrorString(e) + ")");
+}
+
+// ---------------------------------------------------------------------------
+// handle registries: handles are never freed, only marked dead, so a stale
+// handle is recognised instead of being undefined behaviour
+// ---------------------------------------------------------------------------
+namespace {
+std::mutex g_reg_mu;
+std::set<const kvx_pool*> g_pools;
+std::set<const kvx_ready*> g_readies;
+
+std::mutex g_tune_mu;
+Tuning g_tune;
+}  // namespace
+
+bool pool_known(const kvx_pool* p)
+{
+    std::lock_guard<std::mutex> lk(g_reg_mu);
+    return p && g_pools.count(p) && p->magic == POOL_MAGIC;
+}
+
+bool ready_known(const kvx_ready* r)
+{
+    std::lock_guard<std::mutex> lk(g_reg_mu);
+    return r && g_readies.count(r) && r->magic == READY_MAGIC;
+}
+
+Tuning tuning()
+{
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    return g_tune;
+}
+
+// ---------------------------------------------------------------------------
+// device guard
+// ---------------------------------------------------------------------------
+namespace {
+struct DeviceGuard {
+    int prev = -1;
+    bool changed = false;
+    explicit DeviceGuard(int dev)
+    {
+        if (hipGetDevice(&prev) == hipSuccess && prev != dev)
+            changed = (hipSetDevice(dev) == hipSuccess);
+    }
+    ~DeviceGuard()
+    {
+        if (changed) (void)hipSetDevice(prev);
+    }
+};
+
+// ---------------------------------------------------------------------------
+// lanes: per (device, caller stream) state of the executor
+// ---------------------------------------------------------------------------
+struct Lane {
+    int device = -1;
+    hipStream_t caller = nullptr;
+    hipStream_t side = nullptr;     // library-owned, default priority
+    int cu_count = 0;
+    uint8_t* ring = nullptr;        // device staging ring
+    int64_t slot_bytes = 0;
+    int nslots = 0;
+    std::vector<hipEvent_t> slot_free, slot_ready;
+    std::vector<bool> slot_pending;
+    hipEvent_t ev_start = nullptr, ev_done = nullptr;
+    uint32_t* layer_done = nullptr; // per-layer unit counters for publish
+    int64_t layer_cap = 0;
+    bool counters_dirty = false;
+    int next_slot = 0;
+    std::mutex mu;
+};
+
+std::mutex g_lanes_mu;
+std::map<std::pair<int, hipStream_t>, Lane*> g_lanes;
+
+int lane_init(Lane* L)
+{
+    KVX_HIP(hipDeviceGetAttribute(&L->cu_count, hipDeviceAttributeMultiprocessorCount, L->device));
+    KVX_HIP(hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking));
+    KVX_HIP(hipEventCreateWithFlags(&L->ev_start, hipEventDisableTiming));
+    KVX_HIP(hipEventCreateWithFlags(&L->ev_done, hipEventDisableTiming));
+    return KVX_OK;
+}
+
+int get_lane(int device, hipStream_t caller, Lane** out)
+{
+    std::lock_guard<std::mutex> lk(g_lanes_mu);
+    auto key = std::make_pair(device, caller);
+    auto it = g_lanes.find(key);
+    if (it != g_lanes.end()) {
+        *out = it->second;
+        return KVX_OK;
+    }
+    Lane* L = new (std::nothrow) Lane();
+    if (!L) return fail(KVX_E_NOMEM, "cannot allocate an executor lane");
+    L->device = device;
+    L->caller = caller;
+    int rc = lane_init(L);
+    if (rc != KVX_OK) return rc;   // a half-built lane is leaked on purpose: never reused
+    g_lanes[key] = L;
+    *out = L;
+    return KVX_OK;
+}
+
+// waits until no earlier operation of this lane still reads or writes the ring
+int lane_drain_ring(Lane* L)
+{
+    for (int r = 0; r < L->nslots; r++)
+        if (L->slot_pending[r]) KVX_HIP(hipEventSynchronize(L->slot_free[r]));
+    return KVX_OK;
+}
+
+int lane_ring(Lane* L, int64_t slot_bytes, int nslots)
+{
+    if (L->ring && L->slot_bytes == slot_bytes && L->nslots == nslots) return KVX_OK;
+    int rc = lane_drain_ring(L);
+    if (rc != KVX_OK) return rc;
+    if (L->ring) {
+        KVX_HIP(hipFree(L->ring));
+        L->ring = nullptr;
+    }
+    for (hipEvent_t e : L->slot_free) (void)hipEventDestroy(e);
+    for (hipEvent_t e : L->slot_ready) (void)hipEventDestroy(e);
+    L->slot_free.clear();
+    L->slot_ready.clear();
+    L->slot_pending.assign(nslots, false);
+    L->nslots = 0;
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, static_cast<size_t>(slot_bytes) * nslots);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(KVX_E_NOMEM, "cannot allocate the device staging ring (" +
+                                     std::to_string(slot_bytes * nslots) + " bytes)");
+    }
+    L->ring = static_cast<uint8_t*>(p);
+    L->slot_free.resize(nslots);
+    L->slot_ready.resize(nslots);
+    for (int r = 0; r < nslots; r++) {
+        KVX_HIP(hipEventCreateWithFlags(&L->slot_free[r], hipEventDisableTiming));
+        KVX_HIP(hipEventCreateWithFlags(&L->slot_ready[r], hipEventDisableTiming));
+    }
+    L->slot_bytes = slot_bytes;
+    L->nslots = nslots;
+    L->next_slot = 0;
+    return KVX_OK;
+}
+
+int lane_counters(Lane* L, int64_t num_layers)
+{
+    if (L->layer_done && L->layer_cap >= num_layers && !L->counters_dirty) return KVX_OK;
+    if (!L->layer_done || L->layer_cap < num_layers) {
+        if (L->layer_done) {
+            KVX_HIP(hipStreamSynchronize(L->caller));   // earlier publishes may still count
+            KVX_HIP(hipFree(L->layer_done));
+            L->layer_done = nullptr;
+        }
+        const int64_t cap = std::max<int64_t>(num_layers, 256);
+        void* p = nullptr;
+        hipError_t e = hipMalloc(&p, cap * sizeof(uint32_t));
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(KVX_E_NOMEM, "cannot allocate per-layer completion counters");
+        }
+        L->layer_done = static_cast<uint32_t*>(p);
+        L->layer_cap = cap;
+    }
+    // stream-ordered clear before the first kernel that counts into them
+    KVX_HIP(hipMemsetAsync(L->layer_done, 0, L->layer_cap * sizeof(uint32_t), L->caller));
+    L->counters_dirty = false;
+    return KVX_OK;
+}
+
+// ---------------------------------------------------------------------------
+// memory classification
+// ---------------------------------------------------------------------------
+enum class MemKind { PinnedHost, Device, Other };
+
+MemKind classify(const void* p, int device, uint8_t** dev_view)
+{
+    hipPointerAttribute_t at;
+    std::memset(&at, 0, sizeof at);
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return MemKind::Other;
+    }
+    if (at.type == hipMemoryTypeHost) {
+        void* d = nullptr;
+        if (hipHostGetDevicePointer(&d, const_cast<void*>(p), 0) != hipSuccess || !d) {
+            (void)hipGetLastError();
+            return MemKind::Other;
+        }
+        *dev_view = static_cast<uint8_t*>(d);
+        return MemKind::PinnedHost;
+    }
+    if (at.type == hipMemoryTypeDevice && at.device == device) {
+        *dev_view = static_cast<uint8_t*>(const_cast<void*>(p));
+        return MemKind::Device;
+    }
+    return MemKind::Other;
+}
+
+int resolve_device(kvx_pool* pool)
+{
+    std::lock_guard<std::mutex> lk(pool->mu);
+    if (pool->device >= 0) return KVX_OK;
+    hipPointerAttribute_t at;
+    std::memset(&at, 0, sizeof at);
+    hipError_t e = hipPointerGetAttributes(&at, pool->start);
+    if (e != hipSuccess || at.type != hipMemoryTypeDevice) {
+        (void)hipGetLastError();
+        return fail(KVX_E_INVAL, "pool memory is not device memory");
+    }
+    void* abase = nullptr;
+    size_t asize = 0;
+    e = hipMemGetAddressRange(reinterpret_cast<hipDeviceptr_t*>(&abase), &asize, pool->start);
+    if (e == hipSuccess && abase) {
+        const uint64_t end = reinterpret_cast<uintptr_t>(pool->start) + pool->geom.pool_bytes;
+        if (end > reinterpret_cast<uintptr_t>(abase) + asize)
+            return fail(KVX_E_RANGE, "pool (" + std::to_string(pool->geom.pool_bytes) +
+                                         " bytes) extends past the end of its allocation");
+    } else {
+        (void)hipGetLastError();
+    }
+    pool->device = at.device;
+    return KVX_OK;
+}
+
+// ---------------------------------------------------------------------------
+// kernel launches over a layer range and a pair list
+// ---------------------------------------------------------------------------
+struct Target {
+    uint8_t* packed;       // device view of the packed region
+    int32_t pk_layer0, pk_slot0;
+    int64_t pk_slots;      // slots stored per (layer, kv) in `packed`
+};
+
+struct Publish {
+    uint32_t* layer_done = nullptr;
+    uint32_t* ready = nullptr;   // device view of counts + slot_base
+    uint32_t layer_target = 0;
+    uint32_t value = 0;
+};
+
+int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, int32_t lb,
+                 const PageSlot* pairs, size_t npairs, const Publish* pub, const Tuning& t,
+                 int cu_count, hipStream_t s)
+{
+    const PoolGeom& g = pool->geom;
+    MoveArgs a;
+    std::memset(&a, 0, sizeof a);
+    LaunchCfg cfg;
+    cfg.unroll = pick_unroll(g.piece_bytes);
+    cfg.permute = (g.inner == KVX_HND) && g.num_heads > 1 && g.page_size > 1;
+    cfg.publish = pub != nullptr;
+    cfg.nontemporal = t.nontemporal != 0;
+    a.pool = pool->start;
+    a.packed = tg.packed;
+    a.page_stride = g.page_stride;
+    a.layer_stride = g.layer_stride;
+    a.kv_stride = g.kv_stride;
+    a.pk_lc_stride = tg.pk_slots * g.piece_bytes;
+    a.pk_layer0 = tg.pk_layer0;
+    a.pk_slot0 = tg.pk_slot0;
+    a.piece_bytes = static_cast<uint32_t>(g.piece_bytes);
+    a.chunk_bytes = static_cast<uint32_t>(kThreads * kVecBytes * cfg.unroll);
+    a.chunks_per_piece = static_cast<uint32_t>((g.piece_bytes + a.chunk_bytes - 1) / a.chunk_bytes);
+    a.num_kv = static_cast<uint32_t>(g.num_kv);
+    a.T = static_cast<uint32_t>(g.page_size);
+    a.H = static_cast<uint32_t>(g.num_heads);
+    a.row_vec = static_cast<uint32_t>(g.row_bytes / kVecBytes);
+    a.mg_row_vec = magic_u32(a.row_vec);
+    a.mg_H = magic_u32(a.H);
+    a.mg_T = magic_u32(a.T);
+    if (pub) {
+        a.layer_done = pub->layer_done;
+        a.ready = pub->ready;
+        a.layer_target = pub->layer_target;
+        a.publish_value = pub->value;
+    }
+    const int64_t limit = (int64_t(1) << 31) - 1;
+    for (size_t p0 = 0; p0 < npairs; p0 += kMaxPairs) {
+        const size_t np = std::min<size_t>(kMaxPairs, npairs - p0);
+        for (size_t j = 0; j < np; j++) {
+            a.pairs[2 * j] = pairs[p0 + j].page;
+            a.pairs[2 * j + 1] = pairs[p0 + j].slot;
+        }
+        a.npairs = static_cast<uint32_t>(np);
+        const int64_t per_layer = g.num_kv * static_cast<int64_t>(np) * a.chunks_per_piece;
+        if (per_layer > limit) return fail(KVX_E_INVAL, "one layer of this call has too many work units");
+        const int32_t step = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(lb - la, limit / per_layer)));
+        for (int32_t l = la; l < lb; l += step) {
+            const int32_t nl = std::min(step, lb - l);
+            a.layer_begin = l;
+            a.total_units = static_cast<uint32_t>(per_layer * nl);
+            const int64_t gmax = t.grid_max > 0 ? t.grid_max : int64_t(cu_count) * 8;
+            cfg.grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(a.total_units, gmax)));
+            hipError_t e = launch_move(dir, cfg, a, s);
+            if (e != hipSuccess) return hip_fail(e, "kernel launch");
+        }
+    }
+    return KVX_OK;
+}
+
+// ---------------------------------------------------------------------------
+// the operation
+// ---------------------------------------------------------------------------
+int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* host, uint8_t* view,
+            int32_t l0, int32_t l1, kvx_ready* ready, int32_t slot_base, hipStream_t s,
+            int32_t path, const Tuning& t, Lane* L);
+
+int run_op(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, void* buf, uint64_t buf_bytes,
+         int32_t l0, int32_t l1, kvx_ready* ready, int32_t slot_base, void* stream_v, int32_t path)
+{
+    clear_error();
+    const char* op = dir == GATHER ? "backup" : "restore";
+    if (!pool_known(pool)) return fail(KVX_E_INVAL, std::string(op) + ": unknown pool handle");
+    if (!pool->live.load()) return fail(KVX_E_STALE, std::string(op) + ": pool handle was unregistered");
+    const PoolGeom& g = pool->geom;
+    if (path != KVX_PATH_STAGED && path != KVX_PATH_ZEROCOPY && path != KVX_PATH_DEVICE)
+        return fail(KVX_E_INVAL, std::string(op) + ": unknown path " + std::to_string(path));
+    if (l0 < 0 || l1 > g.num_layers || l0 > l1)
+        return fail(KVX_E_RANGE, std::string(op) + ": layer range [" + std::to_string(l0) + ", " +
+                                     std::to_string(l1) + ") is outside [0, " +
+                                     std::to_string(g.num_layers) + ")");
+    int rc = check_page_ids(g, ids, n, dir == SCATTER);
+    if (rc != KVX_OK) return rc;
+    if (ready) {
+        if (!ready_known(ready)) return fail(KVX_E_INVAL, "restore: unknown ready handle");
+        if (!ready->live.load()) return fail(KVX_E_STALE, "restore: ready object was destroyed");
+        if (ready->generation != pool->generation)
+            return fail(KVX_E_STALE, "restore: ready object generation " +
+                                         std::to_string(ready->generation) +
+                                         " does not match pool generation " +
+                                         std::to_string(pool->generation));
+        if (slot_base < 0 || int64_t(slot_base) + l1 > ready->num_slots)
+            return fail(KVX_E_RANGE, "restore: slots [" + std::to_string(int64_t(slot_base) + l0) +
+                                         ", " + std::to_string(int64_t(slot_base) + l1) +
+                                         ") are outside the ready object's " +
+                                         std::to_string(ready->num_slots) + " slots");
+    }
+    if (n == 0 || l0 == l1) return KVX_OK;
+    if (!buf) return fail(KVX_E_INVAL, std::string(op) + ": packed buffer is NULL");
+    const int64_t need = g.num_layers * g.num_kv * int64_t(n) * g.piece_bytes;
+    if (buf_bytes < static_cast<uint64_t>(need))
+        return fail(KVX_E_RANGE, std::string(op) + ": packed buffer holds " +
+                                     std::to_string(buf_bytes) + " bytes, needs " +
+                                     std::to_string(need));
+    if (reinterpret_cast<uintptr_t>(buf) % kVecBytes != 0)
+        return fail(KVX_E_ALIGN, std::string(op) + ": packed buffer is not 16-byte aligned");
+    if (ready && int64_t(n) * g.num_kv * ((g.piece_bytes + 4095) / 4096) >= (int64_t(1) << 32))
+        return fail(KVX_E_INVAL, "restore: too many pages for per-layer publish");
+
+    // ---- HIP from here on; nothing has been enqueued yet ----
+    rc = resolve_device(pool);
+    if (rc != KVX_OK) return rc;
+    DeviceGuard dg(pool->device);
+    hipStream_t s = static_cast<hipStream_t>(stream_v);
+    uint8_t* view = nullptr;
+    const MemKind kind = classify(buf, pool->device, &view);
+    if (path == KVX_PATH_DEVICE && kind != MemKind::Device)
+        return fail(KVX_E_INVAL, std::string(op) + ": path DEVICE needs device memory of the pool's GPU");
+    if (path != KVX_PATH_DEVICE && kind != MemKind::PinnedHost)
+        return fail(kind == MemKind::Device ? KVX_E_INVAL : KVX_E_NOTPINNED,
+                    std::string(op) + (kind == MemKind::Device
+                                           ? ": host path given device memory"
+                                           : ": packed buffer is not pinned host memory (pageable "
+                                             "memory is refused; use kvx_host_alloc)"));
+    const Tuning t = tuning();
+    Lane* L = nullptr;
+    rc = get_lane(pool->device, s, &L);
+    if (rc != KVX_OK) return rc;
+    std::lock_guard<std::mutex> lk(L->mu);
+    rc = enqueue(pool, dir, ids, n, static_cast<uint8_t*>(buf), view, l0, l1, ready, slot_base, s,
+                 path, t, L);
+    if (rc != KVX_OK) {
+        if (ready) L->counters_dirty = true;   // a partial publish may have left counts
+        return rc;
+    }
+    // remember the end of this operation for teardown
+    std::lock_guard<std::mutex> plk(pool->mu);
+    hipEvent_t& ev = pool->last_op[s];
+    if (!ev) KVX_HIP(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    KVX_HIP(hipEventRecord(ev, s));
+    return KVX_OK;
+}
+
+// Enqueues the whole operation on `s` (and the lane's side stream). Called
+// with the lane locked, after every validation has passed.
+int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* host, uint8_t* view,
+            int32_t l0, int32_t l1, kvx_ready* ready, int32_t slot_base, hipStream_t s,
+            int32_t path, const Tuning& t, Lane* L)
+{
+    const PoolGeom& g = pool->geom;
+    int rc = KVX_OK;
+
+    std::vector<PageSlot> pairs;
+    order_pages(ids, n, t.sort_pages != 0, &pairs);
+
+    Publish pub;
+    const Publish* pubp = nullptr;
+    if (ready) {
+        rc = lane_counters(L, g.num_layers);
+        if (rc != KVX_OK) return rc;
+        const int64_t chunk = int64_t(kThreads) * kVecBytes * pick_unroll(g.piece_bytes);
+        pub.layer_done = L->layer_done;
+        pub.ready = ready->counts_dev + slot_base;
+        pub.layer_target = static_cast<uint32_t>(g.num_kv * int64_t(n) * ((g.piece_bytes + chunk - 1) / chunk));
+        pub.value = static_cast<uint32_t>(n);
+        pubp = &pub;
+    }
+    if (path != KVX_PATH_STAGED) {
+        Target tg{view, 0, 0, n};
+        rc = launch_range(dir, pool, tg, l0, l1, pairs.data(), pairs.size(), pubp, t, L->cu_count, s);
+    } else {
+        // chunks of whole layers when one layer fits a ring slot, else slot
+        // ranges of one layer
+        const int64_t layer_bytes = g.num_kv * int64_t(n) * g.piece_bytes;
+        int64_t slot_bytes = std::max<int64_t>(t.stage_slot_bytes, g.num_kv * g.piece_bytes);
+        slot_bytes = (slot_bytes + 4095) / 4096 * 4096;
+        const int nslots = static_cast<int>(std::min<int64_t>(8, std::max<int64_t>(2, t.stage_slots)));
+        rc = lane_ring(L, slot_bytes, nslots);
+        if (rc != KVX_OK) return rc;
+        int32_t layers_per_chunk = 1, slots_per_chunk = n;
+        if (layer_bytes <= slot_bytes) {
+            layers_per_chunk = static_cast<int32_t>(slot_bytes / layer_bytes);
+            if (dir == SCATTER)
+                layers_per_chunk = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(layers_per_chunk, t.restore_chunk_layers)));
+        } else {
+            slots_per_chunk = static_cast<int32_t>(slot_bytes / (g.num_kv * g.piece_bytes));
+        }
+        if (dir == SCATTER) {
+            KVX_HIP(hipEventRecord(L->ev_start, s));
+            KVX_HIP(hipStreamWaitEvent(L->side, L->ev_start, 0));
+        }
+        std::vector<PageSlot> sub;
+        for (int32_t la = l0; la < l1 && rc == KVX_OK; la += layers_per_chunk) {
+            const int32_t lb = std::min(l1, la + layers_per_chunk);
+            for (int32_t s0 = 0; s0 < n && rc == KVX_OK; s0 += slots_per_chunk) {
+                const int32_t s1 = std::min(n, s0 + slots_per_chunk);
+                const bool full = (s0 == 0 && s1 == n);
+                const PageSlot* cp = pairs.data();
+                size_t cn = pairs.size();
+                if (!full) {
+                    sub.clear();
+                    for (const PageSlot& ps : pairs)
+                        if (ps.slot >= s0 && ps.slot < s1) sub.push_back(ps);
+                    cp = sub.data();
+                    cn = sub.size();
+                }
+                const int r = L->next_slot;
+                L->next_slot = (r + 1) % L->nslots;
+                uint8_t* slot_mem = L->ring + int64_t(r) * L->slot_bytes;
+                Target tg{slot_mem, la, s0, s1 - s0};
+                const int64_t strip = int64_t(s1 - s0) * g.piece_bytes;
+                // host byte offset of (layer l, kv c, slot s0) and of its ring copy
+                auto host_off = [&](int32_t l, int64_t c) { return ((int64_t(l) * g.num_kv + c) * n + s0) * g.piece_bytes; };
+                auto ring_off = [&](int32_t l, int64_t c) { return ((int64_t(l - la) * g.num_kv + c) * (s1 - s0)) * g.piece_bytes; };
+                if (dir == GATHER) {
+                    if (L->slot_pending[r]) KVX_HIP(hipStreamWaitEvent(s, L->slot_free[r], 0));
+                    rc = launch_range(dir, pool, tg, la, lb, cp, cn, nullptr, t, L->cu_count, s);
+                    if (rc != KVX_OK) break;
+                    KVX_HIP(hipEventRecord(L->slot_ready[r], s));
+                    KVX_HIP(hipStreamWaitEvent(L->side, L->slot_ready[r], 0));
+                    if (full) {
+                        KVX_HIP(hipMemcpyAsync(host + host_off(la, 0), slot_mem, int64_t(lb - la) * g.num_kv * strip,
+                                               hipMemcpyDeviceToHost, L->side));
+                    } else {
+                        for (int32_t l = la; l < lb; l++)
+                            for (int64_t c = 0; c < g.num_kv; c++)
+                                KVX_HIP(hipMemcpyAsync(host + host_off(l, c), slot_mem + ring_off(l, c), strip,
+                                                       hipMemcpyDeviceToHost, L->side));
+                    }
+                    KVX_HIP(hipEventRecord(L->slot_free[r], L->side));
+                } else {
+                    if (L->slot_pending[r]) KVX_HIP(hipStreamWaitEvent(L->side, L->slot_free[r], 0));
+                    if (full) {
+                        KVX_HIP(hipMemcpyAsync(slot_mem, host + host_off(la, 0), int64_t(lb - la) * g.num_kv * strip,
+                                               hipMemcpyHostToDevice, L->side));
+                    } else {
+                        for (int32_t l = la; l < lb; l++)
+                            for (int64_t c = 0; c < g.num_kv; c++)
+                                KVX_HIP(hipMemcpyAsync(slot_mem + ring_off(l, c), host + host_off(l, c), strip,
+                                                       hipMemcpyHostToDevice, L->side));
+                    }
+                    KVX_HIP(hipEventRecord(L->slot_ready[r], L->side));
+                    KVX_HIP(hipStreamWaitEvent(s, L->slot_ready[r], 0));
+                    rc = launch_range(dir, pool, tg, la, lb, cp, cn, pubp, t, L->cu_count, s);
+                    if (rc != KVX_OK) break;
+                    KVX_HIP(hipEventRecord(L->slot_free[r], s));
+                }
+                L->slot_pending[r] = true;
+            }
+        }
+        if (rc == KVX_OK && dir == GATHER) {
+            KVX_HIP(hipEventRecord(L->ev_done, L->side));
+            KVX_HIP(hipStreamWaitEvent(s, L->ev_done, 0));
+        }
+    }
+    return rc;
+}
+
+}  // namespace
+}  // namespace kvx
+
+using namespace kvx;
+
+// ===========================================================================
+// exported C ABI
+// ===========================================================================
+extern "C" {
+
+int kvx_version(void) { return KVX_ABI_VERSION; }
+
+const char* kvx_last_error(void) { return t_error.c_str(); }
+
+int kvx_register_pool(const kvx_layout* layout, void* base, uint64_t byte_offset,
+                      uint32_t dtype_bytes, int32_t ndim, const int64_t* shape,
+                      const int64_t* stride, uint64_t generation, kvx_pool** out)
+{
+    clear_error();
+    if (!out) return fail(KVX_E_INVAL, "register: out is NULL");
+    *out = nullptr;
+    PoolGeom g;
+    int rc = derive_geometry(layout, base, byte_offset, dtype_bytes, ndim, shape, stride, &g);
+    if (rc != KVX_OK) return rc;
+    kvx_pool* p = new (std::nothrow) kvx_pool();
+    if (!p) return fail(KVX_E_NOMEM, "register: out of host memory");
+    p->geom = g;
+    p->base = static_cast<uint8_t*>(base);
+    p->byte_offset = byte_offset;
+    p->start = p->base + byte_offset;
+    p->generation = generation;
+    {
+        std::lock_guard<std::mutex> lk(g_reg_mu);
+        g_pools.insert(p);
+    }
+    *out = p;
+    return KVX_OK;
+}
+
+int kvx_unregister_pool(kvx_pool* pool)
+{
+    clear_error();
+    if (!pool) return KVX_OK;
+    if (!pool_known(pool)) {
+        log_warn("unregister: unknown pool handle ignored");
+        return fail(KVX_E_INVAL, "unregister: unknown pool handle");
+    }
+    if (!pool->live.exchange(false)) {
+        log_warn("unregister: pool handle was already unregistered");
+        return KVX_OK;
+    }
+    std::lock_guard<std::mutex> lk(pool->mu);
+    if (pool->device >= 0) {
+        DeviceGuard dg(pool->device);
+        for (auto& kv : pool->last_op) {
+            hipError_t e = hipEventSynchronize(kv.second);
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                log_warn(std::string("unregister: waiting for in-flight work failed: ") +
+                         hipGetErrorString(e));
+            }
+            if (hipEventDestroy(kv.second) != hipSuccess) (void)hipGetLastError();
+        }
+    }
+    pool->last_op.clear();
+    return KVX_OK;
+}
+
+int kvx_pool_get_info(const kvx_pool* pool, kvx_pool_info* info)
+{
+    clear_error();
+    if (!pool_known(pool)) return fail(KVX_E_INVAL, "pool_get_info: unknown pool handle");
+    if (!pool->live.load()) return fail(KVX_E_STALE, "pool_get_info: pool handle was unregistered");
+    if (!info) return fail(KVX_E_INVAL, "pool_get_info: info is NULL");
+    const PoolGeom& g = pool->geom;
+    info->row_bytes = g.row_bytes;
+    info->piece_bytes = g.piece_bytes;
+    info->page_stride = g.page_stride;
+    info->layer_stride = g.layer_stride;
+    info->kv_stride = g.kv_stride;
+    info->pool_bytes = g.pool_bytes;
+    info->generation = pool->generation;
+    return KVX_OK;
+}
+
+int kvx_packed_bytes(const kvx_pool* pool, int32_t n, uint64_t* bytes)
+{
+    clear_error();
+    if (!pool_known(pool)) return fail(KVX_E_INVAL, "packed_bytes: unknown pool handle");
+    if (!pool->live.load()) return fail(KVX_E_STALE, "packed_bytes: pool handle was unregistered");
+    if (n < 0 || !bytes) return fail(KVX_E_INVAL, "packed_bytes: bad arguments");
+    const PoolGeom& g = pool->geom;
+    *bytes = static_cast<uint64_t>(g.num_layers * g.num_kv * int64_t(n) * g.piece_bytes);
+    return KVX_OK;
+}
+
+int kvx_backup(kvx_pool* pool, const int32_t* page_ids, int32_t n, void* dst, uint64_t dst_bytes,
+               int32_t layer_begin, int32_t layer_end, void* stream, int32_t path)
+{
+    return run_op(pool, GATHER, page_ids, n, dst, dst_bytes, layer_begin, layer_end, nullptr, 0,
+                stream, path);
+}
+
+int kvx_restore(kvx_pool* pool, const void* src, uint64_t src_bytes, const int32_t* page_ids,
+                int32_t n, int32_t layer_begin, int32_t layer_end, kvx_ready* ready,
+                int32_t slot_base, void* stream, int32_t path)
+{
+    return run_op(pool, SCATTER, page_ids, n, const_cast<void*>(src), src_bytes, layer_begin,
+                layer_end, ready, slot_base, stream, path);
+}
+
+int kvx_plan_runs(const kvx_pool* pool, const int32_t* page_ids, int32_t n, int32_t* runs,
+                  int32_t max_runs, int32_t* num_runs)
+{
+    clear_error();
+    if (!pool_known(pool)) return fail(KVX_E_INVAL, "plan_runs: unknown pool handle");
+    if (!pool->live.load()) return fail(KVX_E_STALE, "plan_runs: pool handle was unregistered");
+    if (!num_runs || (max_runs > 0 && !runs) || max_runs < 0)
+        return fail(KVX_E_INVAL, "plan_runs: bad output arguments");
+    int rc = check_page_ids(pool->geom, page_ids, n, false);
+    if (rc != KVX_OK) return rc;
+    std::vector<PageSlot> pairs;
+    order_pages(page_ids, n, true, &pairs);
+    std::vector<Run> rr;
+    plan_runs(pool->geom, pairs, &rr);
+    *num_runs = static_cast<int32_t>(rr.size());
+    for (int32_t k = 0; k < max_runs && k < *num_runs; k++) {
+        runs[3 * k] = rr[k].page;
+        runs[3 * k + 1] = rr[k].slot;
+        runs[3 * k + 2] = rr[k].count;
+    }
+    return KVX_OK;
+}
+
+// ---- ready objects -----------------------------------------------------------
+
+int kvx_ready_create(int32_t num_slots, uint64_t generation, kvx_ready** out)
+{
+    clear_error();
+    if (!out) return fail(KVX_E_INVAL, "ready_create: out is NULL");
+    *out = nullptr;
+    if (num_slots < 1 || num_slots > (1 << 24))
+        return fail(KVX_E_INVAL, "ready_create: num_slots must be in [1, 2^24]");
+    void* p = nullptr;
+    hipError_t e = hipHostMalloc(&p, sizeof(uint32_t) * num_slots,
+                                 hipHostMallocMapped | hipHostMallocPortable | hipHostMallocCoherent);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(e == hipErrorOutOfMemory ? KVX_E_NOMEM : KVX_E_HIP,
+                    std::string("ready_create: hipHostMalloc failed: ") + hipGetErrorString(e));
+    }
+    void* d = nullptr;
+    e = hipHostGetDevicePointer(&d, p, 0);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipHostFree(p);
+        return hip_fail(e, "hipHostGetDevicePointer");
+    }
+    kvx_ready* r = new (std::nothrow) kvx_ready();
+    if (!r) {
+        (void)hipHostFree(p);
+        return fail(KVX_E_NOMEM, "ready_create: out of host memory");
+    }
+    r->num_slots = num_slots;
+    r->generation = generation;
+    r->counts = static_cast<uint32_t*>(p);
+    r->counts_dev = static_cast<uint32_t*>(d);
+    for (int32_t k = 0; k < num_slots; k++) __atomic_store_n(&r->counts[k], 0u, __ATOMIC_RELEASE);
+    {
+        std::lock_guard<std::mutex> lk(g_reg_mu);
+        g_readies.insert(r);
+    }
+    *out = r;
+    return KVX_OK;
+}
+
+int kvx_ready_reset(kvx_ready* r)
+{
+    clear_error();
+    if (!ready_known(r)) return fail(KVX_E_INVAL, "ready_reset: unknown ready handle");
+    if (!r->live.load()) return fail(KVX_E_STALE, "ready_reset: ready object was destroyed");
+    for (int32_t k = 0; k < r->num_slots; k++) __atomic_store_n(&r->counts[k], 0u, __ATOMIC_RELEASE);
+    return KVX_OK;
+}
+
+int kvx_ready_destroy(kvx_ready* r)
+{
+    clear_error();
+    if (!r) return KVX_OK;
+    if (!ready_known(r)) {
+        log_warn("ready_destroy: unknown ready handle ignored");
+        return fail(KVX_E_INVAL, "ready_destroy: unknown ready handle");
+    }
+    if (!r->live.exchange(false)) {
+        log_warn("ready_destroy: ready object was already destroyed");
+        return KVX_OK;
+    }
+    hipError_t e = hipHostFree(r->counts);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        log_warn(std::string("ready_destroy: hipHostFree failed: ") + hipGetErrorString(e));
+    }
+    r->counts = nullptr;
+    r->counts_dev = nullptr;
+    return KVX_OK;
+}
+
+int kvx_layer_ready(const kvx_ready* r, int32_t slot, int32_t* published)
+{
+    clear_error();
+    if (!ready_known(r)) return fail(KVX_E_INVAL, "layer_ready: unknown ready handle");
+    if (!r->live.load()) return fail(KVX_E_STALE, "layer_ready: ready object was destroyed");
+    if (slot < 0 || slot >= r->num_slots || !published)
+        return fail(KVX_E_RANGE, "layer_ready: slot out of range");
+    *published = static_cast<int32_t>(__atomic_load_n(&r->counts[slot], __ATOMIC_ACQUIRE));
+    return KVX_OK;
+}
+
+int kvx_ready_prefix(const kvx_ready* r, int32_t* prefix)
+{
+    clear_error();
+    if (!ready_known(r)) return fail(KVX_E_INVAL, "ready_prefix: unknown ready handle");
+    if (!r->live.load()) return fail(KVX_E_STALE, "ready_prefix: ready object was destroyed");
+    if (!prefix) return fail(KVX_E_INVAL, "ready_prefix: prefix is NULL");
+    uint32_t m = __atomic_load_n(&r->counts[0], __ATOMIC_ACQUIRE);
+    for (int32_t k = 1; k < r->num_slots; k++)
+        m = std::min(m, __atomic_load_n(&r->counts[k], __ATOMIC_ACQUIRE));
+    *prefix = static_cast<int32_t>(m);
+    return KVX_OK;
+}
+
+int kvx_ready_slot_ptr(const kvx_ready* r, int32_t slot, void** dev_ptr)
+{
+    clear_error();
+    if (!ready_known(r)) return fail(KVX_E_INVAL, "ready_slot_ptr: unknown ready handle");
+    if (!r->live.load()) return fail(KVX_E_STALE, "ready_slot_ptr: ready object was destroyed");
+    if (slot < 0 || slot >= r->num_slots || !dev_ptr)
+        return fail(KVX_E_RANGE, "ready_slot_ptr: slot out of range");
+    *dev_ptr = r->counts_dev + slot;
+    return KVX_OK;
+}
+
+int kvx_ready_wait_gpu(const kvx_ready* r, int32_t slot, int32_t min_count, void* stream,
+                       uint32_t spin_limit, int32_t* status_dev)
+{
+    clear_error();
+    if (!ready_known(r)) return fail(KVX_E_INVAL, "ready_wait_gpu: unknown ready handle");
+    if (!r->live.load()) return fail(KVX_E_STALE, "ready_wait_gpu: ready object was destroyed");
+    if (slot < 0 || slot >= r->num_slots) return fail(KVX_E_RANGE, "ready_wait_gpu: slot out of range");
+    if (min_count < 0 || !status_dev || reinterpret_cast<uintptr_t>(status_dev) % 4)
+        return fail(KVX_E_INVAL, "ready_wait_gpu: bad min_count or status pointer");
+    hipPointerAttribute_t at;
+    std::memset(&at, 0, sizeof at);
+    if (hipPointerGetAttributes(&at, status_dev) != hipSuccess || at.type != hipMemoryTypeDevice) {
+        (void)hipGetLastError();
+        return fail(KVX_E_INVAL, "ready_wait_gpu: status must be device memory");
+    }
+    DeviceGuard dg(at.device);
+    hipError_t e = launch_ready_wait(r->counts_dev + slot, static_cast<uint32_t>(min_count),
+                                     spin_limit, status_dev, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "ready wait launch");
+    return KVX_OK;
+}
+
+// ---- memory / misc -------------------------------------------------------------
+
+int kvx_host_alloc(uint64_t bytes, void** out)
+{
+    clear_error();
+    if (!out || bytes == 0) return fail(KVX_E_INVAL, "host_alloc: bad arguments");
+    *out = nullptr;
+    hipError_t e = hipHostMalloc(out, bytes,
+                                 hipHostMallocMapped | hipHostMallocPortable | hipHostMallocNonCoherent);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        *out = nullptr;
+        return fail(e == hipErrorOutOfMemory ? KVX_E_NOMEM : KVX_E_HIP,
+                    std::string("host_alloc: hipHostMalloc failed: ") + hipGetErrorString(e));
+    }
+    return KVX_OK;
+}
+
+int kvx_host_free(void* p)
+{
+    clear_error();
+    if (!p) return KVX_OK;
+    hipError_t e = hipHostFree(p);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return hip_fail(e, "hipHostFree");
+    }
+    return KVX_OK;
+}
+
+int kvx_alloc_range(const void* ptr, void** base, uint64_t* size)
+{
+    clear_error();
+    if (!ptr || !base || !size) return fail(KVX_E_INVAL, "alloc_range: bad arguments");
+    hipDeviceptr_t b = nullptr;
+    size_t sz = 0;
+    hipError_t e = hipMemGetAddressRange(&b, &sz, const_cast<void*>(ptr));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return hip_fail(e, "hipMemGetAddressRange");
+    }
+    *base = b;
+    *size = sz;
+    return KVX_OK;
+}
+
+int kvx_sync(void* stream)
+{
+    clear_error();
+    hipError_t e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+    return KVX_OK;
+}
+
+int kvx_set_option(int32_t option, int64_t value)
+{
+    clear_error();
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    switch (option) {
+    case KVX_OPT_GRID_MAX:
+        if (value < 0 || value > (1 << 24)) break;
+        g_tune.grid_max = value;
+        return KVX_OK;
+    case KVX_OPT_STAGE_SLOT_BYTES:
+        if (value < (1 << 20) || value > (int64_t(1) << 34)) break;
+        g_tune.stage_slot_bytes = value;
+        return KVX_OK;
+    case KVX_OPT_STAGE_SLOTS:
+        if (value < 2 || value > 8) break;
+        g_tune.stage_slots = value;
+        return KVX_OK;
+    case KVX_OPT_SORT_PAGES:
+        if (value != 0 && value != 1) break;
+        g_tune.sort_pages = value;
+        return KVX_OK;
+    case KVX_OPT_NONTEMPORAL:
+        if (value != 0 && value != 1) break;
+        g_tune.nontemporal = value;
+        return KVX_OK;
+    case KVX_OPT_RESTORE_CHUNK_LAYERS:
+        if (value < 1 || value > 4096) break;
+        g_tune.restore_chunk_layers = value;
+        return KVX_OK;
+    default:
+        return fail(KVX_E_INVAL, "set_option: unknown option " + std::to_string(option));
+    }
+    return fail(KVX_E_INVAL, "set_option: value " + std::to_string(value) +
+                                 " out of range for option " + std::to_string(option));
+}
+
+int kvx_get_option(int32_t option, int64_t* value)
+{
+    clear_error();
+    if (!value) return fail(KVX_E_INVAL, "get_option: value is NULL");
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    switch (option) {
+    case KVX_OPT_GRID_MAX: *value = g_tune.grid_max; return KVX_OK;
+    case KVX_OPT_STAGE_SLOT_BYTES: *value = g_tune.stage_slot_bytes; return KVX_OK;
+    case KVX_OPT_STAGE_SLOTS: *value = g_tune.stage_slots; return KVX_OK;
+    case KVX_OPT_SORT_PAGES: *value = g_tune.sort_pages; return KVX_OK;
+    case KVX_OPT_NONTEMPORAL: *value = g_tune.nontemporal; return KVX_OK;
+    case KVX_OPT_RESTORE_CHUNK_LAYERS: *value = g_tune.restore_chunk_layers; return KVX_OK;
+    default: return fail(KVX_E_INVAL, "get_option: unknown option " + std::to_string(option));
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,238 @@
+// kernels.hip - gfx950 kernels of kvx: the piece gather (BACKUP pack), the
+// piece scatter (RESTORE unpack) with per-layer publish, and the bounded
+// ready-wait used by GPU-side consumers.
+//
+// Work decomposition. A launch moves the pieces (page, layer, kv) of a layer
+// range, every kv and a list of (page, slot) pairs carried in the kernel
+// arguments. Each piece (T*H*D*eb bytes, contiguous in every supported pool
+// layout and in the packed buffer) is cut into units of
+// kThreads * 16 * U bytes; one workgroup moves one unit per iteration of a
+// grid-stride loop, every lane issuing U independent 16-byte (dwordx4)
+// loads before its U stores, so a wave keeps U * 1 KiB in flight. Units are
+// numbered layer-major, so the units of layer l are all handed out before
+// those of layer l+1 and layers complete roughly in order.
+//
+// Head-major pools ([RAWIPC] integration: TRT-LLM's HND pool) are converted
+// row by row: a row of D elements is contiguous on both sides, so every
+// 16-byte access stays within one row and each wave reads and writes whole
+// 64-byte segments; no LDS staging is needed for rows of 16 bytes or more.
+// Destination order is linear (sequential writes), the source address is
+// the permuted row.
+//
+// Publish ([TICKET] "PP Prefetch Ticket Path": layer-wise H2D and a
+// published safe prefix): after a workgroup's stores of a unit of layer l it
+// fences at agent scope and counts the unit into layer_done[l]; the last
+// unit of the layer stores n into the ready slot with a system-scope
+// release, so no reader can see the count before every byte of the layer.
+// The last unit also resets the counter, leaving it zero for the next call
+// on the same stream.
+#include "kvx_internal.h"
+
+namespace kvx {
+
+typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint32_t fast_div(uint32_t x, uint32_t magic)
+{
+    return magic ? __umulhi(x, magic) : x;
+}
+
+template <bool NT>
+__device__ __forceinline__ v4u load16(const uint8_t* p)
+{
+    if constexpr (NT)
+        return __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
+    else
+        return *reinterpret_cast<const v4u*>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ void store16(uint8_t* p, v4u v)
+{
+    if constexpr (NT)
+        __builtin_nontemporal_store(v, reinterpret_cast<v4u*>(p));
+    else
+        *reinterpret_cast<v4u*>(p) = v;
+}
+
+// Byte offset, inside the source piece, of the 16 bytes that land at byte
+// offset `off` of the destination piece.
+template <Dir D, bool PERMUTE>
+__device__ __forceinline__ uint32_t source_offset(const MoveArgs& a, uint32_t off)
+{
+    if constexpr (!PERMUTE) {
+        return off;
+    } else {
+        const uint32_t vi = off >> 4;
+        const uint32_t row = fast_div(vi, a.mg_row_vec);
+        const uint32_t w = vi - row * a.row_vec;
+        uint32_t src_row;
+        if constexpr (D == GATHER) {
+            // destination: packed NHD row t*H + h; source: pool HND row h*T + t
+            const uint32_t t = fast_div(row, a.mg_H);
+            const uint32_t h = row - t * a.H;
+            src_row = h * a.T + t;
+        } else {
+            // destination: pool HND row h*T + t; source: packed NHD row t*H + h
+            const uint32_t h = fast_div(row, a.mg_T);
+            const uint32_t t = row - h * a.T;
+            src_row = t * a.H + h;
+        }
+        return (src_row * a.row_vec + w) << 4;
+    }
+}
+
+template <Dir D, int U, bool PERMUTE, bool PUBLISH, bool NT>
+__global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
+{
+    const uint32_t tid = threadIdx.x;
+    const uint32_t cpp = a.chunks_per_piece;
+    for (uint32_t q = blockIdx.x; q < a.total_units; q += gridDim.x) {
+        // unit q -> (layer, kv, pair, chunk); all wave-uniform scalar math
+        const uint32_t pu = q / cpp;
+        const uint32_t k = q - pu * cpp;
+        const uint32_t lc = pu / a.npairs;
+        const uint32_t j = pu - lc * a.npairs;
+        const uint32_t lrel = lc / a.num_kv;
+        const uint32_t c = lc - lrel * a.num_kv;
+        const int32_t l = a.layer_begin + static_cast<int32_t>(lrel);
+        const int32_t page = a.pairs[2 * j];
+        const int32_t slot = a.pairs[2 * j + 1];
+
+        uint8_t* pool_piece = a.pool + static_cast<int64_t>(page) * a.page_stride +
+                              static_cast<int64_t>(l) * a.layer_stride +
+                              static_cast<int64_t>(c) * a.kv_stride;
+        uint8_t* pk_piece =
+            a.packed +
+            (static_cast<int64_t>(l - a.pk_layer0) * a.num_kv + c) * a.pk_lc_stride +
+            static_cast<int64_t>(slot - a.pk_slot0) * a.piece_bytes;
+        const uint8_t* src = (D == GATHER) ? pool_piece : pk_piece;
+        uint8_t* dst = (D == GATHER) ? pk_piece : pool_piece;
+
+        const uint32_t base = k * a.chunk_bytes + tid * kVecBytes;
+        v4u v[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const uint32_t off = base + u * (kThreads * kVecBytes);
+            if (off < a.piece_bytes) v[u] = load16<NT>(src + source_offset<D, PERMUTE>(a, off));
+        }
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const uint32_t off = base + u * (kThreads * kVecBytes);
+            if (off < a.piece_bytes) store16<NT>(dst + off, v[u]);
+        }
+
+        if constexpr (PUBLISH) {
+            __threadfence();   // this lane's stores are performed at agent scope
+            __syncthreads();   // ... for every lane of the workgroup
+            if (tid == 0) {
+                const uint32_t done = __hip_atomic_fetch_add(&a.layer_done[l], 1u, __ATOMIC_ACQ_REL,
+                                                             __HIP_MEMORY_SCOPE_AGENT) + 1u;
+                if (done == a.layer_target) {
+                    __hip_atomic_store(&a.layer_done[l], 0u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                    __hip_atomic_store(&a.ready[l], a.publish_value, __ATOMIC_RELEASE,
+                                       __HIP_MEMORY_SCOPE_SYSTEM);
+                }
+            }
+        }
+    }
+}
+
+// One wave polls a ready slot with bounded patience; see kvx_ready_wait_gpu.
+__global__ __launch_bounds__(64) void kvx_ready_wait_kernel(const uint32_t* slot, uint32_t min_count,
+                                                            uint32_t spin_limit, int32_t* status)
+{
+    if (threadIdx.x != 0) return;
+    int32_t reached = 0;
+    for (uint32_t i = 0; i < spin_limit; i++) {
+        const uint32_t v = __hip_atomic_load(slot, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_SYSTEM);
+        if (v >= min_count) {
+            reached = 1;
+            break;
+        }
+        __builtin_amdgcn_s_sleep(64);
+    }
+    *status = reached;
+}
+
+// ---------------------------------------------------------------------------
+// host-side dispatch
+// ---------------------------------------------------------------------------
+uint32_t magic_u32(uint32_t d)
+{
+    // floor(x / d) == umulhi(x, floor(2^32 / d) + 1) whenever x * d < 2^32;
+    // divisor 1 is flagged with 0 (the multiplier would not fit in 32 bits)
+    if (d <= 1) return 0;
+    return static_cast<uint32_t>((uint64_t(1) << 32) / d + 1);
+}
+
+int pick_unroll(int64_t piece_bytes)
+{
+    const int64_t step = kThreads * kVecBytes;   // 4 KiB per vector round of a workgroup
+    for (int u : {8, 4, 2})
+        if (piece_bytes % (step * u) == 0) return u;
+    if (piece_bytes % step == 0) return 1;
+    return piece_bytes >= 8 * step ? 8 : (piece_bytes >= 4 * step ? 4 : 1);
+}
+
+namespace {
+
+template <Dir D, int U, bool P, bool PUB, bool NT>
+hipError_t go(const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s)
+{
+    void* args[] = {const_cast<MoveArgs*>(&a)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&kvx_move_kernel<D, U, P, PUB, NT>),
+                           dim3(cfg.grid), dim3(kThreads), args, 0, s);
+}
+
+template <Dir D, int U, bool P, bool PUB>
+hipError_t go_nt(const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s)
+{
+    return cfg.nontemporal ? go<D, U, P, PUB, true>(cfg, a, s) : go<D, U, P, PUB, false>(cfg, a, s);
+}
+
+template <Dir D, int U, bool P>
+hipError_t go_pub(const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s)
+{
+    if constexpr (D == SCATTER) {
+        if (cfg.publish) return go_nt<D, U, P, true>(cfg, a, s);
+    }
+    return go_nt<D, U, P, false>(cfg, a, s);
+}
+
+template <Dir D, int U>
+hipError_t go_perm(const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s)
+{
+    return cfg.permute ? go_pub<D, U, true>(cfg, a, s) : go_pub<D, U, false>(cfg, a, s);
+}
+
+template <Dir D>
+hipError_t go_unroll(const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s)
+{
+    switch (cfg.unroll) {
+    case 8: return go_perm<D, 8>(cfg, a, s);
+    case 4: return go_perm<D, 4>(cfg, a, s);
+    case 2: return go_perm<D, 2>(cfg, a, s);
+    case 1: return go_perm<D, 1>(cfg, a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_move(Dir dir, const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s)
+{
+    if (cfg.grid < 1 || a.total_units == 0) return hipErrorInvalidValue;
+    return dir == GATHER ? go_unroll<GATHER>(cfg, a, s) : go_unroll<SCATTER>(cfg, a, s);
+}
+
+hipError_t launch_ready_wait(const uint32_t* slot, uint32_t min_count, uint32_t spin_limit,
+                             int32_t* status, hipStream_t s)
+{
+    void* args[] = {&slot, &min_count, &spin_limit, &status};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&kvx_ready_wait_kernel), dim3(1), dim3(64),
+                           args, 0, s);
+}
+
+}  // namespace kvx

@@ -1,0 +1,355 @@
+"""ctypes binding of libkvx.so (include/kvx.h).
+
+Argument marshalling only: every step of backup, restore, publish and the
+ready queries runs inside libkvx.so (HIP kernels and the HIP runtime). The
+functions keep the C names. There is no fallback: if the library is not
+built, loading fails with an error.
+
+PyTorch is used only as a source of device memory and streams: a tensor is
+passed as its data pointer, a stream as its hipStream_t handle.
+"""
+import ctypes
+import os
+from typing import Iterable, Optional, Sequence
+
+import numpy as np
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvx.so")
+
+KVX_OK = 0
+KVX_E_INVAL, KVX_E_NONCONTIG, KVX_E_ALIGN, KVX_E_RANGE, KVX_E_DUP = -1, -2, -3, -4, -5
+KVX_E_STALE, KVX_E_NOTPINNED, KVX_E_NOMEM, KVX_E_HIP = -6, -7, -8, -9
+KVX_AX_PAGE, KVX_AX_LAYER, KVX_AX_KV = 0, 1, 2
+KVX_NHD, KVX_HND = 0, 1
+KVX_PATH_STAGED, KVX_PATH_ZEROCOPY, KVX_PATH_DEVICE = 0, 1, 2
+KVX_OPT_GRID_MAX, KVX_OPT_STAGE_SLOT_BYTES, KVX_OPT_STAGE_SLOTS = 0, 1, 2
+KVX_OPT_SORT_PAGES, KVX_OPT_NONTEMPORAL, KVX_OPT_RESTORE_CHUNK_LAYERS = 3, 4, 5
+
+ERROR_NAMES = {0: "KVX_OK", -1: "KVX_E_INVAL", -2: "KVX_E_NONCONTIG", -3: "KVX_E_ALIGN",
+               -4: "KVX_E_RANGE", -5: "KVX_E_DUP", -6: "KVX_E_STALE", -7: "KVX_E_NOTPINNED",
+               -8: "KVX_E_NOMEM", -9: "KVX_E_HIP"}
+PATHS = {"staged": KVX_PATH_STAGED, "zerocopy": KVX_PATH_ZEROCOPY, "device": KVX_PATH_DEVICE}
+_AXES = {"page": KVX_AX_PAGE, "layer": KVX_AX_LAYER, "kv": KVX_AX_KV}
+
+
+class KvxError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{ERROR_NAMES.get(code, code)}: {message}")
+        self.code = code
+        self.message = message
+
+
+class kvx_layout(ctypes.Structure):
+    _fields_ = [("outer", ctypes.c_int32 * 3), ("inner", ctypes.c_int32),
+                ("num_pages", ctypes.c_int32), ("num_layers", ctypes.c_int32),
+                ("num_kv", ctypes.c_int32), ("page_size", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32)]
+
+
+class kvx_pool_info(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_uint64) for k in ("row_bytes", "piece_bytes", "page_stride",
+                                               "layer_stride", "kv_stride", "pool_bytes",
+                                               "generation")]
+
+
+# (name, restype, argtypes) of every exported function
+_vp, _i32, _u32, _i64, _u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_int64, \
+    ctypes.c_uint64
+_P = ctypes.POINTER
+SIGNATURES = [
+    ("kvx_register_pool", ctypes.c_int, [_P(kvx_layout), _vp, _u64, _u32, _i32, _P(_i64), _P(_i64),
+                                         _u64, _P(_vp)]),
+    ("kvx_unregister_pool", ctypes.c_int, [_vp]),
+    ("kvx_pool_get_info", ctypes.c_int, [_vp, _P(kvx_pool_info)]),
+    ("kvx_packed_bytes", ctypes.c_int, [_vp, _i32, _P(_u64)]),
+    ("kvx_backup", ctypes.c_int, [_vp, _P(_i32), _i32, _vp, _u64, _i32, _i32, _vp, _i32]),
+    ("kvx_restore", ctypes.c_int, [_vp, _vp, _u64, _P(_i32), _i32, _i32, _i32, _vp, _i32, _vp,
+                                   _i32]),
+    ("kvx_plan_runs", ctypes.c_int, [_vp, _P(_i32), _i32, _P(_i32), _i32, _P(_i32)]),
+    ("kvx_ready_create", ctypes.c_int, [_i32, _u64, _P(_vp)]),
+    ("kvx_ready_reset", ctypes.c_int, [_vp]),
+    ("kvx_ready_destroy", ctypes.c_int, [_vp]),
+    ("kvx_layer_ready", ctypes.c_int, [_vp, _i32, _P(_i32)]),
+    ("kvx_ready_prefix", ctypes.c_int, [_vp, _P(_i32)]),
+    ("kvx_ready_slot_ptr", ctypes.c_int, [_vp, _i32, _P(_vp)]),
+    ("kvx_ready_wait_gpu", ctypes.c_int, [_vp, _i32, _i32, _vp, _u32, _vp]),
+    ("kvx_host_alloc", ctypes.c_int, [_u64, _P(_vp)]),
+    ("kvx_host_free", ctypes.c_int, [_vp]),
+    ("kvx_alloc_range", ctypes.c_int, [_vp, _P(_vp), _P(_u64)]),
+    ("kvx_sync", ctypes.c_int, [_vp]),
+    ("kvx_last_error", ctypes.c_char_p, []),
+    ("kvx_version", ctypes.c_int, []),
+    ("kvx_set_option", ctypes.c_int, [_i32, _i64]),
+    ("kvx_get_option", ctypes.c_int, [_i32, _P(_i64)]),
+]
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def hip_runtimes_mapped() -> list:
+    """Distinct libamdhip64 files mapped into this process."""
+    paths = set()
+    try:
+        with open("/proc/self/maps") as f:
+            for line in f:
+                if "libamdhip64" in line:
+                    paths.add(os.path.realpath(line.split()[-1]))
+    except OSError:
+        pass
+    return sorted(paths)
+
+
+def lib() -> ctypes.CDLL:
+    """Loads libkvx.so. Raises if it is not built or if the process ends up
+    with two HIP runtimes (torch's and another), which would make torch's
+    streams and pointers meaningless to kvx."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"libkvx.so is not built ({LIB_PATH}); run "
+                              "`python -c 'import __graft_entry__ as g; g.build()'` first")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, res, args in SIGNATURES:
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        if L.kvx_version() != 1:
+            raise ImportError("libkvx.so ABI version mismatch")
+        rts = hip_runtimes_mapped()
+        if len(rts) > 1:
+            raise ImportError(f"two HIP runtimes are loaded: {rts}")
+        _lib = L
+    return _lib
+
+
+def kvx_last_error() -> str:
+    return lib().kvx_last_error().decode(errors="replace")
+
+
+def _check(rc: int) -> None:
+    if rc != KVX_OK:
+        raise KvxError(rc, kvx_last_error())
+
+
+def _ptr(x) -> int:
+    """Address of a tensor, numpy array or integer pointer."""
+    if x is None:
+        return 0
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
+    raise TypeError(f"cannot take the address of {type(x)}")
+
+
+def _stream(s) -> int:
+    if s is None:
+        return 0
+    if isinstance(s, int):
+        return s
+    if hasattr(s, "cuda_stream"):
+        return s.cuda_stream
+    raise TypeError(f"not a stream: {type(s)}")
+
+
+def _ids(page_ids) -> np.ndarray:
+    a = np.ascontiguousarray(np.asarray(page_ids, dtype=np.int32).reshape(-1))
+    return a
+
+
+def _ids_ptr(a: np.ndarray):
+    return a.ctypes.data_as(_P(_i32))
+
+
+# ---------------------------------------------------------------------------
+# layout and registration
+# ---------------------------------------------------------------------------
+def make_layout(outer: Sequence[str], inner: str, num_pages: int, num_layers: int, num_kv: int,
+                page_size: int, num_heads: int, head_dim: int) -> kvx_layout:
+    L = kvx_layout()
+    L.outer[:] = [_AXES[a] for a in outer]
+    L.inner = {"NHD": KVX_NHD, "HND": KVX_HND}[inner]
+    L.num_pages, L.num_layers, L.num_kv = num_pages, num_layers, num_kv
+    L.page_size, L.num_heads, L.head_dim = page_size, num_heads, head_dim
+    return L
+
+
+def kvx_register_pool(layout: kvx_layout, base: int, byte_offset: int, dtype_bytes: int,
+                      shape: Sequence[int], stride: Sequence[int], generation: int) -> int:
+    nd = len(shape)
+    sh = (_i64 * max(nd, 1))(*shape)
+    st = (_i64 * max(nd, 1))(*stride)
+    out = _vp()
+    _check(lib().kvx_register_pool(ctypes.byref(layout), base, byte_offset, dtype_bytes, nd, sh, st,
+                                   generation, ctypes.byref(out)))
+    return out.value
+
+
+def kvx_unregister_pool(pool: int) -> None:
+    _check(lib().kvx_unregister_pool(pool))
+
+
+def kvx_pool_get_info(pool: int) -> kvx_pool_info:
+    info = kvx_pool_info()
+    _check(lib().kvx_pool_get_info(pool, ctypes.byref(info)))
+    return info
+
+
+def kvx_packed_bytes(pool: int, n: int) -> int:
+    out = _u64()
+    _check(lib().kvx_packed_bytes(pool, n, ctypes.byref(out)))
+    return out.value
+
+
+def kvx_alloc_range(ptr: int):
+    base, size = _vp(), _u64()
+    _check(lib().kvx_alloc_range(ptr, ctypes.byref(base), ctypes.byref(size)))
+    return base.value, size.value
+
+
+def permute_to_dense_view(t):
+    """Metadata-only permute of a non-contiguous tensor view to a contiguous
+    one when its strides allow it (the RawCudaIPCWrapper article, sender
+    validation: permute first, then check; never copy)."""
+    if t.is_contiguous():
+        return t
+    order = sorted(range(t.dim()), key=lambda d: (-t.stride(d), d))
+    p = t.permute(*order)
+    return p if p.is_contiguous() else t
+
+
+def register_tensor(t, layout: kvx_layout, generation: int) -> int:
+    """Registers a torch tensor as a pool: permutes it to a dense view if its
+    strides allow (metadata only), finds its allocation base, and passes
+    base, byte offset, element size, shape and stride to kvx_register_pool,
+    which rejects any view that is still not dense."""
+    v = permute_to_dense_view(t)
+    base, _ = kvx_alloc_range(v.data_ptr())
+    return kvx_register_pool(layout, base, v.data_ptr() - base, v.element_size(), list(v.shape),
+                             list(v.stride()), generation)
+
+
+# ---------------------------------------------------------------------------
+# data movement
+# ---------------------------------------------------------------------------
+def kvx_backup(pool: int, page_ids: Iterable[int], dst, dst_bytes: int, layer_begin: int,
+               layer_end: int, stream=None, path: int = KVX_PATH_STAGED) -> None:
+    ids = _ids(page_ids)
+    _check(lib().kvx_backup(pool, _ids_ptr(ids), ids.size, _ptr(dst), dst_bytes, layer_begin,
+                            layer_end, _stream(stream), path))
+
+
+def kvx_restore(pool: int, src, src_bytes: int, page_ids: Iterable[int], layer_begin: int,
+                layer_end: int, ready: int = None, slot_base: int = 0, stream=None,
+                path: int = KVX_PATH_STAGED) -> None:
+    ids = _ids(page_ids)
+    _check(lib().kvx_restore(pool, _ptr(src), src_bytes, _ids_ptr(ids), ids.size, layer_begin,
+                             layer_end, ready or 0, slot_base, _stream(stream), path))
+
+
+def kvx_plan_runs(pool: int, page_ids: Iterable[int]) -> np.ndarray:
+    ids = _ids(page_ids)
+    cap = max(ids.size, 1)
+    runs = np.zeros(3 * cap, dtype=np.int32)
+    num = _i32()
+    _check(lib().kvx_plan_runs(pool, _ids_ptr(ids), ids.size, runs.ctypes.data_as(_P(_i32)), cap,
+                               ctypes.byref(num)))
+    return runs[:3 * num.value].reshape(-1, 3)
+
+
+# ---------------------------------------------------------------------------
+# readiness
+# ---------------------------------------------------------------------------
+def kvx_ready_create(num_slots: int, generation: int) -> int:
+    out = _vp()
+    _check(lib().kvx_ready_create(num_slots, generation, ctypes.byref(out)))
+    return out.value
+
+
+def kvx_ready_reset(ready: int) -> None:
+    _check(lib().kvx_ready_reset(ready))
+
+
+def kvx_ready_destroy(ready: int) -> None:
+    _check(lib().kvx_ready_destroy(ready))
+
+
+def kvx_layer_ready(ready: int, slot: int) -> int:
+    out = _i32()
+    _check(lib().kvx_layer_ready(ready, slot, ctypes.byref(out)))
+    return out.value
+
+
+def kvx_ready_prefix(ready: int) -> int:
+    out = _i32()
+    _check(lib().kvx_ready_prefix(ready, ctypes.byref(out)))
+    return out.value
+
+
+def kvx_ready_slot_ptr(ready: int, slot: int) -> int:
+    out = _vp()
+    _check(lib().kvx_ready_slot_ptr(ready, slot, ctypes.byref(out)))
+    return out.value
+
+
+def kvx_ready_wait_gpu(ready: int, slot: int, min_count: int, stream, spin_limit: int,
+                       status_dev) -> None:
+    _check(lib().kvx_ready_wait_gpu(ready, slot, min_count, _stream(stream), spin_limit,
+                                    _ptr(status_dev)))
+
+
+# ---------------------------------------------------------------------------
+# memory, sync, options
+# ---------------------------------------------------------------------------
+def kvx_host_alloc(nbytes: int) -> int:
+    out = _vp()
+    _check(lib().kvx_host_alloc(nbytes, ctypes.byref(out)))
+    return out.value
+
+
+def kvx_host_free(ptr: int) -> None:
+    _check(lib().kvx_host_free(ptr))
+
+
+def kvx_sync(stream=None) -> None:
+    _check(lib().kvx_sync(_stream(stream)))
+
+
+def kvx_set_option(option: int, value: int) -> None:
+    _check(lib().kvx_set_option(option, value))
+
+
+def kvx_get_option(option: int) -> int:
+    out = _i64()
+    _check(lib().kvx_get_option(option, ctypes.byref(out)))
+    return out.value
+
+
+def kvx_version() -> int:
+    return lib().kvx_version()
+
+
+class HostBuffer:
+    """Pinned, device-mapped host memory from kvx_host_alloc, viewable as a
+    numpy uint8 array."""
+
+    def __init__(self, nbytes: int):
+        self.nbytes = nbytes
+        self.ptr = kvx_host_alloc(nbytes)
+
+    def numpy(self) -> np.ndarray:
+        buf = (ctypes.c_uint8 * self.nbytes).from_address(self.ptr)
+        return np.frombuffer(buf, dtype=np.uint8)
+
+    def free(self) -> None:
+        if self.ptr:
+            kvx_host_free(self.ptr)
+            self.ptr = 0
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass

@@ -53,3 +53,51 @@ def pool_alloc_image(w: "Workload", seed: int) -> np.ndarray:
     img = gen_bytes(seed + 1, 0, w.alloc_bytes)
     img[w.byte_offset:w.byte_offset + w.pool_bytes] = gen_bytes(seed, w.byte_offset, w.pool_bytes)
     return img
+
+
+# ---------------------------------------------------------------------------
+# GPU fill / compare (synth/libkvxsynth.so)
+# ---------------------------------------------------------------------------
+_gpu = None
+
+
+def _gpu_lib():
+    global _gpu
+    if _gpu is None:
+        import ctypes
+        import os
+        path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvxsynth.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is not built")
+        L = ctypes.CDLL(path)
+        vp, u64 = ctypes.c_void_p, ctypes.c_uint64
+        L.synth_fill.argtypes = [vp, u64, u64, u64, vp]
+        L.synth_fill.restype = ctypes.c_int
+        L.synth_diff_blocks.argtypes = [vp, u64, u64, u64, u64, vp, vp]
+        L.synth_diff_blocks.restype = ctypes.c_int
+        _gpu = L
+    return _gpu
+
+
+def fill_gpu(ptr: int, nbytes: int, seed: int, addr0: int, stream: int = 0) -> None:
+    """Writes stream bytes addr0 .. addr0+nbytes-1 of `seed` to the
+    device-visible memory at ptr (device memory or mapped pinned host)."""
+    rc = _gpu_lib().synth_fill(ptr, nbytes, seed, addr0, stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_fill failed ({rc})")
+
+
+def diff_blocks_gpu(ptr: int, nbytes: int, seed: int, addr0: int, block_bytes: int,
+                    flags_ptr: int, stream: int = 0) -> None:
+    """Sets the uint32 flag of every block_bytes block of [ptr, ptr+nbytes)
+    that differs from the stream (flags must be zeroed beforehand)."""
+    rc = _gpu_lib().synth_diff_blocks(ptr, nbytes, seed, addr0, block_bytes, flags_ptr, stream)
+    if rc != 0:
+        raise RuntimeError(f"synth_diff_blocks failed ({rc})")
+
+
+def fill_alloc_gpu(ptr: int, w: "Workload", seed: int, stream: int = 0) -> None:
+    """GPU version of pool_alloc_image: stream seed+1 over the allocation,
+    then stream `seed` over the pool region."""
+    fill_gpu(ptr, w.alloc_bytes, seed + 1, 0, stream)
+    fill_gpu(ptr + w.byte_offset, w.pool_bytes, seed, w.byte_offset, stream)

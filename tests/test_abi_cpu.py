@@ -1,0 +1,224 @@
+"""CPU tests of the C ABI: the library loads and exports every declared
+symbol, and the host-side logic (layout validation, page-list checks, run
+planning, handle lifecycle, fail-closed error paths) behaves as specified.
+No call here reaches the GPU: every call either needs no HIP API or is
+rejected by validation before the first one."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+import paged_kv_offload_amd as kvx
+from paged_kv_offload_amd import kvx as K
+from synth.workloads import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE_BASE = 0x7F0000000000   # never dereferenced: registration is pure validation
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "kvx.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvx_[a-z_0-9]+)\s*\(", text)))
+
+
+def dense_stride(shape):
+    st, acc = [], 1
+    for d in reversed(shape):
+        st.append(acc)
+        acc *= d
+    return list(reversed(st))
+
+
+def layout_of(w):
+    return kvx.make_layout(w.outer, w.inner, w.num_pages, w.num_layers, w.num_kv, w.page_size,
+                           w.num_heads, w.head_dim)
+
+
+def register(w, base=FAKE_BASE, offset=None, shape=None, stride=None, gen=7):
+    shape = shape or w.tensor_shape()
+    stride = stride or dense_stride(shape)
+    off = w.byte_offset if offset is None else offset
+    return K.kvx_register_pool(layout_of(w), base, off, w.dtype_bytes, shape, stride, gen)
+
+
+def test_library_exports_every_header_function():
+    L = kvx.lib()
+    names = header_functions()
+    assert len(names) >= 20
+    for name in names:
+        assert hasattr(L, name), name
+    assert {s[0] for s in K.SIGNATURES} == set(names)
+    assert K.kvx_version() == 1
+
+
+def test_single_hip_runtime_in_process():
+    kvx.lib()
+    assert len(K.hip_runtimes_mapped()) <= 1
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_register_derives_strides(name):
+    w = WORKLOADS[name]
+    p = register(w)
+    info = K.kvx_pool_get_info(p)
+    assert info.piece_bytes == w.piece_bytes
+    assert info.row_bytes == w.row_bytes
+    assert info.pool_bytes == w.pool_bytes
+    assert info.generation == 7
+    size = {"page": w.num_pages, "layer": w.num_layers, "kv": w.num_kv}
+    # row-major over the outer axes in their physical order, pieces innermost
+    s = w.piece_bytes
+    want = {}
+    for a in reversed(w.outer):
+        want[a] = s
+        s *= size[a]
+    assert (info.page_stride, info.layer_stride, info.kv_stride) == \
+        (want["page"], want["layer"], want["kv"])
+    assert K.kvx_packed_bytes(p, 10) == w.num_layers * w.num_kv * 10 * w.piece_bytes
+    K.kvx_unregister_pool(p)
+
+
+def test_noncontiguous_is_hard_error_with_shape_and_stride():
+    w = WORKLOADS["tiny"]
+    shape = w.tensor_shape()
+    stride = dense_stride(shape)
+    stride[0], stride[1] = stride[1], stride[0]   # a transposed view of the same bytes
+    with pytest.raises(kvx.KvxError) as e:
+        register(w, shape=shape, stride=stride)
+    assert e.value.code == K.KVX_E_NONCONTIG
+    assert str(shape).replace(" ", "") in e.value.message.replace(" ", "")
+    assert str(stride).replace(" ", "") in e.value.message.replace(" ", "")
+
+
+def test_padded_stride_rejected_and_size1_stride_ignored():
+    w = WORKLOADS["tiny"]
+    shape = w.tensor_shape()
+    stride = dense_stride(shape)
+    padded = [s * 2 for s in stride[:-1]] + [1]
+    with pytest.raises(kvx.KvxError) as e:
+        register(w, shape=shape, stride=padded)
+    assert e.value.code == K.KVX_E_NONCONTIG
+    # a size-1 dimension may carry any stride
+    sh1 = shape[:1] + [1] + shape[1:]
+    st1 = dense_stride(sh1)
+    st1[1] = 12345
+    K.kvx_unregister_pool(register(w, shape=sh1, stride=st1))
+
+
+def test_merged_and_split_views():
+    w = WORKLOADS["trtllm_hnd"]
+    K.kvx_unregister_pool(register(w, shape=[4096, 32, 2, 8 * 32 * 128]))
+    K.kvx_unregister_pool(register(w, shape=[4096, 32, 2, 8, 32, 128]))
+    K.kvx_unregister_pool(register(w, shape=[4096 * 32 * 2 * 8 * 32 * 128]))
+    with pytest.raises(kvx.KvxError) as e:   # splits inside the head axis
+        register(w, shape=[4096, 32, 2, 4, 64, 128])
+    assert e.value.code == K.KVX_E_INVAL
+    with pytest.raises(kvx.KvxError) as e:   # wrong element count
+        register(w, shape=[4096, 32, 2, 8 * 32 * 64])
+    assert e.value.code == K.KVX_E_INVAL
+
+
+def test_alignment_errors():
+    w = WORKLOADS["trtllm_hnd"]
+    with pytest.raises(kvx.KvxError) as e:
+        register(w, offset=12288 + 8)
+    assert e.value.code == K.KVX_E_ALIGN
+    odd = WORKLOADS["tiny"].scaled(head_dim=60)   # 120-byte rows
+    with pytest.raises(kvx.KvxError) as e:
+        register(odd)
+    assert e.value.code == K.KVX_E_ALIGN
+
+
+def test_bad_layouts():
+    w = WORKLOADS["tiny"]
+    L = layout_of(w)
+    L.outer[:] = [0, 0, 2]
+    shape = w.tensor_shape()
+    with pytest.raises(kvx.KvxError) as e:
+        K.kvx_register_pool(L, FAKE_BASE, 0, 2, shape, dense_stride(shape), 1)
+    assert e.value.code == K.KVX_E_INVAL
+    L = layout_of(w)
+    L.num_heads = 0
+    with pytest.raises(kvx.KvxError):
+        K.kvx_register_pool(L, FAKE_BASE, 0, 2, shape, dense_stride(shape), 1)
+    with pytest.raises(kvx.KvxError):
+        K.kvx_register_pool(layout_of(w), 0, 0, 2, shape, dense_stride(shape), 1)
+
+
+def test_plan_runs_sorted_and_coalesced():
+    w = WORKLOADS["tiny"]   # layer-major: consecutive pages are adjacent
+    p = register(w)
+    ids = [9, 10, 11, 3, 40, 41, 5, 4]
+    runs = K.kvx_plan_runs(p, ids)
+    # (first page, first slot, pages): sorted by page, merged only where page
+    # and slot both continue
+    assert runs.tolist() == [[3, 3, 1], [4, 7, 1], [5, 6, 1], [9, 0, 3], [40, 4, 2]]
+    cover = sorted((int(r[1]) + k, int(r[0]) + k) for r in runs for k in range(r[2]))
+    assert cover == sorted(enumerate(ids))
+    K.kvx_unregister_pool(p)
+    q = register(WORKLOADS["trtllm_hnd"])   # page-major: pages are not adjacent
+    runs = K.kvx_plan_runs(q, [7, 8, 9])
+    assert runs.tolist() == [[7, 0, 1], [8, 1, 1], [9, 2, 1]]
+    K.kvx_unregister_pool(q)
+
+
+def test_validation_fails_closed_before_any_gpu_call():
+    w = WORKLOADS["tiny"]
+    p = register(w)
+    host = np.zeros(w.host_bytes(8) + 64, dtype=np.uint8)
+    hp = (host.ctypes.data + 15) // 16 * 16
+    nb = w.host_bytes(8)
+
+    def code(fn):
+        with pytest.raises(kvx.KvxError) as e:
+            fn()
+        return e.value.code
+
+    assert code(lambda: K.kvx_backup(p, [0, 64], hp, nb, 0, 2)) == K.KVX_E_RANGE
+    assert code(lambda: K.kvx_backup(p, [-1], hp, nb, 0, 2)) == K.KVX_E_RANGE
+    assert code(lambda: K.kvx_backup(p, [1, 2], hp, nb, 0, 3)) == K.KVX_E_RANGE
+    assert code(lambda: K.kvx_backup(p, [1, 2], hp, nb, 1, 0)) == K.KVX_E_RANGE
+    assert code(lambda: K.kvx_backup(p, list(range(8)), hp, nb - 16, 0, 2)) == K.KVX_E_RANGE
+    assert code(lambda: K.kvx_backup(p, list(range(8)), hp + 8, nb, 0, 2)) == K.KVX_E_ALIGN
+    assert code(lambda: K.kvx_backup(p, [1], hp, nb, 0, 2, path=9)) == K.KVX_E_INVAL
+    assert code(lambda: K.kvx_backup(p, [1], 0, nb, 0, 2)) == K.KVX_E_INVAL
+    assert code(lambda: K.kvx_restore(p, hp, nb, [3, 5, 3], 0, 2)) == K.KVX_E_DUP
+    assert code(lambda: K.kvx_restore(p, hp, nb, [3, 64], 0, 2)) == K.KVX_E_RANGE
+    # duplicates are fine for a backup; it fails later only because it reaches HIP
+    # empty work is a no-op that succeeds without touching the GPU
+    K.kvx_backup(p, [], hp, nb, 0, 2)
+    K.kvx_restore(p, hp, nb, [1, 2], 1, 1)
+    K.kvx_unregister_pool(p)
+
+
+def test_handle_lifecycle_and_teardown_never_raises():
+    w = WORKLOADS["tiny"]
+    p = register(w)
+    K.kvx_unregister_pool(p)
+    K.kvx_unregister_pool(p)          # second teardown: logged, not an error
+    K.kvx_unregister_pool(0)          # NULL: nothing to do
+    for fn in (lambda: K.kvx_pool_get_info(p), lambda: K.kvx_packed_bytes(p, 1),
+               lambda: K.kvx_backup(p, [1], 16, 1 << 20, 0, 1),
+               lambda: K.kvx_restore(p, 16, 1 << 20, [1], 0, 1),
+               lambda: K.kvx_plan_runs(p, [1])):
+        with pytest.raises(kvx.KvxError) as e:
+            fn()
+        assert e.value.code == K.KVX_E_STALE
+    with pytest.raises(kvx.KvxError) as e:
+        K.kvx_pool_get_info(0x1234560)
+    assert e.value.code == K.KVX_E_INVAL
+
+
+def test_options_roundtrip():
+    old = K.kvx_get_option(K.KVX_OPT_STAGE_SLOTS)
+    K.kvx_set_option(K.KVX_OPT_STAGE_SLOTS, 4)
+    assert K.kvx_get_option(K.KVX_OPT_STAGE_SLOTS) == 4
+    K.kvx_set_option(K.KVX_OPT_STAGE_SLOTS, old)
+    with pytest.raises(kvx.KvxError):
+        K.kvx_set_option(K.KVX_OPT_STAGE_SLOTS, 1)
+    with pytest.raises(kvx.KvxError):
+        K.kvx_set_option(99, 1)
+    assert "unknown option" in K.kvx_last_error()
