@@ -353,7 +353,11 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
             const int32_t nl = std::min(step, lb - l);
             a.layer_begin = l;
             a.total_units = static_cast<uint32_t>(per_layer * nl);
-            const int64_t gmax = t.grid_max > 0 ? t.grid_max : int64_t(cu_count) * 8;
+            int64_t gmax = t.grid_max > 0 ? t.grid_max : int64_t(cu_count) * 8;
+            // a publishing workgroup fences once per layer it leaves: give each
+            // a few units of every layer so the fences stay rare
+            if (pub && t.grid_max <= 0)
+                gmax = std::min(gmax, std::max<int64_t>(cu_count, per_layer / 4));
             cfg.grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(a.total_units, gmax)));
             hipError_t e = launch_move(dir, cfg, a, s);
             if (e != hipSuccess) return hip_fail(e, "kernel launch");

@@ -20,12 +20,12 @@
 // the permuted row.
 //
 // Publish ([TICKET] "PP Prefetch Ticket Path": layer-wise H2D and a
-// published safe prefix): after a workgroup's stores of a unit of layer l it
-// fences at agent scope and counts the unit into layer_done[l]; the last
-// unit of the layer stores n into the ready slot with a system-scope
-// release, so no reader can see the count before every byte of the layer.
-// The last unit also resets the counter, leaving it zero for the next call
-// on the same stream.
+// published safe prefix): a workgroup counts the units it finished of layer
+// l into layer_done[l] when it moves on to the next layer (one release fence
+// per workgroup and layer, not per unit); the add that completes the layer
+// stores n into the ready slot with a system-scope release, so no reader can
+// see the count before every byte of the layer. That add also resets the
+// counter, leaving it zero for the next call on the same stream.
 #include "kvx_internal.h"
 
 namespace kvx {
@@ -82,11 +82,65 @@ __device__ __forceinline__ uint32_t source_offset(const MoveArgs& a, uint32_t of
     }
 }
 
+// Moves one unit: the bytes [base, base + U * 4 KiB) of one piece, lane tid
+// handling 16 bytes of every 4 KiB round. A unit that lies wholly inside the
+// piece (the wave-uniform common case) runs without per-access predicates so
+// that all U loads are in flight before the first store and the stores issue
+// back to back; the last unit of a piece whose size is not a multiple of the
+// unit is predicated.
+template <Dir D, int U, bool PERMUTE, bool NT>
+__device__ __forceinline__ void move_unit(const MoveArgs& a, const uint8_t* src, uint8_t* dst,
+                                          uint32_t unit_base, uint32_t tid)
+{
+    const uint32_t base = unit_base + tid * kVecBytes;
+    if (unit_base + a.chunk_bytes <= a.piece_bytes) {
+        v4u v[U];
+#pragma unroll
+        for (int u = 0; u < U; u++)
+            v[u] = load16<NT>(src + source_offset<D, PERMUTE>(a, base + u * (kThreads * kVecBytes)));
+#pragma unroll
+        for (int u = 0; u < U; u++) store16<NT>(dst + base + u * (kThreads * kVecBytes), v[u]);
+    } else {
+        // ragged tail of a piece: one predicated vector at a time (rare; kept
+        // small so it does not raise the kernel's register count)
+#pragma unroll 1
+        for (int u = 0; u < U; u++) {
+            const uint32_t off = base + u * (kThreads * kVecBytes);
+            if (off < a.piece_bytes)
+                store16<NT>(dst + off, load16<NT>(src + source_offset<D, PERMUTE>(a, off)));
+        }
+    }
+}
+
+// Counts `units` finished units of layer l. Every lane first makes its own
+// stores visible at agent scope (release fence), the barrier gathers the
+// workgroup, and one lane adds to the layer's counter; the add that completes
+// the layer acquires the other workgroups' releases, clears the counter for
+// the next call and publishes the page count with a system-scope release.
+__device__ __forceinline__ void count_units(const MoveArgs& a, int32_t l, uint32_t units,
+                                            uint32_t tid)
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t done = __hip_atomic_fetch_add(&a.layer_done[l], units, __ATOMIC_RELEASE,
+                                                     __HIP_MEMORY_SCOPE_AGENT) + units;
+        if (done == a.layer_target) {
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            __hip_atomic_store(&a.layer_done[l], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&a.ready[l], a.publish_value, __ATOMIC_RELEASE,
+                               __HIP_MEMORY_SCOPE_SYSTEM);
+        }
+    }
+}
+
 template <Dir D, int U, bool PERMUTE, bool PUBLISH, bool NT>
 __global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
 {
     const uint32_t tid = threadIdx.x;
     const uint32_t cpp = a.chunks_per_piece;
+    int32_t pend_layer = -1;   // PUBLISH: layer of the units finished but not yet counted
+    uint32_t pend = 0;
     for (uint32_t q = blockIdx.x; q < a.total_units; q += gridDim.x) {
         // unit q -> (layer, kv, pair, chunk); all wave-uniform scalar math
         const uint32_t pu = q / cpp;
@@ -99,6 +153,15 @@ __global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
         const int32_t page = a.pairs[2 * j];
         const int32_t slot = a.pairs[2 * j + 1];
 
+        if constexpr (PUBLISH) {
+            // units arrive layer by layer: count a layer once this workgroup leaves it
+            if (l != pend_layer) {
+                if (pend) count_units(a, pend_layer, pend, tid);
+                pend_layer = l;
+                pend = 0;
+            }
+        }
+
         uint8_t* pool_piece = a.pool + static_cast<int64_t>(page) * a.page_stride +
                               static_cast<int64_t>(l) * a.layer_stride +
                               static_cast<int64_t>(c) * a.kv_stride;
@@ -108,34 +171,11 @@ __global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
             static_cast<int64_t>(slot - a.pk_slot0) * a.piece_bytes;
         const uint8_t* src = (D == GATHER) ? pool_piece : pk_piece;
         uint8_t* dst = (D == GATHER) ? pk_piece : pool_piece;
-
-        const uint32_t base = k * a.chunk_bytes + tid * kVecBytes;
-        v4u v[U];
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            const uint32_t off = base + u * (kThreads * kVecBytes);
-            if (off < a.piece_bytes) v[u] = load16<NT>(src + source_offset<D, PERMUTE>(a, off));
-        }
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            const uint32_t off = base + u * (kThreads * kVecBytes);
-            if (off < a.piece_bytes) store16<NT>(dst + off, v[u]);
-        }
-
-        if constexpr (PUBLISH) {
-            __threadfence();   // this lane's stores are performed at agent scope
-            __syncthreads();   // ... for every lane of the workgroup
-            if (tid == 0) {
-                const uint32_t done = __hip_atomic_fetch_add(&a.layer_done[l], 1u, __ATOMIC_ACQ_REL,
-                                                             __HIP_MEMORY_SCOPE_AGENT) + 1u;
-                if (done == a.layer_target) {
-                    __hip_atomic_store(&a.layer_done[l], 0u, __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                    __hip_atomic_store(&a.ready[l], a.publish_value, __ATOMIC_RELEASE,
-                                       __HIP_MEMORY_SCOPE_SYSTEM);
-                }
-            }
-        }
+        move_unit<D, U, PERMUTE, NT>(a, src, dst, k * a.chunk_bytes, tid);
+        if constexpr (PUBLISH) pend++;
+    }
+    if constexpr (PUBLISH) {
+        if (pend) count_units(a, pend_layer, pend, tid);
     }
 }
 

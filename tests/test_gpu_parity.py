@@ -344,3 +344,33 @@ def test_unregister_with_work_in_flight(stream):
     assert np.array_equal(pk.numpy(), want)
     pool.handle = 0
     pk.close()
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("case", ["ragged_hnd2", "trtllm_small"])
+def test_every_page_and_single_page(case, path, stream):
+    """Edge sizes: a request naming every page of the pool (in a random
+    order), and a one-page request, through backup and restore."""
+    w, _ = SMALL[case]
+    L = oracle_layout(w)
+    pool = DevicePool(w, seed=401)
+    img = pool.host_image()
+    for ids in (synth.page_perm(77, w.num_pages), np.array([w.num_pages - 1], dtype=np.int32)):
+        n = len(ids)
+        nb = w.host_bytes(n)
+        pk = Packed(w, n, path, fill_seed=6)
+        K.kvx_backup(pool.handle, ids, pk.ptr, nb, 0, w.num_layers, stream, PATHS[path])
+        K.kvx_sync(stream)
+        want = oracle.backup(L, img, ids, 0, w.num_layers)
+        got = pk.numpy()
+        assert np.array_equal(got, want), f"n={n} " + diff_report(got, want)
+        # restore the same bytes to the reversed page list
+        rev = ids[::-1].copy()
+        K.kvx_restore(pool.handle, pk.ptr, nb, rev, 0, w.num_layers, None, 0, stream, PATHS[path])
+        K.kvx_sync(stream)
+        after = pool.host_image()
+        want_alloc = oracle.restore(L, img, want, rev, 0, w.num_layers)
+        assert np.array_equal(after, want_alloc), f"n={n} " + diff_report(after, want_alloc)
+        img = after
+        pk.close()
+    pool.close()
