@@ -1,21 +1,26 @@
 """Benchmark: KV bytes moved per second by kvx backup (GPU pool -> pinned host)
-and restore (pinned host -> other GPU pages, per-layer publish) on one MI355X.
+and restore (pinned host -> other GPU pages, with per-layer publish) on one
+MI355X.
 
 One step = the whole hot path over one request of the Llama-3-8B-shaped bf16
 pool (32 layers, K+V, 8 KV heads, head_dim 128, page size 64, 2048 pages):
-  backup of 256 fragmented pages (16,384 tokens, 2 GiB) to pinned host,
-  restore of that buffer into 256 other pages with per-layer publish,
-  and the ready-prefix query.
-value = 2 x 2 GiB / step time (GB = 1e9 B). Inputs are resident in HBM when
-the timed region starts; the host transfer is part of the method (the host
-tier is where BACKUP writes and RESTORE reads).
+  BACKUP of 256 fragmented pages (16,384 tokens, 2 GiB) to pinned host
+  (validation + run planning, device pack into the staging ring, DMA),
+  RESTORE of that buffer into 256 other pages (DMA into the ring, device
+  unpack, per-layer publish), and the ready-prefix query, which the host
+  polls until the whole request is published.
+value = 2 x 2 GiB x steps / wall time of the steps (GB = 1e9 B). The pool is
+resident in HBM when the timed region starts; crossing the host link is
+part of the method (the host tier is where BACKUP writes and RESTORE reads).
 
-Also reported: the device pack kernel alone (HBM roofline), the pinned
-hipMemcpyAsync peaks (host-link roofline), the zero-copy path, and the CPU
-oracle on a bounded sample (a baseline only).
+Also reported: the device pack/unpack kernels alone against the HBM peak
+(the roofline), the pinned hipMemcpyAsync peaks (host-link roofline), both
+host paths per direction, a layer-pipelined schedule that overlaps the two
+directions, the layer-0-ready latency, and the CPU oracle on a bounded
+sample (a baseline only).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--path staged|zerocopy]
-       [--no-cpu-baseline] [--kernel-only]
+       [--no-cpu-baseline] [--kernel-only] [--no-extras]
 """
 import argparse
 import json
@@ -29,6 +34,13 @@ sys.path.insert(0, ROOT)
 
 GB = 1e9
 HBM_PEAK_GBS = 8000.0     # MI355X published HBM3E bandwidth
+
+# HBM bytes per launch of the roofline kernel from the two rocprofv3 --pmc runs
+# (FETCH_SIZE, WRITE_SIZE, scaled by a plain 2 GiB device copy in the same
+# run; see profiles/pack_kernel_llama8b.txt). Valid only for the kernel source
+# they were taken on: reported as null once kernels.hip changes.
+MEASURED_TRAFFIC = {"kernels_hip_sha256": "5f7078eb77e6cab51e0e0cadffc4a49e2ffb79853b774b535b39d20786557cc3",
+                    "bytes_per_launch": 4295361403}
 
 
 def log(msg):
@@ -47,12 +59,14 @@ def main():
     ap.add_argument("--path", choices=["staged", "zerocopy"], default="staged")
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the per-path, pipelined and latency measurements")
     ap.add_argument("--kernel-only", action="store_true",
-                    help="time only the device pack/unpack kernels (for profiling runs)")
+                    help="time only the device pack/unpack kernels (for counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "kvx moves KV between one GPU and its host; this build "
-                                   "measures one GPU only (--gpus 1)"}))
+        print(json.dumps({"error": "kvx moves KV between one GPU and its host tier; this benchmark "
+                                   "measures one GPU (run with --gpus 1)"}), flush=True)
         sys.exit(2)
 
     import numpy as np
@@ -82,8 +96,6 @@ def main():
     layout = K.make_layout(w.outer, w.inner, w.num_pages, w.num_layers, w.num_kv, w.page_size,
                            w.num_heads, w.head_dim)
     pool = K.register_tensor(pool_t, layout, 1)
-    host = K.HostBuffer(P)
-    ready = K.kvx_ready_create(w.num_layers, 1)
     dev_packed = torch.empty(P, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
 
@@ -103,6 +115,7 @@ def main():
         return out
 
     # ---- device pack / unpack kernels alone (HBM roofline) ----
+    # one launch packs the whole request: 32 layers x 2 x 256 pieces of 128 KiB
     def pack():
         K.kvx_backup(pool, src, dev_packed, P, 0, w.num_layers, stream, K.KVX_PATH_DEVICE)
 
@@ -110,95 +123,97 @@ def main():
         K.kvx_restore(pool, dev_packed, P, dst, 0, w.num_layers, None, 0, stream,
                       K.KVX_PATH_DEVICE)
 
-    kreps = max(args.steps, 5)
-    timed(pack, 2)
+    kreps = max(args.steps, 10)
+    timed(pack, 3)
     t_pack = timed(pack, kreps)
-    timed(unpack, 2)
+    timed(unpack, 3)
     t_unpack = timed(unpack, kreps)
     pack_gbs = 2 * P / median(t_pack) / GB
     unpack_gbs = 2 * P / median(t_unpack) / GB
     log(f"device pack {median(t_pack) * 1e3:.3f} ms = {pack_gbs:.0f} GB/s (read+write); "
         f"unpack {median(t_unpack) * 1e3:.3f} ms = {unpack_gbs:.0f} GB/s")
 
-    # D2D copy of the same byte count (the in-run achievable line)
+    # a plain device-to-device copy of the same byte count (the in-run
+    # achievable line, and the calibration kernel for the traffic counters)
     d2d_a = torch.empty(P, dtype=torch.uint8, device="cuda")
     with torch.cuda.stream(stream):
+        timed(lambda: d2d_a.copy_(dev_packed), 2)
         t_d2d = timed(lambda: d2d_a.copy_(dev_packed), 5)
     d2d_gbs = 2 * P / median(t_d2d) / GB
     del d2d_a
     log(f"D2D copy {d2d_gbs:.0f} GB/s (read+write)")
-
+    traffic = None
+    try:
+        import hashlib
+        with open(os.path.join(ROOT, "paged_kv_offload_amd", "csrc", "kernels.hip"), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() == MEASURED_TRAFFIC["kernels_hip_sha256"]:
+                traffic = MEASURED_TRAFFIC["bytes_per_launch"]
+    except OSError:
+        pass
+    roofline = {"bound": "hbm",
+                "kernel": "kvx_move_kernel<GATHER> (pack of one 2 GiB request, device path)",
+                "achieved": round(pack_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(pack_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                "algorithmic_bytes_per_launch": 2 * P,
+                "avg_launch_ms": round(median(t_pack) * 1e3, 4)}
     if args.kernel_only:
-        print(json.dumps({"pack_gbs": pack_gbs, "unpack_gbs": unpack_gbs, "d2d_gbs": d2d_gbs}))
+        print(json.dumps({"roofline": roofline, "unpack_gbs": round(unpack_gbs, 1),
+                          "d2d_copy_gbs": round(d2d_gbs, 1)}), flush=True)
         return
 
     # ---- pinned host-link peaks: 1 GiB hipMemcpyAsync, median of 10 ----
     peak_bytes = 1 << 30
     pin = torch.empty(peak_bytes, dtype=torch.uint8, pin_memory=True)
+    pin2 = torch.empty(peak_bytes, dtype=torch.uint8, pin_memory=True)
     dev1 = torch.empty(peak_bytes, dtype=torch.uint8, device="cuda")
+    dev2 = torch.empty(peak_bytes, dtype=torch.uint8, device="cuda")
+    sb = torch.cuda.Stream()
     with torch.cuda.stream(stream):
+        timed(lambda: pin.copy_(dev1, non_blocking=True), 2)
         t_d2h = timed(lambda: pin.copy_(dev1, non_blocking=True), 10)
         t_h2d = timed(lambda: dev1.copy_(pin, non_blocking=True), 10)
+    bidir = []
+    for _ in range(5):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(stream):
+            pin.copy_(dev1, non_blocking=True)
+        with torch.cuda.stream(sb):
+            dev2.copy_(pin2, non_blocking=True)
+        torch.cuda.synchronize()
+        bidir.append(time.perf_counter() - t0)
     d2h_peak = peak_bytes / median(t_d2h) / GB
     h2d_peak = peak_bytes / median(t_h2d) / GB
-    del pin, dev1
-    log(f"pinned memcpy peak: D2H {d2h_peak:.1f} GB/s, H2D {h2d_peak:.1f} GB/s")
+    bidir_peak = 2 * peak_bytes / median(bidir) / GB
+    del pin, pin2, dev1, dev2
+    log(f"pinned memcpy peak: D2H {d2h_peak:.1f} GB/s, H2D {h2d_peak:.1f} GB/s, "
+        f"both directions at once {bidir_peak:.1f} GB/s")
 
     # ---- the step ----
+    host = K.HostBuffer(P)
+    ready = K.kvx_ready_create(w.num_layers, 1)
     path = {"staged": K.KVX_PATH_STAGED, "zerocopy": K.KVX_PATH_ZEROCOPY}[args.path]
 
     def step(path=path):
         K.kvx_ready_reset(ready)
         K.kvx_backup(pool, src, host.ptr, P, 0, w.num_layers, stream, path)
         K.kvx_restore(pool, host.ptr, P, dst, 0, w.num_layers, ready, 0, stream, path)
-
-    def backup_only(path=path):
-        K.kvx_backup(pool, src, host.ptr, P, 0, w.num_layers, stream, path)
-
-    def restore_only(path=path):
-        K.kvx_restore(pool, host.ptr, P, dst, 0, w.num_layers, None, 0, stream, path)
+        while K.kvx_ready_prefix(ready) < n:    # the consumer's view of completion
+            pass
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    a, b = ev(), ev()
     t0 = time.perf_counter()
-    a.record(stream)
     for _ in range(args.steps):
         step()
-    b.record(stream)
-    b.synchronize()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t_total = a.elapsed_time(b) / 1e3
-    prefix = K.kvx_ready_prefix(ready)
-    assert prefix == n, f"ready prefix {prefix} != {n} after the timed steps"
-    ms_per_step = t_total / args.steps * 1e3
-    value = 2 * P * args.steps / t_total / GB
-    log(f"step ({args.path}): {ms_per_step:.2f} ms -> {value:.2f} GB/s (wall {wall:.2f} s)")
-
-    # per-direction end-to-end rates on both paths
-    e2e = {}
-    for name, pth in (("staged", K.KVX_PATH_STAGED), ("zerocopy", K.KVX_PATH_ZEROCOPY)):
-        tb = timed(lambda: backup_only(pth), 3)
-        tr = timed(lambda: restore_only(pth), 3)
-        e2e[name] = {"backup_d2h_gbs": P / median(tb) / GB, "restore_h2d_gbs": P / median(tr) / GB}
-        log(f"{name}: backup {e2e[name]['backup_d2h_gbs']:.1f} GB/s, "
-            f"restore {e2e[name]['restore_h2d_gbs']:.1f} GB/s")
-
-    # layer-0-ready latency of a restore: CPU polls the first layer's count
-    K.kvx_ready_reset(ready)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    K.kvx_restore(pool, host.ptr, P, dst, 0, w.num_layers, ready, 0, stream, path)
-    while K.kvx_layer_ready(ready, 0) < n:
-        pass
-    t_l0 = time.perf_counter() - t0
-    while K.kvx_ready_prefix(ready) < n:
-        pass
-    t_all = time.perf_counter() - t0
-    stream.synchronize()
-    log(f"restore: layer 0 ready after {t_l0 * 1e3:.2f} ms, all layers after {t_all * 1e3:.2f} ms")
+    ms_per_step = wall / args.steps * 1e3
+    value = 2 * P * args.steps / wall / GB
+    serial_peak = 2 / (1 / d2h_peak + 1 / h2d_peak)
+    log(f"step ({args.path}): {ms_per_step:.2f} ms -> {value:.2f} GB/s "
+        f"({100 * value / serial_peak:.1f}% of the serial memcpy peak {serial_peak:.1f} GB/s)")
 
     result = {
         "metric": "KV GB/s moved (backup D2H, restore H2D) + % of HBM / host-link roofline",
@@ -214,24 +229,82 @@ def main():
         "dtype": "u8",
         "data": "synthetic",
         "config": {"workload": w.description, "pages_per_request": n, "layers": w.num_layers,
-                   "payload_bytes_per_op": P, "path": args.path},
-        "roofline": {"bound": "hbm", "kernel": "kvx_move_kernel (pack, device path)",
-                     "achieved": round(pack_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(pack_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                   "payload_bytes_per_op": P, "path": args.path,
+                   "schedule": "backup then restore, host waits for the ready prefix"},
+        "roofline": roofline,
         "unpack_roofline": {"achieved": round(unpack_gbs, 1), "peak": HBM_PEAK_GBS,
-                            "frac": round(unpack_gbs / HBM_PEAK_GBS, 4)},
+                            "unit": "GB/s", "frac": round(unpack_gbs / HBM_PEAK_GBS, 4)},
         "d2d_copy_gbs": round(d2d_gbs, 1),
-        "link": {"d2h_peak_gbs": round(d2h_peak, 2), "h2d_peak_gbs": round(h2d_peak, 2),
-                 "e2e": {k: {kk: round(vv, 2) for kk, vv in v.items()} for k, v in e2e.items()},
-                 # the step moves P one way then P the other way: its link bound is the
-                 # serial combination of the two measured peaks
-                 "step_frac_of_serial_peak": round(value / (2 / (1 / d2h_peak + 1 / h2d_peak)), 4)},
-        "restore_layer0_ready_ms": round(t_l0 * 1e3, 3),
-        "restore_all_ready_ms": round(t_all * 1e3, 3),
+        "link": {"bound": "host link", "unit": "GB/s",
+                 "d2h_peak": round(d2h_peak, 2), "h2d_peak": round(h2d_peak, 2),
+                 "bidirectional_peak": round(bidir_peak, 2),
+                 "step_frac_of_serial_peak": round(value / serial_peak, 4)},
     }
+
+    if not args.no_extras:
+        extras = {}
+        for name, pth in (("staged", K.KVX_PATH_STAGED), ("zerocopy", K.KVX_PATH_ZEROCOPY)):
+            b = lambda: K.kvx_backup(pool, src, host.ptr, P, 0, w.num_layers, stream, pth)  # noqa
+            r = lambda: K.kvx_restore(pool, host.ptr, P, dst, 0, w.num_layers, ready, 0,  # noqa
+                                      stream, pth)
+            timed(b, 1)
+            tb = timed(b, 3)
+            timed(r, 1)
+            tr = timed(r, 3)
+            extras[name] = {"backup_gbs": round(P / median(tb) / GB, 2),
+                            "backup_frac_d2h_peak": round(P / median(tb) / GB / d2h_peak, 4),
+                            "restore_gbs": round(P / median(tr) / GB, 2),
+                            "restore_frac_h2d_peak": round(P / median(tr) / GB / h2d_peak, 4)}
+            log(f"{name}: backup {extras[name]['backup_gbs']} GB/s, "
+                f"restore {extras[name]['restore_gbs']} GB/s")
+        result["link"]["per_path"] = extras
+
+        # layer-pipelined: restore of layer group g runs on a second stream
+        # while group g+1 is backed up, so both link directions carry data
+        def pipelined(pth, group=2):
+            K.kvx_ready_reset(ready)
+            for l0 in range(0, w.num_layers, group):
+                l1 = min(w.num_layers, l0 + group)
+                K.kvx_backup(pool, src, host.ptr, P, l0, l1, stream, pth)
+                e = torch.cuda.Event()
+                e.record(stream)
+                sb.wait_event(e)
+                K.kvx_restore(pool, host.ptr, P, dst, l0, l1, ready, 0, sb, pth)
+            while K.kvx_ready_prefix(ready) < n:
+                pass
+        pipe = {}
+        for name, pth in (("staged", K.KVX_PATH_STAGED), ("zerocopy", K.KVX_PATH_ZEROCOPY)):
+            pipelined(pth)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(3):
+                pipelined(pth)
+            torch.cuda.synchronize()
+            pipe[name] = round(2 * P * 3 / (time.perf_counter() - t0) / GB, 2)
+        result["layer_pipelined_gbs"] = pipe
+        log(f"layer-pipelined step: {pipe}")
+
+        # layer-0-ready latency of a restore: the CPU polls layer 0's count
+        lat = {}
+        for name, pth in (("staged", K.KVX_PATH_STAGED), ("zerocopy", K.KVX_PATH_ZEROCOPY)):
+            K.kvx_ready_reset(ready)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            K.kvx_restore(pool, host.ptr, P, dst, 0, w.num_layers, ready, 0, stream, pth)
+            while K.kvx_layer_ready(ready, 0) < n:
+                pass
+            t_l0 = time.perf_counter() - t0
+            while K.kvx_ready_prefix(ready) < n:
+                pass
+            t_all = time.perf_counter() - t0
+            stream.synchronize()
+            lat[name] = {"layer0_ms": round(t_l0 * 1e3, 3), "all_layers_ms": round(t_all * 1e3, 3)}
+        result["restore_ready_latency"] = lat
+        log(f"restore ready latency: {lat}")
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w)
+        log(f"cpu baseline: {result['cpu_baseline']}")
     print(json.dumps(result), flush=True)
 
     K.kvx_ready_destroy(ready)
@@ -241,8 +314,9 @@ def main():
 
 def cpu_baseline(w, budget_s: float = 12.0):
     """The oracle's backup + restore byte loops, single-threaded, on a host
-    pool with the workload's piece shape and request size but fewer pages
-    and layers; runs layer by layer until about budget_s seconds."""
+    pool with the workload's piece shape and request size (n fragmented
+    pages) but 2n pages and at most 4 layers; one layer per pass, passes
+    repeated until about budget_s seconds of CPU work."""
     import numpy as np
 
     import oracle
@@ -257,23 +331,23 @@ def cpu_baseline(w, budget_s: float = 12.0):
                       num_pages=sample.num_pages, num_layers=nl, num_kv=sample.num_kv,
                       page_size=sample.page_size, num_heads=sample.num_heads,
                       head_dim=sample.head_dim, dtype_bytes=sample.dtype_bytes)
-    # only the shape matters for the timing; the bytes are a cheap pattern
+    # only the shape matters for the timing; the bytes are a constant pattern
     alloc = np.full(sample.pool_bytes, 0x5A, dtype=np.uint8)
-    src = synth.page_perm(w.seed, 2 * n)[:n].copy()
-    dst = synth.page_perm(w.seed, 2 * n)[n:].copy()
+    perm = synth.page_perm(w.seed, 2 * n)
+    src, dst = perm[:n].copy(), perm[n:].copy()
     host = np.zeros(sample.host_bytes(n), dtype=np.uint8)
-    moved, t, layers = 0, 0.0, 0
+    moved, t, passes = 0, 0.0, 0
     while t < budget_s:
-        l = layers % nl
+        l = passes % nl
         t0 = time.perf_counter()
         oracle.backup(L, alloc, src, l, l + 1, host=host)
         oracle.restore(L, alloc, host, dst, l, l + 1, out=alloc)
         t += time.perf_counter() - t0
         moved += 2 * sample.num_kv * n * sample.piece_bytes
-        layers += 1
+        passes += 1
     gbs = moved / t / GB
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{layers} single-layer backup+restore passes of {n} fragmented pages x "
+            "sample": f"{passes} single-layer backup+restore passes of {n} fragmented pages x "
                       f"{sample.num_kv} x {sample.piece_bytes} B pieces on a {2 * n}-page, "
                       f"{nl}-layer host pool ({moved / GB:.2f} GB moved in {t:.1f} s)"}
 

@@ -293,6 +293,7 @@ struct Target {
     uint8_t* packed;       // device view of the packed region
     int32_t pk_layer0, pk_slot0;
     int64_t pk_slots;      // slots stored per (layer, kv) in `packed`
+    bool host;             // `packed` is pinned host memory read or written over the link
 };
 
 struct Publish {
@@ -354,9 +355,14 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
             a.layer_begin = l;
             a.total_units = static_cast<uint32_t>(per_layer * nl);
             int64_t gmax = t.grid_max > 0 ? t.grid_max : int64_t(cu_count) * 8;
+            // a kernel that streams over the host link needs only a few
+            // workgroups to keep it busy (32 x 32 KiB in flight covers the
+            // link's round trip); more only take compute units from
+            // concurrent work
+            if (tg.host) gmax = t.host_grid_max > 0 ? t.host_grid_max : kHostGridAuto;
             // a publishing workgroup fences once per layer it leaves: give each
             // a few units of every layer so the fences stay rare
-            if (pub && t.grid_max <= 0)
+            if (pub && t.grid_max <= 0 && !tg.host)
                 gmax = std::min(gmax, std::max<int64_t>(cu_count, per_layer / 4));
             cfg.grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(a.total_units, gmax)));
             hipError_t e = launch_move(dir, cfg, a, s);
@@ -474,7 +480,7 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
         pubp = &pub;
     }
     if (path != KVX_PATH_STAGED) {
-        Target tg{view, 0, 0, n};
+        Target tg{view, 0, 0, n, path == KVX_PATH_ZEROCOPY};
         rc = launch_range(dir, pool, tg, l0, l1, pairs.data(), pairs.size(), pubp, t, L->cu_count, s);
     } else {
         // chunks of whole layers when one layer fits a ring slot, else slot
@@ -488,8 +494,15 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
         int32_t layers_per_chunk = 1, slots_per_chunk = n;
         if (layer_bytes <= slot_bytes) {
             layers_per_chunk = static_cast<int32_t>(slot_bytes / layer_bytes);
-            if (dir == SCATTER)
-                layers_per_chunk = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(layers_per_chunk, t.restore_chunk_layers)));
+            if (dir == SCATTER) {
+                // restore chunks are kept small so early layers publish early,
+                // but at least kRestoreChunkMin bytes so each DMA runs at speed
+                const int64_t want = t.restore_chunk_layers > 0
+                                         ? t.restore_chunk_layers
+                                         : (kRestoreChunkMin + layer_bytes - 1) / layer_bytes;
+                layers_per_chunk = static_cast<int32_t>(
+                    std::max<int64_t>(1, std::min<int64_t>(layers_per_chunk, want)));
+            }
         } else {
             slots_per_chunk = static_cast<int32_t>(slot_bytes / (g.num_kv * g.piece_bytes));
         }
@@ -515,7 +528,7 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
                 const int r = L->next_slot;
                 L->next_slot = (r + 1) % L->nslots;
                 uint8_t* slot_mem = L->ring + int64_t(r) * L->slot_bytes;
-                Target tg{slot_mem, la, s0, s1 - s0};
+                Target tg{slot_mem, la, s0, s1 - s0, false};
                 const int64_t strip = int64_t(s1 - s0) * g.piece_bytes;
                 // host byte offset of (layer l, kv c, slot s0) and of its ring copy
                 auto host_off = [&](int32_t l, int64_t c) { return ((int64_t(l) * g.num_kv + c) * n + s0) * g.piece_bytes; };
@@ -908,8 +921,12 @@ int kvx_set_option(int32_t option, int64_t value)
         g_tune.nontemporal = value;
         return KVX_OK;
     case KVX_OPT_RESTORE_CHUNK_LAYERS:
-        if (value < 1 || value > 4096) break;
+        if (value < 0 || value > 4096) break;
         g_tune.restore_chunk_layers = value;
+        return KVX_OK;
+    case KVX_OPT_HOST_GRID_MAX:
+        if (value < 0 || value > (1 << 24)) break;
+        g_tune.host_grid_max = value;
         return KVX_OK;
     default:
         return fail(KVX_E_INVAL, "set_option: unknown option " + std::to_string(option));
@@ -930,6 +947,7 @@ int kvx_get_option(int32_t option, int64_t* value)
     case KVX_OPT_SORT_PAGES: *value = g_tune.sort_pages; return KVX_OK;
     case KVX_OPT_NONTEMPORAL: *value = g_tune.nontemporal; return KVX_OK;
     case KVX_OPT_RESTORE_CHUNK_LAYERS: *value = g_tune.restore_chunk_layers; return KVX_OK;
+    case KVX_OPT_HOST_GRID_MAX: *value = g_tune.host_grid_max; return KVX_OK;
     default: return fail(KVX_E_INVAL, "get_option: unknown option " + std::to_string(option));
     }
 }

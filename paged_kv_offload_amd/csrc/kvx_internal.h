@@ -105,11 +105,12 @@ bool ready_known(const kvx_ready* r);
 // ---------------------------------------------------------------------------
 struct Tuning {
     int64_t grid_max = 0;                 // 0 = auto
-    int64_t stage_slot_bytes = 64ll << 20;
+    int64_t stage_slot_bytes = 128ll << 20;
     int64_t stage_slots = 3;
-    int64_t sort_pages = 1;
+    int64_t sort_pages = 0;
     int64_t nontemporal = 1;
-    int64_t restore_chunk_layers = 1;
+    int64_t restore_chunk_layers = 0;     // 0 = auto (chunks of >= kRestoreChunkMin bytes)
+    int64_t host_grid_max = 0;            // 0 = auto
 };
 Tuning tuning();
 
@@ -119,6 +120,8 @@ Tuning tuning();
 constexpr int kThreads = 256;        // 4 wave64 per workgroup
 constexpr int kVecBytes = 16;        // one dwordx4 per lane access
 constexpr int kMaxPairs = 448;       // (page, slot) pairs carried in the kernel arguments
+constexpr int kHostGridAuto = 32;    // default workgroups of a kernel streaming over the host link
+constexpr int64_t kRestoreChunkMin = 32ll << 20;   // default minimum staged restore chunk
 
 enum Dir : int32_t { GATHER = 0, SCATTER = 1 };
 
