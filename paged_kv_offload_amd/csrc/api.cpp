@@ -311,10 +311,13 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
     MoveArgs a;
     std::memset(&a, 0, sizeof a);
     LaunchCfg cfg;
-    cfg.unroll = pick_unroll(g.piece_bytes);
+    cfg.unroll = pick_unroll(g.piece_bytes, static_cast<int>(t.max_unroll));
     cfg.permute = (g.inner == KVX_HND) && g.num_heads > 1 && g.page_size > 1;
     cfg.publish = pub != nullptr;
-    cfg.nontemporal = t.nontemporal != 0;
+    // streaming hints (measured): non-temporal loads and stores for HBM to
+    // HBM; plain stores into pinned host memory
+    cfg.nontemporal = t.nontemporal >= 0 ? static_cast<int>(t.nontemporal)
+                                         : ((tg.host && dir == GATHER) ? 1 : 3);
     a.pool = pool->start;
     a.packed = tg.packed;
     a.page_stride = g.page_stride;
@@ -354,17 +357,35 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
             const int32_t nl = std::min(step, lb - l);
             a.layer_begin = l;
             a.total_units = static_cast<uint32_t>(per_layer * nl);
-            int64_t gmax = t.grid_max > 0 ? t.grid_max : int64_t(cu_count) * 8;
-            // a kernel that streams over the host link needs only a few
-            // workgroups to keep it busy (32 x 32 KiB in flight covers the
-            // link's round trip); more only take compute units from
-            // concurrent work
-            if (tg.host) gmax = t.host_grid_max > 0 ? t.host_grid_max : kHostGridAuto;
-            // a publishing workgroup fences once per layer it leaves: give each
-            // a few units of every layer so the fences stay rare
-            if (pub && t.grid_max <= 0 && !tg.host)
-                gmax = std::min(gmax, std::max<int64_t>(cu_count, per_layer / 4));
-            cfg.grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(a.total_units, gmax)));
+            // Grid policy, all measured on MI355X:
+            //  - a kernel streaming over the host link needs only a few
+            //    workgroups (32 x 32 KiB in flight covers the link's round
+            //    trip); more only take compute units from concurrent work;
+            //  - a publishing workgroup fences once per layer it leaves, so
+            //    each gets a few units of every layer;
+            //  - HBM-to-HBM with units of >= 32 KiB: one workgroup per unit,
+            //    numbered so each XCD takes consecutive units and chunk
+            //    offsets rotate between pieces (5-8% over a persistent grid);
+            //  - smaller units share persistent workgroups (32 per CU).
+            int64_t gmax;
+            uint32_t order = 0;
+            if (t.grid_max > 0) {
+                gmax = t.grid_max;
+            } else if (tg.host) {
+                gmax = t.host_grid_max > 0 ? t.host_grid_max : kHostGridAuto;
+            } else if (pub) {
+                gmax = std::min<int64_t>(int64_t(cu_count) * 8, std::max<int64_t>(cu_count, per_layer / 4));
+            } else if (a.chunk_bytes >= (32u << 10)) {
+                gmax = a.total_units;
+                order = 3;
+            } else {
+                gmax = int64_t(cu_count) * 32;
+            }
+            if (t.unit_order >= 0) order = static_cast<uint32_t>(t.unit_order);
+            a.unit_order = order;
+            int64_t grid = std::max<int64_t>(1, std::min<int64_t>(a.total_units, gmax));
+            if ((order & 1u) && grid > 8) grid &= ~int64_t(7);   // whole rounds of 8 XCDs
+            cfg.grid = static_cast<int>(grid);
             hipError_t e = launch_move(dir, cfg, a, s);
             if (e != hipSuccess) return hip_fail(e, "kernel launch");
         }
@@ -472,7 +493,7 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
     if (ready) {
         rc = lane_counters(L, g.num_layers);
         if (rc != KVX_OK) return rc;
-        const int64_t chunk = int64_t(kThreads) * kVecBytes * pick_unroll(g.piece_bytes);
+        const int64_t chunk = int64_t(kThreads) * kVecBytes * pick_unroll(g.piece_bytes, static_cast<int>(t.max_unroll));
         pub.layer_done = L->layer_done;
         pub.ready = ready->counts_dev + slot_base;
         pub.layer_target = static_cast<uint32_t>(g.num_kv * int64_t(n) * ((g.piece_bytes + chunk - 1) / chunk));
@@ -917,7 +938,7 @@ int kvx_set_option(int32_t option, int64_t value)
         g_tune.sort_pages = value;
         return KVX_OK;
     case KVX_OPT_NONTEMPORAL:
-        if (value != 0 && value != 1) break;
+        if (value < -1 || value > 3) break;
         g_tune.nontemporal = value;
         return KVX_OK;
     case KVX_OPT_RESTORE_CHUNK_LAYERS:
@@ -927,6 +948,14 @@ int kvx_set_option(int32_t option, int64_t value)
     case KVX_OPT_HOST_GRID_MAX:
         if (value < 0 || value > (1 << 24)) break;
         g_tune.host_grid_max = value;
+        return KVX_OK;
+    case KVX_OPT_UNIT_ORDER:
+        if (value < -1 || value > 3) break;
+        g_tune.unit_order = value;
+        return KVX_OK;
+    case KVX_OPT_MAX_UNROLL:
+        if (value < 1 || value > 16) break;
+        g_tune.max_unroll = value;
         return KVX_OK;
     default:
         return fail(KVX_E_INVAL, "set_option: unknown option " + std::to_string(option));
@@ -948,6 +977,8 @@ int kvx_get_option(int32_t option, int64_t* value)
     case KVX_OPT_NONTEMPORAL: *value = g_tune.nontemporal; return KVX_OK;
     case KVX_OPT_RESTORE_CHUNK_LAYERS: *value = g_tune.restore_chunk_layers; return KVX_OK;
     case KVX_OPT_HOST_GRID_MAX: *value = g_tune.host_grid_max; return KVX_OK;
+    case KVX_OPT_UNIT_ORDER: *value = g_tune.unit_order; return KVX_OK;
+    case KVX_OPT_MAX_UNROLL: *value = g_tune.max_unroll; return KVX_OK;
     default: return fail(KVX_E_INVAL, "get_option: unknown option " + std::to_string(option));
     }
 }

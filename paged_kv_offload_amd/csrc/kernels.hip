@@ -88,7 +88,8 @@ __device__ __forceinline__ uint32_t source_offset(const MoveArgs& a, uint32_t of
 // that all U loads are in flight before the first store and the stores issue
 // back to back; the last unit of a piece whose size is not a multiple of the
 // unit is predicated.
-template <Dir D, int U, bool PERMUTE, bool NT>
+// NT bit 0: non-temporal loads; bit 1: non-temporal stores
+template <Dir D, int U, bool PERMUTE, int NT>
 __device__ __forceinline__ void move_unit(const MoveArgs& a, const uint8_t* src, uint8_t* dst,
                                           uint32_t unit_base, uint32_t tid)
 {
@@ -97,9 +98,9 @@ __device__ __forceinline__ void move_unit(const MoveArgs& a, const uint8_t* src,
         v4u v[U];
 #pragma unroll
         for (int u = 0; u < U; u++)
-            v[u] = load16<NT>(src + source_offset<D, PERMUTE>(a, base + u * (kThreads * kVecBytes)));
+            v[u] = load16<(NT & 1) != 0>(src + source_offset<D, PERMUTE>(a, base + u * (kThreads * kVecBytes)));
 #pragma unroll
-        for (int u = 0; u < U; u++) store16<NT>(dst + base + u * (kThreads * kVecBytes), v[u]);
+        for (int u = 0; u < U; u++) store16<(NT & 2) != 0>(dst + base + u * (kThreads * kVecBytes), v[u]);
     } else {
         // ragged tail of a piece: one predicated vector at a time (rare; kept
         // small so it does not raise the kernel's register count)
@@ -107,7 +108,7 @@ __device__ __forceinline__ void move_unit(const MoveArgs& a, const uint8_t* src,
         for (int u = 0; u < U; u++) {
             const uint32_t off = base + u * (kThreads * kVecBytes);
             if (off < a.piece_bytes)
-                store16<NT>(dst + off, load16<NT>(src + source_offset<D, PERMUTE>(a, off)));
+                store16<(NT & 2) != 0>(dst + off, load16<(NT & 1) != 0>(src + source_offset<D, PERMUTE>(a, off)));
         }
     }
 }
@@ -134,19 +135,30 @@ __device__ __forceinline__ void count_units(const MoveArgs& a, int32_t l, uint32
     }
 }
 
-template <Dir D, int U, bool PERMUTE, bool PUBLISH, bool NT>
+template <Dir D, int U, bool PERMUTE, bool PUBLISH, int NT>
 __global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
 {
     const uint32_t tid = threadIdx.x;
     const uint32_t cpp = a.chunks_per_piece;
     int32_t pend_layer = -1;   // PUBLISH: layer of the units finished but not yet counted
     uint32_t pend = 0;
-    for (uint32_t q = blockIdx.x; q < a.total_units; q += gridDim.x) {
+    // Workgroups are dispatched round-robin over the 8 XCDs (block b runs on
+    // XCD b mod 8). With XCD ordering, the workgroups of one XCD take
+    // consecutive unit numbers in every round of the loop, so each XCD walks
+    // whole pieces instead of one fixed chunk offset of many pieces.
+    uint32_t v = blockIdx.x;
+    if ((a.unit_order & 1u) && (gridDim.x & 7u) == 0)
+        v = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+    for (uint32_t q = v; q < a.total_units; q += gridDim.x) {
         // unit q -> (layer, kv, pair, chunk); all wave-uniform scalar math
         const uint32_t pu = q / cpp;
-        const uint32_t k = q - pu * cpp;
+        uint32_t k = q - pu * cpp;
         const uint32_t lc = pu / a.npairs;
         const uint32_t j = pu - lc * a.npairs;
+        if (a.unit_order & 2u) {   // rotate the chunk order from piece to piece
+            k += j % cpp;
+            if (k >= cpp) k -= cpp;
+        }
         const uint32_t lrel = lc / a.num_kv;
         const uint32_t c = lc - lrel * a.num_kv;
         const int32_t l = a.layer_begin + static_cast<int32_t>(lrel);
@@ -207,18 +219,23 @@ uint32_t magic_u32(uint32_t d)
     return static_cast<uint32_t>((uint64_t(1) << 32) / d + 1);
 }
 
-int pick_unroll(int64_t piece_bytes)
+int pick_unroll(int64_t piece_bytes, int max_unroll)
 {
-    const int64_t step = kThreads * kVecBytes;   // 4 KiB per vector round of a workgroup
-    for (int u : {8, 4, 2})
-        if (piece_bytes % (step * u) == 0) return u;
+    // the largest unit (U vector rounds of 4 KiB) that tiles the piece exactly;
+    // pieces that are not a multiple of 4 KiB get the largest unit that fits
+    // and a predicated tail
+    const int64_t step = kThreads * kVecBytes;
+    for (int u : {16, 12, 8, 6, 4, 3, 2})
+        if (u <= max_unroll && piece_bytes % (step * u) == 0) return u;
     if (piece_bytes % step == 0) return 1;
-    return piece_bytes >= 8 * step ? 8 : (piece_bytes >= 4 * step ? 4 : 1);
+    for (int u : {16, 8, 4})
+        if (u <= max_unroll && piece_bytes >= u * step) return u;
+    return 1;
 }
 
 namespace {
 
-template <Dir D, int U, bool P, bool PUB, bool NT>
+template <Dir D, int U, bool P, bool PUB, int NT>
 hipError_t go(const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s)
 {
     void* args[] = {const_cast<MoveArgs*>(&a)};
@@ -229,7 +246,12 @@ hipError_t go(const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s)
 template <Dir D, int U, bool P, bool PUB>
 hipError_t go_nt(const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s)
 {
-    return cfg.nontemporal ? go<D, U, P, PUB, true>(cfg, a, s) : go<D, U, P, PUB, false>(cfg, a, s);
+    switch (cfg.nontemporal & 3) {
+    case 3: return go<D, U, P, PUB, 3>(cfg, a, s);
+    case 2: return go<D, U, P, PUB, 2>(cfg, a, s);
+    case 1: return go<D, U, P, PUB, 1>(cfg, a, s);
+    default: return go<D, U, P, PUB, 0>(cfg, a, s);
+    }
 }
 
 template <Dir D, int U, bool P>
@@ -251,8 +273,12 @@ template <Dir D>
 hipError_t go_unroll(const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s)
 {
     switch (cfg.unroll) {
+    case 16: return go_perm<D, 16>(cfg, a, s);
+    case 12: return go_perm<D, 12>(cfg, a, s);
     case 8: return go_perm<D, 8>(cfg, a, s);
+    case 6: return go_perm<D, 6>(cfg, a, s);
     case 4: return go_perm<D, 4>(cfg, a, s);
+    case 3: return go_perm<D, 3>(cfg, a, s);
     case 2: return go_perm<D, 2>(cfg, a, s);
     case 1: return go_perm<D, 1>(cfg, a, s);
     default: return hipErrorInvalidValue;

@@ -108,9 +108,11 @@ struct Tuning {
     int64_t stage_slot_bytes = 128ll << 20;
     int64_t stage_slots = 3;
     int64_t sort_pages = 0;
-    int64_t nontemporal = 1;
+    int64_t nontemporal = -1;             // bit 0 loads, bit 1 stores; -1 = auto
     int64_t restore_chunk_layers = 0;     // 0 = auto (chunks of >= kRestoreChunkMin bytes)
     int64_t host_grid_max = 0;            // 0 = auto
+    int64_t unit_order = -1;              // MoveArgs::unit_order bits, -1 = auto
+    int64_t max_unroll = 16;              // largest 16-byte vectors per lane per unit
 };
 Tuning tuning();
 
@@ -148,19 +150,20 @@ struct MoveArgs {
     uint32_t* ready;         // device view of counts + slot_base, indexed by layer
     uint32_t layer_target;   // work units of one layer over the whole call
     uint32_t publish_value;  // n
+    uint32_t unit_order;     // bit 0: XCD-contiguous unit numbering; bit 1: rotate chunks
     int32_t pairs[2 * kMaxPairs];
 };
 
 struct LaunchCfg {
-    int unroll;        // 16-byte vectors per lane per unit: 1, 2, 4 or 8
+    int unroll;        // 16-byte vectors per lane per unit: 1, 2, 4, 8 or 16
     bool permute;      // pool inner layout is HND
     bool publish;
-    bool nontemporal;
+    int nontemporal;   // bit 0: non-temporal loads, bit 1: non-temporal stores
     int grid;
 };
 
 uint32_t magic_u32(uint32_t d);   // multiplier for exact x / d with x * d < 2^32
-int pick_unroll(int64_t piece_bytes);
+int pick_unroll(int64_t piece_bytes, int max_unroll);
 hipError_t launch_move(Dir dir, const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s);
 hipError_t launch_ready_wait(const uint32_t* slot, uint32_t min_count, uint32_t spin_limit,
                              int32_t* status, hipStream_t s);

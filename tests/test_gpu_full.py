@@ -148,9 +148,12 @@ def test_full_size_mla_layerwise_ready():
             stop = threading.Event()
 
             def poll():
+                # the prefix is read first: every count is monotonic, so the
+                # counts read after it are each at least the prefix
                 while not stop.is_set():
+                    pfx = K.kvx_ready_prefix(ready)
                     c = [K.kvx_layer_ready(ready, s) for s in range(w.num_layers)]
-                    samples.append((time.perf_counter(), c, K.kvx_ready_prefix(ready)))
+                    samples.append((time.perf_counter(), c, pfx))
                     if min(c) == n:
                         break
 
