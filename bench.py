@@ -5,17 +5,19 @@ MI355X.
 One step = the whole hot path over one request of the Llama-3-8B-shaped bf16
 pool (32 layers, K+V, 8 KV heads, head_dim 128, page size 64, 2048 pages):
   BACKUP of 256 fragmented pages (16,384 tokens, 2 GiB) to pinned host
-  (validation + run planning, device pack into the staging ring, DMA),
-  RESTORE of that buffer into 256 other pages (DMA into the ring, device
-  unpack, per-layer publish), and the ready-prefix query, which the host
-  polls until the whole request is published.
+  (validation + run planning, then the gather kernel writing the packed
+  buffer over the host link on the zero-copy path, or packing into the
+  staging ring followed by DMA on the staged path), RESTORE of that buffer
+  into 256 other pages with per-layer publish, and the ready-prefix query,
+  which the host polls until the whole request is published.
 value = 2 x 2 GiB x steps / wall time of the steps (GB = 1e9 B). The pool is
 resident in HBM when the timed region starts; crossing the host link is
 part of the method (the host tier is where BACKUP writes and RESTORE reads).
 
 Also reported: the device pack/unpack kernels alone against the HBM peak
-(the roofline), the pinned hipMemcpyAsync peaks (host-link roofline), both
-host paths per direction, a layer-pipelined schedule that overlaps the two
+(the roofline), the step's kernels against the host link (link_roofline,
+with the pinned hipMemcpyAsync peaks measured in the same run), both host
+paths per direction, a layer-pipelined schedule that overlaps the two
 directions, the layer-0-ready latency, and the CPU oracle on a bounded
 sample (a baseline only).
 
@@ -34,13 +36,14 @@ sys.path.insert(0, ROOT)
 
 GB = 1e9
 HBM_PEAK_GBS = 8000.0     # MI355X published HBM3E bandwidth
+PCIE_PEAK_GBS = 64.0      # MI355X host interface, PCIe 5.0 x16, published per-direction rate
 
 # HBM bytes per launch of the roofline kernel from the two rocprofv3 --pmc runs
 # (FETCH_SIZE, WRITE_SIZE, scaled by a plain 2 GiB device copy in the same
 # run; see profiles/pack_kernel_llama8b.txt). Valid only for the kernel source
 # they were taken on: reported as null once kernels.hip changes.
-MEASURED_TRAFFIC = {"kernels_hip_sha256": "5f7078eb77e6cab51e0e0cadffc4a49e2ffb79853b774b535b39d20786557cc3",
-                    "bytes_per_launch": 4295361403}
+MEASURED_TRAFFIC = {"kernels_hip_sha256": "befa05be70c7c161f7297855f82e57fb439cc05a2fbfe9c1881a3dd49d9a781a",
+                    "bytes_per_launch": 4295619423}
 
 
 def log(msg):
@@ -56,7 +59,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--path", choices=["staged", "zerocopy"], default="staged")
+    ap.add_argument("--path", choices=["staged", "zerocopy"], default="zerocopy")
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
@@ -194,10 +197,23 @@ def main():
     ready = K.kvx_ready_create(w.num_layers, 1)
     path = {"staged": K.KVX_PATH_STAGED, "zerocopy": K.KVX_PATH_ZEROCOPY}[args.path]
 
-    def step(path=path):
+    # HIP events on the stream the kernels run on bracket the backup and the
+    # restore of every timed step (on the zero-copy path each call is one
+    # kernel launch: the gather writing host memory, the scatter reading it)
+    marks = []
+
+    def step(path=path, record=False):
         K.kvx_ready_reset(ready)
+        e = [ev() for _ in range(3)] if record else None
+        if record:
+            e[0].record(stream)
         K.kvx_backup(pool, src, host.ptr, P, 0, w.num_layers, stream, path)
+        if record:
+            e[1].record(stream)
         K.kvx_restore(pool, host.ptr, P, dst, 0, w.num_layers, ready, 0, stream, path)
+        if record:
+            e[2].record(stream)
+            marks.append(e)
         while K.kvx_ready_prefix(ready) < n:    # the consumer's view of completion
             pass
 
@@ -206,9 +222,11 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step()
+        step(record=True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    t_bk = median([m[0].elapsed_time(m[1]) / 1e3 for m in marks])
+    t_rs = median([m[1].elapsed_time(m[2]) / 1e3 for m in marks])
     ms_per_step = wall / args.steps * 1e3
     value = 2 * P * args.steps / wall / GB
     serial_peak = 2 / (1 / d2h_peak + 1 / h2d_peak)
@@ -235,10 +253,18 @@ def main():
         "unpack_roofline": {"achieved": round(unpack_gbs, 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(unpack_gbs / HBM_PEAK_GBS, 4)},
         "d2d_copy_gbs": round(d2d_gbs, 1),
-        "link": {"bound": "host link", "unit": "GB/s",
-                 "d2h_peak": round(d2h_peak, 2), "h2d_peak": round(h2d_peak, 2),
-                 "bidirectional_peak": round(bidir_peak, 2),
-                 "step_frac_of_serial_peak": round(value / serial_peak, 4)},
+        "link_roofline": {
+            "bound": "host link (PCIe 5.0 x16)",
+            "kernels": f"the step's {args.path} backup and restore, HIP events in the timed region",
+            "backup_achieved": round(P / t_bk / GB, 2), "restore_achieved": round(P / t_rs / GB, 2),
+            "unit": "GB/s", "peak": PCIE_PEAK_GBS,
+            "backup_frac": round(P / t_bk / GB / PCIE_PEAK_GBS, 4),
+            "restore_frac": round(P / t_rs / GB / PCIE_PEAK_GBS, 4),
+            "measured_memcpy_peak": {"d2h": round(d2h_peak, 2), "h2d": round(h2d_peak, 2),
+                                     "both_directions": round(bidir_peak, 2)},
+            "backup_frac_of_measured": round(P / t_bk / GB / d2h_peak, 4),
+            "restore_frac_of_measured": round(P / t_rs / GB / h2d_peak, 4),
+            "step_frac_of_serial_measured_peak": round(value / serial_peak, 4)},
     }
 
     if not args.no_extras:
@@ -257,7 +283,7 @@ def main():
                             "restore_frac_h2d_peak": round(P / median(tr) / GB / h2d_peak, 4)}
             log(f"{name}: backup {extras[name]['backup_gbs']} GB/s, "
                 f"restore {extras[name]['restore_gbs']} GB/s")
-        result["link"]["per_path"] = extras
+        result["link_roofline"]["per_path"] = extras
 
         # layer-pipelined: restore of layer group g runs on a second stream
         # while group g+1 is backed up, so both link directions carry data

@@ -527,9 +527,13 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
         } else {
             slots_per_chunk = static_cast<int32_t>(slot_bytes / (g.num_kv * g.piece_bytes));
         }
-        if (dir == SCATTER) {
+        // DMA on the library's side stream (overlaps the next chunk's kernel)
+        // or on the caller's stream (stream order alone; no cross-stream events)
+        hipStream_t dma = t.staged_dma_on_caller ? s : L->side;
+        const bool split = dma != s;
+        if (dir == SCATTER && split) {
             KVX_HIP(hipEventRecord(L->ev_start, s));
-            KVX_HIP(hipStreamWaitEvent(L->side, L->ev_start, 0));
+            KVX_HIP(hipStreamWaitEvent(dma, L->ev_start, 0));
         }
         std::vector<PageSlot> sub;
         for (int32_t la = l0; la < l1 && rc == KVX_OK; la += layers_per_chunk) {
@@ -555,43 +559,47 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
                 auto host_off = [&](int32_t l, int64_t c) { return ((int64_t(l) * g.num_kv + c) * n + s0) * g.piece_bytes; };
                 auto ring_off = [&](int32_t l, int64_t c) { return ((int64_t(l - la) * g.num_kv + c) * (s1 - s0)) * g.piece_bytes; };
                 if (dir == GATHER) {
-                    if (L->slot_pending[r]) KVX_HIP(hipStreamWaitEvent(s, L->slot_free[r], 0));
+                    if (split && L->slot_pending[r]) KVX_HIP(hipStreamWaitEvent(s, L->slot_free[r], 0));
                     rc = launch_range(dir, pool, tg, la, lb, cp, cn, nullptr, t, L->cu_count, s);
                     if (rc != KVX_OK) break;
-                    KVX_HIP(hipEventRecord(L->slot_ready[r], s));
-                    KVX_HIP(hipStreamWaitEvent(L->side, L->slot_ready[r], 0));
+                    if (split) {
+                        KVX_HIP(hipEventRecord(L->slot_ready[r], s));
+                        KVX_HIP(hipStreamWaitEvent(dma, L->slot_ready[r], 0));
+                    }
                     if (full) {
                         KVX_HIP(hipMemcpyAsync(host + host_off(la, 0), slot_mem, int64_t(lb - la) * g.num_kv * strip,
-                                               hipMemcpyDeviceToHost, L->side));
+                                               hipMemcpyDeviceToHost, dma));
                     } else {
                         for (int32_t l = la; l < lb; l++)
                             for (int64_t c = 0; c < g.num_kv; c++)
                                 KVX_HIP(hipMemcpyAsync(host + host_off(l, c), slot_mem + ring_off(l, c), strip,
-                                                       hipMemcpyDeviceToHost, L->side));
+                                                       hipMemcpyDeviceToHost, dma));
                     }
-                    KVX_HIP(hipEventRecord(L->slot_free[r], L->side));
+                    if (split) KVX_HIP(hipEventRecord(L->slot_free[r], dma));
                 } else {
-                    if (L->slot_pending[r]) KVX_HIP(hipStreamWaitEvent(L->side, L->slot_free[r], 0));
+                    if (split && L->slot_pending[r]) KVX_HIP(hipStreamWaitEvent(dma, L->slot_free[r], 0));
                     if (full) {
                         KVX_HIP(hipMemcpyAsync(slot_mem, host + host_off(la, 0), int64_t(lb - la) * g.num_kv * strip,
-                                               hipMemcpyHostToDevice, L->side));
+                                               hipMemcpyHostToDevice, dma));
                     } else {
                         for (int32_t l = la; l < lb; l++)
                             for (int64_t c = 0; c < g.num_kv; c++)
                                 KVX_HIP(hipMemcpyAsync(slot_mem + ring_off(l, c), host + host_off(l, c), strip,
-                                                       hipMemcpyHostToDevice, L->side));
+                                                       hipMemcpyHostToDevice, dma));
                     }
-                    KVX_HIP(hipEventRecord(L->slot_ready[r], L->side));
-                    KVX_HIP(hipStreamWaitEvent(s, L->slot_ready[r], 0));
+                    if (split) {
+                        KVX_HIP(hipEventRecord(L->slot_ready[r], dma));
+                        KVX_HIP(hipStreamWaitEvent(s, L->slot_ready[r], 0));
+                    }
                     rc = launch_range(dir, pool, tg, la, lb, cp, cn, pubp, t, L->cu_count, s);
                     if (rc != KVX_OK) break;
-                    KVX_HIP(hipEventRecord(L->slot_free[r], s));
+                    if (split) KVX_HIP(hipEventRecord(L->slot_free[r], s));
                 }
-                L->slot_pending[r] = true;
+                L->slot_pending[r] = split;
             }
         }
-        if (rc == KVX_OK && dir == GATHER) {
-            KVX_HIP(hipEventRecord(L->ev_done, L->side));
+        if (rc == KVX_OK && dir == GATHER && split) {
+            KVX_HIP(hipEventRecord(L->ev_done, dma));
             KVX_HIP(hipStreamWaitEvent(s, L->ev_done, 0));
         }
     }
@@ -953,6 +961,10 @@ int kvx_set_option(int32_t option, int64_t value)
         if (value < -1 || value > 3) break;
         g_tune.unit_order = value;
         return KVX_OK;
+    case KVX_OPT_STAGED_DMA_ON_CALLER:
+        if (value != 0 && value != 1) break;
+        g_tune.staged_dma_on_caller = value;
+        return KVX_OK;
     case KVX_OPT_MAX_UNROLL:
         if (value < 1 || value > 16) break;
         g_tune.max_unroll = value;
@@ -979,6 +991,7 @@ int kvx_get_option(int32_t option, int64_t* value)
     case KVX_OPT_HOST_GRID_MAX: *value = g_tune.host_grid_max; return KVX_OK;
     case KVX_OPT_UNIT_ORDER: *value = g_tune.unit_order; return KVX_OK;
     case KVX_OPT_MAX_UNROLL: *value = g_tune.max_unroll; return KVX_OK;
+    case KVX_OPT_STAGED_DMA_ON_CALLER: *value = g_tune.staged_dma_on_caller; return KVX_OK;
     default: return fail(KVX_E_INVAL, "get_option: unknown option " + std::to_string(option));
     }
 }

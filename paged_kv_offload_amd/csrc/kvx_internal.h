@@ -113,6 +113,7 @@ struct Tuning {
     int64_t host_grid_max = 0;            // 0 = auto
     int64_t unit_order = -1;              // MoveArgs::unit_order bits, -1 = auto
     int64_t max_unroll = 16;              // largest 16-byte vectors per lane per unit
+    int64_t staged_dma_on_caller = 0;     // staged DMA on the caller's stream instead of a side stream
 };
 Tuning tuning();
 
