@@ -11,7 +11,7 @@
 #include <cstdio>
 #include <sstream>
 
-#include "kvx_internal.h"
+#include "kvx_host.h"
 
 namespace kvx {
 

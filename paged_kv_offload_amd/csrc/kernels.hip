@@ -13,11 +13,11 @@
 // those of layer l+1 and layers complete roughly in order.
 //
 // Head-major pools ([RAWIPC] integration: TRT-LLM's HND pool) are converted
-// row by row: a row of D elements is contiguous on both sides, so every
-// 16-byte access stays within one row and each wave reads and writes whole
-// 64-byte segments; no LDS staging is needed for rows of 16 bytes or more.
-// Destination order is linear (sequential writes), the source address is
-// the permuted row.
+// either row by row - a row of D elements is contiguous on both sides, so
+// every 16-byte access stays within one row and each wave reads and writes
+// whole 64-byte segments; the destination is walked linearly and the source
+// address is the permuted row - or through LDS in token blocks, where both
+// global sides are linear runs.
 //
 // Publish ([TICKET] "PP Prefetch Ticket Path": layer-wise H2D and a
 // published safe prefix): a workgroup counts the units it finished of layer
@@ -135,7 +135,68 @@ __device__ __forceinline__ void count_units(const MoveArgs& a, int32_t l, uint32
     }
 }
 
-template <Dir D, int U, bool PERMUTE, bool PUBLISH, int NT>
+// One unit of a head-major piece through LDS: tokens [t0, t0 + TU) of all H
+// heads, the token-major (NHD) side one contiguous run and the head-major
+// (HND) side H contiguous segments of TU rows. Global reads and writes are
+// both linear runs; LDS does the (t, h) exchange. Used when a unit is a
+// whole number of token blocks (chunk_bytes = TU * H * row_bytes).
+template <Dir D, int U, int NT>
+__device__ __forceinline__ void move_unit_lds(const MoveArgs& a, const uint8_t* src, uint8_t* dst,
+                                              uint32_t k, uint32_t tid, v4u* lds)
+{
+    const uint32_t t0 = k * a.TU;
+    const uint32_t nhd0 = t0 * a.H * a.row_vec;   // first vector of the unit on the NHD side
+    v4u v[U];
+    __syncthreads();   // the previous unit's readers are done with lds
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const uint32_t i = u * kThreads + tid;
+        if constexpr (D == GATHER) {
+            // source: pool HND, read head segment by head segment
+            const uint32_t h = fast_div(i, a.mg_seg);
+            const uint32_t r = i - h * a.seg;
+            const uint32_t tt = fast_div(r, a.mg_row_vec);
+            const uint32_t w = r - tt * a.row_vec;
+            v[u] = load16<(NT & 1) != 0>(src + (((h * a.T + t0 + tt) * a.row_vec + w) << 4));
+        } else {
+            // source: packed NHD, one contiguous run
+            v[u] = load16<(NT & 1) != 0>(src + ((nhd0 + i) << 4));
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const uint32_t i = u * kThreads + tid;
+        if constexpr (D == GATHER) {
+            const uint32_t h = fast_div(i, a.mg_seg);
+            const uint32_t r = i - h * a.seg;
+            const uint32_t tt = fast_div(r, a.mg_row_vec);
+            const uint32_t w = r - tt * a.row_vec;
+            lds[(tt * a.H + h) * a.row_vec + w] = v[u];   // into NHD order
+        } else {
+            lds[i] = v[u];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        const uint32_t i = u * kThreads + tid;
+        if constexpr (D == GATHER) {
+            store16<(NT & 2) != 0>(dst + ((nhd0 + i) << 4), lds[i]);
+        } else {
+            // destination: pool HND, written head segment by head segment
+            const uint32_t h = fast_div(i, a.mg_seg);
+            const uint32_t r = i - h * a.seg;
+            const uint32_t tt = fast_div(r, a.mg_row_vec);
+            const uint32_t w = r - tt * a.row_vec;
+            store16<(NT & 2) != 0>(dst + (((h * a.T + t0 + tt) * a.row_vec + w) << 4),
+                                   lds[(tt * a.H + h) * a.row_vec + w]);
+        }
+    }
+}
+
+// PERM: 0 = same inner layout, 1 = HND<->NHD row by row, 2 = HND<->NHD
+// through LDS token blocks
+template <Dir D, int U, int PERM, bool PUBLISH, int NT>
 __global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
 {
     const uint32_t tid = threadIdx.x;
@@ -183,7 +244,12 @@ __global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
             static_cast<int64_t>(slot - a.pk_slot0) * a.piece_bytes;
         const uint8_t* src = (D == GATHER) ? pool_piece : pk_piece;
         uint8_t* dst = (D == GATHER) ? pk_piece : pool_piece;
-        move_unit<D, U, PERMUTE, NT>(a, src, dst, k * a.chunk_bytes, tid);
+        if constexpr (PERM == 2) {
+            __shared__ v4u lds[U * kThreads];
+            move_unit_lds<D, U, NT>(a, src, dst, k, tid, lds);
+        } else {
+            move_unit<D, U, PERM == 1, NT>(a, src, dst, k * a.chunk_bytes, tid);
+        }
         if constexpr (PUBLISH) pend++;
     }
     if constexpr (PUBLISH) {
@@ -235,7 +301,7 @@ int pick_unroll(int64_t piece_bytes, int max_unroll)
 
 namespace {
 
-template <Dir D, int U, bool P, bool PUB, int NT>
+template <Dir D, int U, int P, bool PUB, int NT>
 hipError_t go(const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s)
 {
     void* args[] = {const_cast<MoveArgs*>(&a)};
@@ -243,7 +309,7 @@ hipError_t go(const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s)
                            dim3(cfg.grid), dim3(kThreads), args, 0, s);
 }
 
-template <Dir D, int U, bool P, bool PUB>
+template <Dir D, int U, int P, bool PUB>
 hipError_t go_nt(const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s)
 {
     switch (cfg.nontemporal & 3) {
@@ -254,7 +320,7 @@ hipError_t go_nt(const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s)
     }
 }
 
-template <Dir D, int U, bool P>
+template <Dir D, int U, int P>
 hipError_t go_pub(const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s)
 {
     if constexpr (D == SCATTER) {
@@ -266,7 +332,10 @@ hipError_t go_pub(const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s)
 template <Dir D, int U>
 hipError_t go_perm(const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s)
 {
-    return cfg.permute ? go_pub<D, U, true>(cfg, a, s) : go_pub<D, U, false>(cfg, a, s);
+    if constexpr (U == 4 || U == 8 || U == 16) {
+        if (cfg.permute == 2) return go_pub<D, U, 2>(cfg, a, s);
+    }
+    return cfg.permute ? go_pub<D, U, 1>(cfg, a, s) : go_pub<D, U, 0>(cfg, a, s);
 }
 
 template <Dir D>

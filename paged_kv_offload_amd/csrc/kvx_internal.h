@@ -12,16 +12,10 @@
 #include <hip/hip_runtime.h>
 
 #include "kvx.h"
+#include "kvx_host.h"
 
 namespace kvx {
 
-// ---------------------------------------------------------------------------
-// errors and logging
-// ---------------------------------------------------------------------------
-int fail(int code, const std::string& msg);   // records the thread's message, returns code
-void clear_error();
-void log_warn(const std::string& msg);
-void log_info(const std::string& msg);
 int hip_fail(hipError_t e, const char* what);  // KVX_E_HIP with the runtime's message
 
 #define KVX_HIP(call)                                   \
@@ -29,41 +23,6 @@ int hip_fail(hipError_t e, const char* what);  // KVX_E_HIP with the runtime's m
         hipError_t e_ = (call);                         \
         if (e_ != hipSuccess) return hip_fail(e_, #call); \
     } while (0)
-
-// ---------------------------------------------------------------------------
-// pool geometry (derived and validated at registration; host only)
-// ---------------------------------------------------------------------------
-struct PoolGeom {
-    int64_t num_pages = 0, num_layers = 0, num_kv = 0, page_size = 0, num_heads = 0,
-            head_dim = 0;
-    int32_t inner = KVX_NHD;
-    int32_t outer[3] = {0, 1, 2};
-    int64_t dtype_bytes = 0;
-    int64_t row_bytes = 0, piece_bytes = 0, pool_bytes = 0;
-    int64_t page_stride = 0, layer_stride = 0, kv_stride = 0;   // bytes
-    bool pages_adjacent = false;   // page_stride == piece_bytes
-};
-
-// Validates layout + tensor view; fills geom. Host only, calls no HIP API.
-int derive_geometry(const kvx_layout* layout, const void* base, uint64_t byte_offset,
-                    uint32_t dtype_bytes, int32_t ndim, const int64_t* shape,
-                    const int64_t* stride, PoolGeom* geom);
-
-// ---------------------------------------------------------------------------
-// page lists (host only)
-// ---------------------------------------------------------------------------
-struct PageSlot {
-    int32_t page, slot;
-};
-struct Run {
-    int32_t page, slot, count;
-};
-int check_page_ids(const PoolGeom& g, const int32_t* ids, int32_t n, bool reject_dups);
-// Pairs (page, slot) in visiting order: sorted by page when `sorted`, else
-// caller order.
-void order_pages(const int32_t* ids, int32_t n, bool sorted, std::vector<PageSlot>* out);
-void plan_runs(const PoolGeom& g, const std::vector<PageSlot>& sorted_pairs,
-               std::vector<Run>* runs);
 
 // ---------------------------------------------------------------------------
 // handles
@@ -114,6 +73,7 @@ struct Tuning {
     int64_t unit_order = -1;              // MoveArgs::unit_order bits, -1 = auto
     int64_t max_unroll = 16;              // largest 16-byte vectors per lane per unit
     int64_t staged_dma_on_caller = 0;     // staged DMA on the caller's stream instead of a side stream
+    int64_t hnd_lds = -1;                 // HND<->NHD through LDS: 1 both, 0 never, -1 scatter only
 };
 Tuning tuning();
 
@@ -121,7 +81,6 @@ Tuning tuning();
 // kernel launch interface
 // ---------------------------------------------------------------------------
 constexpr int kThreads = 256;        // 4 wave64 per workgroup
-constexpr int kVecBytes = 16;        // one dwordx4 per lane access
 constexpr int kMaxPairs = 448;       // (page, slot) pairs carried in the kernel arguments
 constexpr int kHostGridAuto = 32;    // default workgroups of a kernel streaming over the host link
 constexpr int64_t kRestoreChunkMin = 32ll << 20;   // default minimum staged restore chunk
@@ -146,6 +105,7 @@ struct MoveArgs {
     // pool HND <-> packed NHD permutation (unused for NHD pools)
     uint32_t T, H, row_vec;              // row_vec = row_bytes / 16
     uint32_t mg_row_vec, mg_H, mg_T;     // magic multipliers (0 means divisor 1)
+    uint32_t TU, seg, mg_seg;            // LDS token blocks: tokens per unit, TU * row_vec
     // per-layer publish (RESTORE with a ready object)
     uint32_t* layer_done;    // device counters, indexed by absolute layer
     uint32_t* ready;         // device view of counts + slot_base, indexed by layer
@@ -157,7 +117,7 @@ struct MoveArgs {
 
 struct LaunchCfg {
     int unroll;        // 16-byte vectors per lane per unit: 1, 2, 4, 8 or 16
-    bool permute;      // pool inner layout is HND
+    int permute;       // 0: same inner layout; 1: HND<->NHD by rows; 2: through LDS
     bool publish;
     int nontemporal;   // bit 0: non-temporal loads, bit 1: non-temporal stores
     int grid;

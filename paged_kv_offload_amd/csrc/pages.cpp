@@ -7,7 +7,7 @@
 // only changes the order in which pieces are visited, never where they land.
 #include <algorithm>
 
-#include "kvx_internal.h"
+#include "kvx_host.h"
 
 namespace kvx {
 

@@ -1,0 +1,178 @@
+// host_fuzz.cpp - randomized checks of kvx's host-only logic (pool layout
+// validator, page-list checks, run planning), built with AddressSanitizer
+// and UndefinedBehaviorSanitizer by tests/test_host_sanitizers.py. Each
+// accepted layout is compared with a brute-force row-major index; each plan
+// must cover every (page, slot) pair exactly once with valid runs.
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <random>
+#include <set>
+#include <string>
+#include <vector>
+
+#include "kvx_host.h"
+
+namespace kvx {
+static int g_last_code = 0;
+int fail(int code, const std::string&) { g_last_code = code; return code; }
+void clear_error() {}
+void log_warn(const std::string&) {}
+void log_info(const std::string&) {}
+}  // namespace kvx
+
+using namespace kvx;
+
+#define CHECK(c)                                                            \
+    do {                                                                    \
+        if (!(c)) {                                                         \
+            std::fprintf(stderr, "check failed line %d: %s\n", __LINE__, #c); \
+            std::exit(1);                                                   \
+        }                                                                   \
+    } while (0)
+
+static std::mt19937_64 rng(12345);
+static int64_t rnd(int64_t lo, int64_t hi) { return std::uniform_int_distribution<int64_t>(lo, hi)(rng); }
+
+// byte offset of piece (p, l, c) by brute force: walk the row-major index
+static int64_t piece_offset(const kvx_layout& L, int64_t piece_bytes, int64_t p, int64_t l, int64_t c)
+{
+    const int64_t size[3] = {L.num_pages, L.num_layers, L.num_kv};
+    const int64_t coord[3] = {p, l, c};
+    int64_t idx = 0;
+    for (int k = 0; k < 3; k++) idx = idx * size[L.outer[k]] + coord[L.outer[k]];
+    return idx * piece_bytes;
+}
+
+static void fuzz_geometry(int iters)
+{
+    int accepted = 0;
+    for (int it = 0; it < iters; it++) {
+        kvx_layout L;
+        int perm[3] = {0, 1, 2};
+        std::shuffle(perm, perm + 3, rng);
+        for (int k = 0; k < 3; k++) L.outer[k] = perm[k];
+        L.inner = static_cast<int32_t>(rnd(0, 1));
+        L.num_pages = static_cast<int32_t>(rnd(1, 9));
+        L.num_layers = static_cast<int32_t>(rnd(1, 5));
+        L.num_kv = static_cast<int32_t>(rnd(1, 2));
+        L.page_size = static_cast<int32_t>(rnd(1, 7));
+        L.num_heads = static_cast<int32_t>(rnd(1, 5));
+        L.head_dim = static_cast<int32_t>(8 * rnd(1, 4));
+        const uint32_t eb = static_cast<uint32_t>(1 << rnd(0, 2));
+        if (rnd(0, 20) == 0) L.num_heads = 0;                 // invalid dim
+        if (rnd(0, 20) == 0) L.outer[1] = L.outer[0];          // not a permutation
+        const int64_t sz[3] = {L.num_pages, L.num_layers, L.num_kv};
+        std::vector<int64_t> phys = {sz[L.outer[0]], sz[L.outer[1]], sz[L.outer[2]],
+                                     L.inner ? L.num_heads : L.page_size,
+                                     L.inner ? L.page_size : L.num_heads, L.head_dim};
+        // a view: the physical dims with random neighbours merged, sometimes broken
+        std::vector<int64_t> shape;
+        for (int64_t d : phys) {
+            if (!shape.empty() && rnd(0, 2) == 0) shape.back() *= d;
+            else shape.push_back(d);
+        }
+        if (rnd(0, 15) == 0 && shape.size() > 1) std::swap(shape[0], shape[1]);   // wrong split
+        if (rnd(0, 15) == 0) shape.back() += 1;                                   // wrong count
+        std::vector<int64_t> stride(shape.size());
+        int64_t acc = 1;
+        for (size_t k = shape.size(); k-- > 0;) { stride[k] = acc; acc *= shape[k]; }
+        if (rnd(0, 10) == 0 && shape.size() > 1) stride[0] += 1;                  // not dense
+        const uint64_t base = 0x10000ull * rnd(1, 1000) + (rnd(0, 12) == 0 ? 8 : 0);
+        const uint64_t off = 16ull * rnd(0, 64);
+        PoolGeom g;
+        int rc = derive_geometry(&L, reinterpret_cast<void*>(base), off, eb,
+                                 static_cast<int32_t>(shape.size()), shape.data(), stride.data(), &g);
+        if (rc != KVX_OK) continue;
+        accepted++;
+        CHECK(g.row_bytes == L.head_dim * int64_t(eb));
+        CHECK(g.piece_bytes == L.page_size * L.num_heads * g.row_bytes);
+        CHECK(g.pool_bytes == int64_t(L.num_pages) * L.num_layers * L.num_kv * g.piece_bytes);
+        CHECK((base + off) % 16 == 0 && g.row_bytes % 16 == 0);
+        for (int64_t p = 0; p < L.num_pages; p++)
+            for (int64_t l = 0; l < L.num_layers; l++)
+                for (int64_t c = 0; c < L.num_kv; c++)
+                    CHECK(p * g.page_stride + l * g.layer_stride + c * g.kv_stride ==
+                          piece_offset(L, g.piece_bytes, p, l, c));
+    }
+    CHECK(accepted > iters / 4);
+    std::printf("geometry: %d of %d accepted and verified\n", accepted, iters);
+}
+
+static void fuzz_extremes()
+{
+    kvx_layout L{{0, 1, 2}, 0, 2147483647, 2147483647, 2, 2147483647, 2147483647, 2147483647};
+    int64_t shape[1] = {1}, stride[1] = {1};
+    PoolGeom g;
+    CHECK(derive_geometry(&L, reinterpret_cast<void*>(0x1000), 0, 2, 1, shape, stride, &g) == KVX_E_INVAL);
+    kvx_layout M{{1, 2, 0}, 1, 4, 2, 2, 8, 4, 64};
+    int64_t s9[9] = {1, 1, 1, 1, 1, 1, 1, 1, 1}, t9[9] = {1, 1, 1, 1, 1, 1, 1, 1, 1};
+    CHECK(derive_geometry(&M, reinterpret_cast<void*>(0x1000), 0, 2, 9, s9, t9, &g) == KVX_E_INVAL);
+    CHECK(derive_geometry(&M, reinterpret_cast<void*>(0x1000), 0, 2, 0, s9, t9, &g) == KVX_E_INVAL);
+    CHECK(derive_geometry(nullptr, reinterpret_cast<void*>(0x1000), 0, 2, 1, s9, t9, &g) == KVX_E_INVAL);
+    CHECK(derive_geometry(&M, nullptr, 0, 2, 1, s9, t9, &g) == KVX_E_INVAL);
+    CHECK(derive_geometry(&M, reinterpret_cast<void*>(0x1000), 0, 0, 1, s9, t9, &g) == KVX_E_INVAL);
+    int64_t neg[2] = {-4, 2}, st2[2] = {2, 1};
+    CHECK(derive_geometry(&M, reinterpret_cast<void*>(0x1000), 0, 2, 2, neg, st2, &g) == KVX_E_INVAL);
+    std::printf("extremes: ok\n");
+}
+
+static void fuzz_pages(int iters)
+{
+    for (int it = 0; it < iters; it++) {
+        PoolGeom g;
+        g.num_pages = rnd(1, 5000);
+        g.piece_bytes = 4096;
+        g.pages_adjacent = rnd(0, 1) != 0;
+        const int32_t n = static_cast<int32_t>(rnd(0, 3000));
+        std::vector<int32_t> ids(n);
+        const bool contiguous = rnd(0, 3) == 0;
+        int32_t start = static_cast<int32_t>(rnd(0, g.num_pages - 1));
+        for (int32_t i = 0; i < n; i++)
+            ids[i] = contiguous ? static_cast<int32_t>((start + i) % g.num_pages)
+                                : static_cast<int32_t>(rnd(0, g.num_pages - 1));
+        if (n > 0 && rnd(0, 10) == 0) ids[rnd(0, n - 1)] = static_cast<int32_t>(g.num_pages + rnd(0, 3));
+        if (n > 0 && rnd(0, 10) == 0) ids[rnd(0, n - 1)] = -1 - static_cast<int32_t>(rnd(0, 3));
+        bool in_range = true;
+        for (int32_t v : ids) in_range = in_range && v >= 0 && v < g.num_pages;
+        const int rc = check_page_ids(g, ids.data(), n, false);
+        CHECK((rc == KVX_OK) == in_range);
+        if (!in_range) continue;
+        const bool distinct = std::set<int32_t>(ids.begin(), ids.end()).size() == ids.size();
+        CHECK((check_page_ids(g, ids.data(), n, true) == KVX_OK) == distinct);
+        for (bool sorted : {false, true}) {
+            std::vector<PageSlot> pairs;
+            order_pages(ids.data(), n, sorted, &pairs);
+            CHECK(static_cast<int32_t>(pairs.size()) == n);
+            for (size_t j = 0; j + 1 < pairs.size() && sorted; j++) CHECK(pairs[j].page <= pairs[j + 1].page);
+            std::vector<int> seen(n, 0);
+            for (const PageSlot& ps : pairs) {
+                CHECK(ps.slot >= 0 && ps.slot < n && ids[ps.slot] == ps.page);
+                seen[ps.slot]++;
+            }
+            for (int v : seen) CHECK(v == 1);
+            if (!sorted) continue;
+            std::vector<Run> runs;
+            plan_runs(g, pairs, &runs);
+            std::vector<int> covered(n, 0);
+            for (const Run& r : runs) {
+                CHECK(r.count >= 1 && (r.count == 1 || g.pages_adjacent));
+                for (int32_t k = 0; k < r.count; k++) {
+                    CHECK(r.slot + k < n && ids[r.slot + k] == r.page + k);
+                    covered[r.slot + k]++;
+                }
+            }
+            for (int v : covered) CHECK(v == 1);
+        }
+    }
+    std::printf("pages: %d random lists checked\n", iters);
+}
+
+int main()
+{
+    fuzz_extremes();
+    fuzz_geometry(20000);
+    fuzz_pages(3000);
+    std::printf("host fuzz ok\n");
+    return 0;
+}

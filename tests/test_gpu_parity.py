@@ -374,3 +374,53 @@ def test_every_page_and_single_page(case, path, stream):
         img = after
         pk.close()
     pool.close()
+
+
+HND_LDS_CASES = {
+    "trtllm_small": SMALL["trtllm_small"],
+    # 128 KiB head-major pieces: two 64 KiB LDS token blocks (32 tokens x 8 heads) per piece
+    "hnd_two_blocks": (Workload(name="hnd_two_blocks", outer=("layer", "kv", "page"), inner="HND",
+                                num_pages=64, num_layers=2, num_kv=2, page_size=64, num_heads=8,
+                                head_dim=128, dtype_bytes=2, pages_per_request=16, seed=204,
+                                byte_offset=4096, alloc_tail=4096), 16),
+    # 32 KiB pieces of 2 heads x 128 tokens of 128 B rows: one block of all 128 tokens
+    "hnd_narrow_rows": (Workload(name="hnd_narrow_rows", outer=("page", "layer", "kv"),
+                                 inner="HND", num_pages=48, num_layers=3, num_kv=2, page_size=128,
+                                 num_heads=2, head_dim=64, dtype_bytes=2, pages_per_request=12,
+                                 seed=205), 12),
+}
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("case", list(HND_LDS_CASES))
+def test_hnd_through_lds(case, path, stream):
+    """The LDS token-block conversion gives the oracle's bytes, for backup,
+    restore and restore with publish."""
+    w, n = HND_LDS_CASES[case]
+    L = oracle_layout(w)
+    old = K.kvx_get_option(K.KVX_OPT_HND_LDS)
+    K.kvx_set_option(K.KVX_OPT_HND_LDS, 1)
+    try:
+        pool = DevicePool(w, seed=501)
+        img = pool.host_image()
+        src, dst = pages(w, n)
+        nb = w.host_bytes(n)
+        pk = Packed(w, n, path, fill_seed=7)
+        K.kvx_backup(pool.handle, src, pk.ptr, nb, 0, w.num_layers, stream, PATHS[path])
+        K.kvx_sync(stream)
+        want = oracle.backup(L, img, src, 0, w.num_layers)
+        got = pk.numpy()
+        assert np.array_equal(got, want), diff_report(got, want)
+        ready = K.kvx_ready_create(w.num_layers, 1)
+        K.kvx_restore(pool.handle, pk.ptr, nb, dst, 0, w.num_layers, ready, 0, stream,
+                      PATHS[path])
+        K.kvx_sync(stream)
+        assert K.kvx_ready_prefix(ready) == n
+        K.kvx_ready_destroy(ready)
+        after = pool.host_image()
+        want_alloc = oracle.restore(L, img, want, dst, 0, w.num_layers)
+        assert np.array_equal(after, want_alloc), diff_report(after, want_alloc)
+        pk.close()
+        pool.close()
+    finally:
+        K.kvx_set_option(K.KVX_OPT_HND_LDS, old)
