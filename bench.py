@@ -42,8 +42,8 @@ PCIE_PEAK_GBS = 64.0      # MI355X host interface, PCIe 5.0 x16, published per-d
 # (FETCH_SIZE, WRITE_SIZE, scaled by a plain 2 GiB device copy in the same
 # run; see profiles/pack_kernel_llama8b.txt). Valid only for the kernel source
 # they were taken on: reported as null once kernels.hip changes.
-MEASURED_TRAFFIC = {"kernels_hip_sha256": "befa05be70c7c161f7297855f82e57fb439cc05a2fbfe9c1881a3dd49d9a781a",
-                    "bytes_per_launch": 4295619423}
+MEASURED_TRAFFIC = {"kernels_hip_sha256": "9c909de7b5e51eba2588210bf66c6e6260eb364623881bf5b5ac21d4e06787e3",
+                    "bytes_per_launch": 4295626051}
 
 
 def log(msg):

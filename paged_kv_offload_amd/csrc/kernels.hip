@@ -287,11 +287,12 @@ uint32_t magic_u32(uint32_t d)
 
 int pick_unroll(int64_t piece_bytes, int max_unroll)
 {
-    // the largest unit (U vector rounds of 4 KiB) that tiles the piece exactly;
-    // pieces that are not a multiple of 4 KiB get the largest unit that fits
-    // and a predicated tail
+    // the largest power-of-two unit (U vector rounds of 4 KiB) that tiles the
+    // piece exactly, else 12, 6 or 3 rounds (measured: a 144 KiB piece moves
+    // faster in 16 KiB units than in 48 KiB ones); pieces that are not a
+    // multiple of 4 KiB get the largest unit that fits and a predicated tail
     const int64_t step = kThreads * kVecBytes;
-    for (int u : {16, 12, 8, 6, 4, 3, 2})
+    for (int u : {16, 8, 4, 12, 6, 3, 2})
         if (u <= max_unroll && piece_bytes % (step * u) == 0) return u;
     if (piece_bytes % step == 0) return 1;
     for (int u : {16, 8, 4})
