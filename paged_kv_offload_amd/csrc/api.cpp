@@ -329,10 +329,12 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
     const bool lds = cfg.permute && (t.hnd_lds > 0 || (t.hnd_lds < 0 && dir == SCATTER));
     cfg.unroll = unroll_for(g, dir, t);
     cfg.publish = pub != nullptr;
-    // streaming hints (measured): non-temporal loads and stores for HBM to
-    // HBM; plain stores into pinned host memory
-    cfg.nontemporal = t.nontemporal >= 0 ? static_cast<int>(t.nontemporal)
-                                         : ((tg.host && dir == GATHER) ? 1 : 3);
+    // cache policy (measured on MI355X): HBM to HBM, non-temporal loads and
+    // non-temporal device-scope stores; into pinned host memory, non-temporal
+    // loads and device-scope stores; out of pinned host memory, plain loads
+    int cp = 7;
+    if (tg.host) cp = (dir == GATHER) ? 5 : 6;
+    cfg.cache_policy = t.cache_policy >= 0 ? static_cast<int>(t.cache_policy) : cp;
     a.pool = pool->start;
     a.packed = tg.packed;
     a.page_stride = g.page_stride;
@@ -970,9 +972,9 @@ int kvx_set_option(int32_t option, int64_t value)
         if (value != 0 && value != 1) break;
         g_tune.sort_pages = value;
         return KVX_OK;
-    case KVX_OPT_NONTEMPORAL:
-        if (value < -1 || value > 3) break;
-        g_tune.nontemporal = value;
+    case KVX_OPT_CACHE_POLICY:
+        if (value < -1 || value > 7) break;
+        g_tune.cache_policy = value;
         return KVX_OK;
     case KVX_OPT_RESTORE_CHUNK_LAYERS:
         if (value < 0 || value > 4096) break;
@@ -995,7 +997,7 @@ int kvx_set_option(int32_t option, int64_t value)
         g_tune.hnd_lds = value;
         return KVX_OK;
     case KVX_OPT_MAX_UNROLL:
-        if (value < 1 || value > 16) break;
+        if (value < 1 || value > 32) break;
         g_tune.max_unroll = value;
         return KVX_OK;
     default:
@@ -1015,7 +1017,7 @@ int kvx_get_option(int32_t option, int64_t* value)
     case KVX_OPT_STAGE_SLOT_BYTES: *value = g_tune.stage_slot_bytes; return KVX_OK;
     case KVX_OPT_STAGE_SLOTS: *value = g_tune.stage_slots; return KVX_OK;
     case KVX_OPT_SORT_PAGES: *value = g_tune.sort_pages; return KVX_OK;
-    case KVX_OPT_NONTEMPORAL: *value = g_tune.nontemporal; return KVX_OK;
+    case KVX_OPT_CACHE_POLICY: *value = g_tune.cache_policy; return KVX_OK;
     case KVX_OPT_RESTORE_CHUNK_LAYERS: *value = g_tune.restore_chunk_layers; return KVX_OK;
     case KVX_OPT_HOST_GRID_MAX: *value = g_tune.host_grid_max; return KVX_OK;
     case KVX_OPT_UNIT_ORDER: *value = g_tune.unit_order; return KVX_OK;

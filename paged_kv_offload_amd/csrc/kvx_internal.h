@@ -67,11 +67,11 @@ struct Tuning {
     int64_t stage_slot_bytes = 128ll << 20;
     int64_t stage_slots = 3;
     int64_t sort_pages = 0;
-    int64_t nontemporal = -1;             // bit 0 loads, bit 1 stores; -1 = auto
+    int64_t cache_policy = -1;            // bit 0 nt loads, bit 1 nt stores, bit 2 sc1 stores; -1 = auto
     int64_t restore_chunk_layers = 0;     // 0 = auto (chunks of >= kRestoreChunkMin bytes)
     int64_t host_grid_max = 0;            // 0 = auto
     int64_t unit_order = -1;              // MoveArgs::unit_order bits, -1 = auto
-    int64_t max_unroll = 16;              // largest 16-byte vectors per lane per unit
+    int64_t max_unroll = 32;              // largest 16-byte vectors per lane per unit
     int64_t staged_dma_on_caller = 0;     // staged DMA on the caller's stream instead of a side stream
     int64_t hnd_lds = -1;                 // HND<->NHD through LDS: 1 both, 0 never, -1 scatter only
 };
@@ -119,7 +119,7 @@ struct LaunchCfg {
     int unroll;        // 16-byte vectors per lane per unit: 1, 2, 4, 8 or 16
     int permute;       // 0: same inner layout; 1: HND<->NHD by rows; 2: through LDS
     bool publish;
-    int nontemporal;   // bit 0: non-temporal loads, bit 1: non-temporal stores
+    int cache_policy;  // bit 0: non-temporal loads, bit 1: non-temporal stores, bit 2: device-scope stores
     int grid;
 };
 

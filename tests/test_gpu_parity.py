@@ -57,11 +57,10 @@ def pages(w, n):
     return perm[:n].copy(), perm[n:2 * n].copy()
 
 
-@pytest.mark.parametrize("path", list(PATHS))
-@pytest.mark.parametrize("case", list(SMALL))
-def test_backup_restore_parity(case, path, stream):
-    w, n = SMALL[case]
-    print(f"\n[parity] case={case} path={path} n={n} piece={w.piece_bytes}", flush=True)
+def check_backup_restore(w, n, path, stream):
+    """BACKUP then RESTORE of n pages over two layer ranges on `path`, each
+    compared byte for byte with the oracle (whole packed buffer, whole
+    allocation)."""
     L = oracle_layout(w)
     pool = DevicePool(w)
     img = pool.host_image()
@@ -88,6 +87,51 @@ def test_backup_restore_parity(case, path, stream):
         img = after
         pk.close()
     pool.close()
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("case", list(SMALL))
+def test_backup_restore_parity(case, path, stream):
+    w, n = SMALL[case]
+    print(f"\n[parity] case={case} path={path} n={n} piece={w.piece_bytes}", flush=True)
+    check_backup_restore(w, n, path, stream)
+
+
+# 48 KiB head-major pieces: the only unit that tiles them without a tail is
+# 12 rounds of 4 KiB
+HND48K = Workload(name="hnd48k", outer=("layer", "kv", "page"), inner="HND", num_pages=40,
+                  num_layers=2, num_kv=2, page_size=16, num_heads=12, head_dim=128, dtype_bytes=2,
+                  pages_per_request=12, seed=204)
+
+# (case, largest unroll, cache policy, HND through LDS)
+VARIANTS = [
+    ("llama_small", 32, -1, -1), ("llama_small", 16, 0, -1), ("llama_small", 8, 3, -1),
+    ("llama_small", 4, 4, -1),
+    ("mla_small", 32, 7, -1), ("mla_small", 12, 5, -1),
+    ("trtllm_small", 32, 7, 0), ("trtllm_small", 16, 6, 1), ("trtllm_small", 8, 0, 1),
+    ("trtllm_small", 4, 1, 1),
+    ("hnd48k", 32, -1, -1), ("hnd48k", 16, 2, 1),
+    ("ragged_nhd", 32, 7, -1), ("ragged_hnd", 32, 7, 1),
+]
+
+
+@pytest.mark.parametrize("path", ["device", "zerocopy"])
+@pytest.mark.parametrize("case,unroll,policy,lds", VARIANTS)
+def test_kernel_variants(case, unroll, policy, lds, path, stream):
+    """Every unit size, cache policy and HND conversion form gives the
+    oracle's bytes."""
+    w, n = (HND48K, 12) if case == "hnd48k" else SMALL[case]
+    opts = {K.KVX_OPT_MAX_UNROLL: unroll, K.KVX_OPT_CACHE_POLICY: policy, K.KVX_OPT_HND_LDS: lds}
+    print(f"\n[variant] case={case} path={path} unroll<={unroll} policy={policy} lds={lds} "
+          f"piece={w.piece_bytes}", flush=True)
+    old = {o: K.kvx_get_option(o) for o in opts}
+    try:
+        for o, v in opts.items():
+            K.kvx_set_option(o, v)
+        check_backup_restore(w, n, path, stream)
+    finally:
+        for o, v in old.items():
+            K.kvx_set_option(o, v)
 
 
 @pytest.mark.parametrize("path", ["staged", "zerocopy"])
