@@ -42,8 +42,8 @@ PCIE_PEAK_GBS = 64.0      # MI355X host interface, PCIe 5.0 x16, published per-d
 # (FETCH_SIZE, WRITE_SIZE, scaled by a plain 2 GiB device copy in the same
 # run; see profiles/pack_kernel_llama8b.txt). Valid only for the kernel source
 # they were taken on: reported as null once kernels.hip changes.
-MEASURED_TRAFFIC = {"kernels_hip_sha256": "bd130b9709d0e7c949ef7285462171804803db2bb51d737ee70937d5db02f2a3",
-                    "bytes_per_launch": 4295172224}
+MEASURED_TRAFFIC = {"kernels_hip_sha256": "b6566eab6847ecadd8d70f0a64d5088af70f9b8ac68bfad65f88c9e3681aae36",
+                    "bytes_per_launch": 4295171559}
 
 
 def log(msg):

@@ -114,46 +114,35 @@ __device__ __forceinline__ uint32_t source_offset(const MoveArgs& a, uint32_t of
     }
 }
 
-// Moves one unit: the bytes [unit_base, unit_base + U * 4 KiB) of one piece.
-// A unit that lies wholly inside the piece (the wave-uniform common case)
-// runs without per-access predicates, so that all U loads are in flight
-// before the first store and the stores issue back to back; the last unit
-// of a piece whose size is not a multiple of the unit is predicated.
-// The destination resource (and the source one, when the layouts match)
-// starts at the unit and runs to the end of the piece, so each access's
-// offset is the lane's fixed part plus a per-round constant that the
-// instruction's immediate offset absorbs.
+// Moves one unit: the bytes [unit_base, unit_base + U * 4 KiB) of one piece,
+// without per-access predicates, so that all U loads are in flight before
+// the first store and the stores issue back to back. The destination
+// resource (and the source one, when the layouts match) starts at the unit
+// and ends with the piece: each access's offset is the lane's fixed part
+// plus a per-round constant that the instruction's immediate offset absorbs,
+// and in the last unit of a piece that the unit does not tile, the accesses
+// past the piece are dropped by the hardware's range check (loads read zero,
+// stores are discarded), so a partial unit runs the same code. Piece sizes
+// are multiples of 16 bytes, so no access straddles the end. Reordered
+// (HND<->NHD) sources span the whole piece; a dropped store may pair with
+// any in-range load.
 template <Dir D, int U, bool PERMUTE, int CP>
 __device__ __forceinline__ void move_unit(const MoveArgs& a, const uint8_t* src_piece,
                                           uint8_t* dst_piece, uint32_t unit_base, uint32_t tid)
 {
-    if (unit_base + a.chunk_bytes <= a.piece_bytes) {
-        const uint32_t rest = a.piece_bytes - unit_base;
-        const rsrc_t dst = piece_rsrc(dst_piece + unit_base, rest);
-        const rsrc_t src = PERMUTE ? piece_rsrc(src_piece, a.piece_bytes)
-                                   : piece_rsrc(src_piece + unit_base, rest);
-        const uint32_t lane_off = unit_vec<U>(tid, 0) * kVecBytes;
-        v4u v[U];
+    const uint32_t rest = a.piece_bytes - unit_base;
+    const rsrc_t dst = piece_rsrc(dst_piece + unit_base, rest);
+    const rsrc_t src = PERMUTE ? piece_rsrc(src_piece, a.piece_bytes)
+                               : piece_rsrc(src_piece + unit_base, rest);
+    const uint32_t lane_off = unit_vec<U>(tid, 0) * kVecBytes;
+    v4u v[U];
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            const uint32_t off = lane_off + u * (64u * kVecBytes);
-            v[u] = load16<CP>(src, PERMUTE ? source_offset<D, true>(a, unit_base + off) : off);
-        }
-#pragma unroll
-        for (int u = 0; u < U; u++) store16<CP>(dst, lane_off + u * (64u * kVecBytes), v[u]);
-    } else {
-        // ragged tail of a piece: one predicated vector at a time (rare; kept
-        // small so it does not raise the kernel's register count)
-        const rsrc_t dst = piece_rsrc(dst_piece, a.piece_bytes);
-        const rsrc_t src = piece_rsrc(src_piece, a.piece_bytes);
-        const uint32_t base = unit_base + tid * kVecBytes;
-#pragma unroll 1
-        for (int u = 0; u < U; u++) {
-            const uint32_t off = base + u * (kThreads * kVecBytes);
-            if (off < a.piece_bytes)
-                store16<CP>(dst, off, load16<CP>(src, source_offset<D, PERMUTE>(a, off)));
-        }
+    for (int u = 0; u < U; u++) {
+        const uint32_t off = lane_off + u * (64u * kVecBytes);
+        v[u] = load16<CP>(src, PERMUTE ? source_offset<D, true>(a, unit_base + off) : off);
     }
+#pragma unroll
+    for (int u = 0; u < U; u++) store16<CP>(dst, lane_off + u * (64u * kVecBytes), v[u]);
 }
 
 // Counts `units` finished units of layer l. Every lane first makes its own
@@ -246,15 +235,9 @@ __global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
     const uint32_t cpp = a.chunks_per_piece;
     int32_t pend_layer = -1;   // PUBLISH: layer of the units finished but not yet counted
     uint32_t pend = 0;
-    // Workgroups are dispatched round-robin over the 8 XCDs (block b runs on
-    // XCD b mod 8). With XCD ordering, the workgroups of one XCD take
-    // consecutive unit numbers in every round of the loop, so each XCD walks
-    // whole pieces instead of one fixed chunk offset of many pieces.
-    uint32_t v = blockIdx.x;
-    if ((a.unit_order & 1u) && (gridDim.x & 7u) == 0)
-        v = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-    for (uint32_t q = v; q < a.total_units; q += gridDim.x) {
-        // unit q -> (layer, kv, pair, chunk); all wave-uniform scalar math
+    // unit q -> (layer, kv, pair, chunk), all wave-uniform scalar math, then
+    // the move
+    auto do_unit = [&](uint32_t q) {
         const uint32_t pu = q / cpp;
         uint32_t k = q - pu * cpp;
         const uint32_t lc = pu / a.npairs;
@@ -295,6 +278,47 @@ __global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
             move_unit<D, U, PERM == 1, CP>(a, src, dst, k * a.chunk_bytes, tid);
         }
         if constexpr (PUBLISH) pend++;
+    };
+
+    if constexpr (PUBLISH) {
+        // Units come from a queue in number order, so every unit of layer l
+        // is handed out before any of layer l + 1 and a workgroup that runs
+        // slowly (measured: reads of pinned host memory are not served
+        // evenly across workgroups) holds back at most the unit it is on.
+        // Lane 0 draws the next number while the workgroup moves the current
+        // unit; two LDS slots alternate so one barrier per unit suffices.
+        // Each workgroup stops at its first draw past the end, so the
+        // total_units + gridDim.x - 1 draw is the last one of the launch:
+        // whoever makes it resets the queue for the next launch.
+        __shared__ uint32_t next[2];
+        const uint32_t last_draw = a.total_units + gridDim.x - 1;
+        if (tid == 0) {
+            const uint32_t d = __hip_atomic_fetch_add(a.queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (d == last_draw) __hip_atomic_store(a.queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            next[0] = d;
+        }
+        __syncthreads();
+        uint32_t q = next[0];
+        for (uint32_t it = 1; q < a.total_units; it++) {
+            uint32_t d = 0;
+            if (tid == 0) d = __hip_atomic_fetch_add(a.queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            do_unit(q);
+            if (tid == 0) {
+                if (d == last_draw) __hip_atomic_store(a.queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                next[it & 1u] = d;
+            }
+            __syncthreads();
+            q = next[it & 1u];
+        }
+    } else {
+        // Workgroups are dispatched round-robin over the 8 XCDs (block b runs
+        // on XCD b mod 8). With XCD ordering, the workgroups of one XCD take
+        // consecutive unit numbers in every round of the loop, so each XCD
+        // walks whole pieces instead of one fixed chunk offset of many pieces.
+        uint32_t v = blockIdx.x;
+        if ((a.unit_order & 1u) && (gridDim.x & 7u) == 0)
+            v = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
+        for (uint32_t q = v; q < a.total_units; q += gridDim.x) do_unit(q);
     }
     if constexpr (PUBLISH) {
         if (pend) count_units(a, pend_layer, pend, tid);
@@ -329,20 +353,20 @@ uint32_t magic_u32(uint32_t d)
     return static_cast<uint32_t>((uint64_t(1) << 32) / d + 1);
 }
 
-int pick_unroll(int64_t piece_bytes, int max_unroll)
+int pick_unroll(int64_t piece_bytes, int max_unroll, int forced)
 {
-    // the largest power-of-two unit (U vector rounds of 4 KiB) that tiles the
-    // piece exactly, else 12, 6 or 3 rounds (measured: 128 KiB pieces move
-    // fastest as one 128 KiB unit, a 144 KiB piece faster in 16 KiB units
-    // than in 36, 48, 72 or 144 KiB ones); pieces that are not a multiple of
-    // 4 KiB get the largest unit that fits and a predicated tail
-    const int64_t step = kThreads * kVecBytes;
-    for (int u : {32, 16, 8, 4, 12, 6, 3, 2})
-        if (u <= max_unroll && piece_bytes % (step * u) == 0) return u;
-    if (piece_bytes % step == 0) return 1;
-    for (int u : {16, 8, 4})
-        if (u <= max_unroll && piece_bytes >= u * step) return u;
-    return 1;
+    if (forced > 0) return forced;
+    // the largest power-of-two unit, up to 32 rounds of 4 KiB, that fits in
+    // the piece; what is left of the piece forms one partial unit. Measured
+    // on MI355X (HBM to HBM): 128 KiB pieces move fastest as one 128 KiB
+    // unit (6.3 TB/s against 6.1 in 64 KiB units and 5.3-5.6 in 32 or 48
+    // KiB units); 144 KiB pieces as 128 KiB plus 16 KiB (5.6 TB/s both ways)
+    // rather than nine exact 16 KiB units (5.0 unpack) or three of 48 KiB
+    // (5.0); 64 KiB head-major pieces as one 64 KiB unit
+    const int64_t rounds = piece_bytes / (kThreads * kVecBytes);
+    int u = 1;
+    while (u < 32 && 2 * u <= max_unroll && 2 * u <= rounds) u *= 2;
+    return u;
 }
 
 namespace {

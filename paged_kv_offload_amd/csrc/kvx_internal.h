@@ -72,6 +72,7 @@ struct Tuning {
     int64_t host_grid_max = 0;            // 0 = auto
     int64_t unit_order = -1;              // MoveArgs::unit_order bits, -1 = auto
     int64_t max_unroll = 32;              // largest 16-byte vectors per lane per unit
+    int64_t unit_rounds = 0;              // 0 = auto; else the unit's vector rounds
     int64_t staged_dma_on_caller = 0;     // staged DMA on the caller's stream instead of a side stream
     int64_t hnd_lds = -1;                 // HND<->NHD through LDS: 1 both, 0 never, -1 scatter only
 };
@@ -108,12 +109,14 @@ struct MoveArgs {
     uint32_t TU, seg, mg_seg;            // LDS token blocks: tokens per unit, TU * row_vec
     // per-layer publish (RESTORE with a ready object)
     uint32_t* layer_done;    // device counters, indexed by absolute layer
+    uint32_t* queue;         // publishing kernels: next unit number (zero between launches)
     uint32_t* ready;         // device view of counts + slot_base, indexed by layer
     uint32_t layer_target;   // work units of one layer over the whole call
     uint32_t publish_value;  // n
     uint32_t unit_order;     // bit 0: XCD-contiguous unit numbering; bit 1: rotate chunks
     int32_t pairs[2 * kMaxPairs];
 };
+static_assert(sizeof(MoveArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
 struct LaunchCfg {
     int unroll;        // 16-byte vectors per lane per unit: 1, 2, 4, 8 or 16
@@ -124,7 +127,8 @@ struct LaunchCfg {
 };
 
 uint32_t magic_u32(uint32_t d);   // multiplier for exact x / d with x * d < 2^32
-int pick_unroll(int64_t piece_bytes, int max_unroll);
+// unit rounds for a piece: `forced` (> 0) if given, else the measured choice
+int pick_unroll(int64_t piece_bytes, int max_unroll, int forced);
 hipError_t launch_move(Dir dir, const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s);
 hipError_t launch_ready_wait(const uint32_t* slot, uint32_t min_count, uint32_t spin_limit,
                              int32_t* status, hipStream_t s);

@@ -103,27 +103,31 @@ HND48K = Workload(name="hnd48k", outer=("layer", "kv", "page"), inner="HND", num
                   num_layers=2, num_kv=2, page_size=16, num_heads=12, head_dim=128, dtype_bytes=2,
                   pages_per_request=12, seed=204)
 
-# (case, largest unroll, cache policy, HND through LDS)
+# (case, largest unroll, forced unit rounds, cache policy, HND through LDS);
+# forced units that do not tile the piece leave a partial last unit whose
+# accesses past the piece the hardware drops
 VARIANTS = [
-    ("llama_small", 32, -1, -1), ("llama_small", 16, 0, -1), ("llama_small", 8, 3, -1),
-    ("llama_small", 4, 4, -1),
-    ("mla_small", 32, 7, -1), ("mla_small", 12, 5, -1),
-    ("trtllm_small", 32, 7, 0), ("trtllm_small", 16, 6, 1), ("trtllm_small", 8, 0, 1),
-    ("trtllm_small", 4, 1, 1),
-    ("hnd48k", 32, -1, -1), ("hnd48k", 16, 2, 1),
-    ("ragged_nhd", 32, 7, -1), ("ragged_hnd", 32, 7, 1),
+    ("llama_small", 32, 0, -1, -1), ("llama_small", 16, 0, 0, -1), ("llama_small", 8, 0, 3, -1),
+    ("llama_small", 4, 0, 4, -1), ("llama_small", 32, 12, 7, -1), ("llama_small", 32, 3, 7, -1),
+    ("mla_small", 32, 0, 7, -1), ("mla_small", 12, 0, 5, -1), ("mla_small", 32, 32, 7, -1),
+    ("mla_small", 32, 16, 6, -1),
+    ("trtllm_small", 32, 0, 7, 0), ("trtllm_small", 16, 0, 6, 1), ("trtllm_small", 8, 0, 0, 1),
+    ("trtllm_small", 4, 0, 1, 1), ("trtllm_small", 32, 32, 7, 0), ("trtllm_small", 32, 12, 7, 1),
+    ("hnd48k", 32, 0, -1, -1), ("hnd48k", 16, 0, 2, 1), ("hnd48k", 32, 16, 7, 1),
+    ("ragged_nhd", 32, 0, 7, -1), ("ragged_hnd", 32, 0, 7, 1), ("ragged_hnd", 32, 2, 7, 0),
 ]
 
 
 @pytest.mark.parametrize("path", ["device", "zerocopy"])
-@pytest.mark.parametrize("case,unroll,policy,lds", VARIANTS)
-def test_kernel_variants(case, unroll, policy, lds, path, stream):
-    """Every unit size, cache policy and HND conversion form gives the
-    oracle's bytes."""
+@pytest.mark.parametrize("case,unroll,rounds,policy,lds", VARIANTS)
+def test_kernel_variants(case, unroll, rounds, policy, lds, path, stream):
+    """Every unit size (including partial last units), cache policy and HND
+    conversion form gives the oracle's bytes."""
     w, n = (HND48K, 12) if case == "hnd48k" else SMALL[case]
-    opts = {K.KVX_OPT_MAX_UNROLL: unroll, K.KVX_OPT_CACHE_POLICY: policy, K.KVX_OPT_HND_LDS: lds}
-    print(f"\n[variant] case={case} path={path} unroll<={unroll} policy={policy} lds={lds} "
-          f"piece={w.piece_bytes}", flush=True)
+    opts = {K.KVX_OPT_MAX_UNROLL: unroll, K.KVX_OPT_UNIT_ROUNDS: rounds,
+            K.KVX_OPT_CACHE_POLICY: policy, K.KVX_OPT_HND_LDS: lds}
+    print(f"\n[variant] case={case} path={path} unroll<={unroll} rounds={rounds} policy={policy} "
+          f"lds={lds} piece={w.piece_bytes}", flush=True)
     old = {o: K.kvx_get_option(o) for o in opts}
     try:
         for o, v in opts.items():
