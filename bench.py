@@ -76,6 +76,18 @@ def main():
                                    "measures one GPU (run with --gpus 1)"}), flush=True)
         sys.exit(2)
 
+    if args.all_workloads:
+        # The mixed leg keeps four requests in flight on four streams. HIP
+        # gives a process 4 hardware queues by default and streams share
+        # them round-robin; with the default stream that is five streams, so
+        # two requests would share a queue and run one after the other.
+        try:
+            queues = int(os.environ.get("GPU_MAX_HW_QUEUES", "4"))
+        except ValueError:
+            queues = 4
+        if queues < 8:
+            os.environ["GPU_MAX_HW_QUEUES"] = "8"   # read by the HIP runtime when torch loads it
+
     import numpy as np
     import torch
 
@@ -514,7 +526,27 @@ def all_workloads():
     torch.cuda.synchronize()
     sched = mixed_schedule(w, 128)
     res = {"workload": w.description, "requests": 128, "in_flight": 4,
-           "bytes_total": 128 * P, "unit": "GB/s"}
+           "bytes_total": 128 * P, "unit": "GB/s",
+           "hw_queues": os.environ.get("GPU_MAX_HW_QUEUES", "runtime default")}
+    # both directions at once with plain copies: the peak the mixed stream is
+    # measured against
+    GiB = 1 << 30
+    pin_a = torch.empty(GiB, dtype=torch.uint8, pin_memory=True)
+    pin_b = torch.empty(GiB, dtype=torch.uint8, pin_memory=True)
+    dev_a = torch.empty(GiB, dtype=torch.uint8, device="cuda")
+    dev_b = torch.empty(GiB, dtype=torch.uint8, device="cuda")
+    bid = []
+    for _ in range(4):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(streams[0]):
+            pin_a.copy_(dev_a, non_blocking=True)
+        with torch.cuda.stream(streams[1]):
+            dev_b.copy_(pin_b, non_blocking=True)
+        torch.cuda.synchronize()
+        bid.append(2 * GiB / (time.perf_counter() - t0) / GB)
+    del pin_a, pin_b, dev_a, dev_b
+    res["memcpy_both_directions_gbs"] = round(statistics.median(bid[1:]), 2)
     for name, bpath, rpath in (("zerocopy", K.KVX_PATH_ZEROCOPY, K.KVX_PATH_ZEROCOPY),
                                ("staged", K.KVX_PATH_STAGED, K.KVX_PATH_STAGED),
                                ("zerocopy_backup_staged_restore", K.KVX_PATH_ZEROCOPY,
@@ -535,6 +567,8 @@ def all_workloads():
         t0 = time.perf_counter()
         run()
         res[name] = round(128 * P / (time.perf_counter() - t0) / GB, 2)
+        res[name + "_frac_of_memcpy_both_directions"] = round(
+            res[name] / res["memcpy_both_directions_gbs"], 4)
         log(f"mixed {name}: {res[name]} GB/s")
     print(json.dumps({"mixed": res}), flush=True)
     for h in slots:

@@ -116,7 +116,9 @@ struct DeviceGuard {
 struct Lane {
     int device = -1;
     hipStream_t caller = nullptr;
-    hipStream_t side = nullptr;     // library-owned, default priority
+    hipStream_t side = nullptr;     // library-owned, default priority; created by the first
+                                    // staged operation (a HIP process has few hardware queues,
+                                    // and every stream takes a share of one)
     int cu_count = 0;
     uint8_t* ring = nullptr;        // device staging ring
     int64_t slot_bytes = 0;
@@ -137,7 +139,6 @@ std::map<std::pair<int, hipStream_t>, Lane*> g_lanes;
 int lane_init(Lane* L)
 {
     KVX_HIP(hipDeviceGetAttribute(&L->cu_count, hipDeviceAttributeMultiprocessorCount, L->device));
-    KVX_HIP(hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking));
     KVX_HIP(hipEventCreateWithFlags(&L->ev_start, hipEventDisableTiming));
     KVX_HIP(hipEventCreateWithFlags(&L->ev_done, hipEventDisableTiming));
     return KVX_OK;
@@ -564,6 +565,8 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
         }
         // DMA on the library's side stream (overlaps the next chunk's kernel)
         // or on the caller's stream (stream order alone; no cross-stream events)
+        if (!t.staged_dma_on_caller && !L->side)
+            KVX_HIP(hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking));
         hipStream_t dma = t.staged_dma_on_caller ? s : L->side;
         const bool split = dma != s;
         if (dir == SCATTER && split) {
