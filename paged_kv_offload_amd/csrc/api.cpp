@@ -92,23 +92,7 @@ Tuning tuning()
     return g_tune;
 }
 
-// ---------------------------------------------------------------------------
-// device guard
-// ---------------------------------------------------------------------------
 namespace {
-struct DeviceGuard {
-    int prev = -1;
-    bool changed = false;
-    explicit DeviceGuard(int dev)
-    {
-        if (hipGetDevice(&prev) == hipSuccess && prev != dev)
-            changed = (hipSetDevice(dev) == hipSuccess);
-    }
-    ~DeviceGuard()
-    {
-        if (changed) (void)hipSetDevice(prev);
-    }
-};
 
 // ---------------------------------------------------------------------------
 // lanes: per (device, caller stream) state of the executor
@@ -267,6 +251,16 @@ int resolve_device(kvx_pool* pool)
     if (pool->device >= 0) return KVX_OK;
     hipPointerAttribute_t at;
     std::memset(&at, 0, sizeof at);
+    // a mapping imported with kvx_ipc_import is known by its registry entry
+    int ipc_dev = -1;
+    uint64_t ipc_after = 0;
+    if (ipc_lookup(pool->start, &ipc_dev, &ipc_after)) {
+        if (static_cast<uint64_t>(pool->geom.pool_bytes) > ipc_after)
+            return fail(KVX_E_RANGE, "pool (" + std::to_string(pool->geom.pool_bytes) +
+                                         " bytes) extends past the end of its imported allocation");
+        pool->device = ipc_dev;
+        return KVX_OK;
+    }
     hipError_t e = hipPointerGetAttributes(&at, pool->start);
     if (e != hipSuccess || at.type != hipMemoryTypeDevice) {
         (void)hipGetLastError();

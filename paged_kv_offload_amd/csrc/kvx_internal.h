@@ -126,6 +126,25 @@ struct LaunchCfg {
     int grid;
 };
 
+// Makes `dev` current for the guard's lifetime.
+struct DeviceGuard {
+    int prev = -1;
+    bool changed = false;
+    explicit DeviceGuard(int dev)
+    {
+        if (hipGetDevice(&prev) == hipSuccess && prev != dev)
+            changed = (hipSetDevice(dev) == hipSuccess);
+    }
+    ~DeviceGuard()
+    {
+        if (changed) (void)hipSetDevice(prev);
+    }
+};
+
+// True if `p` lies in a mapping imported with kvx_ipc_import; then *device is
+// its GPU and *bytes_after the mapping's bytes from p to its end.
+bool ipc_lookup(const void* p, int* device, uint64_t* bytes_after);
+
 uint32_t magic_u32(uint32_t d);   // multiplier for exact x / d with x * d < 2^32
 // unit rounds for a piece: `forced` (> 0) if given, else the measured choice
 int pick_unroll(int64_t piece_bytes, int max_unroll, int forced);

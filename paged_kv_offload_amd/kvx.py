@@ -54,6 +54,12 @@ class kvx_pool_info(ctypes.Structure):
                                                "generation")]
 
 
+class kvx_ipc_handle(ctypes.Structure):
+    _fields_ = [("mem_handle", ctypes.c_uint8 * 64), ("device_uuid", ctypes.c_uint8 * 16),
+                ("alloc_bytes", ctypes.c_uint64), ("offset", ctypes.c_uint64),
+                ("version", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
 # (name, restype, argtypes) of every exported function
 _vp, _i32, _u32, _i64, _u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_int64, \
     ctypes.c_uint64
@@ -83,6 +89,9 @@ SIGNATURES = [
     ("kvx_version", ctypes.c_int, []),
     ("kvx_set_option", ctypes.c_int, [_i32, _i64]),
     ("kvx_get_option", ctypes.c_int, [_i32, _P(_i64)]),
+    ("kvx_ipc_export", ctypes.c_int, [_vp, _P(kvx_ipc_handle)]),
+    ("kvx_ipc_import", ctypes.c_int, [_P(kvx_ipc_handle), _P(_vp), _P(_i32)]),
+    ("kvx_ipc_close", ctypes.c_int, [_vp]),
 ]
 
 _lib: Optional[ctypes.CDLL] = None
@@ -209,6 +218,60 @@ def kvx_alloc_range(ptr: int):
     base, size = _vp(), _u64()
     _check(lib().kvx_alloc_range(ptr, ctypes.byref(base), ctypes.byref(size)))
     return base.value, size.value
+
+
+# ---------------------------------------------------------------------------
+# device-memory IPC
+# ---------------------------------------------------------------------------
+def kvx_ipc_export(device_ptr: int) -> bytes:
+    """Handle of the allocation holding device_ptr, as bytes to send to
+    another process."""
+    h = kvx_ipc_handle()
+    _check(lib().kvx_ipc_export(device_ptr, ctypes.byref(h)))
+    return bytes(h)
+
+
+def ipc_handle_from_bytes(data: bytes) -> kvx_ipc_handle:
+    if len(data) != ctypes.sizeof(kvx_ipc_handle):
+        raise KvxError(KVX_E_INVAL, f"an IPC handle is {ctypes.sizeof(kvx_ipc_handle)} bytes, "
+                                    f"got {len(data)}")
+    return kvx_ipc_handle.from_buffer_copy(data)
+
+
+def kvx_ipc_import(data: bytes):
+    """Maps an exported allocation: returns (base, device ordinal, byte
+    offset of the exported pointer, allocation bytes)."""
+    h = ipc_handle_from_bytes(data)
+    base, dev = _vp(), _i32()
+    _check(lib().kvx_ipc_import(ctypes.byref(h), ctypes.byref(base), ctypes.byref(dev)))
+    return base.value, dev.value, h.offset, h.alloc_bytes
+
+
+def kvx_ipc_close(base: int) -> None:
+    _check(lib().kvx_ipc_close(base))
+
+
+def dense_strides(shape: Sequence[int]) -> list:
+    st, acc = [], 1
+    for d in reversed(list(shape)):
+        st.append(acc)
+        acc *= d
+    return st[::-1]
+
+
+def register_imported(data: bytes, layout: kvx_layout, dtype_bytes: int, shape: Sequence[int],
+                      generation: int):
+    """Imports a pool exported by another process and registers it with the
+    given layout and dense shape. Returns (pool handle, mapping base); the
+    base goes to kvx_ipc_close after the pool is unregistered."""
+    base, _, offset, _ = kvx_ipc_import(data)
+    try:
+        pool = kvx_register_pool(layout, base, offset, dtype_bytes, list(shape),
+                                 dense_strides(shape), generation)
+    except KvxError:
+        kvx_ipc_close(base)
+        raise
+    return pool, base
 
 
 def permute_to_dense_view(t):

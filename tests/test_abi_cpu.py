@@ -222,3 +222,52 @@ def test_options_roundtrip():
     with pytest.raises(kvx.KvxError):
         K.kvx_set_option(99, 1)
     assert "unknown option" in K.kvx_last_error()
+
+
+def test_ipc_handle_layout_matches_the_header(tmp_path):
+    """The binding's kvx_ipc_handle has the C struct's size and field
+    offsets (compiled from include/kvx.h with gcc)."""
+    import ctypes
+    import subprocess
+    src = tmp_path / "h.c"
+    src.write_text('#include <stddef.h>\n#include <stdio.h>\n#include "kvx.h"\n'
+                   'int main(void) { printf("%zu %zu %zu %zu %zu %zu %zu\\n", sizeof(kvx_ipc_handle), '
+                   'offsetof(kvx_ipc_handle, mem_handle), offsetof(kvx_ipc_handle, device_uuid), '
+                   'offsetof(kvx_ipc_handle, alloc_bytes), offsetof(kvx_ipc_handle, offset), '
+                   'offsetof(kvx_ipc_handle, version), offsetof(kvx_ipc_handle, reserved)); return 0; }\n')
+    exe = tmp_path / "h"
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    str(src), "-o", str(exe)], check=True)
+    c = [int(x) for x in subprocess.run([str(exe)], check=True, capture_output=True,
+                                        text=True).stdout.split()]
+    H = K.kvx_ipc_handle
+    py = [ctypes.sizeof(H)] + [getattr(H, f).offset for f in
+                               ("mem_handle", "device_uuid", "alloc_bytes", "offset", "version",
+                                "reserved")]
+    assert c == py == [104, 0, 64, 80, 88, 96, 100]
+
+
+def test_ipc_import_and_close_validate_before_any_gpu_call():
+    """Malformed or oversized handles and unknown bases are refused by
+    validation alone (no HIP call is reached)."""
+    h = K.kvx_ipc_handle()
+    h.version, h.alloc_bytes, h.offset = 1, 1 << 20, 0
+    good = bytes(h)
+    for field, value, code in (("version", 0, K.KVX_E_INVAL), ("reserved", 1, K.KVX_E_INVAL),
+                               ("alloc_bytes", 0, K.KVX_E_INVAL),
+                               ("offset", 1 << 20, K.KVX_E_INVAL),
+                               ("alloc_bytes", (2 << 30) + 4096, K.KVX_E_RANGE)):
+        bad = K.kvx_ipc_handle.from_buffer_copy(good)
+        setattr(bad, field, value)
+        with pytest.raises(K.KvxError) as e:
+            K.kvx_ipc_import(bytes(bad))
+        assert e.value.code == code, (field, value)
+    with pytest.raises(K.KvxError) as e:
+        K.kvx_ipc_import(good[:-1])
+    assert e.value.code == K.KVX_E_INVAL
+    with pytest.raises(K.KvxError) as e:
+        K.kvx_ipc_close(FAKE_BASE)
+    assert e.value.code == K.KVX_E_INVAL
+    with pytest.raises(K.KvxError) as e:
+        K.kvx_ipc_export(0)
+    assert e.value.code == K.KVX_E_INVAL

@@ -199,6 +199,45 @@ def test_staged_chunking_by_slot_range(sort_pages, stream):
 
 
 @pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("case", ["ragged_hnd", "llama_small", "mla_small", "trtllm_small"])
+def test_publishing_restore_parity(case, path, stream):
+    """Restores that publish take their work units from a queue that each
+    launch leaves reset for the next: two restores in a row on one stream
+    (ragged_hnd's 500 pages take two launches per layer range) must write
+    exactly the oracle's bytes and publish every layer."""
+    w, n = SMALL[case]
+    print(f"\n[publish-parity] case={case} path={path} n={n}", flush=True)
+    L = oracle_layout(w)
+    pool = DevicePool(w, seed=305, generation=6)
+    img = pool.host_image()
+    perm = synth.page_perm(w.seed + 7, w.num_pages)
+    nb = w.host_bytes(n)
+    ready = K.kvx_ready_create(w.num_layers, 6)
+    pks = []
+    try:
+        want = img
+        for r in range(2):
+            dst = perm[r * n:(r + 1) * n].copy()
+            pk = Packed(w, n, path, fill_seed=w.seed + 10 + r)
+            pks.append(pk)
+            hbytes = synth.gen_bytes(w.seed + 10 + r, 0, nb)
+            want = oracle.restore(L, want, hbytes, dst, 0, w.num_layers)
+            # no host synchronisation between the two: the second launch
+            # depends on the queue the first one left reset
+            K.kvx_restore(pool.handle, pk.ptr, nb, dst, 0, w.num_layers, ready, 0, stream,
+                          PATHS[path])
+        K.kvx_sync(stream)
+        assert [K.kvx_layer_ready(ready, s) for s in range(w.num_layers)] == [n] * w.num_layers
+        after = pool.host_image()
+        assert np.array_equal(after, want), diff_report(after, want)
+    finally:
+        K.kvx_ready_destroy(ready)
+        for pk in pks:
+            pk.close()
+        pool.close()
+
+
+@pytest.mark.parametrize("path", list(PATHS))
 def test_restore_publishes_every_layer(path, stream):
     w, n = SMALL["mla_small"]
     pool = DevicePool(w, seed=303, generation=4)
