@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <iterator>
 #include <set>
 
 #include "kvx_internal.h"
@@ -314,6 +315,55 @@ int unroll_for(const PoolGeom& g, const Tuning& t, bool host)
     return pick_unroll(g.piece_bytes, max_unroll, static_cast<int>(t.unit_rounds));
 }
 
+// Unit geometry of launches on `pool`; sets cfg.unroll and cfg.permute.
+void setup_geom(const kvx_pool* pool, bool host, const Tuning& t, UnitGeom* ug, LaunchCfg* cfg)
+{
+    const PoolGeom& g = pool->geom;
+    std::memset(ug, 0, sizeof *ug);
+    cfg->permute = ((g.inner == KVX_HND) && g.num_heads > 1 && g.page_size > 1) ? 1 : 0;
+    // HND<->NHD through LDS token blocks unless switched off (measured on the
+    // TRT-LLM-shaped pool with equal counter traffic: 64 KiB token blocks
+    // pack at 6.30 TB/s against 5.93 row by row, and unpack at 5.96 against
+    // 5.71)
+    const bool lds = cfg->permute && t.hnd_lds != 0;
+    cfg->unroll = unroll_for(g, t, host);
+    ug->pool = pool->start;
+    ug->page_stride = g.page_stride;
+    ug->layer_stride = g.layer_stride;
+    ug->kv_stride = g.kv_stride;
+    ug->piece_bytes = static_cast<uint32_t>(g.piece_bytes);
+    ug->chunk_bytes = static_cast<uint32_t>(kThreads * kVecBytes * cfg->unroll);
+    ug->chunks_per_piece = static_cast<uint32_t>((g.piece_bytes + ug->chunk_bytes - 1) / ug->chunk_bytes);
+    ug->num_kv = static_cast<uint32_t>(g.num_kv);
+    ug->T = static_cast<uint32_t>(g.page_size);
+    ug->H = static_cast<uint32_t>(g.num_heads);
+    ug->row_vec = static_cast<uint32_t>(g.row_bytes / kVecBytes);
+    ug->mg_row_vec = magic_u32(ug->row_vec);
+    ug->mg_H = magic_u32(ug->H);
+    ug->mg_T = magic_u32(ug->T);
+    if (lds && (cfg->unroll == 4 || cfg->unroll == 8 || cfg->unroll == 16)) {
+        // an LDS unit is a block of whole tokens over all heads
+        const int64_t block = g.num_heads * g.row_bytes;
+        if (ug->chunk_bytes % block == 0 && g.page_size % (ug->chunk_bytes / block) == 0) {
+            cfg->permute = 2;
+            ug->TU = static_cast<uint32_t>(ug->chunk_bytes / block);
+            ug->seg = ug->TU * ug->row_vec;
+            ug->mg_seg = magic_u32(ug->seg);
+        }
+    }
+}
+
+void set_publish(const Publish* pub, PublishArgs* p)
+{
+    std::memset(p, 0, sizeof *p);
+    if (!pub) return;
+    p->layer_done = pub->layer_done;
+    p->queue = pub->queue;
+    p->ready = pub->ready;
+    p->layer_target = pub->layer_target;
+    p->publish_value = pub->value;
+}
+
 int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, int32_t lb,
                  const PageSlot* pairs, size_t npairs, const Publish* pub, const Tuning& t,
                  int cu_count, hipStream_t s)
@@ -322,13 +372,8 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
     MoveArgs a;
     std::memset(&a, 0, sizeof a);
     LaunchCfg cfg;
-    cfg.permute = ((g.inner == KVX_HND) && g.num_heads > 1 && g.page_size > 1) ? 1 : 0;
-    // HND<->NHD through LDS token blocks unless switched off (measured on the
-    // TRT-LLM-shaped pool with equal counter traffic: 64 KiB token blocks
-    // pack at 6.30 TB/s against 5.93 row by row, and unpack at 5.96 against
-    // 5.71)
-    const bool lds = cfg.permute && t.hnd_lds != 0;
-    cfg.unroll = unroll_for(g, t, tg.host);
+    cfg.host_link = tg.host;
+    setup_geom(pool, tg.host, t, &a.g, &cfg);
     cfg.publish = pub != nullptr;
     // cache policy (measured on MI355X): HBM to HBM, non-temporal loads and
     // non-temporal device-scope stores; into pinned host memory, non-temporal
@@ -336,41 +381,11 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
     int cp = 7;
     if (tg.host) cp = (dir == GATHER) ? 5 : 6;
     cfg.cache_policy = t.cache_policy >= 0 ? static_cast<int>(t.cache_policy) : cp;
-    a.pool = pool->start;
-    a.packed = tg.packed;
-    a.page_stride = g.page_stride;
-    a.layer_stride = g.layer_stride;
-    a.kv_stride = g.kv_stride;
-    a.pk_lc_stride = tg.pk_slots * g.piece_bytes;
-    a.pk_layer0 = tg.pk_layer0;
-    a.pk_slot0 = tg.pk_slot0;
-    a.piece_bytes = static_cast<uint32_t>(g.piece_bytes);
-    a.chunk_bytes = static_cast<uint32_t>(kThreads * kVecBytes * cfg.unroll);
-    a.chunks_per_piece = static_cast<uint32_t>((g.piece_bytes + a.chunk_bytes - 1) / a.chunk_bytes);
-    a.num_kv = static_cast<uint32_t>(g.num_kv);
-    a.T = static_cast<uint32_t>(g.page_size);
-    a.H = static_cast<uint32_t>(g.num_heads);
-    a.row_vec = static_cast<uint32_t>(g.row_bytes / kVecBytes);
-    a.mg_row_vec = magic_u32(a.row_vec);
-    a.mg_H = magic_u32(a.H);
-    a.mg_T = magic_u32(a.T);
-    if (lds && (cfg.unroll == 4 || cfg.unroll == 8 || cfg.unroll == 16)) {
-        // an LDS unit is a block of whole tokens over all heads
-        const int64_t block = g.num_heads * g.row_bytes;
-        if (a.chunk_bytes % block == 0 && g.page_size % (a.chunk_bytes / block) == 0) {
-            cfg.permute = 2;
-            a.TU = static_cast<uint32_t>(a.chunk_bytes / block);
-            a.seg = a.TU * a.row_vec;
-            a.mg_seg = magic_u32(a.seg);
-        }
-    }
-    if (pub) {
-        a.layer_done = pub->layer_done;
-        a.queue = pub->queue;
-        a.ready = pub->ready;
-        a.layer_target = pub->layer_target;
-        a.publish_value = pub->value;
-    }
+    a.s.packed = tg.packed;
+    a.s.pk_lc_stride = tg.pk_slots * g.piece_bytes;
+    a.s.pk_layer0 = tg.pk_layer0;
+    a.s.pk_slot0 = tg.pk_slot0;
+    set_publish(pub, &a.p);
     const int64_t limit = (int64_t(1) << 31) - 1;
     for (size_t p0 = 0; p0 < npairs; p0 += kMaxPairs) {
         const size_t np = std::min<size_t>(kMaxPairs, npairs - p0);
@@ -378,14 +393,14 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
             a.pairs[2 * j] = pairs[p0 + j].page;
             a.pairs[2 * j + 1] = pairs[p0 + j].slot;
         }
-        a.npairs = static_cast<uint32_t>(np);
-        const int64_t per_layer = g.num_kv * static_cast<int64_t>(np) * a.chunks_per_piece;
+        a.s.npairs = static_cast<uint32_t>(np);
+        const int64_t per_layer = g.num_kv * static_cast<int64_t>(np) * a.g.chunks_per_piece;
         if (per_layer > limit) return fail(KVX_E_INVAL, "one layer of this call has too many work units");
         const int32_t step = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(lb - la, limit / per_layer)));
         for (int32_t l = la; l < lb; l += step) {
             const int32_t nl = std::min(step, lb - l);
-            a.layer_begin = l;
-            a.total_units = static_cast<uint32_t>(per_layer * nl);
+            a.s.layer_begin = l;
+            a.s.total_units = static_cast<uint32_t>(per_layer * nl);
             // Grid policy, all measured on MI355X:
             //  - a kernel streaming over the host link needs only a few
             //    workgroups (32 x 32 KiB in flight covers the link's round
@@ -404,15 +419,15 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
                 gmax = t.host_grid_max > 0 ? t.host_grid_max : kHostGridAuto;
             } else if (pub) {
                 gmax = std::min<int64_t>(int64_t(cu_count) * 8, std::max<int64_t>(cu_count, per_layer / 4));
-            } else if (a.chunk_bytes >= (32u << 10)) {
-                gmax = a.total_units;
+            } else if (a.g.chunk_bytes >= (32u << 10)) {
+                gmax = a.s.total_units;
                 order = 3;
             } else {
                 gmax = int64_t(cu_count) * 32;
             }
             if (t.unit_order >= 0) order = static_cast<uint32_t>(t.unit_order);
-            a.unit_order = order;
-            int64_t grid = std::max<int64_t>(1, std::min<int64_t>(a.total_units, gmax));
+            a.g.unit_order = order;
+            int64_t grid = std::max<int64_t>(1, std::min<int64_t>(a.s.total_units, gmax));
             if ((order & 1u) && grid > 8) grid &= ~int64_t(7);   // whole rounds of 8 XCDs
             cfg.grid = static_cast<int>(grid);
             hipError_t e = launch_move(dir, cfg, a, s);
@@ -429,6 +444,66 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
             int32_t l0, int32_t l1, kvx_ready* ready, int32_t slot_base, hipStream_t s,
             int32_t path, const Tuning& t, Lane* L);
 
+// Checks of one BACKUP or RESTORE that need no HIP call: layer range, page
+// list, ready object, packed buffer size and alignment. Leaves *active false
+// when there is nothing to move (n == 0 or an empty layer range).
+int validate_side(const kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, const void* buf,
+                  uint64_t buf_bytes, int32_t l0, int32_t l1, const kvx_ready* ready,
+                  int32_t slot_base, const std::string& op, bool* active)
+{
+    const PoolGeom& g = pool->geom;
+    *active = false;
+    if (l0 < 0 || l1 > g.num_layers || l0 > l1)
+        return fail(KVX_E_RANGE, op + ": layer range [" + std::to_string(l0) + ", " +
+                                     std::to_string(l1) + ") is outside [0, " +
+                                     std::to_string(g.num_layers) + ")");
+    int rc = check_page_ids(g, ids, n, dir == SCATTER);
+    if (rc != KVX_OK) return rc;
+    if (ready) {
+        if (!ready_known(ready)) return fail(KVX_E_INVAL, op + ": unknown ready handle");
+        if (!ready->live.load()) return fail(KVX_E_STALE, op + ": ready object was destroyed");
+        if (ready->generation != pool->generation)
+            return fail(KVX_E_STALE, op + ": ready object generation " +
+                                         std::to_string(ready->generation) +
+                                         " does not match pool generation " +
+                                         std::to_string(pool->generation));
+        if (slot_base < 0 || int64_t(slot_base) + l1 > ready->num_slots)
+            return fail(KVX_E_RANGE, op + ": slots [" + std::to_string(int64_t(slot_base) + l0) +
+                                         ", " + std::to_string(int64_t(slot_base) + l1) +
+                                         ") are outside the ready object's " +
+                                         std::to_string(ready->num_slots) + " slots");
+    }
+    if (n == 0 || l0 == l1) return KVX_OK;
+    if (!buf) return fail(KVX_E_INVAL, op + ": packed buffer is NULL");
+    const int64_t need = g.num_layers * g.num_kv * int64_t(n) * g.piece_bytes;
+    if (buf_bytes < static_cast<uint64_t>(need))
+        return fail(KVX_E_RANGE, op + ": packed buffer holds " + std::to_string(buf_bytes) +
+                                     " bytes, needs " + std::to_string(need));
+    if (reinterpret_cast<uintptr_t>(buf) % kVecBytes != 0)
+        return fail(KVX_E_ALIGN, op + ": packed buffer is not 16-byte aligned");
+    if (ready && int64_t(n) * g.num_kv * ((g.piece_bytes + 4095) / 4096) >= (int64_t(1) << 32))
+        return fail(KVX_E_INVAL, op + ": too many pages for per-layer publish");
+    *active = true;
+    return KVX_OK;
+}
+
+// The memory kind `path` needs for a packed buffer (HIP call); *view is its
+// device view.
+int check_packed_kind(const kvx_pool* pool, void* buf, int32_t path, const std::string& op,
+                      uint8_t** view)
+{
+    const MemKind kind = classify(buf, pool->device, view);
+    if (path == KVX_PATH_DEVICE && kind != MemKind::Device)
+        return fail(KVX_E_INVAL, op + ": path DEVICE needs device memory of the pool's GPU");
+    if (path != KVX_PATH_DEVICE && kind != MemKind::PinnedHost)
+        return fail(kind == MemKind::Device ? KVX_E_INVAL : KVX_E_NOTPINNED,
+                    op + (kind == MemKind::Device
+                              ? ": host path given device memory"
+                              : ": packed buffer is not pinned host memory (pageable memory is "
+                                "refused; use kvx_host_alloc)"));
+    return KVX_OK;
+}
+
 int run_op(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, void* buf, uint64_t buf_bytes,
          int32_t l0, int32_t l1, kvx_ready* ready, int32_t slot_base, void* stream_v, int32_t path)
 {
@@ -436,40 +511,11 @@ int run_op(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, void* buf, ui
     const char* op = dir == GATHER ? "backup" : "restore";
     if (!pool_known(pool)) return fail(KVX_E_INVAL, std::string(op) + ": unknown pool handle");
     if (!pool->live.load()) return fail(KVX_E_STALE, std::string(op) + ": pool handle was unregistered");
-    const PoolGeom& g = pool->geom;
     if (path != KVX_PATH_STAGED && path != KVX_PATH_ZEROCOPY && path != KVX_PATH_DEVICE)
         return fail(KVX_E_INVAL, std::string(op) + ": unknown path " + std::to_string(path));
-    if (l0 < 0 || l1 > g.num_layers || l0 > l1)
-        return fail(KVX_E_RANGE, std::string(op) + ": layer range [" + std::to_string(l0) + ", " +
-                                     std::to_string(l1) + ") is outside [0, " +
-                                     std::to_string(g.num_layers) + ")");
-    int rc = check_page_ids(g, ids, n, dir == SCATTER);
-    if (rc != KVX_OK) return rc;
-    if (ready) {
-        if (!ready_known(ready)) return fail(KVX_E_INVAL, "restore: unknown ready handle");
-        if (!ready->live.load()) return fail(KVX_E_STALE, "restore: ready object was destroyed");
-        if (ready->generation != pool->generation)
-            return fail(KVX_E_STALE, "restore: ready object generation " +
-                                         std::to_string(ready->generation) +
-                                         " does not match pool generation " +
-                                         std::to_string(pool->generation));
-        if (slot_base < 0 || int64_t(slot_base) + l1 > ready->num_slots)
-            return fail(KVX_E_RANGE, "restore: slots [" + std::to_string(int64_t(slot_base) + l0) +
-                                         ", " + std::to_string(int64_t(slot_base) + l1) +
-                                         ") are outside the ready object's " +
-                                         std::to_string(ready->num_slots) + " slots");
-    }
-    if (n == 0 || l0 == l1) return KVX_OK;
-    if (!buf) return fail(KVX_E_INVAL, std::string(op) + ": packed buffer is NULL");
-    const int64_t need = g.num_layers * g.num_kv * int64_t(n) * g.piece_bytes;
-    if (buf_bytes < static_cast<uint64_t>(need))
-        return fail(KVX_E_RANGE, std::string(op) + ": packed buffer holds " +
-                                     std::to_string(buf_bytes) + " bytes, needs " +
-                                     std::to_string(need));
-    if (reinterpret_cast<uintptr_t>(buf) % kVecBytes != 0)
-        return fail(KVX_E_ALIGN, std::string(op) + ": packed buffer is not 16-byte aligned");
-    if (ready && int64_t(n) * g.num_kv * ((g.piece_bytes + 4095) / 4096) >= (int64_t(1) << 32))
-        return fail(KVX_E_INVAL, "restore: too many pages for per-layer publish");
+    bool active = false;
+    int rc = validate_side(pool, dir, ids, n, buf, buf_bytes, l0, l1, ready, slot_base, op, &active);
+    if (rc != KVX_OK || !active) return rc;
 
     // ---- HIP from here on; nothing has been enqueued yet ----
     rc = resolve_device(pool);
@@ -477,15 +523,8 @@ int run_op(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, void* buf, ui
     DeviceGuard dg(pool->device);
     hipStream_t s = static_cast<hipStream_t>(stream_v);
     uint8_t* view = nullptr;
-    const MemKind kind = classify(buf, pool->device, &view);
-    if (path == KVX_PATH_DEVICE && kind != MemKind::Device)
-        return fail(KVX_E_INVAL, std::string(op) + ": path DEVICE needs device memory of the pool's GPU");
-    if (path != KVX_PATH_DEVICE && kind != MemKind::PinnedHost)
-        return fail(kind == MemKind::Device ? KVX_E_INVAL : KVX_E_NOTPINNED,
-                    std::string(op) + (kind == MemKind::Device
-                                           ? ": host path given device memory"
-                                           : ": packed buffer is not pinned host memory (pageable "
-                                             "memory is refused; use kvx_host_alloc)"));
+    rc = check_packed_kind(pool, buf, path, op, &view);
+    if (rc != KVX_OK) return rc;
     const Tuning t = tuning();
     Lane* L = nullptr;
     rc = get_lane(pool->device, s, &L);
@@ -638,6 +677,98 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
     return rc;
 }
 
+// BACKUP and RESTORE sides of kvx_exchange, enqueued as launches that each
+// interleave one chunk of pages of both sides (identity slot order).
+int run_exchange(kvx_pool* pool, const kvx_xfer* bk, const kvx_xfer* rs, kvx_ready* ready,
+                 int32_t slot_base, void* stream_v, int32_t path)
+{
+    const PoolGeom& g = pool->geom;
+    const bool host = path == KVX_PATH_ZEROCOPY;
+    int rc = resolve_device(pool);
+    if (rc != KVX_OK) return rc;
+    DeviceGuard dg(pool->device);
+    hipStream_t s = static_cast<hipStream_t>(stream_v);
+    uint8_t *vb = nullptr, *vr = nullptr;
+    rc = check_packed_kind(pool, bk->packed, path, "exchange backup", &vb);
+    if (rc != KVX_OK) return rc;
+    rc = check_packed_kind(pool, rs->packed, path, "exchange restore", &vr);
+    if (rc != KVX_OK) return rc;
+    const Tuning t = tuning();
+    Lane* L = nullptr;
+    rc = get_lane(pool->device, s, &L);
+    if (rc != KVX_OK) return rc;
+    std::lock_guard<std::mutex> lk(L->mu);
+    rc = lane_counters(L, g.num_layers);   // the unit queue, and the publish counters
+    if (rc != KVX_OK) return rc;
+
+    ExchangeArgs a;
+    std::memset(&a, 0, sizeof a);
+    LaunchCfg cfg;
+    cfg.host_link = host;
+    cfg.cache_policy = 0;   // fixed per side inside the exchange kernel
+    setup_geom(pool, host, t, &a.g, &cfg);
+    cfg.publish = ready != nullptr;
+    Publish pub;
+    pub.layer_done = L->layer_done;
+    pub.queue = L->layer_done + L->layer_cap;
+    if (ready) {
+        pub.ready = ready->counts_dev + slot_base;
+        pub.layer_target = static_cast<uint32_t>(g.num_kv * int64_t(rs->n) * a.g.chunks_per_piece);
+        pub.value = static_cast<uint32_t>(rs->n);
+    }
+    set_publish(&pub, &a.p);
+    a.g.unit_order = 0;
+    const int64_t cpp = a.g.chunks_per_piece;
+    auto side = [&](Side* x, const kvx_xfer* xf, uint8_t* view, int32_t* pages, int64_t p0) {
+        const int64_t np = std::max<int64_t>(0, std::min<int64_t>(kMaxPairs, xf->n - p0));
+        x->packed = view;
+        x->pk_lc_stride = int64_t(xf->n) * g.piece_bytes;
+        x->pk_layer0 = 0;
+        x->pk_slot0 = static_cast<int32_t>(p0);
+        x->layer_begin = xf->layer_begin;
+        x->npairs = static_cast<uint32_t>(np);
+        for (int64_t j = 0; j < np; j++) pages[j] = xf->page_ids[p0 + j];
+        return int64_t(xf->layer_end - xf->layer_begin) * g.num_kv * np * cpp;
+    };
+    const int64_t launches = std::max<int64_t>((bk->n + kMaxPairs - 1) / kMaxPairs,
+                                               (rs->n + kMaxPairs - 1) / kMaxPairs);
+    for (int64_t k = 0; k < launches; k++) {
+        const int64_t ub = side(&a.b, bk, vb, a.pages_b, k * kMaxPairs);
+        const int64_t ur = side(&a.r, rs, vr, a.pages_r, k * kMaxPairs);
+        if (ub + ur >= (int64_t(1) << 31)) {
+            rc = fail(KVX_E_INVAL, "exchange: one launch would have too many work units");
+            break;
+        }
+        a.b.total_units = static_cast<uint32_t>(ub);
+        a.r.total_units = static_cast<uint32_t>(ur);
+        // grid: over the host link, the two single-direction host grids
+        // together (measured: 64 workgroups sustain 90-91 GB/s for both
+        // directions); in device memory, a few units per workgroup
+        int64_t gmax;
+        if (t.grid_max > 0)
+            gmax = t.grid_max;
+        else if (host)
+            gmax = 2 * (t.host_grid_max > 0 ? t.host_grid_max : kHostGridAuto);
+        else
+            gmax = int64_t(L->cu_count) * 8;
+        cfg.grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(ub + ur, gmax)));
+        const hipError_t e = launch_exchange(cfg, a, s);
+        if (e != hipSuccess) {
+            rc = hip_fail(e, "exchange kernel launch");
+            break;
+        }
+    }
+    if (rc != KVX_OK) {
+        L->counters_dirty = true;   // a partial launch may have left counts and the queue
+        return rc;
+    }
+    std::lock_guard<std::mutex> plk(pool->mu);
+    hipEvent_t& ev = pool->last_op[s];
+    if (!ev) KVX_HIP(hipEventCreateWithFlags(&ev, hipEventDisableTiming));
+    KVX_HIP(hipEventRecord(ev, s));
+    return KVX_OK;
+}
+
 }  // namespace
 }  // namespace kvx
 
@@ -747,6 +878,55 @@ int kvx_restore(kvx_pool* pool, const void* src, uint64_t src_bytes, const int32
 {
     return run_op(pool, SCATTER, page_ids, n, const_cast<void*>(src), src_bytes, layer_begin,
                 layer_end, ready, slot_base, stream, path);
+}
+
+int kvx_exchange(kvx_pool* pool, const kvx_xfer* backup, const kvx_xfer* restore, kvx_ready* ready,
+                 int32_t slot_base, void* stream, int32_t path)
+{
+    clear_error();
+    if (!backup || !restore) return fail(KVX_E_INVAL, "exchange: NULL transfer description");
+    if (!pool_known(pool)) return fail(KVX_E_INVAL, "exchange: unknown pool handle");
+    if (!pool->live.load()) return fail(KVX_E_STALE, "exchange: pool handle was unregistered");
+    if (path != KVX_PATH_ZEROCOPY && path != KVX_PATH_DEVICE)
+        return fail(KVX_E_INVAL, "exchange: runs on the zero-copy or device path (use kvx_backup and "
+                                 "kvx_restore for the staged path)");
+    bool ab = false, ar = false;
+    int rc = validate_side(pool, GATHER, backup->page_ids, backup->n, backup->packed,
+                           backup->packed_bytes, backup->layer_begin, backup->layer_end, nullptr, 0,
+                           "exchange backup", &ab);
+    if (rc != KVX_OK) return rc;
+    rc = validate_side(pool, SCATTER, restore->page_ids, restore->n, restore->packed,
+                       restore->packed_bytes, restore->layer_begin, restore->layer_end, ready,
+                       slot_base, "exchange restore", &ar);
+    if (rc != KVX_OK) return rc;
+    if (!ab && !ar) return KVX_OK;
+    if (!ar) return kvx_backup(pool, backup->page_ids, backup->n, backup->packed, backup->packed_bytes,
+                               backup->layer_begin, backup->layer_end, stream, path);
+    if (!ab) return kvx_restore(pool, restore->packed, restore->packed_bytes, restore->page_ids,
+                                restore->n, restore->layer_begin, restore->layer_end, ready, slot_base,
+                                stream, path);
+    // the two sides run concurrently: they must not touch the same bytes
+    const PoolGeom& g = pool->geom;
+    const uint64_t nb = uint64_t(g.num_layers * g.num_kv * int64_t(backup->n) * g.piece_bytes);
+    const uint64_t nr = uint64_t(g.num_layers * g.num_kv * int64_t(restore->n) * g.piece_bytes);
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(backup->packed);
+    const uintptr_t r0 = reinterpret_cast<uintptr_t>(restore->packed);
+    if (b0 < r0 + nr && r0 < b0 + nb)
+        return fail(KVX_E_INVAL, "exchange: the backup's and the restore's packed buffers overlap");
+    if (std::max(backup->layer_begin, restore->layer_begin) <
+        std::min(backup->layer_end, restore->layer_end)) {
+        std::vector<int32_t> a(backup->page_ids, backup->page_ids + backup->n);
+        std::vector<int32_t> b(restore->page_ids, restore->page_ids + restore->n);
+        std::sort(a.begin(), a.end());
+        std::sort(b.begin(), b.end());
+        std::vector<int32_t> both;
+        std::set_intersection(a.begin(), a.end(), b.begin(), b.end(), std::back_inserter(both));
+        if (!both.empty())
+            return fail(KVX_E_INVAL, "exchange: page " + std::to_string(both[0]) +
+                                         " is read by the backup and written by the restore in the "
+                                         "same layers; run them one after the other");
+    }
+    return run_exchange(pool, backup, restore, ready, slot_base, stream, path);
 }
 
 int kvx_plan_runs(const kvx_pool* pool, const int32_t* page_ids, int32_t n, int32_t* runs,

@@ -90,7 +90,7 @@ __device__ __forceinline__ uint32_t unit_vec(uint32_t tid, int u)
 // Byte offset, inside the source piece, of the 16 bytes that land at byte
 // offset `off` of the destination piece.
 template <Dir D, bool PERMUTE>
-__device__ __forceinline__ uint32_t source_offset(const MoveArgs& a, uint32_t off)
+__device__ __forceinline__ uint32_t source_offset(const UnitGeom& a, uint32_t off)
 {
     if constexpr (!PERMUTE) {
         return off;
@@ -127,7 +127,7 @@ __device__ __forceinline__ uint32_t source_offset(const MoveArgs& a, uint32_t of
 // (HND<->NHD) sources span the whole piece; a dropped store may pair with
 // any in-range load.
 template <Dir D, int U, bool PERMUTE, int CP>
-__device__ __forceinline__ void move_unit(const MoveArgs& a, const uint8_t* src_piece,
+__device__ __forceinline__ void move_unit(const UnitGeom& a, const uint8_t* src_piece,
                                           uint8_t* dst_piece, uint32_t unit_base, uint32_t tid)
 {
     const uint32_t rest = a.piece_bytes - unit_base;
@@ -150,7 +150,7 @@ __device__ __forceinline__ void move_unit(const MoveArgs& a, const uint8_t* src_
 // workgroup, and one lane adds to the layer's counter; the add that completes
 // the layer acquires the other workgroups' releases, clears the counter for
 // the next call and publishes the page count with a system-scope release.
-__device__ __forceinline__ void count_units(const MoveArgs& a, int32_t l, uint32_t units,
+__device__ __forceinline__ void count_units(const PublishArgs& a, int32_t l, uint32_t units,
                                             uint32_t tid)
 {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
@@ -173,7 +173,7 @@ __device__ __forceinline__ void count_units(const MoveArgs& a, int32_t l, uint32
 // both linear runs; LDS does the (t, h) exchange. Used when a unit is a
 // whole number of token blocks (chunk_bytes = TU * H * row_bytes).
 template <Dir D, int U, int CP>
-__device__ __forceinline__ void move_unit_lds(const MoveArgs& a, rsrc_t src, rsrc_t dst,
+__device__ __forceinline__ void move_unit_lds(const UnitGeom& a, rsrc_t src, rsrc_t dst,
                                               uint32_t k, uint32_t tid, v4u* lds)
 {
     const uint32_t t0 = k * a.TU;
@@ -226,102 +226,172 @@ __device__ __forceinline__ void move_unit_lds(const MoveArgs& a, rsrc_t src, rsr
     }
 }
 
-// PERM: 0 = same inner layout, 1 = HND<->NHD row by row, 2 = HND<->NHD
-// through LDS token blocks
+// Position of unit q of a side: layer, kv, pair index j and chunk k of the
+// piece; all wave-uniform scalar math.
+struct UnitPos {
+    int32_t l;
+    uint32_t c, j, k;
+};
+
+__device__ __forceinline__ UnitPos decode_unit(const UnitGeom& g, const Side& s, uint32_t q)
+{
+    const uint32_t cpp = g.chunks_per_piece;
+    const uint32_t pu = q / cpp;
+    uint32_t k = q - pu * cpp;
+    const uint32_t lc = pu / s.npairs;
+    const uint32_t j = pu - lc * s.npairs;
+    if (g.unit_order & 2u) {   // rotate the chunk order from piece to piece
+        k += j % cpp;
+        if (k >= cpp) k -= cpp;
+    }
+    const uint32_t lrel = lc / g.num_kv;
+    return UnitPos{s.layer_begin + static_cast<int32_t>(lrel), lc - lrel * g.num_kv, j, k};
+}
+
+// Moves the unit at `u` of a side between pool page `page` and packed slot
+// `slot`. PERM: 0 = same inner layout, 1 = HND<->NHD row by row, 2 = HND<->NHD
+// through LDS token blocks (`lds` holds U * kThreads vectors).
+template <Dir D, int U, int PERM, int CP>
+__device__ __forceinline__ void move_at(const UnitGeom& g, const Side& s, const UnitPos& u,
+                                        int32_t page, int32_t slot, uint32_t tid, v4u* lds)
+{
+    uint8_t* pool_piece = g.pool + static_cast<int64_t>(page) * g.page_stride +
+                          static_cast<int64_t>(u.l) * g.layer_stride +
+                          static_cast<int64_t>(u.c) * g.kv_stride;
+    uint8_t* pk_piece = s.packed +
+                        (static_cast<int64_t>(u.l - s.pk_layer0) * g.num_kv + u.c) * s.pk_lc_stride +
+                        static_cast<int64_t>(slot - s.pk_slot0) * g.piece_bytes;
+    const uint8_t* src = (D == GATHER) ? pool_piece : pk_piece;
+    uint8_t* dst = (D == GATHER) ? pk_piece : pool_piece;
+    if constexpr (PERM == 2)
+        move_unit_lds<D, U, CP>(g, piece_rsrc(src, g.piece_bytes), piece_rsrc(dst, g.piece_bytes), u.k,
+                                tid, lds);
+    else
+        move_unit<D, U, PERM == 1, CP>(g, src, dst, u.k * g.chunk_bytes, tid);
+}
+
+// Runs f(q) for the unit numbers [0, total) drawn from `queue` in number
+// order. Lane 0 draws the next number while the workgroup moves the current
+// unit; two LDS words alternate so one barrier per unit suffices. Each
+// workgroup stops at its first draw past the end, so draw number
+// total + gridDim.x - 1 is the launch's last: whoever makes it resets the
+// queue for the next launch on the stream.
+template <class F>
+__device__ __forceinline__ void for_queued_units(uint32_t* queue, uint32_t total, uint32_t tid, F&& f)
+{
+    __shared__ uint32_t next[2];
+    const uint32_t last_draw = total + gridDim.x - 1;
+    if (tid == 0) {
+        const uint32_t d = __hip_atomic_fetch_add(queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == last_draw) __hip_atomic_store(queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        next[0] = d;
+    }
+    __syncthreads();
+    uint32_t q = next[0];
+    for (uint32_t it = 1; q < total; it++) {
+        uint32_t d = 0;
+        if (tid == 0) d = __hip_atomic_fetch_add(queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        f(q);
+        if (tid == 0) {
+            if (d == last_draw) __hip_atomic_store(queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            next[it & 1u] = d;
+        }
+        __syncthreads();
+        q = next[it & 1u];
+    }
+}
+
 template <Dir D, int U, int PERM, bool PUBLISH, int CP>
 __global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
 {
     const uint32_t tid = threadIdx.x;
-    const uint32_t cpp = a.chunks_per_piece;
     int32_t pend_layer = -1;   // PUBLISH: layer of the units finished but not yet counted
     uint32_t pend = 0;
-    // unit q -> (layer, kv, pair, chunk), all wave-uniform scalar math, then
-    // the move
+    __shared__ v4u lds[PERM == 2 ? U * kThreads : 1];
     auto do_unit = [&](uint32_t q) {
-        const uint32_t pu = q / cpp;
-        uint32_t k = q - pu * cpp;
-        const uint32_t lc = pu / a.npairs;
-        const uint32_t j = pu - lc * a.npairs;
-        if (a.unit_order & 2u) {   // rotate the chunk order from piece to piece
-            k += j % cpp;
-            if (k >= cpp) k -= cpp;
-        }
-        const uint32_t lrel = lc / a.num_kv;
-        const uint32_t c = lc - lrel * a.num_kv;
-        const int32_t l = a.layer_begin + static_cast<int32_t>(lrel);
-        const int32_t page = a.pairs[2 * j];
-        const int32_t slot = a.pairs[2 * j + 1];
-
+        const UnitPos u = decode_unit(a.g, a.s, q);
         if constexpr (PUBLISH) {
             // units arrive layer by layer: count a layer once this workgroup leaves it
-            if (l != pend_layer) {
-                if (pend) count_units(a, pend_layer, pend, tid);
-                pend_layer = l;
+            if (u.l != pend_layer) {
+                if (pend) count_units(a.p, pend_layer, pend, tid);
+                pend_layer = u.l;
                 pend = 0;
             }
         }
-
-        uint8_t* pool_piece = a.pool + static_cast<int64_t>(page) * a.page_stride +
-                              static_cast<int64_t>(l) * a.layer_stride +
-                              static_cast<int64_t>(c) * a.kv_stride;
-        uint8_t* pk_piece =
-            a.packed +
-            (static_cast<int64_t>(l - a.pk_layer0) * a.num_kv + c) * a.pk_lc_stride +
-            static_cast<int64_t>(slot - a.pk_slot0) * a.piece_bytes;
-        const uint8_t* src = (D == GATHER) ? pool_piece : pk_piece;
-        uint8_t* dst = (D == GATHER) ? pk_piece : pool_piece;
-        if constexpr (PERM == 2) {
-            __shared__ v4u lds[U * kThreads];
-            move_unit_lds<D, U, CP>(a, piece_rsrc(src, a.piece_bytes), piece_rsrc(dst, a.piece_bytes), k,
-                                    tid, lds);
-        } else {
-            move_unit<D, U, PERM == 1, CP>(a, src, dst, k * a.chunk_bytes, tid);
-        }
+        move_at<D, U, PERM, CP>(a.g, a.s, u, a.pairs[2 * u.j], a.pairs[2 * u.j + 1], tid, lds);
         if constexpr (PUBLISH) pend++;
     };
 
     if constexpr (PUBLISH) {
-        // Units come from a queue in number order, so every unit of layer l
-        // is handed out before any of layer l + 1 and a workgroup that runs
-        // slowly (measured: reads of pinned host memory are not served
+        // Units come from the queue in number order, so every unit of layer
+        // l is handed out before any of layer l + 1 and a workgroup that
+        // runs slowly (measured: reads of pinned host memory are not served
         // evenly across workgroups) holds back at most the unit it is on.
-        // Lane 0 draws the next number while the workgroup moves the current
-        // unit; two LDS slots alternate so one barrier per unit suffices.
-        // Each workgroup stops at its first draw past the end, so the
-        // total_units + gridDim.x - 1 draw is the last one of the launch:
-        // whoever makes it resets the queue for the next launch.
-        __shared__ uint32_t next[2];
-        const uint32_t last_draw = a.total_units + gridDim.x - 1;
-        if (tid == 0) {
-            const uint32_t d = __hip_atomic_fetch_add(a.queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (d == last_draw) __hip_atomic_store(a.queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            next[0] = d;
-        }
-        __syncthreads();
-        uint32_t q = next[0];
-        for (uint32_t it = 1; q < a.total_units; it++) {
-            uint32_t d = 0;
-            if (tid == 0) d = __hip_atomic_fetch_add(a.queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            do_unit(q);
-            if (tid == 0) {
-                if (d == last_draw) __hip_atomic_store(a.queue, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                next[it & 1u] = d;
-            }
-            __syncthreads();
-            q = next[it & 1u];
-        }
+        for_queued_units(a.p.queue, a.s.total_units, tid, do_unit);
+        if (pend) count_units(a.p, pend_layer, pend, tid);
     } else {
         // Workgroups are dispatched round-robin over the 8 XCDs (block b runs
         // on XCD b mod 8). With XCD ordering, the workgroups of one XCD take
         // consecutive unit numbers in every round of the loop, so each XCD
         // walks whole pieces instead of one fixed chunk offset of many pieces.
         uint32_t v = blockIdx.x;
-        if ((a.unit_order & 1u) && (gridDim.x & 7u) == 0)
+        if ((a.g.unit_order & 1u) && (gridDim.x & 7u) == 0)
             v = (blockIdx.x & 7u) * (gridDim.x >> 3) + (blockIdx.x >> 3);
-        for (uint32_t q = v; q < a.total_units; q += gridDim.x) do_unit(q);
+        for (uint32_t q = v; q < a.s.total_units; q += gridDim.x) do_unit(q);
     }
+}
+
+// BACKUP side b and RESTORE side r in one launch. Units are drawn from the
+// queue and alternate between the sides (b, r, b, r, ... until the shorter
+// side runs out), so both directions of the host link stay busy together:
+// measured on MI355X, a gather to pinned host memory and a scatter from it
+// sharing one launch sustain 90-91 GB/s over back-to-back launches, where
+// the same work as two kernels on two streams drifts out of step and falls
+// to 67-76 GB/s. Only the RESTORE side publishes.
+template <int U, int PERM, bool PUBLISH, bool HOST>
+__global__ __launch_bounds__(kThreads) void kvx_exchange_kernel(ExchangeArgs a)
+{
+    // cache policy: pinned host memory is written at device scope and read
+    // plainly; pool memory is read non-temporally
+    constexpr int CPG = HOST ? 5 : 7;
+    constexpr int CPS = HOST ? 6 : 7;
+    const uint32_t tid = threadIdx.x;
+    const uint32_t tb = a.b.total_units, tr = a.r.total_units;
+    const uint32_t m = tb < tr ? tb : tr;
+    int32_t pend_layer = -1;
+    uint32_t pend = 0;
+    __shared__ v4u lds[PERM == 2 ? U * kThreads : 1];
+    auto do_unit = [&](uint32_t q) {
+        bool gather;
+        uint32_t idx;
+        if (q < 2 * m) {
+            gather = (q & 1u) == 0;
+            idx = q >> 1;
+        } else {
+            gather = tb > tr;
+            idx = m + (q - 2 * m);
+        }
+        if (gather) {
+            const UnitPos u = decode_unit(a.g, a.b, idx);
+            move_at<GATHER, U, PERM, CPG>(a.g, a.b, u, a.pages_b[u.j], a.b.pk_slot0 + static_cast<int32_t>(u.j),
+                                          tid, lds);
+        } else {
+            const UnitPos u = decode_unit(a.g, a.r, idx);
+            if constexpr (PUBLISH) {
+                if (u.l != pend_layer) {
+                    if (pend) count_units(a.p, pend_layer, pend, tid);
+                    pend_layer = u.l;
+                    pend = 0;
+                }
+            }
+            move_at<SCATTER, U, PERM, CPS>(a.g, a.r, u, a.pages_r[u.j], a.r.pk_slot0 + static_cast<int32_t>(u.j),
+                                           tid, lds);
+            if constexpr (PUBLISH) pend++;
+        }
+    };
+    for_queued_units(a.p.queue, tb + tr, tid, do_unit);
     if constexpr (PUBLISH) {
-        if (pend) count_units(a, pend_layer, pend, tid);
+        if (pend) count_units(a.p, pend_layer, pend, tid);
     }
 }
 
@@ -433,8 +503,54 @@ hipError_t go_unroll(const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s)
 
 hipError_t launch_move(Dir dir, const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s)
 {
-    if (cfg.grid < 1 || a.total_units == 0) return hipErrorInvalidValue;
+    if (cfg.grid < 1 || a.s.total_units == 0) return hipErrorInvalidValue;
     return dir == GATHER ? go_unroll<GATHER>(cfg, a, s) : go_unroll<SCATTER>(cfg, a, s);
+}
+
+namespace {
+
+template <int U, int P, bool PUB, bool HOST>
+hipError_t xgo(const LaunchCfg& cfg, const ExchangeArgs& a, hipStream_t s)
+{
+    void* args[] = {const_cast<ExchangeArgs*>(&a)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&kvx_exchange_kernel<U, P, PUB, HOST>),
+                           dim3(cfg.grid), dim3(kThreads), args, 0, s);
+}
+
+template <int U, int P>
+hipError_t xgo_pub(const LaunchCfg& cfg, const ExchangeArgs& a, hipStream_t s)
+{
+    if (cfg.publish)
+        return cfg.host_link ? xgo<U, P, true, true>(cfg, a, s) : xgo<U, P, true, false>(cfg, a, s);
+    return cfg.host_link ? xgo<U, P, false, true>(cfg, a, s) : xgo<U, P, false, false>(cfg, a, s);
+}
+
+template <int U>
+hipError_t xgo_perm(const LaunchCfg& cfg, const ExchangeArgs& a, hipStream_t s)
+{
+    if constexpr (U == 4 || U == 8 || U == 16) {
+        if (cfg.permute == 2) return xgo_pub<U, 2>(cfg, a, s);
+    }
+    return cfg.permute ? xgo_pub<U, 1>(cfg, a, s) : xgo_pub<U, 0>(cfg, a, s);
+}
+
+}  // namespace
+
+hipError_t launch_exchange(const LaunchCfg& cfg, const ExchangeArgs& a, hipStream_t s)
+{
+    if (cfg.grid < 1 || a.b.total_units + a.r.total_units == 0 || !a.p.queue) return hipErrorInvalidValue;
+    switch (cfg.unroll) {
+    case 32: return xgo_perm<32>(cfg, a, s);
+    case 16: return xgo_perm<16>(cfg, a, s);
+    case 12: return xgo_perm<12>(cfg, a, s);
+    case 8: return xgo_perm<8>(cfg, a, s);
+    case 6: return xgo_perm<6>(cfg, a, s);
+    case 4: return xgo_perm<4>(cfg, a, s);
+    case 3: return xgo_perm<3>(cfg, a, s);
+    case 2: return xgo_perm<2>(cfg, a, s);
+    case 1: return xgo_perm<1>(cfg, a, s);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_ready_wait(const uint32_t* slot, uint32_t min_count, uint32_t spin_limit,

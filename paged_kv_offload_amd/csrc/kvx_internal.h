@@ -88,41 +88,69 @@ constexpr int64_t kRestoreChunkMin = 32ll << 20;   // default minimum staged res
 
 enum Dir : int32_t { GATHER = 0, SCATTER = 1 };
 
-// One launch moves pieces (page, layer, kv) for layers [layer_begin,
-// layer_begin + num_layers), every kv, and the `npairs` (page, slot) pairs.
-struct MoveArgs {
+// Pool and work-unit geometry shared by every unit of a launch.
+struct UnitGeom {
     uint8_t* pool;           // pool start (base + byte_offset)
-    uint8_t* packed;         // packed buffer holding layers >= pk_layer0, slots >= pk_slot0
     int64_t page_stride, layer_stride, kv_stride;   // pool byte strides
-    int64_t pk_lc_stride;    // packed bytes per (layer, kv) = pk_slots * piece_bytes
-    int32_t pk_layer0, pk_slot0;
     uint32_t piece_bytes;
     uint32_t chunk_bytes;    // bytes of one work unit (kThreads * 16 * unroll)
     uint32_t chunks_per_piece;
-    int32_t layer_begin;
     uint32_t num_kv;
-    uint32_t npairs;
-    uint32_t total_units;    // num_layers * num_kv * npairs * chunks_per_piece
     // pool HND <-> packed NHD permutation (unused for NHD pools)
     uint32_t T, H, row_vec;              // row_vec = row_bytes / 16
     uint32_t mg_row_vec, mg_H, mg_T;     // magic multipliers (0 means divisor 1)
     uint32_t TU, seg, mg_seg;            // LDS token blocks: tokens per unit, TU * row_vec
-    // per-layer publish (RESTORE with a ready object)
+    uint32_t unit_order;     // bit 0: XCD-contiguous unit numbering; bit 1: rotate chunks
+};
+
+// One direction's share of a launch: the pieces (page, layer, kv) of layers
+// [layer_begin, layer_begin + num_layers), every kv, and `npairs` pages,
+// against a packed buffer holding layers >= pk_layer0 and slots >= pk_slot0.
+struct Side {
+    uint8_t* packed;
+    int64_t pk_lc_stride;    // packed bytes per (layer, kv) = pk_slots * piece_bytes
+    int32_t pk_layer0, pk_slot0;
+    int32_t layer_begin;
+    uint32_t npairs;
+    uint32_t total_units;    // num_layers * num_kv * npairs * chunks_per_piece
+};
+
+// Per-layer publish of a RESTORE with a ready object, and the unit queue.
+struct PublishArgs {
     uint32_t* layer_done;    // device counters, indexed by absolute layer
-    uint32_t* queue;         // publishing kernels: next unit number (zero between launches)
+    uint32_t* queue;         // queue-driven kernels: next unit number (zero between launches)
     uint32_t* ready;         // device view of counts + slot_base, indexed by layer
     uint32_t layer_target;   // work units of one layer over the whole call
     uint32_t publish_value;  // n
-    uint32_t unit_order;     // bit 0: XCD-contiguous unit numbering; bit 1: rotate chunks
+};
+
+// One direction: pairs[2j] is the page and pairs[2j + 1] its slot.
+struct MoveArgs {
+    UnitGeom g;
+    Side s;
+    PublishArgs p;
     int32_t pairs[2 * kMaxPairs];
 };
 static_assert(sizeof(MoveArgs) <= 4096, "kernel arguments are limited to 4 KiB");
+
+// Both directions in one launch (kvx_exchange): a BACKUP side `b` and a
+// RESTORE side `r`, each listing its pages in slot order (the slot of
+// pages_x[j] is x.pk_slot0 + j).
+struct ExchangeArgs {
+    UnitGeom g;
+    Side b, r;
+    PublishArgs p;
+    int32_t pages_b[kMaxPairs];
+    int32_t pages_r[kMaxPairs];
+};
+static_assert(sizeof(ExchangeArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
 struct LaunchCfg {
     int unroll;        // 16-byte vectors per lane per unit: 1, 2, 4, 8 or 16
     int permute;       // 0: same inner layout; 1: HND<->NHD by rows; 2: through LDS
     bool publish;
     int cache_policy;  // bit 0: non-temporal loads, bit 1: non-temporal stores, bit 2: device-scope stores
+    bool host_link;    // exchange: both packed buffers are pinned host memory
     int grid;
 };
 
@@ -149,6 +177,7 @@ uint32_t magic_u32(uint32_t d);   // multiplier for exact x / d with x * d < 2^3
 // unit rounds for a piece: `forced` (> 0) if given, else the measured choice
 int pick_unroll(int64_t piece_bytes, int max_unroll, int forced);
 hipError_t launch_move(Dir dir, const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s);
+hipError_t launch_exchange(const LaunchCfg& cfg, const ExchangeArgs& a, hipStream_t s);
 hipError_t launch_ready_wait(const uint32_t* slot, uint32_t min_count, uint32_t spin_limit,
                              int32_t* status, hipStream_t s);
 

@@ -54,6 +54,12 @@ class kvx_pool_info(ctypes.Structure):
                                                "generation")]
 
 
+class kvx_xfer(ctypes.Structure):
+    _fields_ = [("page_ids", ctypes.c_void_p), ("n", ctypes.c_int32), ("packed", ctypes.c_void_p),
+                ("packed_bytes", ctypes.c_uint64), ("layer_begin", ctypes.c_int32),
+                ("layer_end", ctypes.c_int32)]
+
+
 class kvx_ipc_handle(ctypes.Structure):
     _fields_ = [("mem_handle", ctypes.c_uint8 * 64), ("device_uuid", ctypes.c_uint8 * 16),
                 ("alloc_bytes", ctypes.c_uint64), ("offset", ctypes.c_uint64),
@@ -89,6 +95,7 @@ SIGNATURES = [
     ("kvx_version", ctypes.c_int, []),
     ("kvx_set_option", ctypes.c_int, [_i32, _i64]),
     ("kvx_get_option", ctypes.c_int, [_i32, _P(_i64)]),
+    ("kvx_exchange", ctypes.c_int, [_vp, _P(kvx_xfer), _P(kvx_xfer), _vp, _i32, _vp, _i32]),
     ("kvx_ipc_export", ctypes.c_int, [_vp, _P(kvx_ipc_handle)]),
     ("kvx_ipc_import", ctypes.c_int, [_P(kvx_ipc_handle), _P(_vp), _P(_i32)]),
     ("kvx_ipc_close", ctypes.c_int, [_vp]),
@@ -312,6 +319,21 @@ def kvx_restore(pool: int, src, src_bytes: int, page_ids: Iterable[int], layer_b
     ids = _ids(page_ids)
     _check(lib().kvx_restore(pool, _ptr(src), src_bytes, _ids_ptr(ids), ids.size, layer_begin,
                              layer_end, ready or 0, slot_base, _stream(stream), path))
+
+
+def kvx_exchange(pool: int, backup_ids: Iterable[int], backup_dst, backup_bytes: int,
+                 backup_layers, restore_src, restore_bytes: int, restore_ids: Iterable[int],
+                 restore_layers, ready: int = None, slot_base: int = 0, stream=None,
+                 path: int = KVX_PATH_ZEROCOPY) -> None:
+    """BACKUP of backup_ids into backup_dst and RESTORE of restore_src into
+    restore_ids in one launch sequence; *_layers are (begin, end)."""
+    bi, ri = _ids(backup_ids), _ids(restore_ids)
+    b = kvx_xfer(bi.ctypes.data if bi.size else None, bi.size, _ptr(backup_dst), backup_bytes,
+                 *backup_layers)
+    r = kvx_xfer(ri.ctypes.data if ri.size else None, ri.size, _ptr(restore_src), restore_bytes,
+                 *restore_layers)
+    _check(lib().kvx_exchange(pool, ctypes.byref(b), ctypes.byref(r), ready, slot_base,
+                              _stream(stream), path))
 
 
 def kvx_plan_runs(pool: int, page_ids: Iterable[int]) -> np.ndarray:

@@ -271,3 +271,31 @@ def test_ipc_import_and_close_validate_before_any_gpu_call():
     with pytest.raises(K.KvxError) as e:
         K.kvx_ipc_export(0)
     assert e.value.code == K.KVX_E_INVAL
+
+
+def test_exchange_validation_fails_closed():
+    """kvx_exchange refuses the staged path, overlapping packed buffers and a
+    page both sides touch in a common layer before any HIP call."""
+    w = WORKLOADS["tiny"]
+    pool = register(w)
+    nb = w.host_bytes(2)
+    base = dict(pool=pool, backup_ids=[1, 2], backup_dst=0x1000000, backup_bytes=nb,
+                backup_layers=(0, 2), restore_src=0x2000000, restore_bytes=nb, restore_ids=[3, 4],
+                restore_layers=(0, 2), path=K.KVX_PATH_ZEROCOPY)
+    try:
+        for change, code, text in (
+                (dict(path=K.KVX_PATH_STAGED), K.KVX_E_INVAL, "zero-copy or device path"),
+                (dict(restore_ids=[2, 5]), K.KVX_E_INVAL, "page 2 is read by the backup"),
+                (dict(restore_src=0x1000000 + 16), K.KVX_E_INVAL, "overlap"),
+                (dict(backup_dst=0x2000000 + nb - 16), K.KVX_E_INVAL, "overlap"),
+                (dict(restore_ids=[3, 3]), K.KVX_E_DUP, "more than once"),
+                (dict(backup_ids=[1, 64]), K.KVX_E_RANGE, "outside"),
+                (dict(restore_layers=(1, 3)), K.KVX_E_RANGE, "layer range"),
+                (dict(restore_bytes=nb - 1), K.KVX_E_RANGE, "needs")):
+            args = dict(base)
+            args.update(change)
+            with pytest.raises(K.KvxError) as e:
+                K.kvx_exchange(**args)
+            assert e.value.code == code and text in e.value.message, (change, e.value.message)
+    finally:
+        K.kvx_unregister_pool(pool)

@@ -138,6 +138,95 @@ def test_kernel_variants(case, unroll, rounds, policy, lds, path, stream):
             K.kvx_set_option(o, v)
 
 
+# (case, backup pages, restore pages, backup layers, restore layers)
+EXCHANGES = [
+    ("tiny", 8, 8, None, None),
+    ("llama_small", 24, 11, None, (1, 3)),
+    ("mla_small", 10, 10, (0, 2), (2, 5)),
+    ("trtllm_small", 16, 7, None, None),
+    ("ragged_hnd", 460, 130, None, None),      # two launches per call, the second backup only
+    ("ragged_nhd", 100, 50, (1, 2), (0, 2)),
+]
+
+
+@pytest.mark.parametrize("path", ["zerocopy", "device"])
+@pytest.mark.parametrize("case,nb,nr,lb,lr", EXCHANGES)
+def test_exchange_parity(case, nb, nr, lb, lr, path, stream):
+    """kvx_exchange gives the bytes of kvx_backup followed by kvx_restore:
+    the whole packed buffer of the backup and the whole allocation after the
+    restore match the oracle, and the restore publishes its layers. Two
+    exchanges run back to back without a host synchronisation (the second
+    depends on the unit queue the first leaves reset)."""
+    w, _ = SMALL[case]
+    assert 2 * (nb + nr) <= w.num_pages
+    lb = lb or (0, w.num_layers)
+    lr = lr or (0, w.num_layers)
+    print(f"\n[exchange] case={case} path={path} nb={nb} nr={nr} lb={lb} lr={lr}", flush=True)
+    L = oracle_layout(w)
+    pool = DevicePool(w, seed=307, generation=8)
+    img = pool.host_image()
+    perm = synth.page_perm(w.seed + 11, w.num_pages)
+    ready = K.kvx_ready_create(w.num_layers, 8)
+    bufs = []
+    try:
+        want_alloc = img
+        wants = []
+        for r in range(2):
+            off = r * (nb + nr)
+            src = perm[off:off + nb].copy()
+            dst = perm[off + nb:off + nb + nr].copy()
+            pk_b = Packed(w, nb, path, fill_seed=w.seed + 20 + r)
+            pk_r = Packed(w, nr, path, fill_seed=w.seed + 30 + r)
+            bufs += [pk_b, pk_r]
+            # backup reads the pool as the previous exchange left it
+            wants.append(oracle.backup(L, want_alloc, src, *lb,
+                                       host=synth.gen_bytes(w.seed + 20 + r, 0, w.host_bytes(nb))))
+            want_alloc = oracle.restore(L, want_alloc, synth.gen_bytes(w.seed + 30 + r, 0, w.host_bytes(nr)),
+                                        dst, *lr)
+            K.kvx_exchange(pool.handle, src, pk_b.ptr, w.host_bytes(nb), lb, pk_r.ptr, w.host_bytes(nr),
+                           dst, lr, ready, 0, stream, PATHS[path])
+        K.kvx_sync(stream)
+        for r in range(2):
+            got = bufs[2 * r].numpy()
+            assert np.array_equal(got, wants[r]), f"exchange {r} backup: " + diff_report(got, wants[r])
+        after = pool.host_image()
+        assert np.array_equal(after, want_alloc), "exchange restore: " + diff_report(after, want_alloc)
+        counts = [K.kvx_layer_ready(ready, l) for l in range(w.num_layers)]
+        assert counts == [nr if lr[0] <= l < lr[1] else 0 for l in range(w.num_layers)]
+    finally:
+        K.kvx_ready_destroy(ready)
+        for b in bufs:
+            b.close()
+        pool.close()
+
+
+def test_exchange_with_overlapping_pages_in_disjoint_layers(stream):
+    """A page the backup reads in layer 0 may be written by the restore in
+    the other layers."""
+    w, _ = SMALL["llama_small"]
+    L = oracle_layout(w)
+    pool = DevicePool(w, seed=309, generation=9)
+    img = pool.host_image()
+    ids = synth.page_perm(w.seed + 13, w.num_pages)[:12].copy()
+    pk_b = Packed(w, 12, "zerocopy", fill_seed=41)
+    pk_r = Packed(w, 12, "zerocopy", fill_seed=42)
+    try:
+        K.kvx_exchange(pool.handle, ids, pk_b.ptr, w.host_bytes(12), (0, 1), pk_r.ptr,
+                       w.host_bytes(12), ids, (1, w.num_layers), None, 0, stream,
+                       K.KVX_PATH_ZEROCOPY)
+        K.kvx_sync(stream)
+        want_b = oracle.backup(L, img, ids, 0, 1, host=synth.gen_bytes(41, 0, w.host_bytes(12)))
+        want = oracle.restore(L, img, synth.gen_bytes(42, 0, w.host_bytes(12)), ids, 1, w.num_layers)
+        got_b = pk_b.numpy()
+        assert np.array_equal(got_b, want_b), diff_report(got_b, want_b)
+        after = pool.host_image()
+        assert np.array_equal(after, want), diff_report(after, want)
+    finally:
+        pk_b.close()
+        pk_r.close()
+        pool.close()
+
+
 @pytest.mark.parametrize("path", ["staged", "zerocopy"])
 def test_round_trip_and_duplicates(path, stream):
     w, _ = SMALL["trtllm_small"]
