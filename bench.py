@@ -4,25 +4,34 @@ MI355X.
 
 One step = the whole hot path over one request of the Llama-3-8B-shaped bf16
 pool (32 layers, K+V, 8 KV heads, head_dim 128, page size 64, 2048 pages):
-  BACKUP of 256 fragmented pages (16,384 tokens, 2 GiB) to pinned host
-  (validation + run planning, then the gather kernel writing the packed
-  buffer over the host link on the zero-copy path, or packing into the
-  staging ring followed by DMA on the staged path), RESTORE of that buffer
-  into 256 other pages with per-layer publish, and the ready-prefix query,
-  which the host polls until the whole request is published.
+BACKUP of 256 fragmented pages (16,384 tokens, 2 GiB) to pinned host memory
+(validation + run planning, then the gather kernel writing the packed buffer
+over the host link), RESTORE of that buffer into 256 other pages with
+per-layer publish, and the ready-prefix query, which the host polls until
+the whole request is published.
+
+The default schedule is layer-pipelined on the zero-copy path: the backup of
+layer 0, then 31 kvx_exchange launches that each back up layer l + 1 while
+they restore layer l (the restore reads what the previous launch wrote),
+then the restore of layer 31. It moves the same bytes, with the same
+results, as the serial schedule (--schedule serial: backup of every layer,
+then restore of every layer, on --path), but keeps both directions of the
+host link busy at once.
+
 value = 2 x 2 GiB x steps / wall time of the steps (GB = 1e9 B). The pool is
 resident in HBM when the timed region starts; crossing the host link is
 part of the method (the host tier is where BACKUP writes and RESTORE reads).
 
 Also reported: the device pack/unpack kernels alone against the HBM peak
 (the roofline), the step's kernels against the host link (link_roofline,
-with the pinned hipMemcpyAsync peaks measured in the same run), both host
-paths per direction, a layer-pipelined schedule that overlaps the two
-directions, the layer-0-ready latency, and the CPU oracle on a bounded
-sample (a baseline only).
+with the pinned hipMemcpyAsync peaks measured in the same run), the other
+schedule, both host paths per direction, layer-pipelined schedules on two
+streams, the layer-0-ready latency, and the CPU oracle on a bounded sample
+(a baseline only).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--path staged|zerocopy]
-       [--no-cpu-baseline] [--kernel-only] [--no-extras]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--schedule exchange|serial]
+       [--path staged|zerocopy] [--no-cpu-baseline] [--kernel-only] [--no-extras]
+       [--all-workloads]
 """
 import argparse
 import json
@@ -42,8 +51,8 @@ PCIE_PEAK_GBS = 64.0      # MI355X host interface, PCIe 5.0 x16, published per-d
 # (FETCH_SIZE, WRITE_SIZE, scaled by a plain 2 GiB device copy in the same
 # run; see profiles/pack_kernel_llama8b.txt). Valid only for the kernel source
 # they were taken on: reported as null once kernels.hip changes.
-MEASURED_TRAFFIC = {"kernels_hip_sha256": "b6566eab6847ecadd8d70f0a64d5088af70f9b8ac68bfad65f88c9e3681aae36",
-                    "bytes_per_launch": 4295171559}
+MEASURED_TRAFFIC = {"kernels_hip_sha256": "fb6706a77828f1133c0624f8959ef9d7a380a210ed129f9d919ca26fb7883879",
+                    "bytes_per_launch": 4295182166}
 
 
 def log(msg):
@@ -59,7 +68,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--path", choices=["staged", "zerocopy"], default="zerocopy")
+    ap.add_argument("--schedule", choices=["exchange", "serial"], default="exchange",
+                    help="exchange: layer-pipelined kvx_exchange launches (zero-copy); serial: "
+                         "backup then restore on --path")
+    ap.add_argument("--path", choices=["staged", "zerocopy"], default="zerocopy",
+                    help="host path of the serial schedule")
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
@@ -215,44 +228,128 @@ def main():
     host = K.HostBuffer(P)
     ready = K.kvx_ready_create(w.num_layers, 1)
     path = {"staged": K.KVX_PATH_STAGED, "zerocopy": K.KVX_PATH_ZEROCOPY}[args.path]
+    layer_bytes = P // w.num_layers
 
+    # Serial schedule: BACKUP of every layer, then RESTORE of every layer.
     # HIP events on the stream the kernels run on bracket the backup and the
-    # restore of every timed step (on the zero-copy path each call is one
-    # kernel launch: the gather writing host memory, the scatter reading it)
-    marks = []
-
-    def step(path=path, record=False):
+    # restore (on the zero-copy path each call is one kernel launch).
+    def serial_step(marks=None, path=path):
         K.kvx_ready_reset(ready)
-        e = [ev() for _ in range(3)] if record else None
-        if record:
+        e = [ev() for _ in range(3)] if marks is not None else None
+        if e:
             e[0].record(stream)
         K.kvx_backup(pool, src, host.ptr, P, 0, w.num_layers, stream, path)
-        if record:
+        if e:
             e[1].record(stream)
         K.kvx_restore(pool, host.ptr, P, dst, 0, w.num_layers, ready, 0, stream, path)
-        if record:
+        if e:
             e[2].record(stream)
             marks.append(e)
         while K.kvx_ready_prefix(ready) < n:    # the consumer's view of completion
             pass
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step(record=True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    t_bk = median([m[0].elapsed_time(m[1]) / 1e3 for m in marks])
-    t_rs = median([m[1].elapsed_time(m[2]) / 1e3 for m in marks])
-    t_bk_best = min(m[0].elapsed_time(m[1]) / 1e3 for m in marks)
-    t_rs_best = min(m[1].elapsed_time(m[2]) / 1e3 for m in marks)
-    ms_per_step = wall / args.steps * 1e3
-    value = 2 * P * args.steps / wall / GB
+    # Layer-pipelined schedule on the zero-copy path: BACKUP of layer 0, then
+    # one kvx_exchange per layer that backs up layer l + 1 while it restores
+    # layer l (the restore reads what the previous launch wrote), then the
+    # RESTORE of the last layer. Same bytes, same results, per-layer publish;
+    # both directions of the host link carry data at once.
+    def exchange_step(marks=None):
+        K.kvx_ready_reset(ready)
+        e = [ev() for _ in range(4)] if marks is not None else None
+        if e:
+            e[0].record(stream)
+        K.kvx_backup(pool, src, host.ptr, P, 0, 1, stream, K.KVX_PATH_ZEROCOPY)
+        if e:
+            e[1].record(stream)
+        for l in range(1, w.num_layers):
+            K.kvx_exchange(pool, src, host.ptr, P, (l, l + 1), host.ptr, P, dst, (l - 1, l), ready,
+                           0, stream, K.KVX_PATH_ZEROCOPY)
+        if e:
+            e[2].record(stream)
+        K.kvx_restore(pool, host.ptr, P, dst, w.num_layers - 1, w.num_layers, ready, 0, stream,
+                      K.KVX_PATH_ZEROCOPY)
+        if e:
+            e[3].record(stream)
+            marks.append(e)
+        while K.kvx_ready_prefix(ready) < n:
+            pass
+
+    def run(step_fn, steps, warmup):
+        marks = []
+        for _ in range(warmup):
+            step_fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step_fn(marks)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, marks
+
     serial_peak = 2 / (1 / d2h_peak + 1 / h2d_peak)
-    log(f"step ({args.path}): {ms_per_step:.2f} ms -> {value:.2f} GB/s "
-        f"({100 * value / serial_peak:.1f}% of the serial memcpy peak {serial_peak:.1f} GB/s)")
+
+    def serial_report(wall, marks, steps):
+        t_bk = median([m[0].elapsed_time(m[1]) / 1e3 for m in marks])
+        t_rs = median([m[1].elapsed_time(m[2]) / 1e3 for m in marks])
+        t_bk_best = min(m[0].elapsed_time(m[1]) / 1e3 for m in marks)
+        t_rs_best = min(m[1].elapsed_time(m[2]) / 1e3 for m in marks)
+        gbs = 2 * P * steps / wall / GB
+        return gbs, {
+            "gbs": round(gbs, 3), "ms_per_step": round(wall / steps * 1e3, 3),
+            "backup_achieved": round(P / t_bk / GB, 2), "restore_achieved": round(P / t_rs / GB, 2),
+            "backup_best": round(P / t_bk_best / GB, 2), "restore_best": round(P / t_rs_best / GB, 2),
+            "backup_frac_of_pcie": round(P / t_bk / GB / PCIE_PEAK_GBS, 4),
+            "restore_frac_of_pcie": round(P / t_rs / GB / PCIE_PEAK_GBS, 4),
+            "backup_frac_of_measured": round(P / t_bk / GB / d2h_peak, 4),
+            "restore_frac_of_measured": round(P / t_rs / GB / h2d_peak, 4),
+            "frac_of_serial_measured_peak": round(gbs / serial_peak, 4)}
+
+    def exchange_report(wall, marks, steps):
+        per = [m[1].elapsed_time(m[2]) / 1e3 / (w.num_layers - 1) for m in marks]
+        t_x, t_x_best = median(per), min(per)
+        t_b0 = median([m[0].elapsed_time(m[1]) / 1e3 for m in marks])
+        t_rl = median([m[2].elapsed_time(m[3]) / 1e3 for m in marks])
+        gbs = 2 * P * steps / wall / GB
+        both = 2 * PCIE_PEAK_GBS
+        return gbs, {
+            "gbs": round(gbs, 3), "ms_per_step": round(wall / steps * 1e3, 3),
+            "exchange_launch_ms": round(t_x * 1e3, 4),
+            "exchange_achieved": round(2 * layer_bytes / t_x / GB, 2),
+            "exchange_best": round(2 * layer_bytes / t_x_best / GB, 2),
+            "exchange_frac_of_pcie_both_directions": round(2 * layer_bytes / t_x / GB / both, 4),
+            "exchange_frac_of_measured_both_directions": round(2 * layer_bytes / t_x / GB / bidir_peak, 4),
+            "first_backup_gbs": round(layer_bytes / t_b0 / GB, 2),
+            "last_restore_gbs": round(layer_bytes / t_rl / GB, 2)}
+
+    if args.schedule == "exchange":
+        wall, marks = run(exchange_step, args.steps, args.warmup)
+        value, main_rep = exchange_report(wall, marks, args.steps)
+        schedule = ("layer-pipelined: backup of layer 0, then one kvx_exchange per layer (backup of "
+                    "layer l+1 and restore of layer l in one launch), then restore of the last "
+                    "layer; zero-copy; the host waits for the ready prefix")
+        path_name = "zerocopy"
+    else:
+        wall, marks = run(serial_step, args.steps, args.warmup)
+        value, main_rep = serial_report(wall, marks, args.steps)
+        schedule = "backup then restore, host waits for the ready prefix"
+        path_name = args.path
+    ms_per_step = wall / args.steps * 1e3
+    log(f"step ({args.schedule}, {path_name}): {ms_per_step:.2f} ms -> {value:.2f} GB/s")
+
+    if args.schedule == "exchange":
+        link = {"bound": "host link (PCIe 5.0 x16, both directions at once)",
+                "kernels": "the step's kvx_exchange launches (zero-copy backup of one layer and restore "
+                           "of another in each), HIP events in the timed region",
+                "achieved": main_rep["exchange_achieved"], "best": main_rep["exchange_best"],
+                "unit": "GB/s", "peak": 2 * PCIE_PEAK_GBS,
+                "frac": main_rep["exchange_frac_of_pcie_both_directions"],
+                "frac_of_measured_both_directions": main_rep["exchange_frac_of_measured_both_directions"],
+                "step": main_rep}
+    else:
+        link = {"bound": "host link (PCIe 5.0 x16)",
+                "kernels": f"the step's {path_name} backup and restore, HIP events in the timed region",
+                "unit": "GB/s", "peak": PCIE_PEAK_GBS, "step": main_rep}
+    link["measured_memcpy_peak"] = {"d2h": round(d2h_peak, 2), "h2d": round(h2d_peak, 2),
+                                    "both_directions": round(bidir_peak, 2)}
 
     result = {
         "metric": "KV GB/s moved (backup D2H, restore H2D) + % of HBM / host-link roofline",
@@ -268,26 +365,25 @@ def main():
         "dtype": "u8",
         "data": "synthetic",
         "config": {"workload": w.description, "pages_per_request": n, "layers": w.num_layers,
-                   "payload_bytes_per_op": P, "path": args.path,
-                   "schedule": "backup then restore, host waits for the ready prefix"},
+                   "payload_bytes_per_op": P, "path": path_name, "schedule": schedule},
         "roofline": roofline,
         "unpack_roofline": {"achieved": round(unpack_gbs, 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(unpack_gbs / HBM_PEAK_GBS, 4)},
         "d2d_copy_gbs": round(d2d_gbs, 1),
-        "link_roofline": {
-            "bound": "host link (PCIe 5.0 x16)",
-            "kernels": f"the step's {args.path} backup and restore, HIP events in the timed region",
-            "backup_achieved": round(P / t_bk / GB, 2), "restore_achieved": round(P / t_rs / GB, 2),
-            "backup_best": round(P / t_bk_best / GB, 2), "restore_best": round(P / t_rs_best / GB, 2),
-            "unit": "GB/s", "peak": PCIE_PEAK_GBS,
-            "backup_frac": round(P / t_bk / GB / PCIE_PEAK_GBS, 4),
-            "restore_frac": round(P / t_rs / GB / PCIE_PEAK_GBS, 4),
-            "measured_memcpy_peak": {"d2h": round(d2h_peak, 2), "h2d": round(h2d_peak, 2),
-                                     "both_directions": round(bidir_peak, 2)},
-            "backup_frac_of_measured": round(P / t_bk / GB / d2h_peak, 4),
-            "restore_frac_of_measured": round(P / t_rs / GB / h2d_peak, 4),
-            "step_frac_of_serial_measured_peak": round(value / serial_peak, 4)},
+        "link_roofline": link,
     }
+
+    if not args.no_extras:
+        # the other schedule, same number of steps
+        if args.schedule == "exchange":
+            wall2, marks2 = run(lambda m=None: serial_step(m, K.KVX_PATH_ZEROCOPY), args.steps, 1)
+            _, rep2 = serial_report(wall2, marks2, args.steps)
+            result["link_roofline"]["serial_step_zerocopy"] = rep2
+        else:
+            wall2, marks2 = run(exchange_step, args.steps, 1)
+            _, rep2 = exchange_report(wall2, marks2, args.steps)
+            result["link_roofline"]["exchange_step"] = rep2
+        log(f"other schedule: {rep2['gbs']} GB/s")
 
     if not args.no_extras:
         extras = {}
@@ -329,6 +425,28 @@ def main():
                 pipelined(pth)
             torch.cuda.synchronize()
             pipe[name] = round(2 * P * 3 / (time.perf_counter() - t0) / GB, 2)
+        # the same schedule in one stream with kvx_exchange: each launch
+        # backs up layer group g + 1 while it restores group g
+        def exchanged(group):
+            K.kvx_ready_reset(ready)
+            G = (w.num_layers + group - 1) // group
+            rng = lambda g: (g * group, min(w.num_layers, (g + 1) * group))  # noqa: E731
+            K.kvx_backup(pool, src, host.ptr, P, *rng(0), stream, K.KVX_PATH_ZEROCOPY)
+            for g in range(1, G):
+                K.kvx_exchange(pool, src, host.ptr, P, rng(g), host.ptr, P, dst, rng(g - 1),
+                               ready, 0, stream, K.KVX_PATH_ZEROCOPY)
+            K.kvx_restore(pool, host.ptr, P, dst, *rng(G - 1), ready, 0, stream,
+                          K.KVX_PATH_ZEROCOPY)
+            while K.kvx_ready_prefix(ready) < n:
+                pass
+        for group in (1, 2, 4):
+            exchanged(group)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(3):
+                exchanged(group)
+            torch.cuda.synchronize()
+            pipe[f"zerocopy_exchange_group{group}"] = round(2 * P * 3 / (time.perf_counter() - t0) / GB, 2)
         result["layer_pipelined_gbs"] = pipe
         log(f"layer-pipelined step: {pipe}")
 
@@ -561,6 +679,25 @@ def all_workloads():
         bid.append(2 * GiB / (time.perf_counter() - t0) / GB)
     del pin_a, pin_b, dev_a, dev_b
     res["memcpy_both_directions_gbs"] = round(statistics.median(bid[1:]), 2)
+    # backup k and restore k + 1 of the schedule as one kvx_exchange, the
+    # pairs round-robin on two streams (four requests in flight)
+    def run_exchange():
+        nb = nr = 0
+        pairs = [(sched[k], sched[k + 1]) for k in range(0, len(sched), 2)]
+        for i, ((kb, ib), (kr, ir)) in enumerate(pairs):
+            assert kb == "backup" and kr == "restore"
+            K.kvx_exchange(pool, ib, slots[4 + nb % 4].ptr, P, (0, w.num_layers), slots[nr % 4].ptr,
+                           P, ir, (0, w.num_layers), None, 0, streams[i % 2], K.KVX_PATH_ZEROCOPY)
+            nb += 1
+            nr += 1
+        torch.cuda.synchronize()
+    run_exchange()
+    t0 = time.perf_counter()
+    run_exchange()
+    res["zerocopy_exchange"] = round(128 * P / (time.perf_counter() - t0) / GB, 2)
+    res["zerocopy_exchange_frac_of_memcpy_both_directions"] = round(
+        res["zerocopy_exchange"] / res["memcpy_both_directions_gbs"], 4)
+    log(f"mixed zerocopy_exchange: {res['zerocopy_exchange']} GB/s")
     for name, bpath, rpath in (("zerocopy", K.KVX_PATH_ZEROCOPY, K.KVX_PATH_ZEROCOPY),
                                ("staged", K.KVX_PATH_STAGED, K.KVX_PATH_STAGED),
                                ("zerocopy_backup_staged_restore", K.KVX_PATH_ZEROCOPY,

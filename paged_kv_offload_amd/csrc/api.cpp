@@ -724,7 +724,7 @@ int run_exchange(kvx_pool* pool, const kvx_xfer* bk, const kvx_xfer* rs, kvx_rea
         x->packed = view;
         x->pk_lc_stride = int64_t(xf->n) * g.piece_bytes;
         x->pk_layer0 = 0;
-        x->pk_slot0 = static_cast<int32_t>(p0);
+        x->pk_slot0 = 0;
         x->layer_begin = xf->layer_begin;
         x->npairs = static_cast<uint32_t>(np);
         for (int64_t j = 0; j < np; j++) pages[j] = xf->page_ids[p0 + j];
@@ -735,6 +735,7 @@ int run_exchange(kvx_pool* pool, const kvx_xfer* bk, const kvx_xfer* rs, kvx_rea
     for (int64_t k = 0; k < launches; k++) {
         const int64_t ub = side(&a.b, bk, vb, a.pages_b, k * kMaxPairs);
         const int64_t ur = side(&a.r, rs, vr, a.pages_r, k * kMaxPairs);
+        a.first_b = a.first_r = static_cast<int32_t>(k * kMaxPairs);
         if (ub + ur >= (int64_t(1) << 31)) {
             rc = fail(KVX_E_INVAL, "exchange: one launch would have too many work units");
             break;
@@ -906,13 +907,19 @@ int kvx_exchange(kvx_pool* pool, const kvx_xfer* backup, const kvx_xfer* restore
                                 restore->n, restore->layer_begin, restore->layer_end, ready, slot_base,
                                 stream, path);
     // the two sides run concurrently: they must not touch the same bytes
+    // (packed bytes: the layer slices each side touches; the packed layout is
+    // layer-major, so one request's buffer may serve a backup of some layers
+    // and a restore of others)
     const PoolGeom& g = pool->geom;
-    const uint64_t nb = uint64_t(g.num_layers * g.num_kv * int64_t(backup->n) * g.piece_bytes);
-    const uint64_t nr = uint64_t(g.num_layers * g.num_kv * int64_t(restore->n) * g.piece_bytes);
-    const uintptr_t b0 = reinterpret_cast<uintptr_t>(backup->packed);
-    const uintptr_t r0 = reinterpret_cast<uintptr_t>(restore->packed);
-    if (b0 < r0 + nr && r0 < b0 + nb)
-        return fail(KVX_E_INVAL, "exchange: the backup's and the restore's packed buffers overlap");
+    const int64_t lay_b = g.num_kv * int64_t(backup->n) * g.piece_bytes;
+    const int64_t lay_r = g.num_kv * int64_t(restore->n) * g.piece_bytes;
+    const uintptr_t b0 = reinterpret_cast<uintptr_t>(backup->packed) + backup->layer_begin * lay_b;
+    const uintptr_t b1 = reinterpret_cast<uintptr_t>(backup->packed) + backup->layer_end * lay_b;
+    const uintptr_t r0 = reinterpret_cast<uintptr_t>(restore->packed) + restore->layer_begin * lay_r;
+    const uintptr_t r1 = reinterpret_cast<uintptr_t>(restore->packed) + restore->layer_end * lay_r;
+    if (b0 < r1 && r0 < b1)
+        return fail(KVX_E_INVAL, "exchange: the packed bytes the backup writes overlap those the "
+                                 "restore reads");
     if (std::max(backup->layer_begin, restore->layer_begin) <
         std::min(backup->layer_end, restore->layer_end)) {
         std::vector<int32_t> a(backup->page_ids, backup->page_ids + backup->n);

@@ -373,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void kvx_exchange_kernel(ExchangeArgs a)
         }
         if (gather) {
             const UnitPos u = decode_unit(a.g, a.b, idx);
-            move_at<GATHER, U, PERM, CPG>(a.g, a.b, u, a.pages_b[u.j], a.b.pk_slot0 + static_cast<int32_t>(u.j),
+            move_at<GATHER, U, PERM, CPG>(a.g, a.b, u, a.pages_b[u.j], a.first_b + static_cast<int32_t>(u.j),
                                           tid, lds);
         } else {
             const UnitPos u = decode_unit(a.g, a.r, idx);
@@ -384,7 +384,7 @@ __global__ __launch_bounds__(kThreads) void kvx_exchange_kernel(ExchangeArgs a)
                     pend = 0;
                 }
             }
-            move_at<SCATTER, U, PERM, CPS>(a.g, a.r, u, a.pages_r[u.j], a.r.pk_slot0 + static_cast<int32_t>(u.j),
+            move_at<SCATTER, U, PERM, CPS>(a.g, a.r, u, a.pages_r[u.j], a.first_r + static_cast<int32_t>(u.j),
                                            tid, lds);
             if constexpr (PUBLISH) pend++;
         }

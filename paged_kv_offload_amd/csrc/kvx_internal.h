@@ -135,11 +135,12 @@ static_assert(sizeof(MoveArgs) <= 4096, "kernel arguments are limited to 4 KiB")
 
 // Both directions in one launch (kvx_exchange): a BACKUP side `b` and a
 // RESTORE side `r`, each listing its pages in slot order (the slot of
-// pages_x[j] is x.pk_slot0 + j).
+// pages_x[j] is first_x + j; the sides' pk_slot0 is 0, the buffer start).
 struct ExchangeArgs {
     UnitGeom g;
     Side b, r;
     PublishArgs p;
+    int32_t first_b, first_r;
     int32_t pages_b[kMaxPairs];
     int32_t pages_r[kMaxPairs];
 };

@@ -288,6 +288,9 @@ def test_exchange_validation_fails_closed():
                 (dict(restore_ids=[2, 5]), K.KVX_E_INVAL, "page 2 is read by the backup"),
                 (dict(restore_src=0x1000000 + 16), K.KVX_E_INVAL, "overlap"),
                 (dict(backup_dst=0x2000000 + nb - 16), K.KVX_E_INVAL, "overlap"),
+                # one buffer for both sides: their layer slices must not overlap
+                (dict(restore_src=0x1000000, backup_layers=(0, 2), restore_layers=(1, 2)),
+                 K.KVX_E_INVAL, "overlap"),
                 (dict(restore_ids=[3, 3]), K.KVX_E_DUP, "more than once"),
                 (dict(backup_ids=[1, 64]), K.KVX_E_RANGE, "outside"),
                 (dict(restore_layers=(1, 3)), K.KVX_E_RANGE, "layer range"),
