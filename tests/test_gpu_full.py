@@ -187,3 +187,48 @@ def test_full_size_mla_layerwise_ready():
         K.kvx_ready_destroy(ready)
         host.free()
         pool.close()
+
+
+@pytest.mark.parametrize("name", ["llama8b", "trtllm_hnd"])
+def test_full_size_layer_pipelined_exchange(name):
+    """The benchmark's step at full size, in its launch configuration: BACKUP
+    of layer 0, one kvx_exchange per layer (backup of layer l + 1, restore of
+    layer l, both through the same packed buffer), RESTORE of the last
+    layer, zero-copy. The whole packed buffer and the whole allocation are
+    checked against the oracle's closed forms, and every layer is
+    published."""
+    t = torch()
+    w = WORKLOADS[name]
+    n = w.pages_per_request
+    print(f"\n[full] {name} exchange: pool {w.pool_bytes / 2**30:.1f} GiB, n={n}", flush=True)
+    L = oracle_layout(w)
+    src, dst = request_pair(w)
+    pool = DevicePool(w, generation=5)
+    P = w.payload_bytes(n)
+    host = K.HostBuffer(P)
+    synth.fill_gpu(host.ptr, P, w.seed + 2, 0)
+    t.cuda.synchronize()
+    stream = t.cuda.Stream()
+    ready = K.kvx_ready_create(w.num_layers, 5)
+    try:
+        Z = K.KVX_PATH_ZEROCOPY
+        K.kvx_backup(pool.handle, src, host.ptr, P, 0, 1, stream, Z)
+        for l in range(1, w.num_layers):
+            K.kvx_exchange(pool.handle, src, host.ptr, P, (l, l + 1), host.ptr, P, dst, (l - 1, l),
+                           ready, 0, stream, Z)
+        K.kvx_restore(pool.handle, host.ptr, P, dst, w.num_layers - 1, w.num_layers, ready, 0,
+                      stream, Z)
+        K.kvx_sync(stream)
+        assert K.kvx_ready_prefix(ready) == n
+        t0 = time.time()
+        bad, first = check_packed(w, L, w.seed, src, 0, w.num_layers, host.numpy())
+        print(f"[full] packed buffer checked in {time.time() - t0:.1f} s", flush=True)
+        assert bad == 0, f"backup: {bad} bytes differ, first at packed offset {first}"
+        t0 = time.time()
+        bad, first = check_alloc(w, L, w.seed, src, dst, 0, w.num_layers, pool.alloc)
+        print(f"[full] allocation checked in {time.time() - t0:.1f} s", flush=True)
+        assert bad == 0, f"restore: {bad} bytes differ, first at allocation byte {first}"
+    finally:
+        K.kvx_ready_destroy(ready)
+        host.free()
+        pool.close()

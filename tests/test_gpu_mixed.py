@@ -53,7 +53,7 @@ def piece_bytes_of(pool, w, page, layer, kv):
     return pool.tensor[layer, kv, page].contiguous().view(-1).view(torch().uint8).cpu().numpy()
 
 
-@pytest.mark.parametrize("path", ["zerocopy", "staged"])
+@pytest.mark.parametrize("path", ["zerocopy", "staged", "exchange"])
 def test_mixed_stream(path):
     t = torch()
     w = WORKLOADS["mixed"]
@@ -79,13 +79,22 @@ def test_mixed_stream(path):
         # one stream: rotating slots every 8 requests, destination sets every 32)
         t.cuda.synchronize()
         t0 = time.perf_counter()
-        for k, (kind, ids, slot, _) in enumerate(plan):
-            s = streams[k % NSTREAMS]
-            if kind == "backup":
-                K.kvx_backup(pool.handle, ids, slots[slot].ptr, P, 0, w.num_layers, s, PATHS[path])
-            else:
-                K.kvx_restore(pool.handle, slots[slot].ptr, P, ids, 0, w.num_layers, None, 0, s,
-                              PATHS[path])
+        if path == "exchange":
+            # backup k and restore k + 1 as one kvx_exchange, pairs on two streams
+            for i in range(0, len(plan), 2):
+                (kb, ib, sb, _), (kr, ir, sr, _) = plan[i], plan[i + 1]
+                assert kb == "backup" and kr == "restore"
+                K.kvx_exchange(pool.handle, ib, slots[sb].ptr, P, (0, w.num_layers), slots[sr].ptr, P,
+                               ir, (0, w.num_layers), None, 0, streams[(i // 2) % 2],
+                               K.KVX_PATH_ZEROCOPY)
+        else:
+            for k, (kind, ids, slot, _) in enumerate(plan):
+                s = streams[k % NSTREAMS]
+                if kind == "backup":
+                    K.kvx_backup(pool.handle, ids, slots[slot].ptr, P, 0, w.num_layers, s, PATHS[path])
+                else:
+                    K.kvx_restore(pool.handle, slots[slot].ptr, P, ids, 0, w.num_layers, None, 0, s,
+                                  PATHS[path])
         for s in streams:
             K.kvx_sync(s)
         wall = time.perf_counter() - t0
@@ -113,6 +122,8 @@ def test_mixed_stream(path):
         assert bad == 0, f"allocation: {bad} bytes differ, first at {first}"
 
         # untimed replay, one request at a time, sampled check of each
+        if path == "exchange":
+            path = "zerocopy"
         rng = np.random.default_rng(99)
         s = streams[0]
         for k, (kind, ids, slot, src) in enumerate(plan[:32]):
