@@ -52,7 +52,7 @@ PCIE_PEAK_GBS = 64.0      # MI355X host interface, PCIe 5.0 x16, published per-d
 # run; see profiles/pack_kernel_llama8b.txt). Valid only for the kernel source
 # they were taken on: reported as null once kernels.hip changes.
 MEASURED_TRAFFIC = {"kernels_hip_sha256": "fb6706a77828f1133c0624f8959ef9d7a380a210ed129f9d919ca26fb7883879",
-                    "bytes_per_launch": 4295182166}
+                    "bytes_per_launch": 4295182641}
 
 
 def log(msg):

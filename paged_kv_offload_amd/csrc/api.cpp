@@ -308,10 +308,12 @@ int unroll_for(const PoolGeom& g, const Tuning& t, bool host)
     // the LDS form runs units of 4, 8 or 16 rounds
     int max_unroll = static_cast<int>(permute && t.hnd_lds != 0 ? std::min<int64_t>(t.max_unroll, 16)
                                                                 : t.max_unroll);
-    // over the host link, 32 KiB units (measured: a zero-copy restore's
-    // first layer is ready 30% sooner than with 128 KiB units, at the same
-    // total rate)
-    if (host) max_unroll = std::min(max_unroll, 8);
+    // over the host link, 8 KiB units (measured on the llama8b request: the
+    // same 57 GB/s one way as 32 or 128 KiB units, the first layer of a
+    // zero-copy restore ready at 1.19 ms instead of 1.22 and 1.8, and the
+    // layer-pipelined exchange step at 95.4 GB/s against 88.9 with 32 KiB
+    // units; 4 KiB units hold the restore to 42 GB/s)
+    if (host) max_unroll = std::min(max_unroll, 2);
     return pick_unroll(g.piece_bytes, max_unroll, static_cast<int>(t.unit_rounds));
 }
 
