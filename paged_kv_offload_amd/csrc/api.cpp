@@ -1,8 +1,9 @@
 // api.cpp - the C ABI of kvx: handles and their lifecycle, the order of
 // validation (everything is checked before anything is enqueued), the path
 // executor (staged DMA through a device ring on a side stream, zero-copy
-// kernels on pinned host memory, or device-to-device), ready objects and
-// small utilities.
+// kernels on pinned host memory, or device-to-device), the exchange of a
+// backup and a restore in one launch sequence, ready objects and small
+// utilities.
 //
 // Ownership follows the RFC's split ([RFC] "Ownership"): the caller owns the
 // pool allocation, page IDs and the decision that pages are safe to read or

@@ -1,13 +1,14 @@
 // kernels.hip - gfx950 kernels of kvx: the piece gather (BACKUP pack), the
-// piece scatter (RESTORE unpack) with per-layer publish, and the bounded
-// ready-wait used by GPU-side consumers.
+// piece scatter (RESTORE unpack) with per-layer publish, both in one launch
+// (kvx_exchange), and the bounded ready-wait used by GPU-side consumers.
 //
 // Work decomposition. A launch moves the pieces (page, layer, kv) of a layer
 // range, every kv and a list of (page, slot) pairs carried in the kernel
 // arguments. Each piece (T*H*D*eb bytes, contiguous in every supported pool
 // layout and in the packed buffer) is cut into units of
-// kThreads * 16 * U bytes; one workgroup moves one unit per iteration of a
-// grid-stride loop, every lane issuing U independent 16-byte (dwordx4)
+// kThreads * 16 * U bytes; one workgroup moves one unit at a time (a
+// grid-stride loop, or unit numbers drawn from a queue where the order of
+// completion matters), every lane issuing U independent 16-byte (dwordx4)
 // loads before its U stores. Each wave owns U KiB of the unit, contiguous,
 // and moves it 1 KiB per instruction (measured on MI355X: 6-8% faster than
 // the workgroup sweeping the unit 4 KiB per round, for the same bytes).
