@@ -523,6 +523,10 @@ int run_op(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, void* buf, ui
     // ---- HIP from here on; nothing has been enqueued yet ----
     rc = resolve_device(pool);
     if (rc != KVX_OK) return rc;
+    if (ready && ready->device >= 0 && ready->device != pool->device)
+        return fail(KVX_E_INVAL, std::string(op) + ": the ready object's counts are on GPU " +
+                                     std::to_string(ready->device) + ", the pool on GPU " +
+                                     std::to_string(pool->device));
     DeviceGuard dg(pool->device);
     hipStream_t s = static_cast<hipStream_t>(stream_v);
     uint8_t* view = nullptr;
@@ -689,6 +693,10 @@ int run_exchange(kvx_pool* pool, const kvx_xfer* bk, const kvx_xfer* rs, kvx_rea
     const bool host = path == KVX_PATH_ZEROCOPY;
     int rc = resolve_device(pool);
     if (rc != KVX_OK) return rc;
+    if (ready && ready->device >= 0 && ready->device != pool->device)
+        return fail(KVX_E_INVAL, "exchange: the ready object's counts are on GPU " +
+                                     std::to_string(ready->device) + ", the pool on GPU " +
+                                     std::to_string(pool->device));
     DeviceGuard dg(pool->device);
     hipStream_t s = static_cast<hipStream_t>(stream_v);
     uint8_t *vb = nullptr, *vr = nullptr;
@@ -964,6 +972,50 @@ int kvx_plan_runs(const kvx_pool* pool, const int32_t* page_ids, int32_t n, int3
 
 // ---- ready objects -----------------------------------------------------------
 
+namespace {
+
+constexpr size_t kDeviceCountsMin = 2u << 20;   // own allocation, never a carved-out piece
+
+// Register a new ready handle.
+void add_ready(kvx_ready* r)
+{
+    std::lock_guard<std::mutex> lk(g_reg_mu);
+    g_readies.insert(r);
+}
+
+// Copies device counts [0, num) to `out` through the object's own stream.
+int read_device_counts(const kvx_ready* r, uint32_t* out, int32_t num)
+{
+    DeviceGuard dg(r->device);
+    KVX_HIP(hipMemcpyAsync(out, r->counts_dev, sizeof(uint32_t) * num, hipMemcpyDeviceToHost, r->query));
+    KVX_HIP(hipStreamSynchronize(r->query));
+    return KVX_OK;
+}
+
+int make_device_ready(int device, uint32_t* counts, bool owned, int32_t num_slots,
+                      uint64_t generation, kvx_ready** out)
+{
+    DeviceGuard dg(device);
+    hipStream_t q = nullptr;
+    KVX_HIP(hipStreamCreateWithFlags(&q, hipStreamNonBlocking));
+    kvx_ready* r = new (std::nothrow) kvx_ready();
+    if (!r) {
+        (void)hipStreamDestroy(q);
+        return fail(KVX_E_NOMEM, "ready: out of host memory");
+    }
+    r->num_slots = num_slots;
+    r->generation = generation;
+    r->counts_dev = counts;
+    r->device = device;
+    r->owned = owned;
+    r->query = q;
+    add_ready(r);
+    *out = r;
+    return KVX_OK;
+}
+
+}  // namespace
+
 int kvx_ready_create(int32_t num_slots, uint64_t generation, kvx_ready** out)
 {
     clear_error();
@@ -996,12 +1048,81 @@ int kvx_ready_create(int32_t num_slots, uint64_t generation, kvx_ready** out)
     r->counts = static_cast<uint32_t*>(p);
     r->counts_dev = static_cast<uint32_t*>(d);
     for (int32_t k = 0; k < num_slots; k++) __atomic_store_n(&r->counts[k], 0u, __ATOMIC_RELEASE);
-    {
-        std::lock_guard<std::mutex> lk(g_reg_mu);
-        g_readies.insert(r);
-    }
+    add_ready(r);
     *out = r;
     return KVX_OK;
+}
+
+
+int kvx_ready_create_device(int32_t device, int32_t num_slots, uint64_t generation, kvx_ready** out)
+{
+    clear_error();
+    if (!out) return fail(KVX_E_INVAL, "ready_create_device: out is NULL");
+    *out = nullptr;
+    if (num_slots < 1 || num_slots > (1 << 24))
+        return fail(KVX_E_INVAL, "ready_create_device: num_slots must be in [1, 2^24]");
+    int count = 0;
+    KVX_HIP(hipGetDeviceCount(&count));
+    if (device < 0 || device >= count)
+        return fail(KVX_E_INVAL, "ready_create_device: no GPU " + std::to_string(device));
+    DeviceGuard dg(device);
+    const size_t bytes = std::max(kDeviceCountsMin, sizeof(uint32_t) * num_slots);
+    void* p = nullptr;
+    hipError_t e = hipMalloc(&p, bytes);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(KVX_E_NOMEM, std::string("ready_create_device: hipMalloc failed: ") +
+                                     hipGetErrorString(e));
+    }
+    int rc = make_device_ready(device, static_cast<uint32_t*>(p), true, num_slots, generation, out);
+    if (rc != KVX_OK) {
+        (void)hipFree(p);
+        return rc;
+    }
+    e = hipMemsetAsync(p, 0, sizeof(uint32_t) * num_slots, (*out)->query);
+    if (e == hipSuccess) e = hipStreamSynchronize((*out)->query);
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        kvx_ready* r = *out;
+        *out = nullptr;
+        (void)kvx_ready_destroy(r);   // frees the counts and the stream
+        return hip_fail(e, "ready_create_device: clearing the counts");
+    }
+    return KVX_OK;
+}
+
+int kvx_ready_attach_device(void* counts_dev, int32_t num_slots, uint64_t generation, kvx_ready** out)
+{
+    clear_error();
+    if (!out) return fail(KVX_E_INVAL, "ready_attach_device: out is NULL");
+    *out = nullptr;
+    if (num_slots < 1 || num_slots > (1 << 24))
+        return fail(KVX_E_INVAL, "ready_attach_device: num_slots must be in [1, 2^24]");
+    if (!counts_dev || reinterpret_cast<uintptr_t>(counts_dev) % sizeof(uint32_t))
+        return fail(KVX_E_INVAL, "ready_attach_device: counts must be 4-byte aligned device memory");
+    int device = -1;
+    uint64_t after = 0;
+    if (!ipc_lookup(counts_dev, &device, &after)) {
+        hipPointerAttribute_t at;
+        std::memset(&at, 0, sizeof at);
+        if (hipPointerGetAttributes(&at, counts_dev) != hipSuccess || at.type != hipMemoryTypeDevice) {
+            (void)hipGetLastError();
+            return fail(KVX_E_INVAL, "ready_attach_device: counts are not device memory");
+        }
+        device = at.device;
+        hipDeviceptr_t base = nullptr;
+        size_t size = 0;
+        DeviceGuard dg(device);
+        if (hipMemGetAddressRange(&base, &size, counts_dev) == hipSuccess && base)
+            after = reinterpret_cast<uintptr_t>(base) + size - reinterpret_cast<uintptr_t>(counts_dev);
+        else
+            (void)hipGetLastError();
+    }
+    if (after && after < sizeof(uint32_t) * uint64_t(num_slots))
+        return fail(KVX_E_RANGE, "ready_attach_device: the allocation has no room for " +
+                                     std::to_string(num_slots) + " counts");
+    return make_device_ready(device, static_cast<uint32_t*>(counts_dev), false, num_slots, generation,
+                             out);
 }
 
 int kvx_ready_reset(kvx_ready* r)
@@ -1009,6 +1130,12 @@ int kvx_ready_reset(kvx_ready* r)
     clear_error();
     if (!ready_known(r)) return fail(KVX_E_INVAL, "ready_reset: unknown ready handle");
     if (!r->live.load()) return fail(KVX_E_STALE, "ready_reset: ready object was destroyed");
+    if (r->device >= 0) {
+        DeviceGuard dg(r->device);
+        KVX_HIP(hipMemsetAsync(r->counts_dev, 0, sizeof(uint32_t) * r->num_slots, r->query));
+        KVX_HIP(hipStreamSynchronize(r->query));
+        return KVX_OK;
+    }
     for (int32_t k = 0; k < r->num_slots; k++) __atomic_store_n(&r->counts[k], 0u, __ATOMIC_RELEASE);
     return KVX_OK;
 }
@@ -1025,10 +1152,21 @@ int kvx_ready_destroy(kvx_ready* r)
         log_warn("ready_destroy: ready object was already destroyed");
         return KVX_OK;
     }
-    hipError_t e = hipHostFree(r->counts);
-    if (e != hipSuccess) {
-        (void)hipGetLastError();
-        log_warn(std::string("ready_destroy: hipHostFree failed: ") + hipGetErrorString(e));
+    if (r->device >= 0) {
+        DeviceGuard dg(r->device);
+        hipError_t e = hipStreamSynchronize(r->query);
+        if (e == hipSuccess && r->owned) e = hipFree(r->counts_dev);
+        if (e == hipSuccess) e = hipStreamDestroy(r->query);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            log_warn(std::string("ready_destroy: releasing device counts failed: ") + hipGetErrorString(e));
+        }
+    } else {
+        hipError_t e = hipHostFree(r->counts);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            log_warn(std::string("ready_destroy: hipHostFree failed: ") + hipGetErrorString(e));
+        }
     }
     r->counts = nullptr;
     r->counts_dev = nullptr;
@@ -1042,6 +1180,13 @@ int kvx_layer_ready(const kvx_ready* r, int32_t slot, int32_t* published)
     if (!r->live.load()) return fail(KVX_E_STALE, "layer_ready: ready object was destroyed");
     if (slot < 0 || slot >= r->num_slots || !published)
         return fail(KVX_E_RANGE, "layer_ready: slot out of range");
+    if (r->device >= 0) {
+        std::vector<uint32_t> c(slot + 1);
+        int rc = read_device_counts(r, c.data(), slot + 1);
+        if (rc != KVX_OK) return rc;
+        *published = static_cast<int32_t>(c[slot]);
+        return KVX_OK;
+    }
     *published = static_cast<int32_t>(__atomic_load_n(&r->counts[slot], __ATOMIC_ACQUIRE));
     return KVX_OK;
 }
@@ -1052,6 +1197,13 @@ int kvx_ready_prefix(const kvx_ready* r, int32_t* prefix)
     if (!ready_known(r)) return fail(KVX_E_INVAL, "ready_prefix: unknown ready handle");
     if (!r->live.load()) return fail(KVX_E_STALE, "ready_prefix: ready object was destroyed");
     if (!prefix) return fail(KVX_E_INVAL, "ready_prefix: prefix is NULL");
+    if (r->device >= 0) {
+        std::vector<uint32_t> c(r->num_slots);
+        int rc = read_device_counts(r, c.data(), r->num_slots);
+        if (rc != KVX_OK) return rc;
+        *prefix = static_cast<int32_t>(*std::min_element(c.begin(), c.end()));
+        return KVX_OK;
+    }
     uint32_t m = __atomic_load_n(&r->counts[0], __ATOMIC_ACQUIRE);
     for (int32_t k = 1; k < r->num_slots; k++)
         m = std::min(m, __atomic_load_n(&r->counts[k], __ATOMIC_ACQUIRE));

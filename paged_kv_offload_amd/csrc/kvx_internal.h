@@ -50,8 +50,11 @@ struct kvx_ready {
     std::atomic<bool> live{true};
     int32_t num_slots = 0;
     uint64_t generation = 0;
-    uint32_t* counts = nullptr;      // host view (fine-grained pinned)
-    uint32_t* counts_dev = nullptr;  // device view of the same memory
+    uint32_t* counts = nullptr;      // host view (fine-grained pinned); null for device counts
+    uint32_t* counts_dev = nullptr;  // device view of the same memory, or the device counts
+    int device = -1;                 // GPU holding device counts; -1 for pinned host counts
+    bool owned = true;               // allocated here (freed by kvx_ready_destroy)
+    hipStream_t query = nullptr;     // non-blocking stream for copies of device counts
 };
 
 namespace kvx {

@@ -81,6 +81,8 @@ SIGNATURES = [
                                    _i32]),
     ("kvx_plan_runs", ctypes.c_int, [_vp, _P(_i32), _i32, _P(_i32), _i32, _P(_i32)]),
     ("kvx_ready_create", ctypes.c_int, [_i32, _u64, _P(_vp)]),
+    ("kvx_ready_create_device", ctypes.c_int, [_i32, _i32, _u64, _P(_vp)]),
+    ("kvx_ready_attach_device", ctypes.c_int, [_vp, _i32, _u64, _P(_vp)]),
     ("kvx_ready_reset", ctypes.c_int, [_vp]),
     ("kvx_ready_destroy", ctypes.c_int, [_vp]),
     ("kvx_layer_ready", ctypes.c_int, [_vp, _i32, _P(_i32)]),
@@ -352,6 +354,18 @@ def kvx_plan_runs(pool: int, page_ids: Iterable[int]) -> np.ndarray:
 def kvx_ready_create(num_slots: int, generation: int) -> int:
     out = _vp()
     _check(lib().kvx_ready_create(num_slots, generation, ctypes.byref(out)))
+    return out.value
+
+
+def kvx_ready_create_device(device: int, num_slots: int, generation: int) -> int:
+    out = _vp()
+    _check(lib().kvx_ready_create_device(device, num_slots, generation, ctypes.byref(out)))
+    return out.value
+
+
+def kvx_ready_attach_device(counts_dev: int, num_slots: int, generation: int) -> int:
+    out = _vp()
+    _check(lib().kvx_ready_attach_device(counts_dev, num_slots, generation, ctypes.byref(out)))
     return out.value
 
 

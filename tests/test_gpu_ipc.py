@@ -74,13 +74,13 @@ def test_pool_shared_with_a_second_process(case, tmp_path):
     perm = synth.page_perm(w.seed, w.num_pages)
     src, dst = perm[:n].copy(), perm[n:2 * n].copy()
     params = tmp_path / "params.json"
-    params.write_text(json.dumps({"workload": dataclasses.asdict(w), "seed": w.seed}))
+    params.write_text(json.dumps({"workload": dataclasses.asdict(w), "seed": w.seed, "generation": 11}))
     pages = tmp_path / "pages.json"
     pages.write_text(json.dumps({"src": src.tolist(), "dst": dst.tolist()}))
     proc = subprocess.Popen([sys.executable, os.path.join(ROOT, "tests", "ipc_exporter.py"),
                              str(params)], stdin=subprocess.PIPE, stdout=subprocess.PIPE,
                             stderr=subprocess.PIPE, text=True, env=dict(os.environ))
-    pool = base = None
+    pool = base = ready = rbase = None
     try:
         first = read_reply(proc)
         assert "handle" in first, first
@@ -92,6 +92,13 @@ def test_pool_shared_with_a_second_process(case, tmp_path):
         base2, _, off2, _ = K.kvx_ipc_import(handle)
         assert base2 == base and off2 == w.byte_offset
         K.kvx_ipc_close(base2)
+        # the exporter's ready counts: this process publishes into them
+        rbase, _, roff, _ = K.kvx_ipc_import(bytes.fromhex(first["ready_handle"]))
+        ready = K.kvx_ready_attach_device(rbase + roff, w.num_layers, 11)
+        assert K.kvx_ready_prefix(ready) == 0
+        proc.stdin.write(f"arm {n}\n")
+        proc.stdin.flush()
+        assert read_reply(proc).get("armed")
         L = oracle_layout(w)
         P = w.payload_bytes(n)
         host = K.HostBuffer(P)
@@ -100,13 +107,18 @@ def test_pool_shared_with_a_second_process(case, tmp_path):
             K.kvx_sync(None)
             bad, at = oracle.check_backup_gen(L, w.seed, src, 0, w.num_layers, host.numpy(), 0)
             assert bad == 0, f"backup of the imported pool: {bad} bytes differ, first at {at}"
-            K.kvx_restore(pool, host.ptr, P, dst, 0, w.num_layers, None, 0, None,
+            K.kvx_restore(pool, host.ptr, P, dst, 0, w.num_layers, ready, 0, None,
                           K.KVX_PATH_STAGED)
             K.kvx_sync(None)
+            assert K.kvx_ready_prefix(ready) == n
         finally:
             host.free()
         K.kvx_unregister_pool(pool)
         pool = None
+        K.kvx_ready_destroy(ready)
+        ready = None
+        K.kvx_ipc_close(rbase)
+        rbase = None
         K.kvx_ipc_close(base)
         with pytest.raises(K.KvxError):
             K.kvx_ipc_close(base)          # the last open was closed
@@ -115,6 +127,9 @@ def test_pool_shared_with_a_second_process(case, tmp_path):
         proc.stdin.flush()
         res = read_reply(proc)
         assert res.get("bad_bytes") == 0, res
+        # the exporter's GPU wait saw the count this process published, and
+        # so does its host query
+        assert res.get("wait_status") == 1 and res.get("prefix") == n, res
         proc.stdin.write("exit\n")
         proc.stdin.flush()
         assert read_reply(proc).get("exited")
@@ -122,6 +137,10 @@ def test_pool_shared_with_a_second_process(case, tmp_path):
     finally:
         if pool:
             K.kvx_unregister_pool(pool)
+        if ready:
+            K.kvx_ready_destroy(ready)
+        if rbase:
+            K.kvx_ipc_close(rbase)
         if base:
             K.kvx_ipc_close(base)
         if proc.poll() is None:

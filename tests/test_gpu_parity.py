@@ -600,3 +600,50 @@ def test_hnd_through_lds(case, path, stream):
         pool.close()
     finally:
         K.kvx_set_option(K.KVX_OPT_HND_LDS, old)
+
+
+@pytest.mark.parametrize("path", ["staged", "zerocopy", "device"])
+def test_device_ready_object(path, stream):
+    """Ready counts in device memory: a restore publishes into them, the host
+    queries copy them back, a GPU wait sees them, a second handle attached
+    to the same counts reads the same values, and reset clears them."""
+    t = torch()
+    w, n = SMALL["mla_small"]
+    L = oracle_layout(w)
+    pool = DevicePool(w, seed=311, generation=12)
+    img = pool.host_image()
+    src, dst = pages(w, n)
+    nb = w.host_bytes(n)
+    pk = Packed(w, n, path, fill_seed=51)
+    ready = K.kvx_ready_create_device(0, w.num_layers + 2, 12)
+    other = K.kvx_ready_attach_device(K.kvx_ready_slot_ptr(ready, 0), w.num_layers + 2, 12)
+    status = t.zeros(1, dtype=t.int32, device="cuda")
+    consumer = t.cuda.Stream()
+    try:
+        assert K.kvx_ready_prefix(ready) == 0
+        K.kvx_restore(pool.handle, pk.ptr, nb, dst, 0, w.num_layers, ready, 1, stream, PATHS[path])
+        K.kvx_ready_wait_gpu(ready, w.num_layers, n, consumer, 5_000_000, status)
+        K.kvx_sync(stream)
+        K.kvx_sync(consumer)
+        assert int(status.item()) == 1
+        counts = [K.kvx_layer_ready(ready, s) for s in range(w.num_layers + 2)]
+        assert counts == [0] + [n] * w.num_layers + [0]
+        assert [K.kvx_layer_ready(other, s) for s in range(w.num_layers + 2)] == counts
+        assert K.kvx_ready_prefix(ready) == 0 == K.kvx_ready_prefix(other)
+        want = oracle.restore(L, img, synth.gen_bytes(51, 0, nb), dst, 0, w.num_layers)
+        after = pool.host_image()
+        assert np.array_equal(after, want), diff_report(after, want)
+        K.kvx_ready_reset(other)
+        assert [K.kvx_layer_ready(ready, s) for s in range(w.num_layers + 2)] == [0] * (w.num_layers + 2)
+        # a ready object of another generation is refused
+        stale = K.kvx_ready_create_device(0, w.num_layers, 13)
+        with pytest.raises(K.KvxError) as e:
+            K.kvx_restore(pool.handle, pk.ptr, nb, dst, 0, w.num_layers, stale, 0, stream,
+                          PATHS[path])
+        assert e.value.code == K.KVX_E_STALE
+        K.kvx_ready_destroy(stale)
+    finally:
+        K.kvx_ready_destroy(other)
+        K.kvx_ready_destroy(ready)
+        pk.close()
+        pool.close()
