@@ -51,8 +51,8 @@ PCIE_PEAK_GBS = 64.0      # MI355X host interface, PCIe 5.0 x16, published per-d
 # (FETCH_SIZE, WRITE_SIZE, scaled by a plain 2 GiB device copy in the same
 # run; see profiles/pack_kernel_llama8b.txt). Valid only for the kernel source
 # they were taken on: reported as null once kernels.hip changes.
-MEASURED_TRAFFIC = {"kernels_hip_sha256": "fb6706a77828f1133c0624f8959ef9d7a380a210ed129f9d919ca26fb7883879",
-                    "bytes_per_launch": 4295182641}
+MEASURED_TRAFFIC = {"kernels_hip_sha256": "a30559ece8139a73f60a5d1a28a838edaf4f4dcec6497b31a18b9645ea4b7aa1",
+                    "bytes_per_launch": 4295182194}
 
 
 def log(msg):

@@ -36,6 +36,17 @@ SMALL = {
     "ragged_hnd2": (Workload(name="ragged_hnd2", outer=("layer", "page", "kv"), inner="HND",
                              num_pages=300, num_layers=2, num_kv=1, page_size=7, num_heads=3,
                              head_dim=96, dtype_bytes=2, pages_per_request=100, seed=203), 100),
+    # degenerate head-major pools: one head, or one token per page (HND is NHD)
+    "hnd_h1": (Workload(name="hnd_h1", outer=("layer", "kv", "page"), inner="HND", num_pages=100,
+                        num_layers=2, num_kv=2, page_size=16, num_heads=1, head_dim=64, dtype_bytes=2,
+                        pages_per_request=30, seed=205), 30),
+    "hnd_t1": (Workload(name="hnd_t1", outer=("page", "layer", "kv"), inner="HND", num_pages=200,
+                        num_layers=2, num_kv=2, page_size=1, num_heads=8, head_dim=64, dtype_bytes=2,
+                        pages_per_request=50, seed=206), 50),
+    # 4-byte elements, 16-byte rows (one vector per row), head-major
+    "hnd_f32_rows16": (Workload(name="hnd_f32_rows16", outer=("kv", "page", "layer"), inner="HND",
+                                num_pages=64, num_layers=3, num_kv=2, page_size=4, num_heads=3,
+                                head_dim=4, dtype_bytes=4, pages_per_request=20, seed=207), 20),
 }
 
 
@@ -644,6 +655,34 @@ def test_device_ready_object(path, stream):
         K.kvx_ready_destroy(stale)
     finally:
         K.kvx_ready_destroy(other)
+        K.kvx_ready_destroy(ready)
+        pk.close()
+        pool.close()
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+def test_empty_work_is_a_noop_on_the_gpu(path, stream):
+    """n = 0 and empty layer ranges move nothing and publish nothing (a
+    restore of 0 pages has nothing to publish: every count stays at its
+    value, and a count of 0 already equals n)."""
+    w, n = SMALL["llama_small"]
+    pool = DevicePool(w, seed=313, generation=14)
+    img = pool.host_image()
+    pk = Packed(w, n, path, fill_seed=61)
+    ready = K.kvx_ready_create(w.num_layers, 14)
+    try:
+        src, dst = pages(w, n)
+        K.kvx_restore(pool.handle, pk.ptr, pk.nbytes, [], 0, w.num_layers, ready, 0, stream, PATHS[path])
+        K.kvx_restore(pool.handle, pk.ptr, pk.nbytes, dst, 1, 1, ready, 0, stream, PATHS[path])
+        K.kvx_backup(pool.handle, [], pk.ptr, pk.nbytes, 0, w.num_layers, stream, PATHS[path])
+        if path != "staged":
+            K.kvx_exchange(pool.handle, [], pk.ptr, pk.nbytes, (0, w.num_layers), pk.ptr, pk.nbytes,
+                           [], (0, w.num_layers), ready, 0, stream, PATHS[path])
+        K.kvx_sync(stream)
+        assert [K.kvx_layer_ready(ready, s) for s in range(w.num_layers)] == [0] * w.num_layers
+        assert np.array_equal(pool.host_image(), img)
+        assert np.array_equal(pk.numpy(), synth.gen_bytes(61, 0, pk.nbytes))
+    finally:
         K.kvx_ready_destroy(ready)
         pk.close()
         pool.close()
