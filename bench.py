@@ -51,7 +51,7 @@ PCIE_PEAK_GBS = 64.0      # MI355X host interface, PCIe 5.0 x16, published per-d
 # (FETCH_SIZE, WRITE_SIZE, scaled by a plain 2 GiB device copy in the same
 # run; see profiles/pack_kernel_llama8b.txt). Valid only for the kernel source
 # they were taken on: reported as null once kernels.hip changes.
-MEASURED_TRAFFIC = {"kernels_hip_sha256": "a30559ece8139a73f60a5d1a28a838edaf4f4dcec6497b31a18b9645ea4b7aa1",
+MEASURED_TRAFFIC = {"workload": "llama8b", "kernels_hip_sha256": "a30559ece8139a73f60a5d1a28a838edaf4f4dcec6497b31a18b9645ea4b7aa1",
                     "bytes_per_launch": 4295182194}
 
 
@@ -181,12 +181,14 @@ def main():
     try:
         import hashlib
         with open(os.path.join(ROOT, "paged_kv_offload_amd", "csrc", "kernels.hip"), "rb") as f:
-            if hashlib.sha256(f.read()).hexdigest() == MEASURED_TRAFFIC["kernels_hip_sha256"]:
+            if (hashlib.sha256(f.read()).hexdigest() == MEASURED_TRAFFIC["kernels_hip_sha256"]
+                    and w.name == MEASURED_TRAFFIC["workload"]):
                 traffic = MEASURED_TRAFFIC["bytes_per_launch"]
     except OSError:
         pass
     roofline = {"bound": "hbm",
-                "kernel": "kvx_move_kernel<GATHER> (pack of one 2 GiB request, device path)",
+                "kernel": f"kvx_move_kernel<GATHER> (pack of one {P / 2**30:.2f} GiB {w.name} request, "
+                          f"device path)",
                 "achieved": round(pack_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(pack_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
                 "algorithmic_bytes_per_launch": 2 * P,

@@ -390,8 +390,13 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
     a.s.pk_slot0 = tg.pk_slot0;
     set_publish(pub, &a.p);
     const int64_t limit = (int64_t(1) << 31) - 1;
-    for (size_t p0 = 0; p0 < npairs; p0 += kMaxPairs) {
-        const size_t np = std::min<size_t>(kMaxPairs, npairs - p0);
+    // pairs per launch: at most kMaxPairs, spread evenly over the launches
+    // (512 pages as 256 + 256, not 448 + 64)
+    const size_t per_launch = npairs ? (npairs + (npairs + kMaxPairs - 1) / kMaxPairs - 1) /
+                                           ((npairs + kMaxPairs - 1) / kMaxPairs)
+                                     : 1;
+    for (size_t p0 = 0; p0 < npairs; p0 += per_launch) {
+        const size_t np = std::min<size_t>(per_launch, npairs - p0);
         for (size_t j = 0; j < np; j++) {
             a.pairs[2 * j] = pairs[p0 + j].page;
             a.pairs[2 * j + 1] = pairs[p0 + j].slot;
@@ -730,8 +735,13 @@ int run_exchange(kvx_pool* pool, const kvx_xfer* bk, const kvx_xfer* rs, kvx_rea
     set_publish(&pub, &a.p);
     a.g.unit_order = 0;
     const int64_t cpp = a.g.chunks_per_piece;
-    auto side = [&](Side* x, const kvx_xfer* xf, uint8_t* view, int32_t* pages, int64_t p0) {
-        const int64_t np = std::max<int64_t>(0, std::min<int64_t>(kMaxPairs, xf->n - p0));
+    // each side's pages spread evenly over the launches
+    const int64_t launches = std::max<int64_t>((bk->n + kMaxPairs - 1) / kMaxPairs,
+                                               (rs->n + kMaxPairs - 1) / kMaxPairs);
+    const int64_t per_b = (bk->n + launches - 1) / launches;
+    const int64_t per_r = (rs->n + launches - 1) / launches;
+    auto side = [&](Side* x, const kvx_xfer* xf, uint8_t* view, int32_t* pages, int64_t p0, int64_t per) {
+        const int64_t np = std::max<int64_t>(0, std::min<int64_t>(per, xf->n - p0));
         x->packed = view;
         x->pk_lc_stride = int64_t(xf->n) * g.piece_bytes;
         x->pk_layer0 = 0;
@@ -741,12 +751,11 @@ int run_exchange(kvx_pool* pool, const kvx_xfer* bk, const kvx_xfer* rs, kvx_rea
         for (int64_t j = 0; j < np; j++) pages[j] = xf->page_ids[p0 + j];
         return int64_t(xf->layer_end - xf->layer_begin) * g.num_kv * np * cpp;
     };
-    const int64_t launches = std::max<int64_t>((bk->n + kMaxPairs - 1) / kMaxPairs,
-                                               (rs->n + kMaxPairs - 1) / kMaxPairs);
     for (int64_t k = 0; k < launches; k++) {
-        const int64_t ub = side(&a.b, bk, vb, a.pages_b, k * kMaxPairs);
-        const int64_t ur = side(&a.r, rs, vr, a.pages_r, k * kMaxPairs);
-        a.first_b = a.first_r = static_cast<int32_t>(k * kMaxPairs);
+        const int64_t ub = side(&a.b, bk, vb, a.pages_b, k * per_b, per_b);
+        const int64_t ur = side(&a.r, rs, vr, a.pages_r, k * per_r, per_r);
+        a.first_b = static_cast<int32_t>(k * per_b);
+        a.first_r = static_cast<int32_t>(k * per_r);
         if (ub + ur >= (int64_t(1) << 31)) {
             rc = fail(KVX_E_INVAL, "exchange: one launch would have too many work units");
             break;
