@@ -79,6 +79,9 @@ def main():
                     help="skip the per-path, pipelined and latency measurements")
     ap.add_argument("--kernel-only", action="store_true",
                     help="time only the device pack/unpack kernels (for counter runs)")
+    ap.add_argument("--set", action="append", default=[], metavar="OPTION=VALUE",
+                    help="kvx_set_option before timing, e.g. --set hnd_lds=0 (names of the "
+                         "KVX_OPT_* constants, lower case); recorded in config.options")
     ap.add_argument("--all-workloads", action="store_true",
                     help="instead of the headline step, print one line per workload with its own "
                          "figures (tiny: latency; mla: layer-0-ready; trtllm: HND rates; mixed: "
@@ -111,6 +114,15 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     K.lib()
+    options = {}
+    for item in args.set:
+        name, _, value = item.partition("=")
+        const = getattr(K, "KVX_OPT_" + name.upper(), None)
+        if const is None or not value.lstrip("-").isdigit():
+            print(json.dumps({"error": f"--set {item}: unknown option or non-integer value"}), flush=True)
+            sys.exit(2)
+        K.kvx_set_option(const, int(value))
+        options[name.lower()] = int(value)
     if args.all_workloads:
         all_workloads()
         return
@@ -195,7 +207,7 @@ def main():
                 "avg_launch_ms": round(median(t_pack) * 1e3, 4)}
     if args.kernel_only:
         print(json.dumps({"roofline": roofline, "unpack_gbs": round(unpack_gbs, 1),
-                          "d2d_copy_gbs": round(d2d_gbs, 1)}), flush=True)
+                          "d2d_copy_gbs": round(d2d_gbs, 1), "options": options}), flush=True)
         return
 
     # ---- pinned host-link peaks: 1 GiB hipMemcpyAsync, median of 10 ----
@@ -367,7 +379,8 @@ def main():
         "dtype": "u8",
         "data": "synthetic",
         "config": {"workload": w.description, "pages_per_request": n, "layers": w.num_layers,
-                   "payload_bytes_per_op": P, "path": path_name, "schedule": schedule},
+                   "payload_bytes_per_op": P, "path": path_name, "schedule": schedule,
+                   "options": options},
         "roofline": roofline,
         "unpack_roofline": {"achieved": round(unpack_gbs, 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(unpack_gbs / HBM_PEAK_GBS, 4)},
