@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         L.kvxo_piece_start.restype = i64
         L.kvxo_backup.argtypes = [lp, u8p, i32p, i64, i64, i64, u8p]
         L.kvxo_restore.argtypes = [lp, u8p, u8p, i32p, i64, i64, i64]
+        L.kvxo_backup_slots.argtypes = [lp, u8p, i32p, i32p, i64, i64, i64, i64, u8p]
+        L.kvxo_restore_slots.argtypes = [lp, u8p, u8p, i32p, i32p, i64, i64, i64, i64]
         L.kvxo_nhd_to_hnd.argtypes = [u8p, u8p, i64, i64, i64]
         L.kvxo_hnd_to_nhd.argtypes = [u8p, u8p, i64, i64, i64]
         L.kvxo_ready_prefix.argtypes = [ctypes.c_void_p, i64]
@@ -146,6 +148,46 @@ def restore(layout: Layout, alloc: np.ndarray, host: np.ndarray, ids: Sequence[i
     assert host.size >= layout.host_bytes(len(ids))
     c = layout.c()
     lib().kvxo_restore(ctypes.byref(c), _ptr(out), _ptr(host), _ptr(ids), len(ids), l0, l1)
+    return out
+
+
+def host_pool_bytes(layout: Layout, num_slots: int) -> int:
+    """Bytes of a slot-addressed host pool of num_slots slots per (layer, kv)."""
+    return layout.host_bytes(num_slots)
+
+
+def backup_slots(layout: Layout, alloc: np.ndarray, ids: Sequence[int], slots: Sequence[int],
+                 num_slots: int, l0: int, l1: int, host: np.ndarray = None) -> np.ndarray:
+    """BACKUP of `ids` into host slots `slots` of a host pool of num_slots
+    slots per (layer, kv), layers [l0, l1); other slots keep their bytes."""
+    ids, slots = _ids(ids), _ids(slots)
+    assert ids.size == slots.size and (slots.size == 0 or 0 <= slots.min() <= slots.max() < num_slots)
+    assert alloc.dtype == np.uint8 and alloc.flags.c_contiguous
+    if host is None:
+        host = np.zeros(layout.host_bytes(num_slots), dtype=np.uint8)
+    assert host.dtype == np.uint8 and host.flags.c_contiguous
+    assert host.size >= layout.host_bytes(num_slots)
+    c = layout.c()
+    lib().kvxo_backup_slots(ctypes.byref(c), _ptr(alloc), _ptr(ids), _ptr(slots), len(ids), num_slots,
+                            l0, l1, _ptr(host))
+    return host
+
+
+def restore_slots(layout: Layout, alloc: np.ndarray, host: np.ndarray, slots: Sequence[int],
+                  ids: Sequence[int], num_slots: int, l0: int, l1: int,
+                  out: np.ndarray = None) -> np.ndarray:
+    """RESTORE of host slots `slots` into pages `ids`, layers [l0, l1). A new
+    allocation unless `out` is given (it may be `alloc`)."""
+    ids, slots = _ids(ids), _ids(slots)
+    assert ids.size == slots.size and (slots.size == 0 or 0 <= slots.min() <= slots.max() < num_slots)
+    if out is None:
+        out = np.array(alloc, dtype=np.uint8, copy=True)
+    elif out is not alloc:
+        out[...] = alloc
+    assert host.dtype == np.uint8 and host.size >= layout.host_bytes(num_slots)
+    c = layout.c()
+    lib().kvxo_restore_slots(ctypes.byref(c), _ptr(out), _ptr(host), _ptr(slots), _ptr(ids), len(ids),
+                             num_slots, l0, l1)
     return out
 
 

@@ -163,6 +163,53 @@ void kvxo_restore(const kvxo_layout* L, uint8_t* alloc, const uint8_t* host, con
 }
 
 /* ---------------------------------------------------------------------------
+ * BACKUP and RESTORE against a slot-addressed host pool.
+ * [RFC, "Ownership"]: the data plane owns the host KV physical allocation,
+ * so host pages live in slots of a host pool that it hands out, and a
+ * BACKUP names, next to each source page, the host slot that receives it;
+ * a RESTORE names the host slot to read for each destination page. Reading
+ * (the pages give no host layout): the pool is layer-major NHD like the
+ * packed buffer, host[l][c][s][t][h][d] with S slots per (layer, kv), and
+ * host slot slots[i] pairs with page ids[i]. With slots = 0..n-1 and S = n
+ * this is the packed buffer of kvxo_backup / kvxo_restore.
+ * ------------------------------------------------------------------------- */
+void kvxo_backup_slots(const kvxo_layout* L, const uint8_t* alloc, const int32_t* ids,
+                       const int32_t* slots, int64_t n, int64_t num_slots, int64_t l0, int64_t l1,
+                       uint8_t* host)
+{
+    const int64_t rb = kvxo_row_bytes(L);
+    for (int64_t l = l0; l < l1; l++)
+        for (int64_t c = 0; c < L->num_kv; c++)
+            for (int64_t i = 0; i < n; i++)
+                for (int64_t t = 0; t < L->page_size; t++)
+                    for (int64_t h = 0; h < L->num_heads; h++)
+                        for (int64_t b = 0; b < rb; b++) {
+                            int64_t src = kvxo_piece_start(L, ids[i], l, c)
+                                        + kvxo_row_in_piece(L, t, h) * rb + b;
+                            int64_t dst = kvxo_host_row(L, num_slots, l, c, slots[i], t, h) * rb + b;
+                            host[dst] = alloc[src];
+                        }
+}
+
+void kvxo_restore_slots(const kvxo_layout* L, uint8_t* alloc, const uint8_t* host,
+                        const int32_t* slots, const int32_t* ids, int64_t n, int64_t num_slots,
+                        int64_t l0, int64_t l1)
+{
+    const int64_t rb = kvxo_row_bytes(L);
+    for (int64_t l = l0; l < l1; l++)
+        for (int64_t c = 0; c < L->num_kv; c++)
+            for (int64_t i = 0; i < n; i++)
+                for (int64_t t = 0; t < L->page_size; t++)
+                    for (int64_t h = 0; h < L->num_heads; h++)
+                        for (int64_t b = 0; b < rb; b++) {
+                            int64_t dst = kvxo_piece_start(L, ids[i], l, c)
+                                        + kvxo_row_in_piece(L, t, h) * rb + b;
+                            int64_t src = kvxo_host_row(L, num_slots, l, c, slots[i], t, h) * rb + b;
+                            alloc[dst] = host[src];
+                        }
+}
+
+/* ---------------------------------------------------------------------------
  * Layout permutation of one piece.
  * [RAWIPC, "share/rebuild chain" and "integration"]: NHD is token-major,
  * HND is head-major; a row of D elements stays contiguous in both.

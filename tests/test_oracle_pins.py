@@ -280,3 +280,90 @@ def test_ready_prefix_is_minimum():
     assert oracle.ready_prefix([256] * 61) == 256
     assert oracle.ready_prefix([64, 64, 0, 64]) == 0
     assert oracle.ready_prefix([9]) == 9
+
+
+# ---------------------------------------------------------------------------
+# slot-addressed host pool
+# ---------------------------------------------------------------------------
+def numpy_backup_slots(L, alloc, ids, slots, S, l0, l1, host):
+    out = host.copy()
+    hv = out.reshape(L.num_layers, L.num_kv, S, L.page_size, L.num_heads, L.row_bytes)
+    hv[l0:l1, :, np.asarray(slots, dtype=np.int64)] = \
+        numpy_pool_view(L, alloc)[l0:l1][:, :, np.asarray(ids, dtype=np.int64)]
+    return out
+
+
+def numpy_restore_slots(L, alloc, host, slots, ids, S, l0, l1):
+    out = alloc.copy()
+    hv = host.reshape(L.num_layers, L.num_kv, S, L.page_size, L.num_heads, L.row_bytes)
+    pv = numpy_pool_view(L, out)
+    for l in range(l0, l1):
+        pv[l, :, np.asarray(ids, dtype=np.int64)] = \
+            hv[l][:, np.asarray(slots, dtype=np.int64)].transpose(1, 0, 2, 3, 4)
+    return out
+
+
+@pytest.mark.parametrize("outer", OUTER_ORDERS)
+@pytest.mark.parametrize("inner", [NHD, HND])
+def test_slot_backup_restore_match_numpy(outer, inner):
+    """Host slots: the oracle equals numpy advanced-index assignment into a
+    [layer][kv][slot][token][head][row] view of the host pool, slots that
+    no page names keep their bytes, and a restore may read one slot twice."""
+    rng = np.random.default_rng(17 + hash((outer, inner)) % 2**32)
+    L = rand_layout(rng, outer, inner, offset=32)
+    alloc = rand_alloc(rng, L)
+    S = 9
+    ids, slots = [4, 0, 6, 2], [7, 2, 0, 5]
+    host0 = rng.integers(0, 256, L.host_bytes(S), dtype=np.uint8)
+    for l0, l1 in ((0, 3), (1, 2)):
+        got = oracle.backup_slots(L, alloc, ids, slots, S, l0, l1, host=host0.copy())
+        assert np.array_equal(got, numpy_backup_slots(L, alloc, ids, slots, S, l0, l1, host0))
+        rs, rd = [7, 7, 3], [1, 5, 3]          # slot 7 read twice
+        got = oracle.restore_slots(L, alloc, host0, rs, rd, S, l0, l1)
+        assert np.array_equal(got, numpy_restore_slots(L, alloc, host0, rs, rd, S, l0, l1))
+
+
+def test_slot_brute_force_and_round_trip():
+    """Every placement of up to two distinct pages of a 5-page pool into 4
+    host slots, and the round trip restore_slots(backup_slots(x)) back into
+    other pages: those pages receive the source pages' bytes and nothing
+    else changes."""
+    L = Layout(outer=(LAYER, PAGE, KV), inner=HND, num_pages=5, num_layers=2, num_kv=2,
+               page_size=3, num_heads=2, head_dim=1, dtype_bytes=2, byte_offset=8)
+    rng = np.random.default_rng(23)
+    alloc = rand_alloc(rng, L)
+    S = 4
+    host0 = rng.integers(0, 256, L.host_bytes(S), dtype=np.uint8)
+    pb = L.piece_bytes
+    for k in (1, 2):
+        for ids in itertools.permutations(range(5), k):
+            for slots in itertools.permutations(range(S), k):
+                got = oracle.backup_slots(L, alloc, ids, slots, S, 0, 2, host=host0.copy())
+                assert np.array_equal(got, numpy_backup_slots(L, alloc, ids, slots, S, 0, 2, host0))
+                dst = [(p + 2) % 5 for p in ids]
+                if set(dst) & set(ids):
+                    continue
+                out = oracle.restore_slots(L, alloc, got, slots, dst, S, 0, 2)
+                touched = np.zeros(alloc.size, dtype=bool)
+                for s_, d_ in zip(ids, dst):
+                    for l in range(2):
+                        for c in range(2):
+                            a_s, a_d = oracle.piece_start(L, s_, l, c), oracle.piece_start(L, d_, l, c)
+                            assert np.array_equal(out[a_d:a_d + pb], alloc[a_s:a_s + pb])
+                            touched[a_d:a_d + pb] = True
+                assert np.array_equal(out[~touched], alloc[~touched])
+
+
+def test_identity_slots_are_the_packed_buffer():
+    """With slots 0..n-1 and n slots, the host pool is the packed buffer of
+    BACKUP / RESTORE (the reading the slot form generalises)."""
+    rng = np.random.default_rng(29)
+    L = rand_layout(rng, (PAGE, KV, LAYER), NHD, offset=16)
+    alloc = rand_alloc(rng, L)
+    ids = [6, 1, 3]
+    slots = list(range(len(ids)))
+    assert np.array_equal(oracle.backup_slots(L, alloc, ids, slots, len(ids), 0, 3),
+                          numpy_backup(L, alloc, ids, 0, 3))
+    host = rng.integers(0, 256, L.host_bytes(3), dtype=np.uint8)
+    assert np.array_equal(oracle.restore_slots(L, alloc, host, slots, [0, 2, 5], 3, 0, 3),
+                          numpy_restore(L, alloc, host, [0, 2, 5], 0, 3))
