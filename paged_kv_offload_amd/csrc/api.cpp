@@ -448,16 +448,25 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
 // ---------------------------------------------------------------------------
 // the operation
 // ---------------------------------------------------------------------------
+// A slot-addressed host pool: page ids[i] lands in (or comes from) slot
+// slots[i] of a buffer holding `num` slots per (layer, kv). NULL in the
+// functions below means the packed buffer (slot i, n slots).
+struct HostSlots {
+    const int32_t* slots;
+    int64_t num;
+};
+
 int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* host, uint8_t* view,
             int32_t l0, int32_t l1, kvx_ready* ready, int32_t slot_base, hipStream_t s,
-            int32_t path, const Tuning& t, Lane* L);
+            int32_t path, const Tuning& t, Lane* L, const HostSlots* hs);
 
 // Checks of one BACKUP or RESTORE that need no HIP call: layer range, page
 // list, ready object, packed buffer size and alignment. Leaves *active false
 // when there is nothing to move (n == 0 or an empty layer range).
 int validate_side(const kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, const void* buf,
                   uint64_t buf_bytes, int32_t l0, int32_t l1, const kvx_ready* ready,
-                  int32_t slot_base, const std::string& op, bool* active)
+                  int32_t slot_base, const std::string& op, bool* active,
+                  const HostSlots* hs = nullptr)
 {
     const PoolGeom& g = pool->geom;
     *active = false;
@@ -467,6 +476,14 @@ int validate_side(const kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, 
                                      std::to_string(g.num_layers) + ")");
     int rc = check_page_ids(g, ids, n, dir == SCATTER);
     if (rc != KVX_OK) return rc;
+    if (hs) {
+        if (hs->num < 0)
+            return fail(KVX_E_RANGE, op + ": num_host_slots " + std::to_string(hs->num) + " is negative");
+        // a backup writes each named slot once; a restore may read one slot
+        // into several pages
+        rc = check_host_slots(hs->slots, n, hs->num, dir == GATHER);
+        if (rc != KVX_OK) return rc;
+    }
     if (ready) {
         if (!ready_known(ready)) return fail(KVX_E_INVAL, op + ": unknown ready handle");
         if (!ready->live.load()) return fail(KVX_E_STALE, op + ": ready object was destroyed");
@@ -483,7 +500,7 @@ int validate_side(const kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, 
     }
     if (n == 0 || l0 == l1) return KVX_OK;
     if (!buf) return fail(KVX_E_INVAL, op + ": packed buffer is NULL");
-    const int64_t need = g.num_layers * g.num_kv * int64_t(n) * g.piece_bytes;
+    const int64_t need = g.num_layers * g.num_kv * (hs ? hs->num : int64_t(n)) * g.piece_bytes;
     if (buf_bytes < static_cast<uint64_t>(need))
         return fail(KVX_E_RANGE, op + ": packed buffer holds " + std::to_string(buf_bytes) +
                                      " bytes, needs " + std::to_string(need));
@@ -513,16 +530,21 @@ int check_packed_kind(const kvx_pool* pool, void* buf, int32_t path, const std::
 }
 
 int run_op(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, void* buf, uint64_t buf_bytes,
-         int32_t l0, int32_t l1, kvx_ready* ready, int32_t slot_base, void* stream_v, int32_t path)
+         int32_t l0, int32_t l1, kvx_ready* ready, int32_t slot_base, void* stream_v, int32_t path,
+         const HostSlots* hs = nullptr)
 {
     clear_error();
-    const char* op = dir == GATHER ? "backup" : "restore";
+    const char* op = hs ? (dir == GATHER ? "backup_slots" : "restore_slots")
+                        : (dir == GATHER ? "backup" : "restore");
     if (!pool_known(pool)) return fail(KVX_E_INVAL, std::string(op) + ": unknown pool handle");
     if (!pool->live.load()) return fail(KVX_E_STALE, std::string(op) + ": pool handle was unregistered");
     if (path != KVX_PATH_STAGED && path != KVX_PATH_ZEROCOPY && path != KVX_PATH_DEVICE)
         return fail(KVX_E_INVAL, std::string(op) + ": unknown path " + std::to_string(path));
+    if (hs && path == KVX_PATH_STAGED)
+        return fail(KVX_E_INVAL, std::string(op) + ": a slot-addressed host pool is moved on the "
+                                                   "zero-copy or device path");
     bool active = false;
-    int rc = validate_side(pool, dir, ids, n, buf, buf_bytes, l0, l1, ready, slot_base, op, &active);
+    int rc = validate_side(pool, dir, ids, n, buf, buf_bytes, l0, l1, ready, slot_base, op, &active, hs);
     if (rc != KVX_OK || !active) return rc;
 
     // ---- HIP from here on; nothing has been enqueued yet ----
@@ -543,7 +565,7 @@ int run_op(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, void* buf, ui
     if (rc != KVX_OK) return rc;
     std::lock_guard<std::mutex> lk(L->mu);
     rc = enqueue(pool, dir, ids, n, static_cast<uint8_t*>(buf), view, l0, l1, ready, slot_base, s,
-                 path, t, L);
+                 path, t, L, hs);
     if (rc != KVX_OK) {
         if (ready) L->counters_dirty = true;   // a partial publish may have left counts
         return rc;
@@ -560,13 +582,13 @@ int run_op(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, void* buf, ui
 // with the lane locked, after every validation has passed.
 int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* host, uint8_t* view,
             int32_t l0, int32_t l1, kvx_ready* ready, int32_t slot_base, hipStream_t s,
-            int32_t path, const Tuning& t, Lane* L)
+            int32_t path, const Tuning& t, Lane* L, const HostSlots* hs)
 {
     const PoolGeom& g = pool->geom;
     int rc = KVX_OK;
 
     std::vector<PageSlot> pairs;
-    order_pages(ids, n, t.sort_pages != 0, &pairs);
+    order_pairs(ids, hs ? hs->slots : nullptr, n, t.sort_pages != 0, &pairs);
 
     Publish pub;
     const Publish* pubp = nullptr;
@@ -582,7 +604,7 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
         pubp = &pub;
     }
     if (path != KVX_PATH_STAGED) {
-        Target tg{view, 0, 0, n, path == KVX_PATH_ZEROCOPY};
+        Target tg{view, 0, 0, hs ? hs->num : int64_t(n), path == KVX_PATH_ZEROCOPY};
         rc = launch_range(dir, pool, tg, l0, l1, pairs.data(), pairs.size(), pubp, t, L->cu_count, s);
     } else {
         // chunks of whole layers when one layer fits a ring slot, else slot
@@ -899,6 +921,25 @@ int kvx_restore(kvx_pool* pool, const void* src, uint64_t src_bytes, const int32
 {
     return run_op(pool, SCATTER, page_ids, n, const_cast<void*>(src), src_bytes, layer_begin,
                 layer_end, ready, slot_base, stream, path);
+}
+
+int kvx_backup_slots(kvx_pool* pool, const int32_t* page_ids, const int32_t* host_slots, int32_t n,
+                     void* host_pool, uint64_t host_pool_bytes, int32_t num_host_slots,
+                     int32_t layer_begin, int32_t layer_end, void* stream, int32_t path)
+{
+    const HostSlots hs{host_slots, num_host_slots};
+    return run_op(pool, GATHER, page_ids, n, host_pool, host_pool_bytes, layer_begin, layer_end,
+                  nullptr, 0, stream, path, &hs);
+}
+
+int kvx_restore_slots(kvx_pool* pool, const void* host_pool, uint64_t host_pool_bytes,
+                      int32_t num_host_slots, const int32_t* host_slots, const int32_t* page_ids,
+                      int32_t n, int32_t layer_begin, int32_t layer_end, kvx_ready* ready,
+                      int32_t slot_base, void* stream, int32_t path)
+{
+    const HostSlots hs{host_slots, num_host_slots};
+    return run_op(pool, SCATTER, page_ids, n, const_cast<void*>(host_pool), host_pool_bytes,
+                  layer_begin, layer_end, ready, slot_base, stream, path, &hs);
 }
 
 int kvx_exchange(kvx_pool* pool, const kvx_xfer* backup, const kvx_xfer* restore, kvx_ready* ready,

@@ -53,6 +53,11 @@ int check_page_ids(const PoolGeom& g, const int32_t* ids, int32_t n, bool reject
 // Pairs (page, slot) in visiting order: sorted by page when `sorted`, else
 // caller order.
 void order_pages(const int32_t* ids, int32_t n, bool sorted, std::vector<PageSlot>* out);
+// As order_pages with slot slots[i] for page ids[i] (slots == NULL: slot i).
+void order_pairs(const int32_t* ids, const int32_t* slots, int32_t n, bool sorted,
+                 std::vector<PageSlot>* out);
+// Host slots in [0, num_slots); with reject_dups, distinct (KVX_E_DUP).
+int check_host_slots(const int32_t* slots, int32_t n, int64_t num_slots, bool reject_dups);
 void plan_runs(const PoolGeom& g, const std::vector<PageSlot>& sorted_pairs,
                std::vector<Run>* runs);
 

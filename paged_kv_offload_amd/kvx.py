@@ -97,6 +97,10 @@ SIGNATURES = [
     ("kvx_version", ctypes.c_int, []),
     ("kvx_set_option", ctypes.c_int, [_i32, _i64]),
     ("kvx_get_option", ctypes.c_int, [_i32, _P(_i64)]),
+    ("kvx_backup_slots", ctypes.c_int, [_vp, _P(_i32), _P(_i32), _i32, _vp, _u64, _i32, _i32, _i32,
+                                        _vp, _i32]),
+    ("kvx_restore_slots", ctypes.c_int, [_vp, _vp, _u64, _i32, _P(_i32), _P(_i32), _i32, _i32, _i32,
+                                         _vp, _i32, _vp, _i32]),
     ("kvx_exchange", ctypes.c_int, [_vp, _P(kvx_xfer), _P(kvx_xfer), _vp, _i32, _vp, _i32]),
     ("kvx_ipc_export", ctypes.c_int, [_vp, _P(kvx_ipc_handle)]),
     ("kvx_ipc_import", ctypes.c_int, [_P(kvx_ipc_handle), _P(_vp), _P(_i32)]),
@@ -321,6 +325,32 @@ def kvx_restore(pool: int, src, src_bytes: int, page_ids: Iterable[int], layer_b
     ids = _ids(page_ids)
     _check(lib().kvx_restore(pool, _ptr(src), src_bytes, _ids_ptr(ids), ids.size, layer_begin,
                              layer_end, ready or 0, slot_base, _stream(stream), path))
+
+
+def kvx_backup_slots(pool: int, page_ids: Iterable[int], host_slots: Iterable[int], host_pool,
+                     host_pool_bytes: int, num_host_slots: int, layer_begin: int, layer_end: int,
+                     stream=None, path: int = KVX_PATH_ZEROCOPY) -> None:
+    """BACKUP of page_ids[i] into slot host_slots[i] of a host pool of
+    num_host_slots slots per (layer, kv)."""
+    ids, sl = _ids(page_ids), _ids(host_slots)
+    if sl.size != ids.size:
+        raise KvxError(KVX_E_INVAL, f"{ids.size} pages but {sl.size} host slots")
+    _check(lib().kvx_backup_slots(pool, _ids_ptr(ids), _ids_ptr(sl), ids.size, _ptr(host_pool),
+                                  host_pool_bytes, num_host_slots, layer_begin, layer_end,
+                                  _stream(stream), path))
+
+
+def kvx_restore_slots(pool: int, host_pool, host_pool_bytes: int, num_host_slots: int,
+                      host_slots: Iterable[int], page_ids: Iterable[int], layer_begin: int,
+                      layer_end: int, ready: int = None, slot_base: int = 0, stream=None,
+                      path: int = KVX_PATH_ZEROCOPY) -> None:
+    """RESTORE of slot host_slots[i] of a host pool into page page_ids[i]."""
+    ids, sl = _ids(page_ids), _ids(host_slots)
+    if sl.size != ids.size:
+        raise KvxError(KVX_E_INVAL, f"{sl.size} host slots but {ids.size} pages")
+    _check(lib().kvx_restore_slots(pool, _ptr(host_pool), host_pool_bytes, num_host_slots,
+                                   _ids_ptr(sl), _ids_ptr(ids), ids.size, layer_begin, layer_end,
+                                   ready or 0, slot_base, _stream(stream), path))
 
 
 def kvx_exchange(pool: int, backup_ids: Iterable[int], backup_dst, backup_bytes: int,

@@ -168,11 +168,50 @@ static void fuzz_pages(int iters)
     std::printf("pages: %d random lists checked\n", iters);
 }
 
+// Host-slot lists: check_host_slots accepts exactly the in-range lists
+// (and, when asked, only distinct ones); order_pairs keeps every
+// (page, slot) pair of the caller and sorts by page when asked.
+static void fuzz_slots(int iters)
+{
+    for (int it = 0; it < iters; it++) {
+        const int64_t S = rnd(0, 4000);
+        const int32_t n = static_cast<int32_t>(rnd(0, 2000));
+        std::vector<int32_t> slots(n), ids(n);
+        for (int32_t i = 0; i < n; i++) {
+            slots[i] = S ? static_cast<int32_t>(rnd(0, S - 1)) : 0;
+            ids[i] = static_cast<int32_t>(rnd(0, 9999));
+        }
+        if (n > 0 && rnd(0, 8) == 0) slots[rnd(0, n - 1)] = static_cast<int32_t>(S + rnd(0, 3));
+        if (n > 0 && rnd(0, 8) == 0) slots[rnd(0, n - 1)] = -1 - static_cast<int32_t>(rnd(0, 3));
+        bool in_range = true;
+        for (int32_t v : slots) in_range = in_range && v >= 0 && v < S;
+        CHECK((check_host_slots(slots.data(), n, S, false) == KVX_OK) == in_range);
+        if (!in_range) continue;
+        const bool distinct = std::set<int32_t>(slots.begin(), slots.end()).size() == slots.size();
+        CHECK((check_host_slots(slots.data(), n, S, true) == KVX_OK) == distinct);
+        for (bool sorted : {false, true}) {
+            std::vector<PageSlot> pairs;
+            order_pairs(ids.data(), slots.data(), n, sorted, &pairs);
+            CHECK(static_cast<int32_t>(pairs.size()) == n);
+            std::multiset<std::pair<int32_t, int32_t>> want, got;
+            for (int32_t i = 0; i < n; i++) {
+                want.insert({ids[i], slots[i]});
+                got.insert({pairs[i].page, pairs[i].slot});
+                if (!sorted) CHECK(pairs[i].page == ids[i] && pairs[i].slot == slots[i]);
+            }
+            CHECK(want == got);
+            for (size_t j = 0; j + 1 < pairs.size() && sorted; j++) CHECK(pairs[j].page <= pairs[j + 1].page);
+        }
+    }
+    std::printf("slots: %d random lists checked\n", iters);
+}
+
 int main()
 {
     fuzz_extremes();
     fuzz_geometry(20000);
     fuzz_pages(3000);
+    fuzz_slots(3000);
     std::printf("host fuzz ok\n");
     return 0;
 }

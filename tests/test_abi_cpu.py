@@ -302,3 +302,51 @@ def test_exchange_validation_fails_closed():
             assert e.value.code == code and text in e.value.message, (change, e.value.message)
     finally:
         K.kvx_unregister_pool(pool)
+
+
+def test_slot_validation_fails_closed():
+    """kvx_backup_slots / kvx_restore_slots refuse the staged path, slots
+    outside the host pool, a slot a backup would write twice, a page a
+    restore would write twice and a host pool too small for its slots before
+    any HIP call; empty work succeeds without one."""
+    w = WORKLOADS["tiny"]
+    pool = register(w)
+    S = 5
+    nb = w.host_bytes(S)
+    hp = 0x1000000
+    zc = K.KVX_PATH_ZEROCOPY
+    try:
+        for fn, code, text in (
+                (lambda: K.kvx_backup_slots(pool, [1, 2], [0, 1], hp, nb, S, 0, 2,
+                                            path=K.KVX_PATH_STAGED), K.KVX_E_INVAL, "zero-copy"),
+                (lambda: K.kvx_backup_slots(pool, [1, 2], [0, 5], hp, nb, S, 0, 2, path=zc),
+                 K.KVX_E_RANGE, "host_slots[1] = 5"),
+                (lambda: K.kvx_backup_slots(pool, [1, 2], [-1, 0], hp, nb, S, 0, 2, path=zc),
+                 K.KVX_E_RANGE, "host_slots[0]"),
+                (lambda: K.kvx_backup_slots(pool, [1, 2], [3, 3], hp, nb, S, 0, 2, path=zc),
+                 K.KVX_E_DUP, "host slot 3"),
+                (lambda: K.kvx_backup_slots(pool, [1, 64], [0, 1], hp, nb, S, 0, 2, path=zc),
+                 K.KVX_E_RANGE, "page_ids[1]"),
+                (lambda: K.kvx_backup_slots(pool, [1, 2], [0, 1], hp, nb - 16, S, 0, 2, path=zc),
+                 K.KVX_E_RANGE, "needs"),
+                (lambda: K.kvx_backup_slots(pool, [1, 2], [0, 1], hp, nb, -1, 0, 2, path=zc),
+                 K.KVX_E_RANGE, "negative"),
+                (lambda: K.kvx_backup_slots(pool, [1, 2], [0, 1], hp + 8, nb, S, 0, 2, path=zc),
+                 K.KVX_E_ALIGN, "aligned"),
+                (lambda: K.kvx_restore_slots(pool, hp, nb, S, [0, 1], [4, 4], 0, 2, path=zc),
+                 K.KVX_E_DUP, "destination page 4"),
+                (lambda: K.kvx_restore_slots(pool, hp, nb, S, [0, 9], [4, 5], 0, 2, path=zc),
+                 K.KVX_E_RANGE, "host_slots[1] = 9"),
+                (lambda: K.kvx_restore_slots(pool, hp, nb, S, [0, 1], [4, 5], 0, 3, path=zc),
+                 K.KVX_E_RANGE, "layer range"),
+                (lambda: K.kvx_restore_slots(pool, hp, nb, S, [0], [4, 5], 0, 2, path=zc),
+                 K.KVX_E_INVAL, "host slots")):
+            with pytest.raises(K.KvxError) as e:
+                fn()
+            assert e.value.code == code and text in e.value.message, (code, e.value.message)
+        # empty work: no-ops that never reach the GPU
+        K.kvx_backup_slots(pool, [], [], hp, nb, S, 0, 2, path=zc)
+        K.kvx_restore_slots(pool, hp, nb, S, [2, 2], [4, 5], 1, 1, path=zc)
+        K.kvx_backup_slots(pool, [], [], 0, 0, 0, 0, 2, path=zc)
+    finally:
+        K.kvx_unregister_pool(pool)

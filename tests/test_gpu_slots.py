@@ -1,0 +1,137 @@
+"""GPU parity of the slot-addressed host tier: kvx_backup_slots and
+kvx_restore_slots through the C ABI against oracle.backup_slots /
+oracle.restore_slots, byte for byte over the whole host pool and the whole
+pool allocation, on both paths that take a host pool (zero-copy over the host
+link, device memory), for pools of every outer order and both inner layouts,
+ragged pieces and more pages than one launch carries."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from paged_kv_offload_amd import kvx as K
+from tests.gpu_util import PATHS, DevicePool, Packed, oracle_layout, torch
+from tests.test_gpu_parity import SMALL, diff_report
+
+pytestmark = pytest.mark.gpu
+
+SLOT_PATHS = ["zerocopy", "device"]
+CASES = ["tiny", "llama_small", "mla_small", "trtllm_small", "ragged_hnd", "ragged_nhd",
+         "hnd_t1", "hnd_f32_rows16"]
+
+
+@pytest.fixture(scope="module")
+def stream():
+    t = torch()
+    assert t.cuda.is_available(), "GPU tests need a GPU"
+    K.lib()
+    return t.cuda.Stream()
+
+
+def slot_case(w, n):
+    """Host pool of 2n + 3 slots; backup slots distinct and scattered over the
+    pool, restore slots drawn with repeats (one host copy into two pages)."""
+    S = 2 * n + 3
+    rng = np.random.default_rng(w.seed + 40)
+    perm = synth.page_perm(w.seed + 41, w.num_pages)
+    src, dst = perm[:n].copy(), perm[n:2 * n].copy()
+    bslots = rng.permutation(S)[:n].astype(np.int32)
+    rslots = rng.integers(0, S, n).astype(np.int32)
+    return S, src, dst, bslots, rslots
+
+
+@pytest.mark.parametrize("path", SLOT_PATHS)
+@pytest.mark.parametrize("case", CASES)
+def test_slot_backup_restore_parity(case, path, stream):
+    w, n = SMALL[case]
+    S, src, dst, bslots, rslots = slot_case(w, n)
+    print(f"\n[slots] case={case} path={path} n={n} slots={S} piece={w.piece_bytes}", flush=True)
+    L = oracle_layout(w)
+    pool = DevicePool(w, seed=w.seed + 42, generation=3)
+    nb = w.host_bytes(S)
+    hp = Packed(w, S, path, fill_seed=w.seed + 43)
+    ready = K.kvx_ready_create(w.num_layers, 3)
+    try:
+        img = pool.host_image()
+        host = synth.gen_bytes(w.seed + 43, 0, nb)
+        ranges = [(0, w.num_layers), (1, w.num_layers)] if w.num_layers > 1 else [(0, 1)]
+        for l0, l1 in ranges:
+            host = oracle.backup_slots(L, img, src, bslots, S, l0, l1, host=host)
+            K.kvx_backup_slots(pool.handle, src, bslots, hp.ptr, nb, S, l0, l1, stream,
+                               PATHS[path])
+            K.kvx_sync(stream)
+            got = hp.numpy()
+            assert np.array_equal(got, host), f"backup_slots {l0}:{l1} " + diff_report(got, host)
+
+            want = oracle.restore_slots(L, img, host, rslots, dst, S, l0, l1)
+            K.kvx_ready_reset(ready)
+            K.kvx_restore_slots(pool.handle, hp.ptr, nb, S, rslots, dst, l0, l1, ready, 0,
+                                stream, PATHS[path])
+            K.kvx_sync(stream)
+            after = pool.host_image()
+            assert np.array_equal(after, want), f"restore_slots {l0}:{l1} " + \
+                diff_report(after, want)
+            counts = [K.kvx_layer_ready(ready, s) for s in range(w.num_layers)]
+            assert counts == [0] * l0 + [n] * (l1 - l0)
+            img = after
+    finally:
+        K.kvx_ready_destroy(ready)
+        hp.close()
+        pool.close()
+
+
+@pytest.mark.parametrize("path", SLOT_PATHS)
+def test_slot_round_trip_with_sorted_visits(path, stream):
+    """With pages visited in sorted order, a backup into scattered slots and
+    a restore of the same slots into other pages leaves the other pages equal
+    to the source pages (oracle bytes) and every unnamed host slot as it was."""
+    w, n = SMALL["ragged_nhd"]
+    S, src, dst, bslots, _ = slot_case(w, n)
+    print(f"\n[slots-sorted] path={path} n={n} slots={S}", flush=True)
+    L = oracle_layout(w)
+    pool = DevicePool(w, seed=w.seed + 44, generation=2)
+    nb = w.host_bytes(S)
+    hp = Packed(w, S, path, fill_seed=w.seed + 45)
+    old = K.kvx_get_option(K.KVX_OPT_SORT_PAGES)
+    try:
+        K.kvx_set_option(K.KVX_OPT_SORT_PAGES, 1)
+        img = pool.host_image()
+        host = oracle.backup_slots(L, img, src, bslots, S, 0, w.num_layers,
+                                   host=synth.gen_bytes(w.seed + 45, 0, nb))
+        want = oracle.restore_slots(L, img, host, bslots, dst, S, 0, w.num_layers)
+        K.kvx_backup_slots(pool.handle, src, bslots, hp.ptr, nb, S, 0, w.num_layers, stream,
+                           PATHS[path])
+        K.kvx_restore_slots(pool.handle, hp.ptr, nb, S, bslots, dst, 0, w.num_layers, None, 0,
+                            stream, PATHS[path])
+        K.kvx_sync(stream)
+        got = hp.numpy()
+        assert np.array_equal(got, host), diff_report(got, host)
+        after = pool.host_image()
+        assert np.array_equal(after, want), diff_report(after, want)
+    finally:
+        K.kvx_set_option(K.KVX_OPT_SORT_PAGES, old)
+        hp.close()
+        pool.close()
+
+
+def test_slot_memory_kind_checks(stream):
+    """The zero-copy path refuses a device host pool and the device path a
+    pinned one (GPU-side checks: they need the runtime's pointer query)."""
+    w, n = SMALL["tiny"]
+    pool = DevicePool(w)
+    nb = w.host_bytes(4)
+    dev = Packed(w, 4, "device")
+    pin = Packed(w, 4, "zerocopy")
+    try:
+        with pytest.raises(K.KvxError) as e:
+            K.kvx_backup_slots(pool.handle, [1], [2], dev.ptr, nb, 4, 0, 2, stream,
+                               K.KVX_PATH_ZEROCOPY)
+        assert e.value.code == K.KVX_E_INVAL
+        with pytest.raises(K.KvxError) as e:
+            K.kvx_restore_slots(pool.handle, pin.ptr, nb, 4, [2], [1], 0, 2, None, 0, stream,
+                                K.KVX_PATH_DEVICE)
+        assert e.value.code == K.KVX_E_INVAL
+    finally:
+        dev.close()
+        pin.close()
+        pool.close()
