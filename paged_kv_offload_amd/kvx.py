@@ -18,7 +18,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvx.so")
 
 KVX_OK = 0
 KVX_E_INVAL, KVX_E_NONCONTIG, KVX_E_ALIGN, KVX_E_RANGE, KVX_E_DUP = -1, -2, -3, -4, -5
-KVX_E_STALE, KVX_E_NOTPINNED, KVX_E_NOMEM, KVX_E_HIP = -6, -7, -8, -9
+KVX_E_STALE, KVX_E_NOTPINNED, KVX_E_NOMEM, KVX_E_HIP, KVX_E_FULL = -6, -7, -8, -9, -10
+TIER_FREE, TIER_WRITING, TIER_RESIDENT = 0, 1, 2
 KVX_AX_PAGE, KVX_AX_LAYER, KVX_AX_KV = 0, 1, 2
 KVX_NHD, KVX_HND = 0, 1
 KVX_PATH_STAGED, KVX_PATH_ZEROCOPY, KVX_PATH_DEVICE = 0, 1, 2
@@ -29,7 +30,7 @@ KVX_OPT_STAGED_DMA_ON_CALLER, KVX_OPT_HND_LDS, KVX_OPT_UNIT_ROUNDS = 9, 10, 11
 
 ERROR_NAMES = {0: "KVX_OK", -1: "KVX_E_INVAL", -2: "KVX_E_NONCONTIG", -3: "KVX_E_ALIGN",
                -4: "KVX_E_RANGE", -5: "KVX_E_DUP", -6: "KVX_E_STALE", -7: "KVX_E_NOTPINNED",
-               -8: "KVX_E_NOMEM", -9: "KVX_E_HIP"}
+               -8: "KVX_E_NOMEM", -9: "KVX_E_HIP", -10: "KVX_E_FULL"}
 PATHS = {"staged": KVX_PATH_STAGED, "zerocopy": KVX_PATH_ZEROCOPY, "device": KVX_PATH_DEVICE}
 _AXES = {"page": KVX_AX_PAGE, "layer": KVX_AX_LAYER, "kv": KVX_AX_KV}
 
@@ -64,6 +65,12 @@ class kvx_ipc_handle(ctypes.Structure):
     _fields_ = [("mem_handle", ctypes.c_uint8 * 64), ("device_uuid", ctypes.c_uint8 * 16),
                 ("alloc_bytes", ctypes.c_uint64), ("offset", ctypes.c_uint64),
                 ("version", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
+class kvx_tier_info(ctypes.Structure):
+    _fields_ = [(k, ctypes.c_int32) for k in ("num_slots", "free_slots", "writing", "resident",
+                                              "pinned", "doomed")] + \
+               [("evictions", ctypes.c_uint64), ("generation", ctypes.c_uint64)]
 
 
 # (name, restype, argtypes) of every exported function
@@ -105,6 +112,20 @@ SIGNATURES = [
     ("kvx_ipc_export", ctypes.c_int, [_vp, _P(kvx_ipc_handle)]),
     ("kvx_ipc_import", ctypes.c_int, [_P(kvx_ipc_handle), _P(_vp), _P(_i32)]),
     ("kvx_ipc_close", ctypes.c_int, [_vp]),
+    ("kvx_tier_create", ctypes.c_int, [_i32, _u64, _P(_vp)]),
+    ("kvx_tier_destroy", ctypes.c_int, [_vp]),
+    ("kvx_tier_reserve", ctypes.c_int, [_vp, _P(_u64), _i32, _P(_i32), _P(_u64), _P(_i32)]),
+    ("kvx_tier_commit", ctypes.c_int, [_vp, _P(_i32), _i32]),
+    ("kvx_tier_abort", ctypes.c_int, [_vp, _P(_i32), _i32]),
+    ("kvx_tier_lookup", ctypes.c_int, [_vp, _P(_u64), _i32, _P(_i32), _P(_i32)]),
+    ("kvx_tier_release", ctypes.c_int, [_vp, _P(_i32), _i32]),
+    ("kvx_tier_invalidate", ctypes.c_int, [_vp, _P(_u64), _i32, _P(_i32)]),
+    ("kvx_tier_get_info", ctypes.c_int, [_vp, _P(kvx_tier_info)]),
+    ("kvx_tier_slot", ctypes.c_int, [_vp, _i32, _P(_u64), _P(_i32), _P(_i32)]),
+    ("kvx_tier_backup", ctypes.c_int, [_vp, _vp, _P(_u64), _P(_i32), _i32, _vp, _u64, _vp, _i32,
+                                       _P(_i32), _P(_u64), _P(_i32)]),
+    ("kvx_tier_restore", ctypes.c_int, [_vp, _vp, _P(_u64), _P(_i32), _i32, _vp, _u64, _vp, _i32,
+                                        _vp, _i32, _P(_i32), _P(_i32)]),
 ]
 
 _lib: Optional[ctypes.CDLL] = None
@@ -351,6 +372,116 @@ def kvx_restore_slots(pool: int, host_pool, host_pool_bytes: int, num_host_slots
     _check(lib().kvx_restore_slots(pool, _ptr(host_pool), host_pool_bytes, num_host_slots,
                                    _ids_ptr(sl), _ids_ptr(ids), ids.size, layer_begin, layer_end,
                                    ready or 0, slot_base, _stream(stream), path))
+
+
+# ---------------------------------------------------------------------------
+# host tier
+# ---------------------------------------------------------------------------
+def _keys(keys) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(keys, dtype=np.uint64).reshape(-1))
+
+
+def _kp(a: np.ndarray):
+    return a.ctypes.data_as(_P(_u64))
+
+
+def _sp(a: np.ndarray):
+    return a.ctypes.data_as(_P(_i32))
+
+
+def kvx_tier_create(num_slots: int, generation: int) -> int:
+    out = _vp()
+    _check(lib().kvx_tier_create(num_slots, generation, ctypes.byref(out)))
+    return out.value
+
+
+def kvx_tier_destroy(tier: int) -> None:
+    _check(lib().kvx_tier_destroy(tier))
+
+
+def kvx_tier_reserve(tier: int, keys):
+    """(slots, evicted keys) of a reservation; slot -1 for a key present."""
+    k = _keys(keys)
+    slots = np.empty(k.size, dtype=np.int32)
+    ev = np.empty(max(k.size, 1), dtype=np.uint64)
+    ne = _i32()
+    _check(lib().kvx_tier_reserve(tier, _kp(k), k.size, _sp(slots), _kp(ev), ctypes.byref(ne)))
+    return slots, ev[:ne.value].copy()
+
+
+def kvx_tier_commit(tier: int, slots) -> None:
+    s = _ids(slots)
+    _check(lib().kvx_tier_commit(tier, _sp(s), s.size))
+
+
+def kvx_tier_abort(tier: int, slots) -> None:
+    s = _ids(slots)
+    _check(lib().kvx_tier_abort(tier, _sp(s), s.size))
+
+
+def kvx_tier_lookup(tier: int, keys) -> np.ndarray:
+    """Slots of the keys (pinned), -1 for a miss."""
+    k = _keys(keys)
+    slots = np.empty(k.size, dtype=np.int32)
+    hits = _i32()
+    _check(lib().kvx_tier_lookup(tier, _kp(k), k.size, _sp(slots), ctypes.byref(hits)))
+    return slots
+
+
+def kvx_tier_release(tier: int, slots) -> None:
+    s = _ids(slots)
+    _check(lib().kvx_tier_release(tier, _sp(s), s.size))
+
+
+def kvx_tier_invalidate(tier: int, keys) -> int:
+    k = _keys(keys)
+    nd = _i32()
+    _check(lib().kvx_tier_invalidate(tier, _kp(k), k.size, ctypes.byref(nd)))
+    return nd.value
+
+
+def kvx_tier_get_info(tier: int) -> dict:
+    info = kvx_tier_info()
+    _check(lib().kvx_tier_get_info(tier, ctypes.byref(info)))
+    return {k: getattr(info, k) for k, _ in kvx_tier_info._fields_}
+
+
+def kvx_tier_slot(tier: int, slot: int):
+    """(key, state, pins) of one slot."""
+    key, state, pins = _u64(), _i32(), _i32()
+    _check(lib().kvx_tier_slot(tier, slot, ctypes.byref(key), ctypes.byref(state),
+                               ctypes.byref(pins)))
+    return key.value, state.value, pins.value
+
+
+def kvx_tier_backup(tier: int, pool: int, keys, page_ids, host_pool, host_pool_bytes: int,
+                    stream=None, path: int = KVX_PATH_ZEROCOPY):
+    """Reserve + backup of the new keys' pages; (slots, evicted keys)."""
+    k, ids = _keys(keys), _ids(page_ids)
+    if k.size != ids.size:
+        raise KvxError(KVX_E_INVAL, f"{k.size} keys but {ids.size} pages")
+    slots = np.empty(k.size, dtype=np.int32)
+    ev = np.empty(max(k.size, 1), dtype=np.uint64)
+    ne = _i32()
+    _check(lib().kvx_tier_backup(tier, pool, _kp(k), _ids_ptr(ids), k.size, _ptr(host_pool),
+                                 host_pool_bytes, _stream(stream), path, _sp(slots), _kp(ev),
+                                 ctypes.byref(ne)))
+    return slots, ev[:ne.value].copy()
+
+
+def kvx_tier_restore(tier: int, pool: int, keys, page_ids, host_pool, host_pool_bytes: int,
+                     ready: int = None, slot_base: int = 0, stream=None,
+                     path: int = KVX_PATH_ZEROCOPY) -> np.ndarray:
+    """Lookup + restore of the hits into their pages; the slots (-1 = miss)."""
+    k, ids = _keys(keys), _ids(page_ids)
+    if k.size != ids.size:
+        raise KvxError(KVX_E_INVAL, f"{k.size} keys but {ids.size} pages")
+    slots = np.empty(k.size, dtype=np.int32)
+    hits = _i32()
+    _check(lib().kvx_tier_restore(tier, pool, _kp(k), _ids_ptr(ids), k.size, _ptr(host_pool),
+                                  host_pool_bytes, ready or 0, slot_base, _stream(stream), path,
+                                  _sp(slots), ctypes.byref(hits)))
+    return slots
 
 
 def kvx_exchange(pool: int, backup_ids: Iterable[int], backup_dst, backup_bytes: int,

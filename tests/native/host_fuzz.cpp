@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "kvx_host.h"
+#include "tier.h"
 
 namespace kvx {
 static int g_last_code = 0;
@@ -206,12 +207,107 @@ static void fuzz_slots(int iters)
     std::printf("slots: %d random lists checked\n", iters);
 }
 
+// Host tier: random operations through the C entry points; after each
+// one the tier's index structures must agree with its entries (the free set
+// holds exactly the FREE slots, the key map exactly the present entries,
+// the LRU set exactly the evictable ones) and every count must add up.
+static void check_tier(const kvx_tier* t)
+{
+    size_t nfree = 0, npresent = 0, nevict = 0;
+    for (int32_t s = 0; s < int32_t(t->e.size()); s++) {
+        const TierEntry& x = t->e[s];
+        CHECK(x.pins >= 0);
+        CHECK(x.pins == 0 || x.state == TIER_RESIDENT);
+        if (x.state == TIER_FREE) {
+            CHECK(t->free_slots.count(s) && x.key == 0 && !x.doomed && x.pins == 0);
+            nfree++;
+            continue;
+        }
+        CHECK(!t->free_slots.count(s));
+        if (!x.doomed) {
+            auto it = t->where.find(x.key);
+            CHECK(it != t->where.end() && it->second == s);
+            npresent++;
+        }
+        const bool ev = x.state == TIER_RESIDENT && x.pins == 0 && !x.doomed;
+        CHECK(t->lru.count({x.last, s}) == (ev ? 1u : 0u));
+        nevict += ev;
+        CHECK(x.last <= t->clock);
+    }
+    CHECK(nfree == t->free_slots.size() && npresent == t->where.size() && nevict == t->lru.size());
+}
+
+static void fuzz_tier(int iters)
+{
+    int ok = 0;
+    for (int it = 0; it < iters; it++) {
+        const int32_t S = static_cast<int32_t>(rnd(0, 40));
+        kvx_tier* t = nullptr;
+        CHECK(kvx_tier_create(S, 1, &t) == KVX_OK);
+        std::vector<int32_t> writing, held;
+        const uint64_t nkeys = static_cast<uint64_t>(rnd(1, 3 * S + 3));
+        for (int step = 0; step < 200; step++) {
+            const int op = static_cast<int>(rnd(0, 6));
+            const int32_t n = static_cast<int32_t>(rnd(0, S + 2));
+            std::vector<uint64_t> keys(n), ev(n + 1);
+            std::vector<int32_t> slots(n + 1);
+            for (auto& k : keys) k = static_cast<uint64_t>(rnd(0, nkeys - 1)) * 0x9E3779B97F4A7C15ull;
+            int32_t cnt = 0;
+            int rc = KVX_OK;
+            if (op == 0) {
+                rc = kvx_tier_reserve(t, keys.data(), n, slots.data(), ev.data(), &cnt);
+                if (rc == KVX_OK) {
+                    CHECK(cnt >= 0 && cnt <= n);
+                    for (int32_t i = 0; i < n; i++) if (slots[i] >= 0) writing.push_back(slots[i]);
+                } else {
+                    CHECK(rc == KVX_E_FULL);
+                }
+            } else if (op == 1 || op == 2) {
+                std::shuffle(writing.begin(), writing.end(), rng);
+                const size_t k = static_cast<size_t>(rnd(0, int64_t(writing.size())));
+                std::vector<int32_t> sl(writing.begin(), writing.begin() + k);
+                writing.erase(writing.begin(), writing.begin() + k);
+                if (rnd(0, 9) == 0) sl.push_back(static_cast<int32_t>(rnd(-3, S + 3)));
+                rc = op == 1 ? kvx_tier_commit(t, sl.data(), int32_t(sl.size()))
+                             : kvx_tier_abort(t, sl.data(), int32_t(sl.size()));
+            } else if (op == 3) {
+                rc = kvx_tier_lookup(t, keys.data(), n, slots.data(), &cnt);
+                CHECK(rc == KVX_OK);
+                for (int32_t i = 0; i < n; i++) if (slots[i] >= 0) held.push_back(slots[i]);
+            } else if (op == 4) {
+                std::shuffle(held.begin(), held.end(), rng);
+                const size_t k = static_cast<size_t>(rnd(0, int64_t(held.size())));
+                std::vector<int32_t> sl(held.begin(), held.begin() + k);
+                held.erase(held.begin(), held.begin() + k);
+                if (rnd(0, 9) == 0) sl.push_back(static_cast<int32_t>(rnd(-3, S + 3)));
+                rc = kvx_tier_release(t, sl.data(), int32_t(sl.size()));
+                if (rc != KVX_OK) held.insert(held.end(), sl.begin(), sl.end() - 1);
+            } else {
+                rc = kvx_tier_invalidate(t, keys.data(), n, &cnt);
+                CHECK(rc == KVX_OK && cnt >= 0 && cnt <= n);
+            }
+            ok += rc == KVX_OK;
+            std::vector<int32_t> still;
+            for (int32_t s : writing) if (t->e[s].state == TIER_WRITING) still.push_back(s);
+            writing.swap(still);
+            check_tier(t);
+        }
+        kvx_tier_info info;
+        CHECK(kvx_tier_get_info(t, &info) == KVX_OK);
+        CHECK(info.num_slots == S && info.free_slots + info.writing + info.resident == S);
+        CHECK(kvx_tier_destroy(t) == KVX_OK);
+        CHECK(kvx_tier_lookup(t, nullptr, 0, nullptr, &info.pinned) == KVX_E_STALE);
+    }
+    std::printf("tier: %d sequences, %d successful operations checked\n", iters, ok);
+}
+
 int main()
 {
     fuzz_extremes();
     fuzz_geometry(20000);
     fuzz_pages(3000);
     fuzz_slots(3000);
+    fuzz_tier(300);
     std::printf("host fuzz ok\n");
     return 0;
 }

@@ -350,3 +350,47 @@ def test_slot_validation_fails_closed():
         K.kvx_backup_slots(pool, [], [], 0, 0, 0, 0, 2, path=zc)
     finally:
         K.kvx_unregister_pool(pool)
+
+
+def test_tier_policy_calls_fail_closed():
+    """kvx_tier_backup / kvx_tier_restore: a tier of another generation is
+    STALE; a refusal by the transfer's own checks (here a host pool too
+    small) leaves the tier exactly as it was, evictions included; all
+    before any HIP call."""
+    w = WORKLOADS["tiny"]
+    pool = register(w, gen=7)
+    S = 2
+    nb = w.host_bytes(S)
+    hp = 0x1000000
+    t = K.kvx_tier_create(S, 7)
+    old = K.kvx_tier_create(S, 6)
+    try:
+        slots, _ = K.kvx_tier_reserve(t, [11, 12])
+        K.kvx_tier_commit(t, slots)
+        view = [K.kvx_tier_slot(t, s) for s in range(S)]
+        info = K.kvx_tier_get_info(t)
+        for fn, code, text in (
+                (lambda: K.kvx_tier_backup(old, pool, [13], [1], hp, nb), K.KVX_E_STALE,
+                 "generation"),
+                # 13 and 14 would evict 11 and 12, then the transfer refuses
+                (lambda: K.kvx_tier_backup(t, pool, [13, 14], [1, 2], hp, nb - 16), K.KVX_E_RANGE,
+                 "needs"),
+                (lambda: K.kvx_tier_backup(t, pool, [13, 14], [1, 2], hp, nb,
+                                           path=K.KVX_PATH_STAGED), K.KVX_E_INVAL, "zero-copy"),
+                (lambda: K.kvx_tier_backup(t, pool, [13], [64], hp, nb), K.KVX_E_RANGE, "outside"),
+                (lambda: K.kvx_tier_restore(t, pool, [11, 12], [3, 3], hp, nb), K.KVX_E_DUP,
+                 "destination page 3"),
+                (lambda: K.kvx_tier_restore(t, pool, [11, 12], [3, 4], hp, nb - 1), K.KVX_E_RANGE,
+                 "needs")):
+            with pytest.raises(K.KvxError) as e:
+                fn()
+            assert e.value.code == code and text in e.value.message, (code, e.value.message)
+            assert [K.kvx_tier_slot(t, s) for s in range(S)] == view
+            assert K.kvx_tier_get_info(t) == info
+        # nothing new and no hit: no transfer, no HIP call
+        assert K.kvx_tier_backup(t, pool, [11], [1], hp, nb)[0].tolist() == [-1]
+        assert K.kvx_tier_restore(t, pool, [99], [1], hp, nb).tolist() == [-1]
+    finally:
+        K.kvx_tier_destroy(t)
+        K.kvx_tier_destroy(old)
+        K.kvx_unregister_pool(pool)

@@ -135,3 +135,66 @@ def test_slot_memory_kind_checks(stream):
         dev.close()
         pin.close()
         pool.close()
+
+
+@pytest.mark.parametrize("path", SLOT_PATHS)
+@pytest.mark.parametrize("case", ["llama_small", "ragged_hnd"])
+def test_tier_write_through_sequence(case, path, stream):
+    """A write-through host tier of 8 slots: kvx_tier_backup of six pages,
+    then of six more (two already present, two evictions), then
+    kvx_tier_restore of a hit, an evicted key and another hit into fresh
+    pages. Slots and evictions equal the tier model's, the host pool equals
+    the oracle's slot backups, the pool equals the oracle's slot restore of
+    the hits (the miss's page untouched), and each layer publishes the hits."""
+    from oracle.tier_model import TierModel
+    w, _ = SMALL[case]
+    S = 8
+    print(f"\n[tier] case={case} path={path} slots={S}", flush=True)
+    L = oracle_layout(w)
+    pool = DevicePool(w, seed=w.seed + 50, generation=9)
+    nb = w.host_bytes(S)
+    hp = Packed(w, S, path, fill_seed=w.seed + 51)
+    tier = K.kvx_tier_create(S, 9)
+    ready = K.kvx_ready_create(w.num_layers, 9)
+    model = TierModel(S)
+    perm = synth.page_perm(w.seed + 52, w.num_pages)
+    keys = [1000 + 7 * i for i in range(10)]
+    try:
+        img = pool.host_image()
+        host = synth.gen_bytes(w.seed + 51, 0, nb)
+        for kk, pages in ((keys[0:6], perm[0:6]), (keys[4:10], perm[4:10])):
+            slots, ev = K.kvx_tier_backup(tier, pool.handle, kk, pages, hp.ptr, nb, stream,
+                                          PATHS[path])
+            want_slots, want_ev = model.reserve(kk)
+            assert (slots.tolist(), ev.tolist()) == (want_slots, want_ev)
+            new = slots >= 0
+            host = oracle.backup_slots(L, img, pages[new], slots[new], S, 0, w.num_layers,
+                                       host=host)
+            K.kvx_sync(stream)
+            K.kvx_tier_commit(tier, slots)
+            model.commit(want_slots)
+        assert model.evictions == 2
+        got = hp.numpy()
+        assert np.array_equal(got, host), "host tier " + diff_report(got, host)
+
+        rkeys = [keys[2], keys[0], keys[7]]
+        dst = perm[20:23].copy()
+        rslots = K.kvx_tier_restore(tier, pool.handle, rkeys, dst, hp.ptr, nb, ready, 0, stream,
+                                    PATHS[path])
+        assert rslots.tolist() == model.lookup(rkeys)
+        assert rslots[1] == -1 and rslots[0] >= 0 and rslots[2] >= 0
+        hit = rslots >= 0
+        want = oracle.restore_slots(L, img, host, rslots[hit], dst[hit], S, 0, w.num_layers)
+        K.kvx_sync(stream)
+        after = pool.host_image()
+        assert np.array_equal(after, want), "restore " + diff_report(after, want)
+        assert [K.kvx_layer_ready(ready, s) for s in range(w.num_layers)] == \
+            [2] * w.num_layers
+        K.kvx_tier_release(tier, rslots)
+        model.release(rslots.tolist())
+        assert [K.kvx_tier_slot(tier, s) for s in range(S)] == model.view()
+    finally:
+        K.kvx_ready_destroy(ready)
+        K.kvx_tier_destroy(tier)
+        hp.close()
+        pool.close()
