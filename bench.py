@@ -52,7 +52,7 @@ PCIE_PEAK_GBS = 64.0      # MI355X host interface, PCIe 5.0 x16, published per-d
 # run; see profiles/pack_kernel_llama8b.txt). Valid only for the kernel source
 # they were taken on: reported as null once kernels.hip changes.
 MEASURED_TRAFFIC = {"workload": "llama8b", "kernels_hip_sha256": "a30559ece8139a73f60a5d1a28a838edaf4f4dcec6497b31a18b9645ea4b7aa1",
-                    "bytes_per_launch": 4295182194}
+                    "bytes_per_launch": 4295187581}
 
 
 def log(msg):
@@ -656,6 +656,64 @@ def all_workloads():
     print(json.dumps({"trtllm_hnd": res}), flush=True)
     K.kvx_unregister_pool(pool)
     host.free()
+    del alloc
+    torch.cuda.empty_cache()
+
+    # ---- host tier: the llama8b request through slot-addressed host pools ----
+    w = WORKLOADS["llama8b"]
+    n, S = w.pages_per_request, 1024
+    P, HB = w.payload_bytes(n), w.payload_bytes(S)
+    alloc, pool = make_pool(w)
+    rng = np.random.default_rng(w.seed + 70)
+    res = {"workload": w.description + f"; host tier of {S} slots", "payload_bytes_per_op": P}
+    host = K.HostBuffer(HB)
+    dev = torch.empty(HB, dtype=torch.uint8, device="cuda")
+    for name, pth, buf in (("zerocopy", K.KVX_PATH_ZEROCOPY, host.ptr),
+                           ("device", K.KVX_PATH_DEVICE, dev.data_ptr())):
+        src, dst = request_pair(w)
+        slots = rng.permutation(S)[:n].astype(np.int32)
+        b = lambda: K.kvx_backup_slots(pool, src, slots, buf, HB, S, 0, w.num_layers, stream, pth)  # noqa
+        r = lambda: K.kvx_restore_slots(pool, buf, HB, S, slots, dst, 0, w.num_layers, None, 0,  # noqa
+                                        stream, pth)
+        timed(b, 2)
+        timed(r, 2)
+        tb, tr = median(timed(b, 5)), median(timed(r, 5))
+        if pth == K.KVX_PATH_DEVICE:
+            res[name] = {"backup_slots_gbs": round(2 * P / tb / GB, 1),
+                         "backup_slots_frac_hbm": round(2 * P / tb / GB / HBM_PEAK_GBS, 4),
+                         "restore_slots_gbs": round(2 * P / tr / GB, 1),
+                         "restore_slots_frac_hbm": round(2 * P / tr / GB / HBM_PEAK_GBS, 4)}
+        else:
+            res[name] = {"backup_slots_gbs": round(P / tb / GB, 2),
+                         "restore_slots_gbs": round(P / tr / GB, 2)}
+    del dev
+    # write-through: eight requests in a row, each reserved, backed up and
+    # committed; from the fifth on the tier is full and evicts a request's
+    # worth of entries per call
+    tier = K.kvx_tier_create(S, 1)
+    perm = synth.page_perm(w.seed + 71, w.num_pages)
+    t_res, evicted = [], 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r in range(8):
+        pages = perm[r * n:(r + 1) * n]
+        keys = np.arange(r * n, (r + 1) * n, dtype=np.uint64) + 1
+        c0 = time.perf_counter()
+        sl, ev_keys = K.kvx_tier_backup(tier, pool, keys, pages, host.ptr, HB, stream,
+                                        K.KVX_PATH_ZEROCOPY)
+        t_res.append(time.perf_counter() - c0)
+        evicted += ev_keys.size
+        stream.synchronize()
+        K.kvx_tier_commit(tier, sl)
+    wall = time.perf_counter() - t0
+    res["write_through"] = {"requests": 8, "gbs": round(8 * P / wall / GB, 2),
+                            "evicted_entries": int(evicted),
+                            "call_enqueue_us": round(median(t_res) * 1e6, 1)}
+    K.kvx_tier_destroy(tier)
+    print(json.dumps({"host_tier": res}), flush=True)
+    log(f"host tier: {res}")
+    host.free()
+    K.kvx_unregister_pool(pool)
     del alloc
     torch.cuda.empty_cache()
 

@@ -232,3 +232,73 @@ def test_full_size_layer_pipelined_exchange(name):
         K.kvx_ready_destroy(ready)
         host.free()
         pool.close()
+
+
+def test_full_size_host_tier_slots():
+    """The llama8b request through a slot-addressed host tier of 640 slots
+    (5 GiB pinned), zero-copy: BACKUP into 256 scattered slots, then RESTORE
+    of those slots into the request's destination pages with per-layer
+    publish. The named slots, gathered in page order, are checked against
+    the oracle's closed form of BACKUP; every unnamed slot of the first and
+    last layer keeps its prefill; the whole allocation is checked against
+    the closed form of the same round trip."""
+    t = torch()
+    w = WORKLOADS["llama8b"]
+    n, S = w.pages_per_request, 640
+    print(f"\n[full] llama8b host tier: {S} slots, n={n}", flush=True)
+    L = oracle_layout(w)
+    src, dst = request_pair(w)
+    slots = np.random.default_rng(w.seed + 60).permutation(S)[:n].astype(np.int32)
+    pool = DevicePool(w, generation=5)
+    HB = w.payload_bytes(S)
+    host = K.HostBuffer(HB)
+    synth.fill_gpu(host.ptr, HB, w.seed + 2, 0)
+    t.cuda.synchronize()
+    stream = t.cuda.Stream()
+    ready = K.kvx_ready_create(w.num_layers, 5)
+    Z = K.KVX_PATH_ZEROCOPY
+    try:
+        K.kvx_backup_slots(pool.handle, src, slots, host.ptr, HB, S, 0, w.num_layers, stream, Z)
+        K.kvx_sync(stream)
+        rows = w.num_layers * w.num_kv
+        hv = host.numpy().reshape(rows, S, w.piece_bytes)
+        t0 = time.time()
+        gathered = np.ascontiguousarray(hv[:, slots]).reshape(-1)
+        bad, first = check_packed_named(L, w.seed, src, gathered)
+        assert bad == 0, f"backup_slots: {bad} bytes differ, first at gathered offset {first}"
+        unnamed = np.setdiff1d(np.arange(S), slots)
+        jobs = [(r, s) for r in (0, 1, rows - 2, rows - 1) for s in unnamed]
+
+        def keep(job):
+            r, s = job
+            a = (r * S + s) * w.piece_bytes
+            return int(np.count_nonzero(hv[r, s] != synth.gen_bytes(w.seed + 2, a, w.piece_bytes)))
+
+        with ThreadPoolExecutor(THREADS) as ex:
+            assert sum(ex.map(keep, jobs)) == 0, "backup_slots wrote an unnamed slot"
+        print(f"[full] host tier checked in {time.time() - t0:.1f} s", flush=True)
+        del gathered
+        K.kvx_restore_slots(pool.handle, host.ptr, HB, S, slots, dst, 0, w.num_layers, ready, 0,
+                            stream, Z)
+        K.kvx_sync(stream)
+        assert K.kvx_ready_prefix(ready) == n
+        t0 = time.time()
+        bad, first = check_alloc(w, L, w.seed, src, dst, 0, w.num_layers, pool.alloc)
+        print(f"[full] allocation checked in {time.time() - t0:.1f} s", flush=True)
+        assert bad == 0, f"restore_slots: {bad} bytes differ, first at allocation byte {first}"
+    finally:
+        K.kvx_ready_destroy(ready)
+        host.free()
+        pool.close()
+
+
+def check_packed_named(L, seed, ids, packed):
+    """A whole packed buffer of every layer against the closed form of BACKUP,
+    in parallel 64 MiB ranges."""
+    def one(r):
+        a, b = r
+        return oracle.check_backup_gen(L, seed, ids, 0, L.num_layers, packed[a:b], a)
+
+    with ThreadPoolExecutor(THREADS) as ex:
+        res = list(ex.map(one, _ranges(packed.size)))
+    return sum(r[0] for r in res), min((r[1] for r in res if r[0]), default=-1)
