@@ -19,6 +19,7 @@
 #include <set>
 
 #include "kvx_internal.h"
+#include "ring.h"
 #include "tier.h"
 
 namespace kvx {
@@ -1046,6 +1047,167 @@ int kvx_tier_restore(kvx_tier* tier, kvx_pool* pool, const uint64_t* keys, const
         return rc;
     }
     tier->end();
+    return KVX_OK;
+}
+
+// ---- ring executor ---------------------------------------------------------
+
+namespace {
+
+void release_ring_flights(kvx_ring* r)
+{
+    for (RingFlight& f : r->flights)
+        if (f.event) {
+            (void)hipEventSynchronize(static_cast<hipEvent_t>(f.event));
+            (void)hipEventDestroy(static_cast<hipEvent_t>(f.event));
+            f.event = nullptr;
+        }
+}
+
+// Runs one descriptor: the call it names, against the data plane's tables.
+int run_sqe(const kvx_sqe& q, kvx_pool* const* pools, int32_t num_pools, void* const* buffers,
+            const uint64_t* buffer_bytes, int32_t num_buffers, kvx_ready* ready, void* stream)
+{
+    if (q.pool < 0 || q.pool >= num_pools || !pools[q.pool])
+        return fail(KVX_E_RANGE, "ring op " + std::to_string(q.op_id) + ": pool " +
+                                     std::to_string(q.pool) + " is not in the data plane's table");
+    if (q.buffer < 0 || q.buffer >= num_buffers || !buffers[q.buffer])
+        return fail(KVX_E_RANGE, "ring op " + std::to_string(q.op_id) + ": buffer " +
+                                     std::to_string(q.buffer) + " is not in the data plane's table");
+    if (q.buffer_offset > buffer_bytes[q.buffer])
+        return fail(KVX_E_RANGE, "ring op " + std::to_string(q.op_id) + ": buffer offset " +
+                                     std::to_string(q.buffer_offset) + " is past the buffer's " +
+                                     std::to_string(buffer_bytes[q.buffer]) + " bytes");
+    if (q.n < 0 || q.n > KVX_RING_MAX_PAGES)
+        return fail(KVX_E_RANGE, "ring op " + std::to_string(q.op_id) + ": bad page count");
+    kvx_pool* pool = pools[q.pool];
+    if (!pool_known(pool)) return fail(KVX_E_INVAL, "ring op: unknown pool handle in the table");
+    if (q.generation != pool->generation)
+        return fail(KVX_E_STALE, "ring op " + std::to_string(q.op_id) + ": generation " +
+                                     std::to_string(q.generation) + " does not match pool generation " +
+                                     std::to_string(pool->generation));
+    uint8_t* buf = static_cast<uint8_t*>(buffers[q.buffer]) + q.buffer_offset;
+    const uint64_t bytes = buffer_bytes[q.buffer] - q.buffer_offset;
+    kvx_ready* rd = q.ready_slot_base >= 0 ? ready : nullptr;
+    if (q.ready_slot_base >= 0 && !ready)
+        return fail(KVX_E_INVAL, "ring op " + std::to_string(q.op_id) +
+                                     ": publish asked for but the data plane has no ready object");
+    const int32_t sb = q.ready_slot_base >= 0 ? q.ready_slot_base : 0;
+    switch (q.op) {
+    case KVX_OP_BACKUP:
+        return kvx_backup(pool, q.page_ids, q.n, buf, bytes, q.layer_begin, q.layer_end, stream, q.path);
+    case KVX_OP_RESTORE:
+        return kvx_restore(pool, buf, bytes, q.page_ids, q.n, q.layer_begin, q.layer_end, rd, sb, stream,
+                           q.path);
+    case KVX_OP_BACKUP_SLOTS:
+        return kvx_backup_slots(pool, q.page_ids, q.host_slots, q.n, buf, bytes, q.num_host_slots,
+                                q.layer_begin, q.layer_end, stream, q.path);
+    case KVX_OP_RESTORE_SLOTS:
+        return kvx_restore_slots(pool, buf, bytes, q.num_host_slots, q.host_slots, q.page_ids, q.n,
+                                 q.layer_begin, q.layer_end, rd, sb, stream, q.path);
+    default:
+        return fail(KVX_E_INVAL, "ring op " + std::to_string(q.op_id) + ": unknown operation " +
+                                     std::to_string(q.op));
+    }
+}
+
+// Posts the completions of finished operations at the front, in order,
+// while the completion ring has room. With `wait`, waits for each.
+int post_finished(kvx_ring* r, bool wait, int32_t* posted)
+{
+    while (!r->flights.empty() && r->cq_room() > 0) {
+        RingFlight& f = r->flights.front();
+        if (f.event) {
+            hipEvent_t ev = static_cast<hipEvent_t>(f.event);
+            hipError_t e = wait ? hipEventSynchronize(ev) : hipEventQuery(ev);
+            if (e == hipErrorNotReady) break;
+            if (e != hipSuccess) {
+                (void)hipGetLastError();
+                f.status = KVX_E_HIP;
+            }
+            (void)hipEventDestroy(ev);
+            f.event = nullptr;
+        }
+        kvx_cqe c{};
+        c.op_id = f.op_id;
+        c.generation = f.generation;
+        c.status = f.status;
+        r->push_cqe(c);
+        r->flights.pop_front();
+        (*posted)++;
+    }
+    return KVX_OK;
+}
+
+int open_server(kvx_ring* r, const char* op)
+{
+    clear_error();
+    if (!ring_known(r)) return fail(KVX_E_INVAL, std::string(op) + ": unknown ring handle");
+    if (!r->live.load()) return fail(KVX_E_STALE, std::string(op) + ": ring was closed");
+    if (r->creator) return fail(KVX_E_INVAL, std::string(op) + ": only the data-plane side serves");
+    return KVX_OK;
+}
+
+}  // namespace
+
+int kvx_ring_serve(kvx_ring* r, kvx_pool* const* pools, int32_t num_pools, void* const* buffers,
+                   const uint64_t* buffer_bytes, int32_t num_buffers, kvx_ready* ready, void* stream,
+                   int32_t max_ops, int32_t* taken, int32_t* completed)
+{
+    int rc = open_server(r, "ring_serve");
+    if (rc != KVX_OK) return rc;
+    if (!taken || !completed) return fail(KVX_E_INVAL, "ring_serve: NULL output");
+    if (num_pools < 0 || num_buffers < 0 || (num_pools > 0 && !pools) ||
+        (num_buffers > 0 && (!buffers || !buffer_bytes)))
+        return fail(KVX_E_INVAL, "ring_serve: malformed tables");
+    *taken = *completed = 0;
+    std::lock_guard<std::mutex> lk(r->mu);
+    r->release_flights = release_ring_flights;
+    post_finished(r, false, completed);
+    kvx_sqe q;
+    while (*taken < max_ops && r->pop_sqe(&q)) {
+        (*taken)++;
+        RingFlight f;
+        f.op_id = q.op_id;
+        f.generation = q.generation;
+        f.status = run_sqe(q, pools, num_pools, buffers, buffer_bytes, num_buffers, ready, stream);
+        if (f.status == KVX_OK) {
+            hipEvent_t ev = nullptr;
+            hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+            if (e == hipSuccess) e = hipEventRecord(ev, static_cast<hipStream_t>(stream));
+            if (e != hipSuccess) {
+                // the work is enqueued but cannot be tracked: wait for it
+                if (ev) (void)hipEventDestroy(ev);
+                ev = nullptr;
+                f.status = hipStreamSynchronize(static_cast<hipStream_t>(stream)) == hipSuccess
+                               ? KVX_OK : KVX_E_HIP;
+            }
+            f.event = ev;
+        }
+        r->flights.push_back(f);
+    }
+    post_finished(r, false, completed);
+    return KVX_OK;
+}
+
+int kvx_ring_drain(kvx_ring* r, int32_t* completed)
+{
+    int rc = open_server(r, "ring_drain");
+    if (rc != KVX_OK) return rc;
+    if (!completed) return fail(KVX_E_INVAL, "ring_drain: completed is NULL");
+    *completed = 0;
+    std::lock_guard<std::mutex> lk(r->mu);
+    post_finished(r, true, completed);
+    // completions that do not fit (nobody reaps any more) are dropped once
+    // their work has finished
+    for (RingFlight& f : r->flights) {
+        if (f.event) {
+            (void)hipEventSynchronize(static_cast<hipEvent_t>(f.event));
+            (void)hipEventDestroy(static_cast<hipEvent_t>(f.event));
+        }
+        (*completed)++;
+    }
+    r->flights.clear();
     return KVX_OK;
 }
 

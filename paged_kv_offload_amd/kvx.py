@@ -20,6 +20,8 @@ KVX_OK = 0
 KVX_E_INVAL, KVX_E_NONCONTIG, KVX_E_ALIGN, KVX_E_RANGE, KVX_E_DUP = -1, -2, -3, -4, -5
 KVX_E_STALE, KVX_E_NOTPINNED, KVX_E_NOMEM, KVX_E_HIP, KVX_E_FULL = -6, -7, -8, -9, -10
 TIER_FREE, TIER_WRITING, TIER_RESIDENT = 0, 1, 2
+KVX_RING_MAX_PAGES = 1024
+KVX_OP_BACKUP, KVX_OP_RESTORE, KVX_OP_BACKUP_SLOTS, KVX_OP_RESTORE_SLOTS = 1, 2, 3, 4
 KVX_AX_PAGE, KVX_AX_LAYER, KVX_AX_KV = 0, 1, 2
 KVX_NHD, KVX_HND = 0, 1
 KVX_PATH_STAGED, KVX_PATH_ZEROCOPY, KVX_PATH_DEVICE = 0, 1, 2
@@ -73,6 +75,21 @@ class kvx_tier_info(ctypes.Structure):
                [("evictions", ctypes.c_uint64), ("generation", ctypes.c_uint64)]
 
 
+class kvx_sqe(ctypes.Structure):
+    _fields_ = [("op_id", ctypes.c_uint64), ("generation", ctypes.c_uint64),
+                ("buffer_offset", ctypes.c_uint64)] + \
+               [(k, ctypes.c_int32) for k in ("op", "pool", "buffer", "n", "layer_begin",
+                                              "layer_end", "path", "ready_slot_base",
+                                              "num_host_slots", "reserved")] + \
+               [("page_ids", ctypes.c_int32 * KVX_RING_MAX_PAGES),
+                ("host_slots", ctypes.c_int32 * KVX_RING_MAX_PAGES)]
+
+
+class kvx_cqe(ctypes.Structure):
+    _fields_ = [("op_id", ctypes.c_uint64), ("generation", ctypes.c_uint64),
+                ("status", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+
+
 # (name, restype, argtypes) of every exported function
 _vp, _i32, _u32, _i64, _u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_int64, \
     ctypes.c_uint64
@@ -112,6 +129,19 @@ SIGNATURES = [
     ("kvx_ipc_export", ctypes.c_int, [_vp, _P(kvx_ipc_handle)]),
     ("kvx_ipc_import", ctypes.c_int, [_P(kvx_ipc_handle), _P(_vp), _P(_i32)]),
     ("kvx_ipc_close", ctypes.c_int, [_vp]),
+    ("kvx_ring_create", ctypes.c_int, [ctypes.c_char_p, _i32, _u64, _P(_vp)]),
+    ("kvx_ring_open", ctypes.c_int, [ctypes.c_char_p, _P(_vp)]),
+    ("kvx_ring_close", ctypes.c_int, [_vp]),
+    ("kvx_ring_submit", ctypes.c_int, [_vp, _P(kvx_sqe)]),
+    ("kvx_ring_reap", ctypes.c_int, [_vp, _P(kvx_cqe), _i32, _P(_i32)]),
+    ("kvx_ring_take", ctypes.c_int, [_vp, _P(kvx_sqe), _P(_i32)]),
+    ("kvx_ring_complete", ctypes.c_int, [_vp, _P(kvx_cqe)]),
+    ("kvx_ring_peer_alive", ctypes.c_int, [_vp, _P(_i32)]),
+    ("kvx_ring_pending", ctypes.c_int, [_vp, _P(_i32), _P(_i32)]),
+    ("kvx_ring_serve", ctypes.c_int, [_vp, _P(_vp), _i32, _P(_vp), _P(_u64), _i32, _vp, _vp, _i32,
+                                      _P(_i32), _P(_i32)]),
+    ("kvx_ring_drain", ctypes.c_int, [_vp, _P(_i32)]),
+    ("kvx_ring_discard", ctypes.c_int, [_vp, _P(_i32)]),
     ("kvx_tier_create", ctypes.c_int, [_i32, _u64, _P(_vp)]),
     ("kvx_tier_destroy", ctypes.c_int, [_vp]),
     ("kvx_tier_reserve", ctypes.c_int, [_vp, _P(_u64), _i32, _P(_i32), _P(_u64), _P(_i32)]),
@@ -482,6 +512,108 @@ def kvx_tier_restore(tier: int, pool: int, keys, page_ids, host_pool, host_pool_
                                   host_pool_bytes, ready or 0, slot_base, _stream(stream), path,
                                   _sp(slots), ctypes.byref(hits)))
     return slots
+
+
+# ---------------------------------------------------------------------------
+# submission / completion rings
+# ---------------------------------------------------------------------------
+def make_sqe(op: int, op_id: int, generation: int, pool: int, buffer: int, page_ids,
+             layer_begin: int, layer_end: int, path: int = KVX_PATH_ZEROCOPY,
+             buffer_offset: int = 0, ready_slot_base: int = -1, host_slots=None,
+             num_host_slots: int = 0) -> kvx_sqe:
+    ids = _ids(page_ids)
+    if ids.size > KVX_RING_MAX_PAGES:
+        raise KvxError(KVX_E_RANGE, f"{ids.size} pages exceed {KVX_RING_MAX_PAGES} per descriptor")
+    q = kvx_sqe()
+    q.op_id, q.generation, q.buffer_offset = op_id, generation, buffer_offset
+    q.op, q.pool, q.buffer, q.n = op, pool, buffer, ids.size
+    q.layer_begin, q.layer_end, q.path = layer_begin, layer_end, path
+    q.ready_slot_base, q.num_host_slots = ready_slot_base, num_host_slots
+    ctypes.memmove(q.page_ids, ids.ctypes.data, ids.nbytes)
+    if host_slots is not None:
+        sl = _ids(host_slots)
+        if sl.size != ids.size:
+            raise KvxError(KVX_E_INVAL, f"{ids.size} pages but {sl.size} host slots")
+        ctypes.memmove(q.host_slots, sl.ctypes.data, sl.nbytes)
+    return q
+
+
+def kvx_ring_create(name: str, entries: int, generation: int) -> int:
+    out = _vp()
+    _check(lib().kvx_ring_create(name.encode(), entries, generation, ctypes.byref(out)))
+    return out.value
+
+
+def kvx_ring_open(name: str) -> int:
+    out = _vp()
+    _check(lib().kvx_ring_open(name.encode(), ctypes.byref(out)))
+    return out.value
+
+
+def kvx_ring_close(ring: int) -> None:
+    _check(lib().kvx_ring_close(ring))
+
+
+def kvx_ring_submit(ring: int, sqe: kvx_sqe) -> None:
+    _check(lib().kvx_ring_submit(ring, ctypes.byref(sqe)))
+
+
+def kvx_ring_reap(ring: int, max_n: int = 64) -> list:
+    """[(op_id, generation, status), ...] of up to max_n completions."""
+    buf = (kvx_cqe * max(max_n, 1))()
+    got = _i32()
+    _check(lib().kvx_ring_reap(ring, buf, max_n, ctypes.byref(got)))
+    return [(buf[i].op_id, buf[i].generation, buf[i].status) for i in range(got.value)]
+
+
+def kvx_ring_take(ring: int):
+    """The next descriptor, or None."""
+    q = kvx_sqe()
+    got = _i32()
+    _check(lib().kvx_ring_take(ring, ctypes.byref(q), ctypes.byref(got)))
+    return q if got.value else None
+
+
+def kvx_ring_complete(ring: int, op_id: int, generation: int, status: int) -> None:
+    c = kvx_cqe(op_id, generation, status, 0)
+    _check(lib().kvx_ring_complete(ring, ctypes.byref(c)))
+
+
+def kvx_ring_peer_alive(ring: int) -> bool:
+    a = _i32()
+    _check(lib().kvx_ring_peer_alive(ring, ctypes.byref(a)))
+    return bool(a.value)
+
+
+def kvx_ring_pending(ring: int):
+    """(submitted and not taken, completed and not reaped)."""
+    a, b = _i32(), _i32()
+    _check(lib().kvx_ring_pending(ring, ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def kvx_ring_serve(ring: int, pools, buffers, buffer_bytes, ready: int = None, stream=None,
+                   max_ops: int = 64):
+    """Runs up to max_ops descriptors against the tables; (taken, completed)."""
+    P = (_vp * max(len(pools), 1))(*pools)
+    B = (_vp * max(len(buffers), 1))(*[_ptr(b) for b in buffers])
+    N = (_u64 * max(len(buffer_bytes), 1))(*buffer_bytes)
+    taken, done = _i32(), _i32()
+    _check(lib().kvx_ring_serve(ring, P, len(pools), B, N, len(buffers), ready or 0,
+                                _stream(stream), max_ops, ctypes.byref(taken), ctypes.byref(done)))
+    return taken.value, done.value
+
+
+def kvx_ring_drain(ring: int) -> int:
+    d = _i32()
+    _check(lib().kvx_ring_drain(ring, ctypes.byref(d)))
+    return d.value
+
+
+def kvx_ring_discard(ring: int) -> int:
+    d = _i32()
+    _check(lib().kvx_ring_discard(ring, ctypes.byref(d)))
+    return d.value
 
 
 def kvx_exchange(pool: int, backup_ids: Iterable[int], backup_dst, backup_bytes: int,

@@ -4,14 +4,19 @@
 // accepted layout is compared with a brute-force row-major index; each plan
 // must cover every (page, slot) pair exactly once with valid runs.
 #include <algorithm>
+#include <deque>
+#include <thread>
+#include <unistd.h>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <random>
 #include <set>
 #include <string>
 #include <vector>
 
 #include "kvx_host.h"
+#include "ring.h"
 #include "tier.h"
 
 namespace kvx {
@@ -301,6 +306,113 @@ static void fuzz_tier(int iters)
     std::printf("tier: %d sequences, %d successful operations checked\n", iters, ok);
 }
 
+// Rings: random submit / take / complete / reap / discard on one ring from
+// both ends, against two deques; then a producer and a consumer thread
+// pushing 200000 descriptors through a small ring, in order.
+static void fuzz_ring(int iters)
+{
+    char name[64];
+    for (int it = 0; it < iters; it++) {
+        std::snprintf(name, sizeof name, "/kvx-fuzz-%d-%d", int(getpid()), it);
+        const int32_t entries = 1 << rnd(1, 6);
+        kvx_ring *r = nullptr, *o = nullptr;
+        CHECK(kvx_ring_create(name, entries, 3, &r) == KVX_OK);
+        CHECK(kvx_ring_open(name, &o) == KVX_OK);
+        std::deque<uint64_t> sq, cq;
+        uint64_t next = 1;
+        kvx_sqe q;
+        kvx_cqe c;
+        for (int step = 0; step < 400; step++) {
+            const int op = static_cast<int>(rnd(0, 4));
+            int32_t got = 0;
+            if (op == 0) {
+                std::memset(&q, 0, sizeof q);
+                q.op_id = next;
+                q.n = static_cast<int32_t>(rnd(0, KVX_RING_MAX_PAGES));
+                for (int32_t i = 0; i < q.n; i++) q.page_ids[i] = static_cast<int32_t>(next + i);
+                const int rc = kvx_ring_submit(r, &q);
+                CHECK((rc == KVX_OK) == (sq.size() < size_t(entries)));
+                if (rc == KVX_OK) sq.push_back(next++);
+            } else if (op == 1) {
+                CHECK(kvx_ring_take(o, &q, &got) == KVX_OK);
+                CHECK(got == (sq.empty() ? 0 : 1));
+                if (got) {
+                    CHECK(q.op_id == sq.front());
+                    for (int32_t i = 0; i < q.n; i++) CHECK(q.page_ids[i] == int32_t(q.op_id + i));
+                    sq.pop_front();
+                    c = kvx_cqe{q.op_id, 3, -static_cast<int32_t>(q.n), 0};
+                    if (kvx_ring_complete(o, &c) == KVX_OK) {
+                        cq.push_back(q.op_id);
+                    } else {
+                        CHECK(cq.size() == size_t(entries));
+                    }
+                }
+            } else if (op == 2) {
+                kvx_cqe out[8];
+                const int32_t max = static_cast<int32_t>(rnd(0, 8));
+                CHECK(kvx_ring_reap(r, out, max, &got) == KVX_OK);
+                CHECK(got == std::min<int32_t>(max, int32_t(cq.size())));
+                for (int32_t i = 0; i < got; i++) {
+                    CHECK(out[i].op_id == cq.front() && out[i].generation == 3);
+                    cq.pop_front();
+                }
+            } else if (op == 3 && rnd(0, 9) == 0) {
+                CHECK(kvx_ring_discard(o, &got) == KVX_OK);
+                CHECK(got == int32_t(sq.size()));
+                sq.clear();
+            } else {
+                int32_t a = 0, b = 0;
+                CHECK(kvx_ring_pending(r, &a, &b) == KVX_OK);
+                CHECK(a == int32_t(sq.size()) && b == int32_t(cq.size()));
+            }
+        }
+        int32_t alive = 0;
+        CHECK(kvx_ring_peer_alive(r, &alive) == KVX_OK && alive == 1);
+        CHECK(kvx_ring_close(o) == KVX_OK);
+        CHECK(kvx_ring_peer_alive(r, &alive) == KVX_OK && alive == 0);
+        CHECK(kvx_ring_close(r) == KVX_OK);
+        CHECK(kvx_ring_open(name, &o) == KVX_E_INVAL);   // the name is gone
+    }
+    // two threads, one per side
+    std::snprintf(name, sizeof name, "/kvx-fuzz-%d-threads", int(getpid()));
+    kvx_ring *r = nullptr, *o = nullptr;
+    CHECK(kvx_ring_create(name, 8, 1, &r) == KVX_OK);
+    CHECK(kvx_ring_open(name, &o) == KVX_OK);
+    const uint64_t total = 200000;
+    std::thread consumer([&] {
+        kvx_sqe q;
+        uint64_t want = 1;
+        while (want <= total) {
+            int32_t got = 0;
+            CHECK(kvx_ring_take(o, &q, &got) == KVX_OK);
+            if (!got) continue;
+            CHECK(q.op_id == want && q.n == 1 && q.page_ids[0] == int32_t(want % 1000));
+            kvx_cqe c{want, 1, 0, 0};
+            while (kvx_ring_complete(o, &c) != KVX_OK) {}
+            want++;
+        }
+    });
+    uint64_t sent = 1, reaped = 1;
+    kvx_sqe q;
+    std::memset(&q, 0, sizeof q);
+    while (reaped <= total) {
+        if (sent <= total) {
+            q.op_id = sent;
+            q.n = 1;
+            q.page_ids[0] = int32_t(sent % 1000);
+            if (kvx_ring_submit(r, &q) == KVX_OK) sent++;
+        }
+        kvx_cqe out[4];
+        int32_t got = 0;
+        CHECK(kvx_ring_reap(r, out, 4, &got) == KVX_OK);
+        for (int32_t i = 0; i < got; i++) CHECK(out[i].op_id == reaped++);
+    }
+    consumer.join();
+    CHECK(kvx_ring_close(o) == KVX_OK && kvx_ring_close(r) == KVX_OK);
+    std::printf("ring: %d random sequences and %llu descriptors across two threads checked\n",
+                iters, static_cast<unsigned long long>(total));
+}
+
 int main()
 {
     fuzz_extremes();
@@ -308,6 +420,7 @@ int main()
     fuzz_pages(3000);
     fuzz_slots(3000);
     fuzz_tier(300);
+    fuzz_ring(100);
     std::printf("host fuzz ok\n");
     return 0;
 }

@@ -1,5 +1,5 @@
 """The host-only parts of the runtime (pool layout validator, page-list
-checks, run planning, host-tier allocator) built with AddressSanitizer and
+checks, run planning, host-tier allocator, shared-memory rings) built with AddressSanitizer and
 UndefinedBehaviorSanitizer by the host compiler and fuzzed (CPU only)."""
 import os
 import shutil
@@ -18,8 +18,8 @@ def test_host_logic_under_asan_ubsan(tmp_path):
            "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
            "-I", os.path.join(ROOT, "include"), "-I", CSRC,
            os.path.join(CSRC, "geometry.cpp"), os.path.join(CSRC, "pages.cpp"),
-           os.path.join(CSRC, "tier.cpp"),
-           os.path.join(ROOT, "tests", "native", "host_fuzz.cpp"), "-o", exe]
+           os.path.join(CSRC, "tier.cpp"), os.path.join(CSRC, "ring.cpp"),
+           os.path.join(ROOT, "tests", "native", "host_fuzz.cpp"), "-o", exe, "-lpthread"]
     subprocess.run(cmd, check=True)
     # verify_asan_link_order=0: another preloaded library may come before the
     # ASan runtime in the process; the checks do not depend on the order
