@@ -51,8 +51,8 @@ PCIE_PEAK_GBS = 64.0      # MI355X host interface, PCIe 5.0 x16, published per-d
 # (FETCH_SIZE, WRITE_SIZE, scaled by a plain 2 GiB device copy in the same
 # run; see profiles/pack_kernel_llama8b.txt). Valid only for the kernel source
 # they were taken on: reported as null once kernels.hip changes.
-MEASURED_TRAFFIC = {"workload": "llama8b", "kernels_hip_sha256": "a30559ece8139a73f60a5d1a28a838edaf4f4dcec6497b31a18b9645ea4b7aa1",
-                    "bytes_per_launch": 4295187581}
+MEASURED_TRAFFIC = {"workload": "llama8b", "kernels_hip_sha256": "779679bd75d4412940d2ba1fe14fa1167f1611ae33d8b3a79d7217e3f3434d7c",
+                    "bytes_per_launch": 4295173010}
 
 
 def log(msg):

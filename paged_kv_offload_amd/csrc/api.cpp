@@ -215,7 +215,7 @@ int lane_counters(Lane* L, int64_t num_layers)
         L->layer_cap = cap;
     }
     // stream-ordered clear before the first kernel that counts into them
-    KVX_HIP(hipMemsetAsync(L->layer_done, 0, (L->layer_cap + 1) * sizeof(uint32_t), L->caller));
+    KVX_HIP(launch_clear_u32(L->layer_done, static_cast<uint32_t>(L->layer_cap + 1), L->caller));
     L->counters_dirty = false;
     return KVX_OK;
 }

@@ -397,6 +397,15 @@ __global__ __launch_bounds__(kThreads) void kvx_exchange_kernel(ExchangeArgs a)
 }
 
 // One wave polls a ready slot with bounded patience; see kvx_ready_wait_gpu.
+// Zeroes count words: clears the per-layer counters and the unit queue in
+// stream order. A kernel rather than a memset node, so that a caller who
+// captures the stream into a graph records a node that replays correctly.
+__global__ __launch_bounds__(256) void kvx_clear_kernel(uint32_t* p, uint32_t count)
+{
+    const uint32_t i = blockIdx.x * 256u + threadIdx.x;
+    if (i < count) p[i] = 0u;
+}
+
 __global__ __launch_bounds__(64) void kvx_ready_wait_kernel(const uint32_t* slot, uint32_t min_count,
                                                             uint32_t spin_limit, int32_t* status)
 {
@@ -552,6 +561,15 @@ hipError_t launch_exchange(const LaunchCfg& cfg, const ExchangeArgs& a, hipStrea
     case 1: return xgo_perm<1>(cfg, a, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+hipError_t launch_clear_u32(uint32_t* p, uint32_t count, hipStream_t s)
+{
+    if (count == 0) return hipSuccess;
+    const uint32_t blocks = (count + 255u) / 256u;
+    void* args[] = {&p, &count};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&kvx_clear_kernel), dim3(blocks), dim3(256),
+                           args, 0, s);
 }
 
 hipError_t launch_ready_wait(const uint32_t* slot, uint32_t min_count, uint32_t spin_limit,

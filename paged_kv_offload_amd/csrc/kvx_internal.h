@@ -182,6 +182,7 @@ uint32_t magic_u32(uint32_t d);   // multiplier for exact x / d with x * d < 2^3
 int pick_unroll(int64_t piece_bytes, int max_unroll, int forced);
 hipError_t launch_move(Dir dir, const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s);
 hipError_t launch_exchange(const LaunchCfg& cfg, const ExchangeArgs& a, hipStream_t s);
+hipError_t launch_clear_u32(uint32_t* p, uint32_t count, hipStream_t s);
 hipError_t launch_ready_wait(const uint32_t* slot, uint32_t min_count, uint32_t spin_limit,
                              int32_t* status, hipStream_t s);
 
