@@ -302,3 +302,53 @@ def check_packed_named(L, seed, ids, packed):
     with ThreadPoolExecutor(THREADS) as ex:
         res = list(ex.map(one, _ranges(packed.size)))
     return sum(r[0] for r in res), min((r[1] for r in res if r[0]), default=-1)
+
+
+@pytest.mark.parametrize("name", ["llama8b", "trtllm_hnd"])
+def test_whole_pool_in_one_call(name):
+    """Maximum size: every page of a 16 GiB pool (llama8b: 2048 pages in five
+    launches of at most 448; trtllm_hnd: 4096 head-major pages in ten) in one
+    BACKUP into a device buffer, in a random order, then one RESTORE of that
+    buffer into another random order of all pages with per-layer publish.
+    512 sampled pieces of the packed buffer and 512 sampled pieces of the
+    allocation, plus the padding before and after the pool, are checked
+    against the oracle's closed forms."""
+    t = torch()
+    w = WORKLOADS[name]
+    NB, NL = w.num_pages, w.num_layers
+    print(f"\n[full] {name} whole pool: {NB} pages, {w.payload_bytes(NB) / 2**30:.0f} GiB per call",
+          flush=True)
+    L = oracle_layout(w)
+    src = synth.page_perm(w.seed + 90, NB)
+    dst = synth.page_perm(w.seed + 91, NB)
+    pool = DevicePool(w, generation=5)
+    P = w.payload_bytes(NB)
+    pb = w.piece_bytes
+    dev = t.empty(P, dtype=t.uint8, device="cuda")
+    stream = t.cuda.Stream()
+    ready = K.kvx_ready_create(NL, 5)
+    rng = np.random.default_rng(w.seed + 92)
+    D = K.KVX_PATH_DEVICE
+    try:
+        K.kvx_backup(pool.handle, src, dev.data_ptr(), P, 0, NL, stream, D)
+        K.kvx_sync(stream)
+        for q in rng.choice(NL * w.num_kv * NB, 512, replace=False):
+            a = int(q) * pb
+            bad, first = oracle.check_backup_gen(L, w.seed, src, 0, NL, dev[a:a + pb].cpu().numpy(), a)
+            assert bad == 0, f"backup: piece at packed offset {a}: {bad} bytes differ, first {first}"
+        K.kvx_restore(pool.handle, dev.data_ptr(), P, dst, 0, NL, ready, 0, stream, D)
+        K.kvx_sync(stream)
+        assert K.kvx_ready_prefix(ready) == NB
+        ranges = [(0, w.byte_offset), (w.byte_offset + w.pool_bytes, w.alloc_bytes)]
+        ranges += [(w.byte_offset + int(q) * pb, w.byte_offset + (int(q) + 1) * pb)
+                   for q in rng.choice(NL * w.num_kv * NB, 512, replace=False)]
+        for a, b in ranges:
+            if a == b:
+                continue
+            bad, first = oracle.check_alloc_roundtrip(L, w.seed, w.seed + 1, src, dst, 0, NL,
+                                                      pool.alloc[a:b].cpu().numpy(), a)
+            assert bad == 0, f"restore: allocation bytes [{a}, {b}): {bad} differ, first at {first}"
+    finally:
+        K.kvx_ready_destroy(ready)
+        del dev
+        pool.close()
