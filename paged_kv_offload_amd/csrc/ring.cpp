@@ -10,11 +10,16 @@
 // survivor releases what it held for it. Each side therefore records its
 // process ID and start time in the ring; either can tell whether the other
 // still runs (a reused process ID has another start time).
+#include <algorithm>
 #include <cerrno>
 #include <cstdio>
 #include <cstring>
+#include <climits>
+#include <ctime>
 #include <fcntl.h>
+#include <linux/futex.h>
 #include <new>
+#include <sys/syscall.h>
 #include <set>
 #include <sys/mman.h>
 #include <sys/stat.h>
@@ -128,12 +133,38 @@ bool ring_known(const kvx_ring* r)
 
 using namespace kvx;
 
+namespace {
+
+// futex on a word of the shared mapping (not FUTEX_PRIVATE: the other
+// process waits on the same physical word)
+void futex_wake_all(std::atomic<uint32_t>* w)
+{
+    syscall(SYS_futex, reinterpret_cast<uint32_t*>(w), FUTEX_WAKE, INT_MAX, nullptr, nullptr, 0);
+}
+
+void futex_wait_for(std::atomic<uint32_t>* w, uint32_t expected, int64_t ns)
+{
+    struct timespec ts;
+    ts.tv_sec = static_cast<time_t>(ns / 1000000000);
+    ts.tv_nsec = static_cast<long>(ns % 1000000000);
+    syscall(SYS_futex, reinterpret_cast<uint32_t*>(w), FUTEX_WAIT, expected, &ts, nullptr, 0);
+}
+
+void bump(std::atomic<uint32_t>& seq, std::atomic<uint32_t>& waiters)
+{
+    seq.fetch_add(1, std::memory_order_seq_cst);
+    if (waiters.load(std::memory_order_seq_cst) != 0) futex_wake_all(&seq);
+}
+
+}  // namespace
+
 bool kvx_ring::push_sqe(const kvx_sqe& e)
 {
     const uint64_t tail = sh->sq_tail.load(std::memory_order_relaxed);
     if (tail - sh->sq_head.load(std::memory_order_acquire) >= sh->entries) return false;
     sq[tail & mask] = e;
     sh->sq_tail.store(tail + 1, std::memory_order_release);
+    bump(sh->sq_seq, sh->sq_waiters);
     return true;
 }
 
@@ -152,6 +183,7 @@ bool kvx_ring::push_cqe(const kvx_cqe& e)
     if (tail - sh->cq_head.load(std::memory_order_acquire) >= sh->entries) return false;
     cq[tail & mask] = e;
     sh->cq_tail.store(tail + 1, std::memory_order_release);
+    bump(sh->cq_seq, sh->cq_waiters);
     return true;
 }
 
@@ -215,6 +247,10 @@ int kvx_ring_create(const char* name, int32_t entries, uint64_t generation, kvx_
     sh->sq_tail.store(0);
     sh->cq_head.store(0);
     sh->cq_tail.store(0);
+    sh->sq_seq.store(0);
+    sh->sq_waiters.store(0);
+    sh->cq_seq.store(0);
+    sh->cq_waiters.store(0);
     std::atomic_thread_fence(std::memory_order_release);
     reinterpret_cast<std::atomic<uint32_t>*>(&sh->magic)->store(RING_SHM_MAGIC, std::memory_order_release);
     attach_arrays(r);
@@ -381,6 +417,47 @@ int kvx_ring_pending(const kvx_ring* r, int32_t* submitted, int32_t* completed)
     *completed = static_cast<int32_t>(sh->cq_tail.load(std::memory_order_acquire) -
                                       sh->cq_head.load(std::memory_order_acquire));
     return KVX_OK;
+}
+
+int kvx_ring_wait(kvx_ring* r, int32_t timeout_us, int32_t* ready)
+{
+    clear_error();
+    if (!ring_known(r)) return fail(KVX_E_INVAL, "ring_wait: unknown ring handle");
+    if (!r->live.load()) return fail(KVX_E_STALE, "ring_wait: ring was closed");
+    if (!ready) return fail(KVX_E_INVAL, "ring_wait: ready is NULL");
+    if (timeout_us < 0) return fail(KVX_E_RANGE, "ring_wait: negative timeout");
+    RingShared* sh = r->sh;
+    // the data plane waits for descriptors, the scheduler for completions
+    std::atomic<uint64_t>& head = r->creator ? sh->cq_head : sh->sq_head;
+    std::atomic<uint64_t>& tail = r->creator ? sh->cq_tail : sh->sq_tail;
+    std::atomic<uint32_t>& seq = r->creator ? sh->cq_seq : sh->sq_seq;
+    std::atomic<uint32_t>& waiters = r->creator ? sh->cq_waiters : sh->sq_waiters;
+    struct timespec t0;
+    clock_gettime(CLOCK_MONOTONIC, &t0);
+    const int64_t limit = int64_t(timeout_us) * 1000;
+    for (;;) {
+        const uint32_t s = seq.load(std::memory_order_seq_cst);
+        if (tail.load(std::memory_order_acquire) != head.load(std::memory_order_acquire)) {
+            *ready = 1;
+            return KVX_OK;
+        }
+        struct timespec t1;
+        clock_gettime(CLOCK_MONOTONIC, &t1);
+        const int64_t spent = (t1.tv_sec - t0.tv_sec) * 1000000000ll + (t1.tv_nsec - t0.tv_nsec);
+        const int32_t peer = r->creator ? sh->opener_pid.load() : sh->creator_pid.load();
+        const uint64_t peer_start = r->creator ? sh->opener_start.load() : sh->creator_start.load();
+        const bool peer_alive = peer != 0 && peer_start != 0 && process_start(peer) == peer_start;
+        if (spent >= limit || !peer_alive) {
+            *ready = 0;
+            return KVX_OK;
+        }
+        // sleep until the next push (the sequence word moves) or 10 ms, then
+        // look again (a dead peer never pushes)
+        waiters.fetch_add(1, std::memory_order_seq_cst);
+        if (seq.load(std::memory_order_seq_cst) == s)
+            futex_wait_for(&seq, s, std::min<int64_t>(limit - spent, 10000000));
+        waiters.fetch_sub(1, std::memory_order_seq_cst);
+    }
 }
 
 int kvx_ring_discard(kvx_ring* r, int32_t* dropped)

@@ -18,7 +18,7 @@ namespace kvx {
 
 constexpr uint32_t RING_MAGIC = 0x6b767867u;        // "kvxg": the local handle
 constexpr uint32_t RING_SHM_MAGIC = 0x6b767853u;    // "kvxS": the shared header
-constexpr uint32_t RING_SHM_VERSION = 1;
+constexpr uint32_t RING_SHM_VERSION = 2;
 
 static_assert(std::atomic<uint64_t>::is_always_lock_free, "shared atomics must be lock free");
 static_assert(std::atomic<int32_t>::is_always_lock_free, "shared atomics must be lock free");
@@ -42,7 +42,14 @@ struct RingShared {
     alignas(64) std::atomic<uint64_t> sq_tail;
     alignas(64) std::atomic<uint64_t> cq_head;
     alignas(64) std::atomic<uint64_t> cq_tail;
+    // wakeups: each push bumps its ring's sequence word and, if a waiter
+    // has announced itself, wakes it with a futex on that word
+    alignas(64) std::atomic<uint32_t> sq_seq;
+    std::atomic<uint32_t> sq_waiters;
+    alignas(64) std::atomic<uint32_t> cq_seq;
+    std::atomic<uint32_t> cq_waiters;
 };
+static_assert(sizeof(std::atomic<uint32_t>) == 4, "futex words are 32 bits");
 
 // Bytes of the shared object for `entries` descriptors per ring, and the
 // offsets of the two arrays in it.

@@ -138,6 +138,7 @@ SIGNATURES = [
     ("kvx_ring_complete", ctypes.c_int, [_vp, _P(kvx_cqe)]),
     ("kvx_ring_peer_alive", ctypes.c_int, [_vp, _P(_i32)]),
     ("kvx_ring_pending", ctypes.c_int, [_vp, _P(_i32), _P(_i32)]),
+    ("kvx_ring_wait", ctypes.c_int, [_vp, _i32, _P(_i32)]),
     ("kvx_ring_serve", ctypes.c_int, [_vp, _P(_vp), _i32, _P(_vp), _P(_u64), _i32, _vp, _vp, _i32,
                                       _P(_i32), _P(_i32)]),
     ("kvx_ring_drain", ctypes.c_int, [_vp, _P(_i32)]),
@@ -583,6 +584,14 @@ def kvx_ring_peer_alive(ring: int) -> bool:
     a = _i32()
     _check(lib().kvx_ring_peer_alive(ring, ctypes.byref(a)))
     return bool(a.value)
+
+
+def kvx_ring_wait(ring: int, timeout_us: int) -> bool:
+    """True once the caller's side has something to take; False on timeout
+    or when the other side has died."""
+    r = _i32()
+    _check(lib().kvx_ring_wait(ring, timeout_us, ctypes.byref(r)))
+    return bool(r.value)
 
 
 def kvx_ring_pending(ring: int):

@@ -219,3 +219,50 @@ def test_executor_refusals_complete_at_once():
         K.kvx_ring_close(o)
         K.kvx_ring_close(r)
         K.kvx_unregister_pool(pool)
+
+
+WAITER = textwrap.dedent("""
+    import sys, time
+    sys.path.insert(0, {root!r})
+    from paged_kv_offload_amd import kvx as K
+    o = K.kvx_ring_open({name!r})
+    print("open", flush=True)
+    t0 = time.monotonic()
+    got = K.kvx_ring_wait(o, 5_000_000)
+    waited = time.monotonic() - t0
+    q = K.kvx_ring_take(o)
+    K.kvx_ring_complete(o, q.op_id, q.generation, 0)
+    print(f"{{int(got)}} {{waited:.4f}}", flush=True)
+    K.kvx_ring_close(o)
+""")
+
+
+def test_wait_sleeps_until_a_push_and_honours_timeouts_and_death():
+    """A data-plane process sleeps in kvx_ring_wait until the scheduler
+    submits (woken within milliseconds, not at its 5 s limit); the
+    scheduler's own wait returns the completion; a wait with nothing to take
+    returns False at its timeout, and at once when the other side is gone."""
+    name = ring_name()
+    r = K.kvx_ring_create(name, 4, 2)
+    p = subprocess.Popen([sys.executable, "-c", WAITER.format(root=ROOT, name=name)],
+                         stdout=subprocess.PIPE, text=True)
+    try:
+        assert p.stdout.readline().strip() == "open"
+        t0 = time.monotonic()
+        assert not K.kvx_ring_wait(r, 200_000)                 # nothing posted yet
+        assert 0.15 < time.monotonic() - t0 < 2.0
+        K.kvx_ring_submit(r, K.make_sqe(K.KVX_OP_BACKUP, 77, 2, 0, 0, [1], 0, 1))
+        assert K.kvx_ring_wait(r, 5_000_000)
+        assert K.kvx_ring_reap(r) == [(77, 2, 0)]
+        got, waited = p.stdout.readline().split()
+        assert got == "1" and 0.15 < float(waited) < 2.0, (got, waited)
+        assert p.wait(30) == 0
+        t0 = time.monotonic()
+        assert not K.kvx_ring_wait(r, 5_000_000)               # the data plane is gone
+        assert time.monotonic() - t0 < 1.0
+        assert not K.kvx_ring_wait(r, 0)
+    finally:
+        if p.poll() is None:
+            p.kill()
+            p.wait()
+        K.kvx_ring_close(r)
