@@ -456,6 +456,58 @@ def test_gpu_consumer_waits_for_published_layer(stream):
         pool.close()
 
 
+@pytest.mark.parametrize("path", ["zerocopy", "staged"])
+def test_gpu_consumer_reads_layer0_while_later_layers_are_held_back(path, stream):
+    """The producer restores layer 0, then is held back on its stream by a
+    bounded wait that cannot succeed (about 0.1-0.2 s), then restores the
+    other layers. A consumer stream waits for layer 0's count and copies
+    layer 0 out: the copy equals the oracle's restored bytes, and it is done
+    while the last layer is still unpublished."""
+    t = torch()
+    w, n = SMALL["llama_small"]
+    print(f"\n[layer0-consumer] path={path} n={n}", flush=True)
+    L = oracle_layout(w)
+    pool = DevicePool(w, seed=306, generation=2)
+    img = pool.host_image()
+    _, dst = pages(w, n)
+    nb = w.host_bytes(n)
+    pk = Packed(w, n, path, fill_seed=12)
+    hbytes = synth.gen_bytes(12, 0, nb)
+    ready = K.kvx_ready_create(w.num_layers, 2)
+    never = K.kvx_ready_create(1, 2)          # its count stays 0: the hold-back wait times out
+    consumer = t.cuda.Stream()
+    status = t.zeros(2, dtype=t.int32, device="cuda")
+    out = Packed(w, n, "device")
+    t.cuda.synchronize()
+    last = w.num_layers - 1
+    P = PATHS[path]
+    try:
+        K.kvx_restore(pool.handle, pk.ptr, nb, dst, 0, 1, ready, 0, stream, P)
+        K.kvx_ready_wait_gpu(never, 0, 1, stream, 100_000, status.data_ptr() + 4)
+        K.kvx_restore(pool.handle, pk.ptr, nb, dst, 1, w.num_layers, ready, 0, stream, P)
+        K.kvx_ready_wait_gpu(ready, 0, n, consumer, 5_000_000, status.data_ptr())
+        K.kvx_backup(pool.handle, dst, out.ptr, nb, 0, 1, consumer, K.KVX_PATH_DEVICE)
+        K.kvx_sync(consumer)
+        later = K.kvx_layer_ready(ready, last)
+        K.kvx_sync(stream)
+        st = status.cpu().tolist()
+        assert st == [1, 0], st               # the consumer saw layer 0; the hold-back timed out
+        assert later == 0, "the last layer was published before the held-back restore ran"
+        restored = oracle.restore(L, img, hbytes, dst, 0, w.num_layers)
+        want = oracle.backup(L, restored, dst, 0, 1)
+        hi = w.num_kv * n * w.piece_bytes
+        got = out.numpy()
+        assert np.array_equal(got[:hi], want[:hi]), diff_report(got[:hi], want[:hi])
+        assert [K.kvx_layer_ready(ready, s) for s in range(w.num_layers)] == [n] * w.num_layers
+        assert np.array_equal(pool.host_image(), restored)
+    finally:
+        K.kvx_ready_destroy(never)
+        K.kvx_ready_destroy(ready)
+        out.close()
+        pk.close()
+        pool.close()
+
+
 def test_sidecar_prefix_is_min_over_pools(stream):
     """Two pools restored with the same page IDs publish into one ready
     object; the prefix is the minimum over all their slots."""
