@@ -96,6 +96,16 @@ Tuning tuning()
     return g_tune;
 }
 
+// Test hook (KVX_OPT_FAIL_ALLOCS): true if this internal allocation is to
+// fail as if the device were out of memory.
+bool injected_alloc_failure()
+{
+    std::lock_guard<std::mutex> lk(g_tune_mu);
+    if (g_tune.fail_allocs <= 0) return false;
+    g_tune.fail_allocs--;
+    return true;
+}
+
 namespace {
 
 // ---------------------------------------------------------------------------
@@ -176,7 +186,8 @@ int lane_ring(Lane* L, int64_t slot_bytes, int nslots)
     L->slot_pending.assign(nslots, false);
     L->nslots = 0;
     void* p = nullptr;
-    hipError_t e = hipMalloc(&p, static_cast<size_t>(slot_bytes) * nslots);
+    hipError_t e = injected_alloc_failure() ? hipErrorOutOfMemory
+                                            : hipMalloc(&p, static_cast<size_t>(slot_bytes) * nslots);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         return fail(KVX_E_NOMEM, "cannot allocate the device staging ring (" +
@@ -206,7 +217,8 @@ int lane_counters(Lane* L, int64_t num_layers)
         }
         const int64_t cap = std::max<int64_t>(num_layers, 256);
         void* p = nullptr;
-        hipError_t e = hipMalloc(&p, (cap + 1) * sizeof(uint32_t));
+        hipError_t e = injected_alloc_failure() ? hipErrorOutOfMemory
+                                                : hipMalloc(&p, (cap + 1) * sizeof(uint32_t));
         if (e != hipSuccess) {
             (void)hipGetLastError();
             return fail(KVX_E_NOMEM, "cannot allocate per-layer completion counters");
@@ -1672,6 +1684,10 @@ int kvx_set_option(int32_t option, int64_t value)
             break;
         g_tune.unit_rounds = value;
         return KVX_OK;
+    case KVX_OPT_FAIL_ALLOCS:
+        if (value < 0 || value > 1000) break;
+        g_tune.fail_allocs = value;
+        return KVX_OK;
     default:
         return fail(KVX_E_INVAL, "set_option: unknown option " + std::to_string(option));
     }
@@ -1697,6 +1713,7 @@ int kvx_get_option(int32_t option, int64_t* value)
     case KVX_OPT_UNIT_ROUNDS: *value = g_tune.unit_rounds; return KVX_OK;
     case KVX_OPT_STAGED_DMA_ON_CALLER: *value = g_tune.staged_dma_on_caller; return KVX_OK;
     case KVX_OPT_HND_LDS: *value = g_tune.hnd_lds; return KVX_OK;
+    case KVX_OPT_FAIL_ALLOCS: *value = g_tune.fail_allocs; return KVX_OK;
     default: return fail(KVX_E_INVAL, "get_option: unknown option " + std::to_string(option));
     }
 }

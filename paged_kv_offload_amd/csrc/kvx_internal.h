@@ -78,6 +78,7 @@ struct Tuning {
     int64_t unit_rounds = 0;              // 0 = auto; else the unit's vector rounds
     int64_t staged_dma_on_caller = 0;     // staged DMA on the caller's stream instead of a side stream
     int64_t hnd_lds = -1;                 // HND<->NHD through LDS: 1 both, 0 never, -1 scatter only
+    int64_t fail_allocs = 0;              // test hook: internal device allocations left to fail
 };
 Tuning tuning();
 

@@ -508,6 +508,115 @@ def test_gpu_consumer_reads_layer0_while_later_layers_are_held_back(path, stream
         pool.close()
 
 
+# bf16 words a float path would change: quiet and signalling NaNs with
+# payloads and either sign, infinities, denormals, negative zero
+BF16_SPECIALS = [0x7FC0, 0xFFC0, 0x7F81, 0xFF81, 0x7FBF, 0x7FC1, 0x7F80, 0xFF80, 0x0001, 0x8001,
+                 0x007F, 0x807F, 0x8000, 0x0000, 0xFFFF, 0x7FFF]
+
+
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("case", ["llama_small", "mla_small"])
+def test_bits_survive_whatever_they_would_mean(case, path, stream):
+    """Dtype neutrality: a bf16 pool holding every NaN, infinity, denormal and
+    signed-zero class in every position of a row, and an fp8 pool holding
+    all 256 byte values, round-trip through BACKUP and RESTORE bit for bit
+    (the oracle's bytes, and the restored pages equal the sources)."""
+    t = torch()
+    w, n = SMALL[case]
+    print(f"\n[dtype] case={case} eb={w.dtype_bytes} path={path}", flush=True)
+    L = oracle_layout(w)
+    pool = DevicePool(w, seed=308, generation=4)
+    rng = np.random.default_rng(308)
+    if w.dtype_bytes == 2:
+        words = rng.integers(0, 1 << 16, w.alloc_bytes // 2, dtype=np.uint16)
+        specials = np.array(BF16_SPECIALS, dtype=np.uint16)
+        # runs of the special words, shifted by one word each row of 64 so
+        # every class meets every position of a row
+        idx = np.arange(words.size)
+        pick = (idx // 64 + idx) % (2 * specials.size)
+        words = np.where(pick < specials.size, specials[pick % specials.size], words)
+        img = words.view(np.uint8)
+    else:
+        img = (np.arange(w.alloc_bytes, dtype=np.int64) * 73 % 256).astype(np.uint8)
+        assert np.unique(img).size == 256
+    pool.alloc.copy_(t.from_numpy(img.copy()))
+    t.cuda.synchronize()
+    src, dst = pages(w, n)
+    nb = w.host_bytes(n)
+    pk = Packed(w, n, path, fill_seed=22)
+    try:
+        K.kvx_backup(pool.handle, src, pk.ptr, nb, 0, w.num_layers, stream, PATHS[path])
+        K.kvx_sync(stream)
+        want = oracle.backup(L, img, src, 0, w.num_layers)
+        got = pk.numpy()
+        assert np.array_equal(got, want), "backup " + diff_report(got, want)
+        K.kvx_restore(pool.handle, pk.ptr, nb, dst, 0, w.num_layers, None, 0, stream, PATHS[path])
+        K.kvx_sync(stream)
+        want_alloc = oracle.restore(L, img, want, dst, 0, w.num_layers)
+        after = pool.host_image()
+        assert np.array_equal(after, want_alloc), "restore " + diff_report(after, want_alloc)
+        for i in (0, n - 1):
+            for l in range(w.num_layers):
+                for c in range(w.num_kv):
+                    a, b = oracle.piece_start(L, src[i], l, c), oracle.piece_start(L, dst[i], l, c)
+                    assert np.array_equal(after[b:b + w.piece_bytes], img[a:a + w.piece_bytes])
+    finally:
+        pk.close()
+        pool.close()
+
+
+def test_injected_allocation_failures_fail_closed_and_recover():
+    """With the allocation test hook armed, a staged BACKUP whose staging ring
+    cannot be allocated and a publishing RESTORE whose per-layer counters
+    cannot be allocated both return KVX_E_NOMEM with nothing written (pool,
+    packed buffer and ready counts unchanged); the hook is spent, the ready
+    object resets, and the same calls then succeed with the oracle's bytes."""
+    t = torch()
+    w, n = SMALL["llama_small"]
+    L = oracle_layout(w)
+    pool = DevicePool(w, seed=307, generation=3)
+    img = pool.host_image()
+    src, dst = pages(w, n)
+    nb = w.host_bytes(n)
+    s_staged, s_zc = t.cuda.Stream(), t.cuda.Stream()   # fresh lanes: nothing allocated yet
+    pk = Packed(w, n, "staged", fill_seed=21)
+    ready = K.kvx_ready_create(w.num_layers, 3)
+    try:
+        K.kvx_set_option(K.KVX_OPT_FAIL_ALLOCS, 1)
+        with pytest.raises(K.KvxError) as e:
+            K.kvx_backup(pool.handle, src, pk.ptr, nb, 0, w.num_layers, s_staged, K.KVX_PATH_STAGED)
+        assert e.value.code == K.KVX_E_NOMEM, e.value.message
+        assert K.kvx_get_option(K.KVX_OPT_FAIL_ALLOCS) == 0
+        K.kvx_sync(s_staged)
+        assert np.array_equal(pk.numpy(), synth.gen_bytes(21, 0, nb))
+        K.kvx_backup(pool.handle, src, pk.ptr, nb, 0, w.num_layers, s_staged, K.KVX_PATH_STAGED)
+        K.kvx_sync(s_staged)
+        want = oracle.backup(L, img, src, 0, w.num_layers)
+        assert np.array_equal(pk.numpy(), want), diff_report(pk.numpy(), want)
+
+        K.kvx_set_option(K.KVX_OPT_FAIL_ALLOCS, 1)
+        with pytest.raises(K.KvxError) as e:
+            K.kvx_restore(pool.handle, pk.ptr, nb, dst, 0, w.num_layers, ready, 0, s_zc,
+                          K.KVX_PATH_ZEROCOPY)
+        assert e.value.code == K.KVX_E_NOMEM, e.value.message
+        K.kvx_sync(s_zc)
+        assert np.array_equal(pool.host_image(), img)
+        assert [K.kvx_layer_ready(ready, s) for s in range(w.num_layers)] == [0] * w.num_layers
+        K.kvx_ready_reset(ready)
+        K.kvx_restore(pool.handle, pk.ptr, nb, dst, 0, w.num_layers, ready, 0, s_zc,
+                      K.KVX_PATH_ZEROCOPY)
+        K.kvx_sync(s_zc)
+        assert K.kvx_ready_prefix(ready) == n
+        want_alloc = oracle.restore(L, img, want, dst, 0, w.num_layers)
+        after = pool.host_image()
+        assert np.array_equal(after, want_alloc), diff_report(after, want_alloc)
+    finally:
+        K.kvx_set_option(K.KVX_OPT_FAIL_ALLOCS, 0)
+        K.kvx_ready_destroy(ready)
+        pk.close()
+        pool.close()
+
+
 def test_sidecar_prefix_is_min_over_pools(stream):
     """Two pools restored with the same page IDs publish into one ready
     object; the prefix is the minimum over all their slots."""
