@@ -412,10 +412,15 @@ int kvx_ring_pending(const kvx_ring* r, int32_t* submitted, int32_t* completed)
     if (!r->live.load()) return fail(KVX_E_STALE, "ring_pending: ring was closed");
     if (!submitted || !completed) return fail(KVX_E_INVAL, "ring_pending: NULL output");
     const RingShared* sh = r->sh;
-    *submitted = static_cast<int32_t>(sh->sq_tail.load(std::memory_order_acquire) -
-                                      sh->sq_head.load(std::memory_order_acquire));
-    *completed = static_cast<int32_t>(sh->cq_tail.load(std::memory_order_acquire) -
-                                      sh->cq_head.load(std::memory_order_acquire));
+    // a snapshot while both sides run: each head is read before its tail, so
+    // the difference is never negative; it is capped at the ring's size
+    auto count = [&](const std::atomic<uint64_t>& head, const std::atomic<uint64_t>& tail) {
+        const uint64_t h = head.load(std::memory_order_acquire);
+        const uint64_t t = tail.load(std::memory_order_acquire);
+        return static_cast<int32_t>(std::min<uint64_t>(t - h, sh->entries));
+    };
+    *submitted = count(sh->sq_head, sh->sq_tail);
+    *completed = count(sh->cq_head, sh->cq_tail);
     return KVX_OK;
 }
 

@@ -28,3 +28,19 @@ def test_host_logic_under_asan_ubsan(tmp_path):
     out = subprocess.run([exe], env=env, capture_output=True, text=True, timeout=300)
     assert out.returncode == 0, out.stdout + out.stderr
     assert "host fuzz ok" in out.stdout
+
+
+@pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
+def test_rings_and_tier_under_tsan(tmp_path):
+    """The rings and the host tier used from several threads at once, built
+    with ThreadSanitizer: no data race, and every count adds up."""
+    exe = str(tmp_path / "host_threads")
+    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=thread",
+           "-I", os.path.join(ROOT, "include"), "-I", CSRC,
+           os.path.join(CSRC, "ring.cpp"), os.path.join(CSRC, "tier.cpp"),
+           os.path.join(ROOT, "tests", "native", "host_threads.cpp"), "-o", exe, "-lpthread"]
+    subprocess.run(cmd, check=True)
+    env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1:second_deadlock_stack=1")
+    out = subprocess.run([exe], env=env, capture_output=True, text=True, timeout=300)
+    assert out.returncode == 0, out.stdout + out.stderr
+    assert "host threads ok" in out.stdout
