@@ -458,11 +458,12 @@ def test_gpu_consumer_waits_for_published_layer(stream):
 
 @pytest.mark.parametrize("path", ["zerocopy", "staged"])
 def test_gpu_consumer_reads_layer0_while_later_layers_are_held_back(path, stream):
-    """The producer restores layer 0, then is held back on its stream by a
-    bounded wait that cannot succeed (about 0.1-0.2 s), then restores the
-    other layers. A consumer stream waits for layer 0's count and copies
-    layer 0 out: the copy equals the oracle's restored bytes, and it is done
-    while the last layer is still unpublished."""
+    """The producer restores layer 0; the later layers are held back on the
+    host until a consumer stream, waiting for layer 0's count, has copied
+    layer 0 out. The copy equals the oracle's restored bytes, no later layer
+    is published while it runs, and the later layers then complete. (The
+    hold-back is on the host: streams may share a hardware queue, so a
+    kernel-side delay on the producer could also delay the consumer.)"""
     t = torch()
     w, n = SMALL["llama_small"]
     print(f"\n[layer0-consumer] path={path} n={n}", flush=True)
@@ -474,34 +475,29 @@ def test_gpu_consumer_reads_layer0_while_later_layers_are_held_back(path, stream
     pk = Packed(w, n, path, fill_seed=12)
     hbytes = synth.gen_bytes(12, 0, nb)
     ready = K.kvx_ready_create(w.num_layers, 2)
-    never = K.kvx_ready_create(1, 2)          # its count stays 0: the hold-back wait times out
     consumer = t.cuda.Stream()
-    status = t.zeros(2, dtype=t.int32, device="cuda")
+    status = t.zeros(1, dtype=t.int32, device="cuda")
     out = Packed(w, n, "device")
     t.cuda.synchronize()
-    last = w.num_layers - 1
     P = PATHS[path]
     try:
         K.kvx_restore(pool.handle, pk.ptr, nb, dst, 0, 1, ready, 0, stream, P)
-        K.kvx_ready_wait_gpu(never, 0, 1, stream, 100_000, status.data_ptr() + 4)
-        K.kvx_restore(pool.handle, pk.ptr, nb, dst, 1, w.num_layers, ready, 0, stream, P)
         K.kvx_ready_wait_gpu(ready, 0, n, consumer, 5_000_000, status.data_ptr())
         K.kvx_backup(pool.handle, dst, out.ptr, nb, 0, 1, consumer, K.KVX_PATH_DEVICE)
         K.kvx_sync(consumer)
-        later = K.kvx_layer_ready(ready, last)
-        K.kvx_sync(stream)
-        st = status.cpu().tolist()
-        assert st == [1, 0], st               # the consumer saw layer 0; the hold-back timed out
-        assert later == 0, "the last layer was published before the held-back restore ran"
+        assert int(status.item()) == 1
+        assert [K.kvx_layer_ready(ready, s) for s in range(1, w.num_layers)] == \
+            [0] * (w.num_layers - 1)
         restored = oracle.restore(L, img, hbytes, dst, 0, w.num_layers)
         want = oracle.backup(L, restored, dst, 0, 1)
         hi = w.num_kv * n * w.piece_bytes
         got = out.numpy()
         assert np.array_equal(got[:hi], want[:hi]), diff_report(got[:hi], want[:hi])
+        K.kvx_restore(pool.handle, pk.ptr, nb, dst, 1, w.num_layers, ready, 0, stream, P)
+        K.kvx_sync(stream)
         assert [K.kvx_layer_ready(ready, s) for s in range(w.num_layers)] == [n] * w.num_layers
         assert np.array_equal(pool.host_image(), restored)
     finally:
-        K.kvx_ready_destroy(never)
         K.kvx_ready_destroy(ready)
         out.close()
         pk.close()
@@ -565,23 +561,39 @@ def test_bits_survive_whatever_they_would_mean(case, path, stream):
         pool.close()
 
 
+# 300 layers: more than the per-layer counters a lane starts with (256)
+MANY_LAYERS = Workload(name="many_layers", outer=("layer", "kv", "page"), inner="NHD", num_pages=16,
+                       num_layers=300, num_kv=2, page_size=2, num_heads=1, head_dim=64,
+                       dtype_bytes=2, pages_per_request=4, seed=211)
+
+
 def test_injected_allocation_failures_fail_closed_and_recover():
     """With the allocation test hook armed, a staged BACKUP whose staging ring
-    cannot be allocated and a publishing RESTORE whose per-layer counters
-    cannot be allocated both return KVX_E_NOMEM with nothing written (pool,
-    packed buffer and ready counts unchanged); the hook is spent, the ready
-    object resets, and the same calls then succeed with the oracle's bytes."""
+    must be (re)allocated (a slot size no other test uses) and a publishing
+    RESTORE of a 300-layer pool whose per-layer counters must grow both
+    return KVX_E_NOMEM with nothing written (pool, packed buffer and ready
+    counts unchanged); the hook is spent, the ready object resets, and the
+    same calls then succeed with the oracle's bytes."""
     t = torch()
     w, n = SMALL["llama_small"]
     L = oracle_layout(w)
     pool = DevicePool(w, seed=307, generation=3)
     img = pool.host_image()
-    src, dst = pages(w, n)
+    src, _ = pages(w, n)
     nb = w.host_bytes(n)
-    s_staged, s_zc = t.cuda.Stream(), t.cuda.Stream()   # fresh lanes: nothing allocated yet
+    s_staged, s_zc = t.cuda.Stream(), t.cuda.Stream()
     pk = Packed(w, n, "staged", fill_seed=21)
-    ready = K.kvx_ready_create(w.num_layers, 3)
+    w2, n2 = MANY_LAYERS, MANY_LAYERS.pages_per_request
+    L2 = oracle_layout(w2)
+    pool2 = DevicePool(w2, generation=3)
+    img2 = pool2.host_image()
+    src2, dst2 = pages(w2, n2)
+    nb2 = w2.host_bytes(n2)
+    pk2 = Packed(w2, n2, "zerocopy", fill_seed=23)
+    ready = K.kvx_ready_create(w2.num_layers, 3)
+    old_slot = K.kvx_get_option(K.KVX_OPT_STAGE_SLOT_BYTES)
     try:
+        K.kvx_set_option(K.KVX_OPT_STAGE_SLOT_BYTES, (96 << 20) + 4096)
         K.kvx_set_option(K.KVX_OPT_FAIL_ALLOCS, 1)
         with pytest.raises(K.KvxError) as e:
             K.kvx_backup(pool.handle, src, pk.ptr, nb, 0, w.num_layers, s_staged, K.KVX_PATH_STAGED)
@@ -594,27 +606,32 @@ def test_injected_allocation_failures_fail_closed_and_recover():
         want = oracle.backup(L, img, src, 0, w.num_layers)
         assert np.array_equal(pk.numpy(), want), diff_report(pk.numpy(), want)
 
+        hbytes = synth.gen_bytes(23, 0, nb2)
         K.kvx_set_option(K.KVX_OPT_FAIL_ALLOCS, 1)
         with pytest.raises(K.KvxError) as e:
-            K.kvx_restore(pool.handle, pk.ptr, nb, dst, 0, w.num_layers, ready, 0, s_zc,
+            K.kvx_restore(pool2.handle, pk2.ptr, nb2, dst2, 0, w2.num_layers, ready, 0, s_zc,
                           K.KVX_PATH_ZEROCOPY)
         assert e.value.code == K.KVX_E_NOMEM, e.value.message
+        assert K.kvx_get_option(K.KVX_OPT_FAIL_ALLOCS) == 0
         K.kvx_sync(s_zc)
-        assert np.array_equal(pool.host_image(), img)
-        assert [K.kvx_layer_ready(ready, s) for s in range(w.num_layers)] == [0] * w.num_layers
+        assert np.array_equal(pool2.host_image(), img2)
+        assert K.kvx_ready_prefix(ready) == 0
         K.kvx_ready_reset(ready)
-        K.kvx_restore(pool.handle, pk.ptr, nb, dst, 0, w.num_layers, ready, 0, s_zc,
+        K.kvx_restore(pool2.handle, pk2.ptr, nb2, dst2, 0, w2.num_layers, ready, 0, s_zc,
                       K.KVX_PATH_ZEROCOPY)
         K.kvx_sync(s_zc)
-        assert K.kvx_ready_prefix(ready) == n
-        want_alloc = oracle.restore(L, img, want, dst, 0, w.num_layers)
-        after = pool.host_image()
-        assert np.array_equal(after, want_alloc), diff_report(after, want_alloc)
+        assert K.kvx_ready_prefix(ready) == n2
+        want2 = oracle.restore(L2, img2, hbytes, dst2, 0, w2.num_layers)
+        after = pool2.host_image()
+        assert np.array_equal(after, want2), diff_report(after, want2)
     finally:
         K.kvx_set_option(K.KVX_OPT_FAIL_ALLOCS, 0)
+        K.kvx_set_option(K.KVX_OPT_STAGE_SLOT_BYTES, old_slot)
         K.kvx_ready_destroy(ready)
         pk.close()
+        pk2.close()
         pool.close()
+        pool2.close()
 
 
 def test_sidecar_prefix_is_min_over_pools(stream):
