@@ -5,10 +5,10 @@ this model operation by operation; the product path never imports it.
 
 What it models. The out-of-process HiCache RFC (SGLang issue #37372,
 section "Ownership") gives host KV physical allocation to the data plane and
-keeps cache semantics with the scheduler's index, and asks for an explicit
-eviction and invalidation protocol under which neither side can see stale
-residency. The pages fix no algorithm for it; the reading taken here is
-the plainest that keeps that promise:
+keeps cache semantics with the scheduler's index, and leaves open how the
+two sides agree on eviction and invalidation so that a lookup is never
+answered from an outdated view. The pages fix no algorithm for it; the
+reading taken here is the plainest one that makes every answer current:
 
   * a slot is FREE, WRITING (a backup in flight: invisible to lookups,
     never evicted) or RESIDENT (readable; a lookup hit pins it until the

@@ -2,9 +2,8 @@
 //
 // The data plane owns the host KV physical allocation while the scheduler's
 // cache index stays authoritative for cache semantics ([RFC] "Ownership",
-// and its note that host-tier eviction and invalidation then need an
-// explicit protocol so that neither side can see stale residency). The
-// protocol here:
+// which leaves open how the two sides then agree on when a page's host copy
+// exists). The rules here make every answer current:
 //   - a backup first reserves slots (WRITING: invisible to lookups, never
 //     evicted) and commits them once its bytes have landed;
 //   - a restore looks keys up, which pins their slots until it releases
