@@ -843,6 +843,44 @@ def all_workloads():
     res["zerocopy_exchange_frac_of_memcpy_both_directions"] = round(
         res["zerocopy_exchange"] / res["memcpy_both_directions_gbs"], 4)
     log(f"mixed zerocopy_exchange: {res['zerocopy_exchange']} GB/s")
+    # the same schedule as descriptors through a submission ring, served on
+    # one stream by the library's executor; with pairing on it runs each
+    # backup and the restore after it as one exchange by itself
+    rname = f"/kvx-bench-mixed-{os.getpid()}"
+    ring = K.kvx_ring_create(rname, 256, 1)
+    srv = K.kvx_ring_open(rname)
+    rbufs, rsizes = [h.ptr for h in slots], [P] * len(slots)
+
+    def run_ring():
+        nb = nr = 0
+        for k, (kind, ids) in enumerate(sched):
+            if kind == "backup":
+                q = K.make_sqe(K.KVX_OP_BACKUP, k, 1, 0, 4 + nb % 4, ids, 0, w.num_layers,
+                               K.KVX_PATH_ZEROCOPY)
+                nb += 1
+            else:
+                q = K.make_sqe(K.KVX_OP_RESTORE, k, 1, 0, nr % 4, ids, 0, w.num_layers,
+                               K.KVX_PATH_ZEROCOPY)
+                nr += 1
+            K.kvx_ring_submit(ring, q)
+        done = []
+        while len(done) < len(sched):
+            K.kvx_ring_serve(srv, [pool], rbufs, rsizes, None, streams[0], 256)
+            done += K.kvx_ring_reap(ring, 256)
+            time.sleep(0.0002)
+        assert all(c[2] == 0 for c in done), [c for c in done if c[2] != 0][:3]
+
+    for pairing in (1, 0):
+        K.kvx_set_option(K.KVX_OPT_RING_PAIRING, pairing)
+        run_ring()
+        t0 = time.perf_counter()
+        run_ring()
+        key = "ring_zerocopy_paired" if pairing else "ring_zerocopy_one_by_one"
+        res[key] = round(128 * P / (time.perf_counter() - t0) / GB, 2)
+        log(f"mixed {key}: {res[key]} GB/s")
+    K.kvx_set_option(K.KVX_OPT_RING_PAIRING, 1)
+    K.kvx_ring_close(srv)
+    K.kvx_ring_close(ring)
     for name, bpath, rpath in (("zerocopy", K.KVX_PATH_ZEROCOPY, K.KVX_PATH_ZEROCOPY),
                                ("staged", K.KVX_PATH_STAGED, K.KVX_PATH_STAGED),
                                ("zerocopy_backup_staged_restore", K.KVX_PATH_ZEROCOPY,

@@ -1076,9 +1076,11 @@ void release_ring_flights(kvx_ring* r)
         }
 }
 
-// Runs one descriptor: the call it names, against the data plane's tables.
-int run_sqe(const kvx_sqe& q, kvx_pool* const* pools, int32_t num_pools, void* const* buffers,
-            const uint64_t* buffer_bytes, int32_t num_buffers, kvx_ready* ready, void* stream)
+// Looks a descriptor's pool and buffer up in the data plane's tables and
+// checks its generation: *pool, and the buffer from its offset on.
+int resolve_sqe(const kvx_sqe& q, kvx_pool* const* pools, int32_t num_pools, void* const* buffers,
+                const uint64_t* buffer_bytes, int32_t num_buffers, kvx_pool** pool, uint8_t** buf,
+                uint64_t* bytes)
 {
     if (q.pool < 0 || q.pool >= num_pools || !pools[q.pool])
         return fail(KVX_E_RANGE, "ring op " + std::to_string(q.op_id) + ": pool " +
@@ -1092,18 +1094,41 @@ int run_sqe(const kvx_sqe& q, kvx_pool* const* pools, int32_t num_pools, void* c
                                      std::to_string(buffer_bytes[q.buffer]) + " bytes");
     if (q.n < 0 || q.n > KVX_RING_MAX_PAGES)
         return fail(KVX_E_RANGE, "ring op " + std::to_string(q.op_id) + ": bad page count");
-    kvx_pool* pool = pools[q.pool];
-    if (!pool_known(pool)) return fail(KVX_E_INVAL, "ring op: unknown pool handle in the table");
-    if (q.generation != pool->generation)
+    *pool = pools[q.pool];
+    if (!pool_known(*pool)) return fail(KVX_E_INVAL, "ring op: unknown pool handle in the table");
+    if (q.generation != (*pool)->generation)
         return fail(KVX_E_STALE, "ring op " + std::to_string(q.op_id) + ": generation " +
                                      std::to_string(q.generation) + " does not match pool generation " +
-                                     std::to_string(pool->generation));
-    uint8_t* buf = static_cast<uint8_t*>(buffers[q.buffer]) + q.buffer_offset;
-    const uint64_t bytes = buffer_bytes[q.buffer] - q.buffer_offset;
-    kvx_ready* rd = q.ready_slot_base >= 0 ? ready : nullptr;
-    if (q.ready_slot_base >= 0 && !ready)
+                                     std::to_string((*pool)->generation));
+    *buf = static_cast<uint8_t*>(buffers[q.buffer]) + q.buffer_offset;
+    *bytes = buffer_bytes[q.buffer] - q.buffer_offset;
+    return KVX_OK;
+}
+
+// The ready object a RESTORE descriptor publishes into (NULL: none).
+int sqe_ready(const kvx_sqe& q, kvx_ready* ready, kvx_ready** out)
+{
+    *out = nullptr;
+    if (q.ready_slot_base < 0) return KVX_OK;
+    if (!ready)
         return fail(KVX_E_INVAL, "ring op " + std::to_string(q.op_id) +
                                      ": publish asked for but the data plane has no ready object");
+    *out = ready;
+    return KVX_OK;
+}
+
+// Runs one descriptor: the call it names, against the data plane's tables.
+int run_sqe(const kvx_sqe& q, kvx_pool* const* pools, int32_t num_pools, void* const* buffers,
+            const uint64_t* buffer_bytes, int32_t num_buffers, kvx_ready* ready, void* stream)
+{
+    kvx_pool* pool = nullptr;
+    uint8_t* buf = nullptr;
+    uint64_t bytes = 0;
+    int rc = resolve_sqe(q, pools, num_pools, buffers, buffer_bytes, num_buffers, &pool, &buf, &bytes);
+    if (rc != KVX_OK) return rc;
+    kvx_ready* rd = nullptr;
+    rc = sqe_ready(q, ready, &rd);
+    if (rc != KVX_OK) return rc;
     const int32_t sb = q.ready_slot_base >= 0 ? q.ready_slot_base : 0;
     switch (q.op) {
     case KVX_OP_BACKUP:
@@ -1121,6 +1146,66 @@ int run_sqe(const kvx_sqe& q, kvx_pool* const* pools, int32_t num_pools, void* c
         return fail(KVX_E_INVAL, "ring op " + std::to_string(q.op_id) + ": unknown operation " +
                                      std::to_string(q.op));
     }
+}
+
+// A BACKUP and a RESTORE of one pool on the zero-copy or device path, taken
+// one after the other, can run as one kvx_exchange (both link directions
+// busy together).
+bool pairable(const kvx_sqe& a, const kvx_sqe& b)
+{
+    const bool ops = (a.op == KVX_OP_BACKUP && b.op == KVX_OP_RESTORE) ||
+                     (a.op == KVX_OP_RESTORE && b.op == KVX_OP_BACKUP);
+    return ops && a.pool == b.pool && a.path == b.path &&
+           (a.path == KVX_PATH_ZEROCOPY || a.path == KVX_PATH_DEVICE);
+}
+
+// Runs a pairable BACKUP and RESTORE as one kvx_exchange. Any refusal
+// (either descriptor's checks, or the two touching the same bytes) leaves
+// nothing enqueued, and the caller runs them one by one instead.
+int run_pair(const kvx_sqe& a, const kvx_sqe& b, kvx_pool* const* pools, int32_t num_pools,
+             void* const* buffers, const uint64_t* buffer_bytes, int32_t num_buffers, kvx_ready* ready,
+             void* stream)
+{
+    const kvx_sqe& bk = a.op == KVX_OP_BACKUP ? a : b;
+    const kvx_sqe& rs = a.op == KVX_OP_BACKUP ? b : a;
+    kvx_pool *pb = nullptr, *pr = nullptr;
+    uint8_t *bb = nullptr, *br = nullptr;
+    uint64_t nb = 0, nr = 0;
+    int rc = resolve_sqe(bk, pools, num_pools, buffers, buffer_bytes, num_buffers, &pb, &bb, &nb);
+    if (rc != KVX_OK) return rc;
+    rc = resolve_sqe(rs, pools, num_pools, buffers, buffer_bytes, num_buffers, &pr, &br, &nr);
+    if (rc != KVX_OK) return rc;
+    kvx_ready* rd = nullptr;
+    rc = sqe_ready(rs, ready, &rd);
+    if (rc != KVX_OK) return rc;
+    const kvx_xfer xb{bk.page_ids, bk.n, bb, nb, bk.layer_begin, bk.layer_end};
+    const kvx_xfer xr{rs.page_ids, rs.n, br, nr, rs.layer_begin, rs.layer_end};
+    return kvx_exchange(pb, &xb, &xr, rd, rs.ready_slot_base >= 0 ? rs.ready_slot_base : 0, stream,
+                        bk.path);
+}
+
+// Queues the completion of descriptor q whose call returned `status`; a
+// call that enqueued work completes when an event recorded after it fires.
+void push_flight(kvx_ring* r, const kvx_sqe& q, int status, void* stream)
+{
+    RingFlight f;
+    f.op_id = q.op_id;
+    f.generation = q.generation;
+    f.status = status;
+    if (f.status == KVX_OK) {
+        hipEvent_t ev = nullptr;
+        hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventRecord(ev, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) {
+            // the work is enqueued but cannot be tracked: wait for it
+            if (ev) (void)hipEventDestroy(ev);
+            ev = nullptr;
+            f.status = hipStreamSynchronize(static_cast<hipStream_t>(stream)) == hipSuccess ? KVX_OK
+                                                                                             : KVX_E_HIP;
+        }
+        f.event = ev;
+    }
+    r->flights.push_back(f);
 }
 
 // Posts the completions of finished operations at the front, in order,
@@ -1176,27 +1261,45 @@ int kvx_ring_serve(kvx_ring* r, kvx_pool* const* pools, int32_t num_pools, void*
     std::lock_guard<std::mutex> lk(r->mu);
     r->release_flights = release_ring_flights;
     post_finished(r, false, completed);
-    kvx_sqe q;
-    while (*taken < max_ops && r->pop_sqe(&q)) {
-        (*taken)++;
-        RingFlight f;
-        f.op_id = q.op_id;
-        f.generation = q.generation;
-        f.status = run_sqe(q, pools, num_pools, buffers, buffer_bytes, num_buffers, ready, stream);
-        if (f.status == KVX_OK) {
-            hipEvent_t ev = nullptr;
-            hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
-            if (e == hipSuccess) e = hipEventRecord(ev, static_cast<hipStream_t>(stream));
-            if (e != hipSuccess) {
-                // the work is enqueued but cannot be tracked: wait for it
-                if (ev) (void)hipEventDestroy(ev);
-                ev = nullptr;
-                f.status = hipStreamSynchronize(static_cast<hipStream_t>(stream)) == hipSuccess
-                               ? KVX_OK : KVX_E_HIP;
-            }
-            f.event = ev;
+    const bool pairing = tuning().ring_pairing != 0;
+    static thread_local kvx_sqe qa, qb;   // 8 KiB each: kept off the stack
+    kvx_sqe* cur = &qa;
+    kvx_sqe* nxt = &qb;
+    bool has_nxt = false;
+    while (*taken < max_ops) {
+        if (has_nxt) {
+            std::swap(cur, nxt);
+            has_nxt = false;
+        } else if (!r->pop_sqe(cur)) {
+            break;
         }
-        r->flights.push_back(f);
+        (*taken)++;
+        // a BACKUP next to a RESTORE of the same pool share one launch
+        // sequence ([RFC] "Ownership": the data plane batches transfers)
+        if (pairing && *taken < max_ops && (cur->op == KVX_OP_BACKUP || cur->op == KVX_OP_RESTORE) &&
+            r->pop_sqe(nxt)) {
+            has_nxt = true;
+            if (pairable(*cur, *nxt)) {
+                const int prc = run_pair(*cur, *nxt, pools, num_pools, buffers, buffer_bytes,
+                                         num_buffers, ready, stream);
+                if (prc == KVX_OK || prc == KVX_E_HIP) {
+                    (*taken)++;
+                    has_nxt = false;
+                    push_flight(r, *cur, prc, stream);
+                    push_flight(r, *nxt, prc, stream);
+                    continue;
+                }
+            }
+        }
+        push_flight(r, *cur, run_sqe(*cur, pools, num_pools, buffers, buffer_bytes, num_buffers, ready,
+                                     stream),
+                    stream);
+    }
+    if (has_nxt) {
+        (*taken)++;
+        push_flight(r, *nxt, run_sqe(*nxt, pools, num_pools, buffers, buffer_bytes, num_buffers, ready,
+                                     stream),
+                    stream);
     }
     post_finished(r, false, completed);
     return KVX_OK;
@@ -1688,6 +1791,10 @@ int kvx_set_option(int32_t option, int64_t value)
         if (value < 0 || value > 1000) break;
         g_tune.fail_allocs = value;
         return KVX_OK;
+    case KVX_OPT_RING_PAIRING:
+        if (value != 0 && value != 1) break;
+        g_tune.ring_pairing = value;
+        return KVX_OK;
     default:
         return fail(KVX_E_INVAL, "set_option: unknown option " + std::to_string(option));
     }
@@ -1714,6 +1821,7 @@ int kvx_get_option(int32_t option, int64_t* value)
     case KVX_OPT_STAGED_DMA_ON_CALLER: *value = g_tune.staged_dma_on_caller; return KVX_OK;
     case KVX_OPT_HND_LDS: *value = g_tune.hnd_lds; return KVX_OK;
     case KVX_OPT_FAIL_ALLOCS: *value = g_tune.fail_allocs; return KVX_OK;
+    case KVX_OPT_RING_PAIRING: *value = g_tune.ring_pairing; return KVX_OK;
     default: return fail(KVX_E_INVAL, "get_option: unknown option " + std::to_string(option));
     }
 }

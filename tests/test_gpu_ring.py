@@ -102,6 +102,62 @@ def test_ring_ops_match_the_oracle(case, path):
         pool.close()
 
 
+@pytest.mark.parametrize("pairing", [1, 0])
+@pytest.mark.parametrize("path", ["zerocopy", "device"])
+def test_ring_runs_backup_and_restore_together(path, pairing):
+    """A BACKUP followed by a RESTORE of other pages runs as one exchange
+    (or, with pairing off, one after the other) with the same bytes; a
+    RESTORE followed by a BACKUP of the pages it writes is refused as a pair
+    and runs in submission order, so the BACKUP reads the restored bytes."""
+    t = torch()
+    w, n = SMALL["llama_small"]
+    print(f"\n[ring-pair] path={path} pairing={pairing} n={n}", flush=True)
+    L = oracle_layout(w)
+    pool = DevicePool(w, seed=w.seed + 85, generation=4)
+    nb = w.host_bytes(n)
+    bufs = [Packed(w, n, path, fill_seed=w.seed + 86 + k) for k in range(3)]
+    ready = K.kvx_ready_create(w.num_layers, 4)
+    stream = t.cuda.Stream()
+    name = f"/kvx-pair-{os.getpid()}-{path}-{pairing}"
+    ring = K.kvx_ring_create(name, 8, 4)
+    o = K.kvx_ring_open(name)
+    P = K.PATHS[path]
+    nl = w.num_layers
+    perm = synth.page_perm(w.seed + 87, w.num_pages)
+    src, dst, dst2 = perm[:n], perm[n:2 * n], perm[2 * n:3 * n]
+    old = K.kvx_get_option(K.KVX_OPT_RING_PAIRING)
+    try:
+        K.kvx_set_option(K.KVX_OPT_RING_PAIRING, pairing)
+        img = pool.host_image()
+        h0 = synth.gen_bytes(w.seed + 86, 0, nb)
+        ops = [K.make_sqe(K.KVX_OP_BACKUP, 1, 4, 0, 1, src, 0, nl, P),
+               K.make_sqe(K.KVX_OP_RESTORE, 2, 4, 0, 0, dst, 0, nl, P, ready_slot_base=0),
+               K.make_sqe(K.KVX_OP_RESTORE, 3, 4, 0, 1, dst2, 0, nl, P),
+               K.make_sqe(K.KVX_OP_BACKUP, 4, 4, 0, 2, dst2, 0, nl, P)]
+        for q in ops:
+            K.kvx_ring_submit(ring, q)
+        got = serve_until(ring, o, [pool.handle], [b.ptr for b in bufs], [b.nbytes for b in bufs],
+                          len(ops), ready, stream)
+        assert [(g[0], g[2]) for g in got] == [(1, 0), (2, 0), (3, 0), (4, 0)]
+        b1 = oracle.backup(L, img, src, 0, nl)
+        assert np.array_equal(bufs[1].numpy(), b1)
+        want = oracle.restore(L, img, h0, dst, 0, nl)
+        want = oracle.restore(L, want, b1, dst2, 0, nl)
+        after = pool.host_image()
+        assert np.array_equal(after, want), diff_report(after, want)
+        # the BACKUP of dst2 ran after the RESTORE into it: it read b1
+        assert np.array_equal(bufs[2].numpy(), b1), diff_report(bufs[2].numpy(), b1)
+        assert K.kvx_ready_prefix(ready) == n
+    finally:
+        K.kvx_set_option(K.KVX_OPT_RING_PAIRING, old)
+        K.kvx_ring_close(o)
+        K.kvx_ring_close(ring)
+        K.kvx_ready_destroy(ready)
+        for b in bufs:
+            b.close()
+        pool.close()
+
+
 IPC_CASE = Workload(name="ring_ipc", outer=("layer", "kv", "page"), inner="HND", num_pages=200,
                     num_layers=3, num_kv=2, page_size=16, num_heads=4, head_dim=64, dtype_bytes=2,
                     pages_per_request=40, seed=231, byte_offset=4096, alloc_tail=4096)
