@@ -725,35 +725,64 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
     return rc;
 }
 
-// BACKUP and RESTORE sides of kvx_exchange, enqueued as launches that each
-// interleave one chunk of pages of both sides (identity slot order).
-int run_exchange(kvx_pool* pool, const kvx_xfer* bk, const kvx_xfer* rs, kvx_ready* ready,
-                 int32_t slot_base, void* stream_v, int32_t path)
+// One side of an exchange: pages in visiting order with their packed slots
+// (slots == NULL: slot i), the device view of the packed buffer or host pool
+// of pk_slots slots per (layer, kv), and the layer range.
+struct XSide {
+    const int32_t* pages;
+    const int32_t* slots;
+    int32_t n;
+    void* packed;
+    int64_t pk_slots;
+    int32_t l0, l1;
+    uint8_t* view = nullptr;
+};
+
+// Fills side x of launch args `a` with pairs [p0, p0 + per) of `xs`;
+// returns the side's work units.
+int64_t exchange_side(const PoolGeom& g, int64_t cpp, const XSide& xs, Side* x, int64_t p0, int64_t per,
+                      ExchangeArgs& a, bool backup)
+{
+    const int64_t np = std::max<int64_t>(0, std::min<int64_t>(per, xs.n - p0));
+    x->packed = xs.view;
+    x->pk_lc_stride = xs.pk_slots * g.piece_bytes;
+    x->pk_layer0 = 0;
+    x->pk_slot0 = 0;
+    x->layer_begin = xs.l0;
+    x->npairs = static_cast<uint32_t>(np);
+    int32_t* pages = backup ? a.pages_b : a.pages_r;
+    for (int64_t j = 0; j < np; j++) pages[j] = xs.pages[p0 + j];
+    (backup ? a.first_b : a.first_r) = static_cast<int32_t>(p0);
+    return int64_t(xs.l1 - xs.l0) * g.num_kv * np * cpp;
+}
+
+int64_t exchange_side(const PoolGeom& g, int64_t cpp, const XSide& xs, Side* x, int64_t p0, int64_t per,
+                      ExchangeSlotArgs& a, bool backup)
+{
+    const int64_t np = std::max<int64_t>(0, std::min<int64_t>(per, xs.n - p0));
+    x->packed = xs.view;
+    x->pk_lc_stride = xs.pk_slots * g.piece_bytes;
+    x->pk_layer0 = 0;
+    x->pk_slot0 = 0;
+    x->layer_begin = xs.l0;
+    x->npairs = static_cast<uint32_t>(np);
+    int32_t* pairs = backup ? a.pairs_b : a.pairs_r;
+    for (int64_t j = 0; j < np; j++) {
+        pairs[2 * j] = xs.pages[p0 + j];
+        pairs[2 * j + 1] = xs.slots[p0 + j];
+    }
+    return int64_t(xs.l1 - xs.l0) * g.num_kv * np * cpp;
+}
+
+// The launches of one exchange: each interleaves one share of both sides'
+// pages (at most max_pairs per side per launch, spread evenly).
+template <class A>
+int exchange_launches(kvx_pool* pool, const XSide& bk, const XSide& rs, kvx_ready* ready,
+                      int32_t slot_base, hipStream_t s, bool host, const Tuning& t, Lane* L,
+                      int64_t max_pairs)
 {
     const PoolGeom& g = pool->geom;
-    const bool host = path == KVX_PATH_ZEROCOPY;
-    int rc = resolve_device(pool);
-    if (rc != KVX_OK) return rc;
-    if (ready && ready->device >= 0 && ready->device != pool->device)
-        return fail(KVX_E_INVAL, "exchange: the ready object's counts are on GPU " +
-                                     std::to_string(ready->device) + ", the pool on GPU " +
-                                     std::to_string(pool->device));
-    DeviceGuard dg(pool->device);
-    hipStream_t s = static_cast<hipStream_t>(stream_v);
-    uint8_t *vb = nullptr, *vr = nullptr;
-    rc = check_packed_kind(pool, bk->packed, path, "exchange backup", &vb);
-    if (rc != KVX_OK) return rc;
-    rc = check_packed_kind(pool, rs->packed, path, "exchange restore", &vr);
-    if (rc != KVX_OK) return rc;
-    const Tuning t = tuning();
-    Lane* L = nullptr;
-    rc = get_lane(pool->device, s, &L);
-    if (rc != KVX_OK) return rc;
-    std::lock_guard<std::mutex> lk(L->mu);
-    rc = lane_counters(L, g.num_layers);   // the unit queue, and the publish counters
-    if (rc != KVX_OK) return rc;
-
-    ExchangeArgs a;
+    A a;
     std::memset(&a, 0, sizeof a);
     LaunchCfg cfg;
     cfg.host_link = host;
@@ -765,37 +794,21 @@ int run_exchange(kvx_pool* pool, const kvx_xfer* bk, const kvx_xfer* rs, kvx_rea
     pub.queue = L->layer_done + L->layer_cap;
     if (ready) {
         pub.ready = ready->counts_dev + slot_base;
-        pub.layer_target = static_cast<uint32_t>(g.num_kv * int64_t(rs->n) * a.g.chunks_per_piece);
-        pub.value = static_cast<uint32_t>(rs->n);
+        pub.layer_target = static_cast<uint32_t>(g.num_kv * int64_t(rs.n) * a.g.chunks_per_piece);
+        pub.value = static_cast<uint32_t>(rs.n);
     }
     set_publish(&pub, &a.p);
     a.g.unit_order = 0;
     const int64_t cpp = a.g.chunks_per_piece;
-    // each side's pages spread evenly over the launches
-    const int64_t launches = std::max<int64_t>((bk->n + kMaxPairs - 1) / kMaxPairs,
-                                               (rs->n + kMaxPairs - 1) / kMaxPairs);
-    const int64_t per_b = (bk->n + launches - 1) / launches;
-    const int64_t per_r = (rs->n + launches - 1) / launches;
-    auto side = [&](Side* x, const kvx_xfer* xf, uint8_t* view, int32_t* pages, int64_t p0, int64_t per) {
-        const int64_t np = std::max<int64_t>(0, std::min<int64_t>(per, xf->n - p0));
-        x->packed = view;
-        x->pk_lc_stride = int64_t(xf->n) * g.piece_bytes;
-        x->pk_layer0 = 0;
-        x->pk_slot0 = 0;
-        x->layer_begin = xf->layer_begin;
-        x->npairs = static_cast<uint32_t>(np);
-        for (int64_t j = 0; j < np; j++) pages[j] = xf->page_ids[p0 + j];
-        return int64_t(xf->layer_end - xf->layer_begin) * g.num_kv * np * cpp;
-    };
+    const int64_t launches = std::max<int64_t>((bk.n + max_pairs - 1) / max_pairs,
+                                               (rs.n + max_pairs - 1) / max_pairs);
+    const int64_t per_b = (bk.n + launches - 1) / launches;
+    const int64_t per_r = (rs.n + launches - 1) / launches;
     for (int64_t k = 0; k < launches; k++) {
-        const int64_t ub = side(&a.b, bk, vb, a.pages_b, k * per_b, per_b);
-        const int64_t ur = side(&a.r, rs, vr, a.pages_r, k * per_r, per_r);
-        a.first_b = static_cast<int32_t>(k * per_b);
-        a.first_r = static_cast<int32_t>(k * per_r);
-        if (ub + ur >= (int64_t(1) << 31)) {
-            rc = fail(KVX_E_INVAL, "exchange: one launch would have too many work units");
-            break;
-        }
+        const int64_t ub = exchange_side(g, cpp, bk, &a.b, k * per_b, per_b, a, true);
+        const int64_t ur = exchange_side(g, cpp, rs, &a.r, k * per_r, per_r, a, false);
+        if (ub + ur >= (int64_t(1) << 31))
+            return fail(KVX_E_INVAL, "exchange: one launch would have too many work units");
         a.b.total_units = static_cast<uint32_t>(ub);
         a.r.total_units = static_cast<uint32_t>(ur);
         // grid: over the host link, the two single-direction host grids
@@ -810,11 +823,41 @@ int run_exchange(kvx_pool* pool, const kvx_xfer* bk, const kvx_xfer* rs, kvx_rea
             gmax = int64_t(L->cu_count) * 8;
         cfg.grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(ub + ur, gmax)));
         const hipError_t e = launch_exchange(cfg, a, s);
-        if (e != hipSuccess) {
-            rc = hip_fail(e, "exchange kernel launch");
-            break;
-        }
+        if (e != hipSuccess) return hip_fail(e, "exchange kernel launch");
     }
+    return KVX_OK;
+}
+
+// BACKUP and RESTORE sides of kvx_exchange / kvx_exchange_slots, enqueued as
+// launches that each interleave one share of the pages of both sides.
+int run_exchange(kvx_pool* pool, XSide bk, XSide rs, kvx_ready* ready, int32_t slot_base,
+                 void* stream_v, int32_t path)
+{
+    const PoolGeom& g = pool->geom;
+    const bool host = path == KVX_PATH_ZEROCOPY;
+    int rc = resolve_device(pool);
+    if (rc != KVX_OK) return rc;
+    if (ready && ready->device >= 0 && ready->device != pool->device)
+        return fail(KVX_E_INVAL, "exchange: the ready object's counts are on GPU " +
+                                     std::to_string(ready->device) + ", the pool on GPU " +
+                                     std::to_string(pool->device));
+    DeviceGuard dg(pool->device);
+    hipStream_t s = static_cast<hipStream_t>(stream_v);
+    rc = check_packed_kind(pool, bk.packed, path, "exchange backup", &bk.view);
+    if (rc != KVX_OK) return rc;
+    rc = check_packed_kind(pool, rs.packed, path, "exchange restore", &rs.view);
+    if (rc != KVX_OK) return rc;
+    const Tuning t = tuning();
+    Lane* L = nullptr;
+    rc = get_lane(pool->device, s, &L);
+    if (rc != KVX_OK) return rc;
+    std::lock_guard<std::mutex> lk(L->mu);
+    rc = lane_counters(L, g.num_layers);   // the unit queue, and the publish counters
+    if (rc != KVX_OK) return rc;
+    rc = bk.slots ? exchange_launches<ExchangeSlotArgs>(pool, bk, rs, ready, slot_base, s, host, t, L,
+                                                        kMaxSlotPairs)
+                  : exchange_launches<ExchangeArgs>(pool, bk, rs, ready, slot_base, s, host, t, L,
+                                                    kMaxPairs);
     if (rc != KVX_OK) {
         L->counters_dirty = true;   // a partial launch may have left counts and the queue
         return rc;
@@ -1154,7 +1197,9 @@ int run_sqe(const kvx_sqe& q, kvx_pool* const* pools, int32_t num_pools, void* c
 bool pairable(const kvx_sqe& a, const kvx_sqe& b)
 {
     const bool ops = (a.op == KVX_OP_BACKUP && b.op == KVX_OP_RESTORE) ||
-                     (a.op == KVX_OP_RESTORE && b.op == KVX_OP_BACKUP);
+                     (a.op == KVX_OP_RESTORE && b.op == KVX_OP_BACKUP) ||
+                     (a.op == KVX_OP_BACKUP_SLOTS && b.op == KVX_OP_RESTORE_SLOTS) ||
+                     (a.op == KVX_OP_RESTORE_SLOTS && b.op == KVX_OP_BACKUP_SLOTS);
     return ops && a.pool == b.pool && a.path == b.path &&
            (a.path == KVX_PATH_ZEROCOPY || a.path == KVX_PATH_DEVICE);
 }
@@ -1166,8 +1211,9 @@ int run_pair(const kvx_sqe& a, const kvx_sqe& b, kvx_pool* const* pools, int32_t
              void* const* buffers, const uint64_t* buffer_bytes, int32_t num_buffers, kvx_ready* ready,
              void* stream)
 {
-    const kvx_sqe& bk = a.op == KVX_OP_BACKUP ? a : b;
-    const kvx_sqe& rs = a.op == KVX_OP_BACKUP ? b : a;
+    const bool a_backs_up = a.op == KVX_OP_BACKUP || a.op == KVX_OP_BACKUP_SLOTS;
+    const kvx_sqe& bk = a_backs_up ? a : b;
+    const kvx_sqe& rs = a_backs_up ? b : a;
     kvx_pool *pb = nullptr, *pr = nullptr;
     uint8_t *bb = nullptr, *br = nullptr;
     uint64_t nb = 0, nr = 0;
@@ -1178,10 +1224,17 @@ int run_pair(const kvx_sqe& a, const kvx_sqe& b, kvx_pool* const* pools, int32_t
     kvx_ready* rd = nullptr;
     rc = sqe_ready(rs, ready, &rd);
     if (rc != KVX_OK) return rc;
+    const int32_t sb = rs.ready_slot_base >= 0 ? rs.ready_slot_base : 0;
+    if (bk.op == KVX_OP_BACKUP_SLOTS) {
+        const kvx_xfer_slots xb{bk.page_ids, bk.host_slots, bk.n, bk.num_host_slots, bb, nb,
+                                bk.layer_begin, bk.layer_end};
+        const kvx_xfer_slots xr{rs.page_ids, rs.host_slots, rs.n, rs.num_host_slots, br, nr,
+                                rs.layer_begin, rs.layer_end};
+        return kvx_exchange_slots(pb, &xb, &xr, rd, sb, stream, bk.path);
+    }
     const kvx_xfer xb{bk.page_ids, bk.n, bb, nb, bk.layer_begin, bk.layer_end};
     const kvx_xfer xr{rs.page_ids, rs.n, br, nr, rs.layer_begin, rs.layer_end};
-    return kvx_exchange(pb, &xb, &xr, rd, rs.ready_slot_base >= 0 ? rs.ready_slot_base : 0, stream,
-                        bk.path);
+    return kvx_exchange(pb, &xb, &xr, rd, sb, stream, bk.path);
 }
 
 // Queues the completion of descriptor q whose call returned `status`; a
@@ -1276,7 +1329,7 @@ int kvx_ring_serve(kvx_ring* r, kvx_pool* const* pools, int32_t num_pools, void*
         (*taken)++;
         // a BACKUP next to a RESTORE of the same pool share one launch
         // sequence ([RFC] "Ownership": the data plane batches transfers)
-        if (pairing && *taken < max_ops && (cur->op == KVX_OP_BACKUP || cur->op == KVX_OP_RESTORE) &&
+        if (pairing && *taken < max_ops && cur->op >= KVX_OP_BACKUP && cur->op <= KVX_OP_RESTORE_SLOTS &&
             r->pop_sqe(nxt)) {
             has_nxt = true;
             if (pairable(*cur, *nxt)) {
@@ -1378,7 +1431,85 @@ int kvx_exchange(kvx_pool* pool, const kvx_xfer* backup, const kvx_xfer* restore
                                          " is read by the backup and written by the restore in the "
                                          "same layers; run them one after the other");
     }
-    return run_exchange(pool, backup, restore, ready, slot_base, stream, path);
+    const XSide xb{backup->page_ids, nullptr, backup->n, backup->packed, backup->n,
+                   backup->layer_begin, backup->layer_end};
+    const XSide xr{restore->page_ids, nullptr, restore->n, restore->packed, restore->n,
+                   restore->layer_begin, restore->layer_end};
+    return run_exchange(pool, xb, xr, ready, slot_base, stream, path);
+}
+
+int kvx_exchange_slots(kvx_pool* pool, const kvx_xfer_slots* backup, const kvx_xfer_slots* restore,
+                       kvx_ready* ready, int32_t slot_base, void* stream, int32_t path)
+{
+    clear_error();
+    if (!backup || !restore) return fail(KVX_E_INVAL, "exchange_slots: NULL transfer description");
+    if (!pool_known(pool)) return fail(KVX_E_INVAL, "exchange_slots: unknown pool handle");
+    if (!pool->live.load()) return fail(KVX_E_STALE, "exchange_slots: pool handle was unregistered");
+    if (path != KVX_PATH_ZEROCOPY && path != KVX_PATH_DEVICE)
+        return fail(KVX_E_INVAL, "exchange_slots: runs on the zero-copy or device path");
+    const HostSlots hb{backup->host_slots, backup->num_host_slots};
+    const HostSlots hr{restore->host_slots, restore->num_host_slots};
+    bool ab = false, ar = false;
+    int rc = validate_side(pool, GATHER, backup->page_ids, backup->n, backup->host_pool,
+                           backup->host_pool_bytes, backup->layer_begin, backup->layer_end, nullptr, 0,
+                           "exchange_slots backup", &ab, &hb);
+    if (rc != KVX_OK) return rc;
+    rc = validate_side(pool, SCATTER, restore->page_ids, restore->n, restore->host_pool,
+                       restore->host_pool_bytes, restore->layer_begin, restore->layer_end, ready,
+                       slot_base, "exchange_slots restore", &ar, &hr);
+    if (rc != KVX_OK) return rc;
+    if (!ab && !ar) return KVX_OK;
+    if (!ar)
+        return kvx_backup_slots(pool, backup->page_ids, backup->host_slots, backup->n, backup->host_pool,
+                                backup->host_pool_bytes, backup->num_host_slots, backup->layer_begin,
+                                backup->layer_end, stream, path);
+    if (!ab)
+        return kvx_restore_slots(pool, restore->host_pool, restore->host_pool_bytes,
+                                 restore->num_host_slots, restore->host_slots, restore->page_ids,
+                                 restore->n, restore->layer_begin, restore->layer_end, ready, slot_base,
+                                 stream, path);
+    // the two sides run concurrently: they must not touch the same bytes
+    const PoolGeom& g = pool->geom;
+    const bool common_layers = std::max(backup->layer_begin, restore->layer_begin) <
+                               std::min(backup->layer_end, restore->layer_end);
+    auto intersect = [](const int32_t* x, int32_t nx, const int32_t* y, int32_t ny, int32_t* first) {
+        std::vector<int32_t> a(x, x + nx), b(y, y + ny);
+        std::sort(a.begin(), a.end());
+        std::sort(b.begin(), b.end());
+        std::vector<int32_t> both;
+        std::set_intersection(a.begin(), a.end(), b.begin(), b.end(), std::back_inserter(both));
+        if (!both.empty()) *first = both[0];
+        return !both.empty();
+    };
+    int32_t first = 0;
+    if (backup->host_pool == restore->host_pool && backup->num_host_slots == restore->num_host_slots) {
+        // one host pool: a slot the backup writes and the restore reads in a
+        // common layer
+        if (common_layers &&
+            intersect(backup->host_slots, backup->n, restore->host_slots, restore->n, &first))
+            return fail(KVX_E_INVAL, "exchange_slots: host slot " + std::to_string(first) +
+                                         " is written by the backup and read by the restore in the "
+                                         "same layers");
+    } else {
+        const int64_t lay_b = g.num_kv * int64_t(backup->num_host_slots) * g.piece_bytes;
+        const int64_t lay_r = g.num_kv * int64_t(restore->num_host_slots) * g.piece_bytes;
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(backup->host_pool) + backup->layer_begin * lay_b;
+        const uintptr_t b1 = reinterpret_cast<uintptr_t>(backup->host_pool) + backup->layer_end * lay_b;
+        const uintptr_t r0 = reinterpret_cast<uintptr_t>(restore->host_pool) + restore->layer_begin * lay_r;
+        const uintptr_t r1 = reinterpret_cast<uintptr_t>(restore->host_pool) + restore->layer_end * lay_r;
+        if (b0 < r1 && r0 < b1)
+            return fail(KVX_E_INVAL, "exchange_slots: the host bytes the backup writes overlap those "
+                                     "the restore reads");
+    }
+    if (common_layers && intersect(backup->page_ids, backup->n, restore->page_ids, restore->n, &first))
+        return fail(KVX_E_INVAL, "exchange_slots: page " + std::to_string(first) +
+                                     " is read by the backup and written by the restore in the same "
+                                     "layers; run them one after the other");
+    const XSide xb{backup->page_ids, backup->host_slots, backup->n, backup->host_pool,
+                   backup->num_host_slots, backup->layer_begin, backup->layer_end};
+    const XSide xr{restore->page_ids, restore->host_slots, restore->n, restore->host_pool,
+                   restore->num_host_slots, restore->layer_begin, restore->layer_end};
+    return run_exchange(pool, xb, xr, ready, slot_base, stream, path);
 }
 
 int kvx_plan_runs(const kvx_pool* pool, const int32_t* page_ids, int32_t n, int32_t* runs,

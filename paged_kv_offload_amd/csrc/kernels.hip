@@ -349,8 +349,25 @@ __global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
 // sharing one launch sustain 90-91 GB/s over back-to-back launches, where
 // the same work as two kernels on two streams drifts out of step and falls
 // to 67-76 GB/s. Only the RESTORE side publishes.
-template <int U, int PERM, bool PUBLISH, bool HOST>
-__global__ __launch_bounds__(kThreads) void kvx_exchange_kernel(ExchangeArgs a)
+// Page and packed slot of pair j of a side: listed in slot order from
+// first_x (packed buffers), or as explicit (page, slot) pairs (host pools).
+__device__ __forceinline__ int32_t page_b(const ExchangeArgs& a, uint32_t j) { return a.pages_b[j]; }
+__device__ __forceinline__ int32_t slot_b(const ExchangeArgs& a, uint32_t j)
+{
+    return a.first_b + static_cast<int32_t>(j);
+}
+__device__ __forceinline__ int32_t page_r(const ExchangeArgs& a, uint32_t j) { return a.pages_r[j]; }
+__device__ __forceinline__ int32_t slot_r(const ExchangeArgs& a, uint32_t j)
+{
+    return a.first_r + static_cast<int32_t>(j);
+}
+__device__ __forceinline__ int32_t page_b(const ExchangeSlotArgs& a, uint32_t j) { return a.pairs_b[2 * j]; }
+__device__ __forceinline__ int32_t slot_b(const ExchangeSlotArgs& a, uint32_t j) { return a.pairs_b[2 * j + 1]; }
+__device__ __forceinline__ int32_t page_r(const ExchangeSlotArgs& a, uint32_t j) { return a.pairs_r[2 * j]; }
+__device__ __forceinline__ int32_t slot_r(const ExchangeSlotArgs& a, uint32_t j) { return a.pairs_r[2 * j + 1]; }
+
+template <int U, int PERM, bool PUBLISH, bool HOST, class A>
+__global__ __launch_bounds__(kThreads) void kvx_exchange_kernel(A a)
 {
     // cache policy: pinned host memory is written at device scope and read
     // plainly; pool memory is read non-temporally
@@ -374,8 +391,7 @@ __global__ __launch_bounds__(kThreads) void kvx_exchange_kernel(ExchangeArgs a)
         }
         if (gather) {
             const UnitPos u = decode_unit(a.g, a.b, idx);
-            move_at<GATHER, U, PERM, CPG>(a.g, a.b, u, a.pages_b[u.j], a.first_b + static_cast<int32_t>(u.j),
-                                          tid, lds);
+            move_at<GATHER, U, PERM, CPG>(a.g, a.b, u, page_b(a, u.j), slot_b(a, u.j), tid, lds);
         } else {
             const UnitPos u = decode_unit(a.g, a.r, idx);
             if constexpr (PUBLISH) {
@@ -385,8 +401,7 @@ __global__ __launch_bounds__(kThreads) void kvx_exchange_kernel(ExchangeArgs a)
                     pend = 0;
                 }
             }
-            move_at<SCATTER, U, PERM, CPS>(a.g, a.r, u, a.pages_r[u.j], a.first_r + static_cast<int32_t>(u.j),
-                                           tid, lds);
+            move_at<SCATTER, U, PERM, CPS>(a.g, a.r, u, page_r(a, u.j), slot_r(a, u.j), tid, lds);
             if constexpr (PUBLISH) pend++;
         }
     };
@@ -519,24 +534,24 @@ hipError_t launch_move(Dir dir, const LaunchCfg& cfg, const MoveArgs& a, hipStre
 
 namespace {
 
-template <int U, int P, bool PUB, bool HOST>
-hipError_t xgo(const LaunchCfg& cfg, const ExchangeArgs& a, hipStream_t s)
+template <int U, int P, bool PUB, bool HOST, class A>
+hipError_t xgo(const LaunchCfg& cfg, const A& a, hipStream_t s)
 {
-    void* args[] = {const_cast<ExchangeArgs*>(&a)};
-    return hipLaunchKernel(reinterpret_cast<const void*>(&kvx_exchange_kernel<U, P, PUB, HOST>),
+    void* args[] = {const_cast<A*>(&a)};
+    return hipLaunchKernel(reinterpret_cast<const void*>(&kvx_exchange_kernel<U, P, PUB, HOST, A>),
                            dim3(cfg.grid), dim3(kThreads), args, 0, s);
 }
 
-template <int U, int P>
-hipError_t xgo_pub(const LaunchCfg& cfg, const ExchangeArgs& a, hipStream_t s)
+template <int U, int P, class A>
+hipError_t xgo_pub(const LaunchCfg& cfg, const A& a, hipStream_t s)
 {
     if (cfg.publish)
         return cfg.host_link ? xgo<U, P, true, true>(cfg, a, s) : xgo<U, P, true, false>(cfg, a, s);
     return cfg.host_link ? xgo<U, P, false, true>(cfg, a, s) : xgo<U, P, false, false>(cfg, a, s);
 }
 
-template <int U>
-hipError_t xgo_perm(const LaunchCfg& cfg, const ExchangeArgs& a, hipStream_t s)
+template <int U, class A>
+hipError_t xgo_perm(const LaunchCfg& cfg, const A& a, hipStream_t s)
 {
     if constexpr (U == 4 || U == 8 || U == 16) {
         if (cfg.permute == 2) return xgo_pub<U, 2>(cfg, a, s);
@@ -544,9 +559,8 @@ hipError_t xgo_perm(const LaunchCfg& cfg, const ExchangeArgs& a, hipStream_t s)
     return cfg.permute ? xgo_pub<U, 1>(cfg, a, s) : xgo_pub<U, 0>(cfg, a, s);
 }
 
-}  // namespace
-
-hipError_t launch_exchange(const LaunchCfg& cfg, const ExchangeArgs& a, hipStream_t s)
+template <class A>
+hipError_t xgo_unroll(const LaunchCfg& cfg, const A& a, hipStream_t s)
 {
     if (cfg.grid < 1 || a.b.total_units + a.r.total_units == 0 || !a.p.queue) return hipErrorInvalidValue;
     switch (cfg.unroll) {
@@ -561,6 +575,18 @@ hipError_t launch_exchange(const LaunchCfg& cfg, const ExchangeArgs& a, hipStrea
     case 1: return xgo_perm<1>(cfg, a, s);
     default: return hipErrorInvalidValue;
     }
+}
+
+}  // namespace
+
+hipError_t launch_exchange(const LaunchCfg& cfg, const ExchangeArgs& a, hipStream_t s)
+{
+    return xgo_unroll(cfg, a, s);
+}
+
+hipError_t launch_exchange(const LaunchCfg& cfg, const ExchangeSlotArgs& a, hipStream_t s)
+{
+    return xgo_unroll(cfg, a, s);
 }
 
 hipError_t launch_clear_u32(uint32_t* p, uint32_t count, hipStream_t s)

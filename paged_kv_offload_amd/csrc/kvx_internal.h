@@ -151,6 +151,18 @@ struct ExchangeArgs {
 };
 static_assert(sizeof(ExchangeArgs) <= 4096, "kernel arguments are limited to 4 KiB");
 
+// Both directions against slot-addressed host pools (kvx_exchange_slots):
+// pairs_x[2j] is a page and pairs_x[2j + 1] its host slot.
+constexpr int kMaxSlotPairs = 224;
+struct ExchangeSlotArgs {
+    UnitGeom g;
+    Side b, r;
+    PublishArgs p;
+    int32_t pairs_b[2 * kMaxSlotPairs];
+    int32_t pairs_r[2 * kMaxSlotPairs];
+};
+static_assert(sizeof(ExchangeSlotArgs) <= 4096, "kernel arguments are limited to 4 KiB");
+
 struct LaunchCfg {
     int unroll;        // 16-byte vectors per lane per unit: 1, 2, 4, 8 or 16
     int permute;       // 0: same inner layout; 1: HND<->NHD by rows; 2: through LDS
@@ -184,6 +196,7 @@ uint32_t magic_u32(uint32_t d);   // multiplier for exact x / d with x * d < 2^3
 int pick_unroll(int64_t piece_bytes, int max_unroll, int forced);
 hipError_t launch_move(Dir dir, const LaunchCfg& cfg, const MoveArgs& a, hipStream_t s);
 hipError_t launch_exchange(const LaunchCfg& cfg, const ExchangeArgs& a, hipStream_t s);
+hipError_t launch_exchange(const LaunchCfg& cfg, const ExchangeSlotArgs& a, hipStream_t s);
 hipError_t launch_clear_u32(uint32_t* p, uint32_t count, hipStream_t s);
 hipError_t launch_ready_wait(const uint32_t* slot, uint32_t min_count, uint32_t spin_limit,
                              int32_t* status, hipStream_t s);

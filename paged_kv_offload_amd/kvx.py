@@ -64,6 +64,13 @@ class kvx_xfer(ctypes.Structure):
                 ("layer_end", ctypes.c_int32)]
 
 
+class kvx_xfer_slots(ctypes.Structure):
+    _fields_ = [("page_ids", ctypes.c_void_p), ("host_slots", ctypes.c_void_p), ("n", ctypes.c_int32),
+                ("num_host_slots", ctypes.c_int32), ("host_pool", ctypes.c_void_p),
+                ("host_pool_bytes", ctypes.c_uint64), ("layer_begin", ctypes.c_int32),
+                ("layer_end", ctypes.c_int32)]
+
+
 class kvx_ipc_handle(ctypes.Structure):
     _fields_ = [("mem_handle", ctypes.c_uint8 * 64), ("device_uuid", ctypes.c_uint8 * 16),
                 ("alloc_bytes", ctypes.c_uint64), ("offset", ctypes.c_uint64),
@@ -127,6 +134,8 @@ SIGNATURES = [
     ("kvx_restore_slots", ctypes.c_int, [_vp, _vp, _u64, _i32, _P(_i32), _P(_i32), _i32, _i32, _i32,
                                          _vp, _i32, _vp, _i32]),
     ("kvx_exchange", ctypes.c_int, [_vp, _P(kvx_xfer), _P(kvx_xfer), _vp, _i32, _vp, _i32]),
+    ("kvx_exchange_slots", ctypes.c_int, [_vp, _P(kvx_xfer_slots), _P(kvx_xfer_slots), _vp, _i32, _vp,
+                                          _i32]),
     ("kvx_ipc_export", ctypes.c_int, [_vp, _P(kvx_ipc_handle)]),
     ("kvx_ipc_import", ctypes.c_int, [_P(kvx_ipc_handle), _P(_vp), _P(_i32)]),
     ("kvx_ipc_close", ctypes.c_int, [_vp]),
@@ -639,6 +648,25 @@ def kvx_exchange(pool: int, backup_ids: Iterable[int], backup_dst, backup_bytes:
                  *restore_layers)
     _check(lib().kvx_exchange(pool, ctypes.byref(b), ctypes.byref(r), ready, slot_base,
                               _stream(stream), path))
+
+
+def kvx_exchange_slots(pool: int, backup_ids, backup_slots, backup_pool, backup_pool_bytes: int,
+                       backup_num_slots: int, backup_layers, restore_pool, restore_pool_bytes: int,
+                       restore_num_slots: int, restore_slots, restore_ids, restore_layers,
+                       ready: int = None, slot_base: int = 0, stream=None,
+                       path: int = KVX_PATH_ZEROCOPY) -> None:
+    """kvx_backup_slots of backup_ids into backup_slots and kvx_restore_slots
+    of restore_slots into restore_ids in one launch sequence."""
+    bi, bs, ri, rsl = _ids(backup_ids), _ids(backup_slots), _ids(restore_ids), _ids(restore_slots)
+    if bi.size != bs.size or ri.size != rsl.size:
+        raise KvxError(KVX_E_INVAL, "each side needs one host slot per page")
+    b = kvx_xfer_slots(bi.ctypes.data if bi.size else None, bs.ctypes.data if bs.size else None,
+                       bi.size, backup_num_slots, _ptr(backup_pool), backup_pool_bytes, *backup_layers)
+    r = kvx_xfer_slots(ri.ctypes.data if ri.size else None, rsl.ctypes.data if rsl.size else None,
+                       ri.size, restore_num_slots, _ptr(restore_pool), restore_pool_bytes,
+                       *restore_layers)
+    _check(lib().kvx_exchange_slots(pool, ctypes.byref(b), ctypes.byref(r), ready, slot_base,
+                                    _stream(stream), path))
 
 
 def kvx_plan_runs(pool: int, page_ids: Iterable[int]) -> np.ndarray:

@@ -394,3 +394,39 @@ def test_tier_policy_calls_fail_closed():
         K.kvx_tier_destroy(t)
         K.kvx_tier_destroy(old)
         K.kvx_unregister_pool(pool)
+
+
+def test_exchange_slots_validation_fails_closed():
+    """kvx_exchange_slots refuses the staged path, a host slot both sides use
+    in a common layer of one host pool, overlapping layer slices of two host
+    pools, a page both sides touch in a common layer, and each side's own
+    slot and page errors, before any HIP call."""
+    w = WORKLOADS["tiny"]
+    pool = register(w)
+    S = 6
+    nb = w.host_bytes(S)
+    base = dict(pool=pool, backup_ids=[1, 2], backup_slots=[0, 1], backup_pool=0x1000000,
+                backup_pool_bytes=nb, backup_num_slots=S, backup_layers=(0, 2),
+                restore_pool=0x1000000, restore_pool_bytes=nb, restore_num_slots=S,
+                restore_slots=[2, 3], restore_ids=[3, 4], restore_layers=(0, 2),
+                path=K.KVX_PATH_ZEROCOPY)
+    try:
+        for change, code, text in (
+                (dict(path=K.KVX_PATH_STAGED), K.KVX_E_INVAL, "zero-copy or device path"),
+                (dict(restore_slots=[1, 5]), K.KVX_E_INVAL, "host slot 1"),
+                (dict(restore_ids=[2, 5]), K.KVX_E_INVAL, "page 2 is read by the backup"),
+                (dict(restore_pool=0x1000000 + 16), K.KVX_E_INVAL, "overlap"),
+                (dict(backup_slots=[4, 4]), K.KVX_E_DUP, "host slot 4"),
+                (dict(restore_ids=[3, 3]), K.KVX_E_DUP, "destination page 3"),
+                (dict(restore_slots=[2, 6]), K.KVX_E_RANGE, "host_slots[1] = 6"),
+                (dict(backup_pool_bytes=nb - 16), K.KVX_E_RANGE, "needs")):
+            args = dict(base)
+            args.update(change)
+            with pytest.raises(K.KvxError) as e:
+                K.kvx_exchange_slots(**args)
+            assert e.value.code == code and text in e.value.message, (change, e.value.message)
+        # nothing to move on either side is a no-op that touches no GPU
+        K.kvx_exchange_slots(**dict(base, backup_ids=[], backup_slots=[], restore_ids=[],
+                                    restore_slots=[]))
+    finally:
+        K.kvx_unregister_pool(pool)

@@ -158,6 +158,53 @@ def test_ring_runs_backup_and_restore_together(path, pairing):
         pool.close()
 
 
+@pytest.mark.parametrize("path", ["zerocopy", "device"])
+def test_ring_pairs_slot_descriptors(path):
+    """BACKUP_SLOTS followed by RESTORE_SLOTS of other slots and pages of one
+    host tier run as one exchange: the tier and the pool hold the oracle's
+    bytes, and the restore publishes."""
+    t = torch()
+    w, n = SMALL["ragged_hnd"]
+    n = 300
+    S = 2 * n + 8
+    print(f"\n[ring-pair-slots] path={path} n={n} slots={S}", flush=True)
+    L = oracle_layout(w)
+    pool = DevicePool(w, seed=w.seed + 95, generation=4)
+    tier = Packed(w, S, path, fill_seed=w.seed + 96)
+    ready = K.kvx_ready_create(w.num_layers, 4)
+    stream = t.cuda.Stream()
+    name = f"/kvx-pair-slots-{os.getpid()}-{path}"
+    ring = K.kvx_ring_create(name, 8, 4)
+    o = K.kvx_ring_open(name)
+    P = K.PATHS[path]
+    nl = w.num_layers
+    perm = synth.page_perm(w.seed + 97, w.num_pages)
+    src, dst = perm[:n], perm[n:2 * n]
+    order = np.random.default_rng(w.seed + 98).permutation(S).astype(np.int32)
+    bsl, rsl = order[:n], order[n:2 * n]
+    try:
+        img = pool.host_image()
+        host0 = synth.gen_bytes(w.seed + 96, 0, tier.nbytes)
+        K.kvx_ring_submit(ring, K.make_sqe(K.KVX_OP_BACKUP_SLOTS, 1, 4, 0, 0, src, 0, nl, P,
+                                           host_slots=bsl, num_host_slots=S))
+        K.kvx_ring_submit(ring, K.make_sqe(K.KVX_OP_RESTORE_SLOTS, 2, 4, 0, 0, dst, 0, nl, P,
+                                           ready_slot_base=0, host_slots=rsl, num_host_slots=S))
+        got = serve_until(ring, o, [pool.handle], [tier.ptr], [tier.nbytes], 2, ready, stream)
+        assert [(g[0], g[2]) for g in got] == [(1, 0), (2, 0)]
+        want_tier = oracle.backup_slots(L, img, src, bsl, S, 0, nl, host=host0.copy())
+        assert np.array_equal(tier.numpy(), want_tier), diff_report(tier.numpy(), want_tier)
+        want = oracle.restore_slots(L, img, host0, rsl, dst, S, 0, nl)
+        after = pool.host_image()
+        assert np.array_equal(after, want), diff_report(after, want)
+        assert K.kvx_ready_prefix(ready) == n
+    finally:
+        K.kvx_ring_close(o)
+        K.kvx_ring_close(ring)
+        K.kvx_ready_destroy(ready)
+        tier.close()
+        pool.close()
+
+
 IPC_CASE = Workload(name="ring_ipc", outer=("layer", "kv", "page"), inner="HND", num_pages=200,
                     num_layers=3, num_kv=2, page_size=16, num_heads=4, head_dim=64, dtype_bytes=2,
                     pages_per_request=40, seed=231, byte_offset=4096, alloc_tail=4096)

@@ -198,3 +198,60 @@ def test_tier_write_through_sequence(case, path, stream):
         K.kvx_tier_destroy(tier)
         hp.close()
         pool.close()
+
+
+# (case, backup pages, restore pages, backup layers, restore layers, one host pool)
+EXCHANGE_SLOTS = [
+    ("llama_small", 24, 11, None, (1, 3), True),
+    ("ragged_hnd", 460, 230, None, None, False),     # three launches of at most 224 pages
+    ("trtllm_small", 16, 16, (0, 2), (2, 3), True),  # disjoint layers: slots may repeat
+    ("mla_small", 10, 7, None, None, True),
+]
+
+
+@pytest.mark.parametrize("path", SLOT_PATHS)
+@pytest.mark.parametrize("case,nb_,nr,lb,lr,shared", EXCHANGE_SLOTS)
+def test_exchange_slots_parity(case, nb_, nr, lb, lr, shared, path, stream):
+    """kvx_exchange_slots gives the bytes of kvx_backup_slots followed by
+    kvx_restore_slots (oracle), publishes the restore's layers, and leaves
+    every host slot it does not write as it was."""
+    w, _ = SMALL[case]
+    print(f"\n[xslots] case={case} path={path} backup={nb_} restore={nr} shared={shared}", flush=True)
+    L = oracle_layout(w)
+    lb = lb or (0, w.num_layers)
+    lr = lr or (0, w.num_layers)
+    S = nb_ + nr + 5
+    pool = DevicePool(w, seed=w.seed + 90, generation=5)
+    rng = np.random.default_rng(w.seed + 91)
+    perm = synth.page_perm(w.seed + 92, w.num_pages)
+    bids, rids = perm[:nb_].copy(), perm[nb_:nb_ + nr].copy()
+    order = rng.permutation(S).astype(np.int32)
+    bsl = order[:nb_]
+    # restore slots: disjoint from the backup's in a shared pool when layers overlap
+    overlap = max(lb[0], lr[0]) < min(lb[1], lr[1])
+    rsl = order[nb_:nb_ + nr] if (shared and overlap) else rng.permutation(S)[:nr].astype(np.int32)
+    hb = Packed(w, S, path, fill_seed=w.seed + 93)
+    hr = hb if shared else Packed(w, S, path, fill_seed=w.seed + 94)
+    ready = K.kvx_ready_create(w.num_layers, 5)
+    try:
+        img = pool.host_image()
+        host_b = synth.gen_bytes(w.seed + 93, 0, hb.nbytes)
+        host_r = host_b if shared else synth.gen_bytes(w.seed + 94, 0, hr.nbytes)
+        want_b = oracle.backup_slots(L, img, bids, bsl, S, lb[0], lb[1], host=host_b.copy())
+        src_r = want_b if shared else host_r
+        want_alloc = oracle.restore_slots(L, img, src_r, rsl, rids, S, lr[0], lr[1])
+        K.kvx_exchange_slots(pool.handle, bids, bsl, hb.ptr, hb.nbytes, S, lb, hr.ptr, hr.nbytes, S,
+                             rsl, rids, lr, ready, 0, stream, PATHS[path])
+        K.kvx_sync(stream)
+        got = hb.numpy()
+        assert np.array_equal(got, want_b), "backup side " + diff_report(got, want_b)
+        after = pool.host_image()
+        assert np.array_equal(after, want_alloc), "restore side " + diff_report(after, want_alloc)
+        counts = [K.kvx_layer_ready(ready, s) for s in range(w.num_layers)]
+        assert counts == [nr if lr[0] <= s < lr[1] else 0 for s in range(w.num_layers)]
+    finally:
+        K.kvx_ready_destroy(ready)
+        hb.close()
+        if not shared:
+            hr.close()
+        pool.close()
