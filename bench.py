@@ -781,6 +781,24 @@ def all_workloads():
     res["write_through"] = {"requests": 8, "gbs": round(8 * P / wall / GB, 2),
                             "evicted_entries": int(evicted),
                             "call_enqueue_us": round(median(t_res) * 1e6, 1)}
+    # a miss stored while a hit is loaded: kvx_tier_exchange backs up a new
+    # request (evicting a request's worth of entries) while it restores a
+    # resident one into other pages, both directions at once
+    rates = []
+    hkeys = np.arange(7 * n, 8 * n, dtype=np.uint64) + 1     # the last request is resident
+    for r in range(6):
+        nkeys = np.arange((8 + r) * n, (9 + r) * n, dtype=np.uint64) + 1
+        stream.synchronize()
+        t0 = time.perf_counter()
+        bsl, _, rsl = K.kvx_tier_exchange(tier, pool, nkeys, perm[:n], hkeys, perm[n:2 * n], host.ptr,
+                                          HB, None, 0, stream, K.KVX_PATH_ZEROCOPY)
+        stream.synchronize()
+        rates.append(2 * P / (time.perf_counter() - t0) / GB)
+        assert (rsl >= 0).all(), "a resident request missed"
+        K.kvx_tier_commit(tier, bsl)
+        K.kvx_tier_release(tier, rsl)
+        K.kvx_tier_invalidate(tier, nkeys)              # room for the next round's request
+    res["tier_exchange"] = {"gbs": round(median(rates[1:]), 2), "bytes_per_call": 2 * P}
     K.kvx_tier_destroy(tier)
     print(json.dumps({"host_tier": res}), flush=True)
     log(f"host tier: {res}")

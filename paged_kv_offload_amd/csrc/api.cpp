@@ -1105,6 +1105,72 @@ int kvx_tier_restore(kvx_tier* tier, kvx_pool* pool, const uint64_t* keys, const
     return KVX_OK;
 }
 
+int kvx_tier_exchange(kvx_tier* tier, kvx_pool* pool, const uint64_t* backup_keys,
+                      const int32_t* backup_pages, int32_t nb, const uint64_t* restore_keys,
+                      const int32_t* restore_pages, int32_t nr, void* host_pool,
+                      uint64_t host_pool_bytes, kvx_ready* ready, int32_t slot_base, void* stream,
+                      int32_t path, int32_t* backup_slots, uint64_t* evicted, int32_t* num_evicted,
+                      int32_t* restore_slots, int32_t* hits)
+{
+    clear_error();
+    int rc = tier_for_pool(tier, pool, "tier_exchange");
+    if (rc != KVX_OK) return rc;
+    rc = check_page_ids(pool->geom, backup_pages, nb, false);
+    if (rc != KVX_OK) return rc;
+    rc = check_page_ids(pool->geom, restore_pages, nr, true);
+    if (rc != KVX_OK) return rc;
+    std::lock_guard<std::mutex> lk(tier->mu);
+    if (!tier->live.load()) return fail(KVX_E_STALE, "tier_exchange: tier was destroyed");
+    tier->begin();
+    // hits first: pinned, they cannot be the reservation's victims
+    rc = tier->lookup(restore_keys, nr, restore_slots, hits);
+    if (rc == KVX_OK) rc = tier->reserve(backup_keys, nb, backup_slots, evicted, num_evicted);
+    if (rc != KVX_OK) {
+        tier->rollback();
+        return rc;
+    }
+    std::vector<int32_t> bi, bs, ri, rs;
+    for (int32_t i = 0; i < nb; i++)
+        if (backup_slots[i] >= 0) {
+            bi.push_back(backup_pages[i]);
+            bs.push_back(backup_slots[i]);
+        }
+    for (int32_t i = 0; i < nr; i++)
+        if (restore_slots[i] >= 0) {
+            ri.push_back(restore_pages[i]);
+            rs.push_back(restore_slots[i]);
+        }
+    const int32_t S = static_cast<int32_t>(tier->e.size());
+    const int32_t L = static_cast<int32_t>(pool->geom.num_layers);
+    const kvx_xfer_slots xb{bi.data(), bs.data(), static_cast<int32_t>(bi.size()), S, host_pool,
+                            host_pool_bytes, 0, L};
+    const kvx_xfer_slots xr{ri.data(), rs.data(), static_cast<int32_t>(ri.size()), S, host_pool,
+                            host_pool_bytes, 0, L};
+    rc = kvx_exchange_slots(pool, &xb, &xr, ready, slot_base, stream, path);
+    if (rc != KVX_OK && rc != KVX_E_HIP) {
+        tier->rollback();   // refused before anything was enqueued
+        for (int32_t i = 0; i < nb; i++) backup_slots[i] = -1;
+        for (int32_t i = 0; i < nr; i++) restore_slots[i] = -1;
+        *num_evicted = 0;
+        *hits = 0;
+        return rc;
+    }
+    if (rc != KVX_OK) {
+        // a launch failed part way: free the reservations (they may hold part
+        // of a backup) and drop the pins; the evictions stand
+        tier->end();
+        for (int32_t i = 0; i < nb; i++)
+            if (backup_slots[i] >= 0) tier->set(backup_slots[i], TierEntry());
+        (void)tier->release(restore_slots, nr);
+        for (int32_t i = 0; i < nb; i++) backup_slots[i] = -1;
+        for (int32_t i = 0; i < nr; i++) restore_slots[i] = -1;
+        *hits = 0;
+        return rc;
+    }
+    tier->end();
+    return KVX_OK;
+}
+
 // ---- ring executor ---------------------------------------------------------
 
 namespace {

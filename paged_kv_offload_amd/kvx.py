@@ -167,6 +167,9 @@ SIGNATURES = [
                                        _P(_i32), _P(_u64), _P(_i32)]),
     ("kvx_tier_restore", ctypes.c_int, [_vp, _vp, _P(_u64), _P(_i32), _i32, _vp, _u64, _vp, _i32,
                                         _vp, _i32, _P(_i32), _P(_i32)]),
+    ("kvx_tier_exchange", ctypes.c_int, [_vp, _vp, _P(_u64), _P(_i32), _i32, _P(_u64), _P(_i32), _i32,
+                                         _vp, _u64, _vp, _i32, _vp, _i32, _P(_i32), _P(_u64),
+                                         _P(_i32), _P(_i32), _P(_i32)]),
 ]
 
 _lib: Optional[ctypes.CDLL] = None
@@ -523,6 +526,25 @@ def kvx_tier_restore(tier: int, pool: int, keys, page_ids, host_pool, host_pool_
                                   host_pool_bytes, ready or 0, slot_base, _stream(stream), path,
                                   _sp(slots), ctypes.byref(hits)))
     return slots
+
+
+def kvx_tier_exchange(tier: int, pool: int, backup_keys, backup_pages, restore_keys,
+                      restore_pages, host_pool, host_pool_bytes: int, ready: int = None,
+                      slot_base: int = 0, stream=None, path: int = KVX_PATH_ZEROCOPY):
+    """Lookup of restore_keys + reserve of backup_keys + one exchange;
+    (backup slots, evicted keys, restore slots)."""
+    bk, bp, rk, rp = _keys(backup_keys), _ids(backup_pages), _keys(restore_keys), _ids(restore_pages)
+    if bk.size != bp.size or rk.size != rp.size:
+        raise KvxError(KVX_E_INVAL, "one page per key on each side")
+    bs = np.empty(bk.size, dtype=np.int32)
+    rs = np.empty(rk.size, dtype=np.int32)
+    ev = np.empty(max(bk.size, 1), dtype=np.uint64)
+    ne, hits = _i32(), _i32()
+    _check(lib().kvx_tier_exchange(tier, pool, _kp(bk), _ids_ptr(bp), bk.size, _kp(rk), _ids_ptr(rp),
+                                   rk.size, _ptr(host_pool), host_pool_bytes, ready or 0, slot_base,
+                                   _stream(stream), path, _sp(bs), _kp(ev), ctypes.byref(ne),
+                                   _sp(rs), ctypes.byref(hits)))
+    return bs, ev[:ne.value].copy(), rs
 
 
 # ---------------------------------------------------------------------------

@@ -430,3 +430,32 @@ def test_exchange_slots_validation_fails_closed():
                                     restore_slots=[]))
     finally:
         K.kvx_unregister_pool(pool)
+
+
+def test_tier_exchange_fails_closed():
+    """kvx_tier_exchange: when the exchange refuses the pair (a page the
+    backup reads is one the restore writes), the lookup's pins and the
+    reservation's evictions are undone; all before any HIP call."""
+    w = WORKLOADS["tiny"]
+    pool = register(w, gen=7)
+    S = 2
+    nb = w.host_bytes(S)
+    t = K.kvx_tier_create(S, 7)
+    try:
+        slots, _ = K.kvx_tier_reserve(t, [11, 12])
+        K.kvx_tier_commit(t, slots)
+        view = [K.kvx_tier_slot(t, s) for s in range(S)]
+        info = K.kvx_tier_get_info(t)
+        with pytest.raises(K.KvxError) as e:
+            K.kvx_tier_exchange(t, pool, [13], [1], [11], [1], 0x1000000, nb)
+        assert e.value.code == K.KVX_E_INVAL and "page 1" in e.value.message, e.value.message
+        assert [K.kvx_tier_slot(t, s) for s in range(S)] == view
+        assert K.kvx_tier_get_info(t) == info
+        old = K.kvx_tier_create(S, 6)
+        with pytest.raises(K.KvxError) as e:
+            K.kvx_tier_exchange(old, pool, [13], [1], [11], [2], 0x1000000, nb)
+        assert e.value.code == K.KVX_E_STALE
+        K.kvx_tier_destroy(old)
+    finally:
+        K.kvx_tier_destroy(t)
+        K.kvx_unregister_pool(pool)

@@ -255,3 +255,62 @@ def test_exchange_slots_parity(case, nb_, nr, lb, lr, shared, path, stream):
         if not shared:
             hr.close()
         pool.close()
+
+
+@pytest.mark.parametrize("path", SLOT_PATHS)
+def test_tier_exchange_stores_misses_while_loading_hits(path, stream):
+    """A tier of 8 slots holding 6 entries: kvx_tier_exchange restores two
+    hits (pinned first, so never evicted) while it backs up four new keys
+    (two into free slots, two evicting the least recently used unpinned
+    entries). Slots and evictions equal the model's; the tier and the pool
+    hold the oracle's bytes; the restore publishes the two hits."""
+    from oracle.tier_model import TierModel
+    w, _ = SMALL["llama_small"]
+    S = 8
+    print(f"\n[tier-exchange] path={path}", flush=True)
+    L = oracle_layout(w)
+    pool = DevicePool(w, seed=w.seed + 99, generation=9)
+    nb = w.host_bytes(S)
+    hp = Packed(w, S, path, fill_seed=w.seed + 100)
+    tier = K.kvx_tier_create(S, 9)
+    ready = K.kvx_ready_create(w.num_layers, 9)
+    model = TierModel(S)
+    perm = synth.page_perm(w.seed + 101, w.num_pages)
+    keys = [500 + 3 * i for i in range(10)]
+    try:
+        img = pool.host_image()
+        host = synth.gen_bytes(w.seed + 100, 0, nb)
+        slots, _ = K.kvx_tier_backup(tier, pool.handle, keys[:6], perm[:6], hp.ptr, nb, stream,
+                                     PATHS[path])
+        assert slots.tolist() == model.reserve(keys[:6])[0]
+        host = oracle.backup_slots(L, img, perm[:6], slots, S, 0, w.num_layers, host=host)
+        K.kvx_sync(stream)
+        K.kvx_tier_commit(tier, slots)
+        model.commit(slots.tolist())
+
+        rkeys, rpages = [keys[0], keys[5]], perm[20:22]
+        bkeys, bpages = keys[6:10], perm[6:10]
+        bs, ev, rs = K.kvx_tier_exchange(tier, pool.handle, bkeys, bpages, rkeys, rpages, hp.ptr, nb,
+                                         ready, 0, stream, PATHS[path])
+        want_rs = model.lookup(rkeys)
+        want_bs, want_ev = model.reserve(bkeys)
+        assert (bs.tolist(), ev.tolist(), rs.tolist()) == (want_bs, want_ev, want_rs)
+        assert sorted(want_ev) == [keys[1], keys[2]]
+        restored = oracle.restore_slots(L, img, host, rs, rpages, S, 0, w.num_layers)
+        host = oracle.backup_slots(L, img, bpages, bs, S, 0, w.num_layers, host=host)
+        K.kvx_sync(stream)
+        got = hp.numpy()
+        assert np.array_equal(got, host), "tier " + diff_report(got, host)
+        after = pool.host_image()
+        assert np.array_equal(after, restored), "pool " + diff_report(after, restored)
+        assert K.kvx_ready_prefix(ready) == 2
+        K.kvx_tier_commit(tier, bs)
+        K.kvx_tier_release(tier, rs)
+        model.commit(want_bs)
+        model.release(want_rs)
+        assert [K.kvx_tier_slot(tier, s) for s in range(S)] == model.view()
+    finally:
+        K.kvx_ready_destroy(ready)
+        K.kvx_tier_destroy(tier)
+        hp.close()
+        pool.close()
