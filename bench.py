@@ -51,8 +51,8 @@ PCIE_PEAK_GBS = 64.0      # MI355X host interface, PCIe 5.0 x16, published per-d
 # (FETCH_SIZE, WRITE_SIZE, scaled by a plain 2 GiB device copy in the same
 # run; see profiles/pack_kernel_llama8b.txt). Valid only for the kernel source
 # they were taken on: reported as null once kernels.hip changes.
-MEASURED_TRAFFIC = {"workload": "llama8b", "kernels_hip_sha256": "779679bd75d4412940d2ba1fe14fa1167f1611ae33d8b3a79d7217e3f3434d7c",
-                    "bytes_per_launch": 4295173010}
+MEASURED_TRAFFIC = {"workload": "llama8b", "kernels_hip_sha256": "8a4c2ab761262bf77676478e68ddbfdbbd245967f7435837fff080153c0c82f0",
+                    "bytes_per_launch": 4295177102}
 
 
 def log(msg):
