@@ -1,7 +1,7 @@
 // ring.cpp - submission / completion rings in POSIX shared memory between a
 // scheduler process (creator: submits descriptors, reaps completions) and a
 // data-plane process (opener: takes descriptors, posts completions). Host
-// only; the executor that runs descriptors on the GPU is in api.cpp.
+// only; the executor that runs descriptors on the GPU is in ring_exec.cpp.
 //
 // [RFC] "Device IPC data path" gives the control path its shape (BACKUP /
 // RESTORE descriptors, completions), and "Failure and lifecycle handling"

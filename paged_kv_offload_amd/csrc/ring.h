@@ -1,7 +1,7 @@
 // ring.h - submission / completion rings between a scheduler process and a
 // data-plane process, in POSIX shared memory (host only, no HIP). The C
 // entry points are declared in kvx.h; the executor (kvx_ring_serve /
-// kvx_ring_drain, which enqueue GPU work) lives in api.cpp and keeps its
+// kvx_ring_drain, which enqueue GPU work) lives in ring_exec.cpp and keeps its
 // in-flight list here.
 #pragma once
 
