@@ -292,6 +292,70 @@ def test_full_size_host_tier_slots():
         pool.close()
 
 
+def test_full_size_tier_exchange():
+    """The llama8b request through a host tier of 640 slots (5 GiB pinned),
+    zero-copy, in the benchmark's default launch configuration:
+    kvx_tier_backup stores the request's 256 source pages under 256 keys;
+    then one kvx_tier_exchange restores those keys into the destination
+    pages while it stores 256 other pages under new keys. The hits come back
+    in their original slots and nothing is evicted; the new keys' slots,
+    gathered in key order, hold the closed form of BACKUP of their pages;
+    the hit slots still hold the first BACKUP (the exchange wrote none of
+    them); the whole allocation is the closed form of the round trip; every
+    layer publishes 256."""
+    from synth import page_perm
+    t = torch()
+    w = WORKLOADS["llama8b"]
+    n, S = w.pages_per_request, 640
+    print(f"\n[full] llama8b tier exchange: {S} slots, n={n} per side", flush=True)
+    L = oracle_layout(w)
+    src, dst = request_pair(w)
+    src2 = page_perm(w.seed, w.num_pages)[2 * n:3 * n].copy()   # disjoint from both
+    keys1 = np.arange(1000, 1000 + n, dtype=np.uint64)
+    keys2 = np.arange(5000, 5000 + n, dtype=np.uint64)
+    pool = DevicePool(w, generation=6)
+    HB = w.payload_bytes(S)
+    host = K.HostBuffer(HB)
+    synth.fill_gpu(host.ptr, HB, w.seed + 2, 0)
+    t.cuda.synchronize()
+    stream = t.cuda.Stream()
+    ready = K.kvx_ready_create(w.num_layers, 6)
+    tier = K.kvx_tier_create(S, 6)
+    Z = K.KVX_PATH_ZEROCOPY
+    try:
+        s1, ev = K.kvx_tier_backup(tier, pool.handle, keys1, src, host.ptr, HB, stream, Z)
+        K.kvx_sync(stream)
+        K.kvx_tier_commit(tier, s1)
+        assert ev.size == 0
+        bs, ev, rs = K.kvx_tier_exchange(tier, pool.handle, keys2, src2, keys1, dst, host.ptr, HB,
+                                         ready, 0, stream, Z)
+        K.kvx_sync(stream)
+        K.kvx_tier_commit(tier, bs)
+        K.kvx_tier_release(tier, rs)
+        assert ev.size == 0 and np.array_equal(rs, s1)
+        assert np.intersect1d(bs, s1).size == 0 and np.unique(bs).size == n
+        assert K.kvx_ready_prefix(ready) == n
+        assert K.kvx_tier_get_info(tier)["resident"] == 2 * n
+        rows = w.num_layers * w.num_kv
+        hv = host.numpy().reshape(rows, S, w.piece_bytes)
+        t0 = time.time()
+        for what, ids, slots in (("new keys", src2, bs), ("hit slots", src, s1)):
+            gathered = np.ascontiguousarray(hv[:, slots]).reshape(-1)
+            bad, first = check_packed_named(L, w.seed, ids, gathered)
+            del gathered
+            assert bad == 0, f"{what}: {bad} bytes differ, first at gathered offset {first}"
+        print(f"[full] tier slots checked in {time.time() - t0:.1f} s", flush=True)
+        t0 = time.time()
+        bad, first = check_alloc(w, L, w.seed, src, dst, 0, w.num_layers, pool.alloc)
+        print(f"[full] allocation checked in {time.time() - t0:.1f} s", flush=True)
+        assert bad == 0, f"tier exchange: {bad} bytes differ, first at allocation byte {first}"
+    finally:
+        K.kvx_tier_destroy(tier)
+        K.kvx_ready_destroy(ready)
+        host.free()
+        pool.close()
+
+
 def check_packed_named(L, seed, ids, packed):
     """A whole packed buffer of every layer against the closed form of BACKUP,
     in parallel 64 MiB ranges."""
