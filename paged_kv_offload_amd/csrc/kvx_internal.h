@@ -76,7 +76,7 @@ struct Tuning {
     int64_t unit_order = -1;              // MoveArgs::unit_order bits, -1 = auto
     int64_t max_unroll = 32;              // largest 16-byte vectors per lane per unit
     int64_t unit_rounds = 0;              // 0 = auto; else the unit's vector rounds
-    int64_t staged_dma_on_caller = 0;     // staged DMA on the caller's stream instead of a side stream
+    int64_t staged_dma_on_caller = -1;    // staged DMA: 1 caller's stream, 0 side stream, -1 auto
     int64_t hnd_lds = -1;                 // HND<->NHD through LDS: 1 both, 0 never, -1 scatter only
     int64_t fail_allocs = 0;              // test hook: internal device allocations left to fail
     int64_t ring_pairing = 1;             // ring executor runs BACKUP + RESTORE as one exchange

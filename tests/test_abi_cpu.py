@@ -222,6 +222,16 @@ def test_options_roundtrip():
     with pytest.raises(kvx.KvxError):
         K.kvx_set_option(99, 1)
     assert "unknown option" in K.kvx_last_error()
+    # staged DMA stream: -1 auto (the default), 0 side stream, 1 caller's stream
+    dma = K.KVX_OPT_STAGED_DMA_ON_CALLER
+    assert K.kvx_get_option(dma) == -1
+    for v in (0, 1, -1):
+        K.kvx_set_option(dma, v)
+        assert K.kvx_get_option(dma) == v
+    for v in (-2, 2):
+        with pytest.raises(kvx.KvxError):
+            K.kvx_set_option(dma, v)
+    assert K.kvx_get_option(dma) == -1
 
 
 def test_ipc_handle_layout_matches_the_header(tmp_path):

@@ -265,16 +265,23 @@ def test_round_trip_and_duplicates(path, stream):
     pool.close()
 
 
+@pytest.mark.parametrize("dma_on_caller", [-1, 0, 1])
+@pytest.mark.parametrize("slot_bytes", [1 << 20, 64 << 20])
 @pytest.mark.parametrize("sort_pages", [0, 1])
-def test_staged_chunking_by_slot_range(sort_pages, stream):
+def test_staged_chunking_by_slot_range(sort_pages, slot_bytes, dma_on_caller, stream):
     """A 1 MiB ring slot forces layers to be split into slot ranges, several
-    DMA strips per chunk and ring reuse; bytes must not change."""
+    DMA strips per chunk and ring reuse; a 64 MiB slot holds the whole
+    request in one chunk. The staged DMA runs on the library's side stream,
+    on the caller's stream, or on whichever the library picks (the caller's
+    for one chunk); bytes must not change."""
     w, n = SMALL["llama_small"]
     L = oracle_layout(w)
-    old = {o: K.kvx_get_option(o) for o in (K.KVX_OPT_STAGE_SLOT_BYTES, K.KVX_OPT_SORT_PAGES)}
+    old = {o: K.kvx_get_option(o) for o in (K.KVX_OPT_STAGE_SLOT_BYTES, K.KVX_OPT_SORT_PAGES,
+                                            K.KVX_OPT_STAGED_DMA_ON_CALLER)}
     try:
-        K.kvx_set_option(K.KVX_OPT_STAGE_SLOT_BYTES, 1 << 20)
+        K.kvx_set_option(K.KVX_OPT_STAGE_SLOT_BYTES, slot_bytes)
         K.kvx_set_option(K.KVX_OPT_SORT_PAGES, sort_pages)
+        K.kvx_set_option(K.KVX_OPT_STAGED_DMA_ON_CALLER, dma_on_caller)
         pool = DevicePool(w, seed=302)
         img = pool.host_image()
         src, dst = pages(w, n)
