@@ -11,6 +11,7 @@
 #include <deque>
 #include <mutex>
 #include <string>
+#include <vector>
 
 #include "kvx_host.h"
 
@@ -88,6 +89,7 @@ struct kvx_ring {
 
     // executor state (data-plane side, this process only)
     std::deque<kvx::RingFlight> flights;
+    std::vector<void*> spare_events;                // fired events, reused by later flights
     void (*release_flights)(kvx_ring*) = nullptr;   // frees events at close
 
     // SPSC steps, called with `mu` held

@@ -27,6 +27,20 @@ void release_ring_flights(kvx_ring* r)
             (void)hipEventDestroy(static_cast<hipEvent_t>(f.event));
             f.event = nullptr;
         }
+    for (void* ev : r->spare_events) (void)hipEventDestroy(static_cast<hipEvent_t>(ev));
+    r->spare_events.clear();
+}
+
+// Events of finished flights are reused by later flights instead of one
+// create / destroy pair per operation. At most this many are kept.
+constexpr size_t kSpareEvents = 256;
+
+void recycle_event(kvx_ring* r, hipEvent_t ev)
+{
+    if (r->spare_events.size() < kSpareEvents)
+        r->spare_events.push_back(ev);
+    else
+        (void)hipEventDestroy(ev);
 }
 
 // Looks a descriptor's pool and buffer up in the data plane's tables and
@@ -157,7 +171,13 @@ void push_flight(kvx_ring* r, const kvx_sqe& q, int status, void* stream)
     f.status = status;
     if (f.status == KVX_OK) {
         hipEvent_t ev = nullptr;
-        hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        hipError_t e = hipSuccess;
+        if (!r->spare_events.empty()) {
+            ev = static_cast<hipEvent_t>(r->spare_events.back());
+            r->spare_events.pop_back();
+        } else {
+            e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+        }
         if (e == hipSuccess) e = hipEventRecord(ev, static_cast<hipStream_t>(stream));
         if (e != hipSuccess) {
             // the work is enqueued but cannot be tracked: wait for it
@@ -184,8 +204,10 @@ int post_finished(kvx_ring* r, bool wait, int32_t* posted)
             if (e != hipSuccess) {
                 (void)hipGetLastError();
                 f.status = KVX_E_HIP;
+                (void)hipEventDestroy(ev);
+            } else {
+                recycle_event(r, ev);
             }
-            (void)hipEventDestroy(ev);
             f.event = nullptr;
         }
         kvx_cqe c{};
