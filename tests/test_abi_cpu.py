@@ -469,3 +469,16 @@ def test_tier_exchange_fails_closed():
     finally:
         K.kvx_tier_destroy(t)
         K.kvx_unregister_pool(pool)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built HIP library every entry point raises; there is no
+    other implementation to fall back to."""
+    monkeypatch.setattr(K, "_lib", None)
+    monkeypatch.setattr(K, "LIB_PATH", str(tmp_path / "libkvx.so"))
+    with pytest.raises(ImportError, match="not built"):
+        K.lib()
+    with pytest.raises(ImportError, match="not built"):
+        K.kvx_version()
+    with pytest.raises(ImportError, match="not built"):
+        K.kvx_backup(1, [0], 16, 4096, 0, 1)
