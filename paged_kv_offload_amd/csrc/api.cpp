@@ -161,11 +161,15 @@ int get_lane(int device, hipStream_t caller, Lane** out)
     return KVX_OK;
 }
 
-// waits until no earlier operation of this lane still reads or writes the ring
+// waits until no earlier operation of this lane still reads or writes the
+// ring: DMA on the side stream through the slots' events, and operations
+// that ran on the caller's stream alone (their slots are not pending)
+// through the caller's stream, which is live: this runs inside a call on it
 int lane_drain_ring(Lane* L)
 {
     for (int r = 0; r < L->nslots; r++)
         if (L->slot_pending[r]) KVX_HIP(hipEventSynchronize(L->slot_free[r]));
+    if (L->ring) KVX_HIP(hipStreamSynchronize(L->caller));
     return KVX_OK;
 }
 

@@ -65,11 +65,51 @@ def stream():
     return t.cuda.Stream()
 
 
+# every tuning knob with the values it accepts (a sample of the wide ranges)
+TUNING = {
+    "GRID_MAX": [0, 0, 1, 3, 8, 13, 64, 1024],
+    "HOST_GRID_MAX": [0, 0, 1, 2, 7, 32, 100],
+    "UNIT_ORDER": [-1, -1, 0, 1, 2, 3],
+    "MAX_UNROLL": [32, 32, 1, 2, 3, 4, 8, 16],
+    "UNIT_ROUNDS": [0, 0, 0, 1, 2, 3, 4, 6, 8, 12, 16, 32],
+    "CACHE_POLICY": [-1, -1, 0, 1, 2, 3, 4, 5, 6, 7],
+    "HND_LDS": [-1, -1, 0, 1],
+    "SORT_PAGES": [0, 1],
+    "STAGE_SLOT_BYTES": [128 << 20, 1 << 20, 3 << 20],
+    "STAGE_SLOTS": [3, 2, 8],
+    "RESTORE_CHUNK_LAYERS": [0, 0, 1, 2],
+    "STAGED_DMA_ON_CALLER": [-1, 0, 1],
+}
+NUM_TUNED = 60
+
+
 @pytest.mark.gpu
 @pytest.mark.parametrize("k", range(NUM_GEOMS))
 def test_random_geometry_parity(k, stream):
+    run_geometry(k, np.random.default_rng(9500 + k), stream)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("k", range(NUM_TUNED))
+def test_random_geometry_with_random_tuning(k, stream):
+    """The same sequence with every tuning knob drawn at random (grid caps,
+    unit order, unit size, cache policy, HND form, page sorting, staging
+    ring and chunking, staged DMA stream): knobs change speed, never bytes."""
+    rng = np.random.default_rng(9700 + k)
+    opts = {name: int(rng.choice(vals)) for name, vals in TUNING.items()}
+    print(f"\n[random] tuning {opts}", flush=True)
+    old = {name: K.kvx_get_option(getattr(K, "KVX_OPT_" + name)) for name in TUNING}
+    try:
+        for name, v in opts.items():
+            K.kvx_set_option(getattr(K, "KVX_OPT_" + name), v)
+        run_geometry(k, rng, stream)
+    finally:
+        for name, v in old.items():
+            K.kvx_set_option(getattr(K, "KVX_OPT_" + name), v)
+
+
+def run_geometry(k, rng, stream):
     w = GEOMS[k]
-    rng = np.random.default_rng(9500 + k)
     NB, NL = w.num_pages, w.num_layers
     print(f"\n[random] k={k} outer={w.outer} inner={w.inner} NB={NB} NL={NL} KV={w.num_kv} "
           f"T={w.page_size} H={w.num_heads} row={w.row_bytes} eb={w.dtype_bytes} "
@@ -221,3 +261,18 @@ def test_random_geometries_are_valid_pools():
     assert any(w.piece_bytes > 128 * 1024 for w in GEOMS)
     assert any(w.piece_bytes % 4096 for w in GEOMS)
     assert any(w.inner == "HND" and w.num_heads > 1 and w.page_size > 1 for w in GEOMS)
+
+
+def test_random_tuning_values_are_accepted():
+    """Every knob value the tuned GPU cases draw is one kvx_set_option
+    accepts (host only); the defaults come back afterwards."""
+    old = {name: K.kvx_get_option(getattr(K, "KVX_OPT_" + name)) for name in TUNING}
+    try:
+        for name, vals in TUNING.items():
+            for v in vals:
+                K.kvx_set_option(getattr(K, "KVX_OPT_" + name), v)
+                assert K.kvx_get_option(getattr(K, "KVX_OPT_" + name)) == v
+    finally:
+        for name, v in old.items():
+            K.kvx_set_option(getattr(K, "KVX_OPT_" + name), v)
+    assert {name: K.kvx_get_option(getattr(K, "KVX_OPT_" + name)) for name in TUNING} == old
