@@ -47,6 +47,27 @@ GB = 1e9
 HBM_PEAK_GBS = 8000.0     # MI355X published HBM3E bandwidth
 PCIE_PEAK_GBS = 64.0      # MI355X host interface, PCIe 5.0 x16, published per-direction rate
 
+
+def pcie_protocol_bound(payload=256, write_overhead=24, completion_overhead=20, request_bytes=24):
+    """The host link's transaction-layer bound in GB/s, before link-layer
+    acknowledgement and flow-control packets. PCIe 5.0 x16 signals at 32
+    GT/s on 16 lanes with 128b/130b coding: 63.0 GB/s each way. Data moves
+    in packets of `payload` bytes: a posted write (the backup's stores into
+    host memory) adds 4 bytes of start token, a 16-byte header and a 4-byte
+    CRC; a completion with data (the restore's loads from host memory) a
+    12-byte header instead; each read request is a 24-byte packet on the
+    link towards the host, one per completion. With both directions busy
+    that link carries the backup's writes and the restore's requests."""
+    raw = 32e9 * 16 / 8 * 128 / 130 / GB
+    d2h = raw * payload / (payload + write_overhead)
+    h2d = raw * payload / (payload + completion_overhead)
+    each = min(raw * payload / (payload + write_overhead + request_bytes), h2d)
+    return {"d2h": round(d2h, 2), "h2d": round(h2d, 2), "both_directions": round(2 * each, 2),
+            "assumes": f"PCIe 5.0 x16, 128b/130b, {payload} B payload per packet, "
+                       f"{write_overhead} B per write, {completion_overhead} B per completion, "
+                       f"one {request_bytes} B read request per completion, no link-layer packets"}
+
+
 # HBM bytes per launch of the roofline kernel from the two rocprofv3 --pmc runs
 # (FETCH_SIZE, WRITE_SIZE, scaled by a plain 2 GiB device copy in the same
 # run; see profiles/pack_kernel_llama8b.txt). Valid only for the kernel source
@@ -381,6 +402,10 @@ def main():
                 "unit": "GB/s", "peak": PCIE_PEAK_GBS, "step": main_rep}
     link["measured_memcpy_peak"] = {"d2h": round(d2h_peak, 2), "h2d": round(h2d_peak, 2),
                                     "both_directions": round(bidir_peak, 2)}
+    proto = pcie_protocol_bound()
+    link["protocol_bound"] = proto
+    if args.schedule == "exchange":
+        link["frac_of_protocol_bound"] = round(main_rep["exchange_achieved"] / proto["both_directions"], 4)
 
     result = {
         "metric": "KV GB/s moved (backup D2H, restore H2D) + % of HBM / host-link roofline",
