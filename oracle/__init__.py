@@ -72,12 +72,18 @@ _P = ctypes.POINTER
 
 
 def lib() -> ctypes.CDLL:
-    """Loads oracle/libkvx_oracle.so, compiling it first only if it is absent."""
+    """Loads oracle/libkvx_oracle.so, compiling it first only if it is absent.
+    KVX_ORACLE_LIB names another build of the same source instead: the
+    mutation tests point it at copies with a planted mistake to show that the
+    pins catch each one."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
-            _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        path = os.environ.get("KVX_ORACLE_LIB")
+        if not path:
+            path = _build.LIB
+            if not os.path.exists(path):
+                _build.build()
+        L = ctypes.CDLL(path)
         lp = _P(_CLayout)
         i64, u64, u8p, i32p = ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p, ctypes.c_void_p
         L.kvxo_piece_start.argtypes = [lp, i64, i64, i64]
