@@ -1,11 +1,16 @@
-"""The oracle's pins have teeth (CPU only): copies of oracle/kvx_oracle.c
-with one planted mistake each - a transposed index, a dropped term, a
-swapped axis, a wrong bound, an off-by-one step, a wrong comparison - are
-compiled next to an unchanged copy, and the pin tests
-(tests/test_oracle_pins.py) are run against each through KVX_ORACLE_LIB.
-The unchanged copy passes them; every mutant fails at least one. Every
-planted mistake keeps the oracle's memory accesses inside its buffers, so
-a mutant fails by a pin's assertion, never by a crash."""
+"""The oracle's pins have teeth (CPU only).
+
+Copies of oracle/kvx_oracle.c with one planted mistake each - a transposed
+index, a dropped term, a swapped axis, a wrong bound, an off-by-one step, a
+wrong comparison - are compiled next to an unchanged copy, and the pin
+tests (tests/test_oracle_pins.py) are run against each through
+KVX_ORACLE_LIB. The unchanged copy passes them; every mutant fails at least
+one. Every planted mistake keeps the oracle's memory accesses inside its
+buffers, so a mutant fails by a pin's assertion, never by a crash.
+
+The same for the host tier's model (oracle/tier_model.py): each mutant
+replaces the model for a run of the hand-worked tier scenarios of
+tests/test_tier_cpu.py (their model variants), and fails one of them."""
 import os
 import subprocess
 import sys
@@ -130,3 +135,75 @@ def test_pins_catch_the_planted_mistake(source, tmp_path, name, func, old, new):
     # 1: a pin's assertion failed (a crash would give a negative code)
     assert r.returncode == 1, f"{name}: pins returned {r.returncode}\n" + r.stdout[-1500:]
     assert " failed" in r.stdout
+
+
+# ---------------------------------------------------------------------------
+# the host tier's model
+# ---------------------------------------------------------------------------
+MODEL = os.path.join(ROOT, "oracle", "tier_model.py")
+
+# (name, text, replacement) in oracle/tier_model.py
+MODEL_MUTANTS = [
+    ("evicts_most_recent", "s = min(cands, key=lambda t: self.slots[t].last)",
+     "s = max(cands, key=lambda t: self.slots[t].last)"),
+    ("evicts_pinned", "return x.state == RESIDENT and x.pins == 0 and not x.doomed",
+     "return x.state == RESIDENT and not x.doomed"),
+    ("highest_free_slot_first", "s = free[0]", "s = free[-1]"),
+    ("lookup_leaves_recency", "self.slots[s].pins += 1\n            self.slots[s].last = self.tick()",
+     "self.slots[s].pins += 1"),
+    ("commit_leaves_recency", "self.slots[s].state = RESIDENT\n                self.slots[s].last = self.tick()",
+     "self.slots[s].state = RESIDENT"),
+    ("writing_entries_hit", "if s is None or self.slots[s].state != RESIDENT:", "if s is None:"),
+    ("invalidate_ignores_pins", "if x.state == RESIDENT and x.pins == 0:", "if x.state == RESIDENT:"),
+    ("named_keys_can_be_victims",
+     "cands = [t for t in range(self.num_slots) if self.evictable(t) and t not in present]",
+     "cands = [t for t in range(self.num_slots) if self.evictable(t)]"),
+    ("doomed_slot_kept_after_release",
+     "if self.slots[s].pins == 0 and self.slots[s].doomed:\n                self.slots[s] = Slot()",
+     "if self.slots[s].pins == 0 and self.slots[s].doomed:\n                pass"),
+    ("doomed_backup_committed", "if self.slots[s].doomed:\n                self.slots[s] = Slot()\n            else:",
+     "if False:\n                self.slots[s] = Slot()\n            else:"),
+    ("release_unchecked", "self.slots[s].pins < named.count(s)", "self.slots[s].pins < 0"),
+]
+
+RUN_MODEL = """
+import importlib.util, sys
+spec = importlib.util.spec_from_file_location("oracle.tier_model", sys.argv[1])
+m = importlib.util.module_from_spec(spec)
+sys.modules["oracle.tier_model"] = m
+spec.loader.exec_module(m)
+import pytest
+sys.exit(pytest.main([sys.argv[2], "-q", "-x", "-p", "no:cacheprovider", "-k", "model and not runtime"]))
+"""
+
+
+def run_model_scenarios(model_path: str) -> subprocess.CompletedProcess:
+    return subprocess.run([sys.executable, "-c", RUN_MODEL, model_path,
+                           os.path.join(ROOT, "tests", "test_tier_cpu.py")],
+                          cwd=ROOT, capture_output=True, text=True, timeout=300)
+
+
+@pytest.fixture(scope="module")
+def model_source():
+    with open(MODEL) as f:
+        return f.read()
+
+
+def write_model(text: str, out_dir: str) -> str:
+    path = os.path.join(out_dir, "tier_model.py")
+    with open(path, "w") as f:
+        f.write(text)
+    return path
+
+
+def test_unchanged_model_passes_the_scenarios(model_source, tmp_path):
+    r = run_model_scenarios(write_model(model_source, str(tmp_path)))
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    assert " passed" in r.stdout and "deselected" in r.stdout
+
+
+@pytest.mark.parametrize("name,old,new", MODEL_MUTANTS, ids=[m[0] for m in MODEL_MUTANTS])
+def test_scenarios_catch_the_planted_model_mistake(model_source, tmp_path, name, old, new):
+    assert model_source.count(old) == 1, f"{name}: {old!r} is not unique"
+    r = run_model_scenarios(write_model(model_source.replace(old, new), str(tmp_path)))
+    assert r.returncode == 1, f"{name}: scenarios returned {r.returncode}\n" + r.stdout[-1500:]

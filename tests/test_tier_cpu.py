@@ -117,6 +117,21 @@ def test_keys_named_by_a_reserve_are_not_its_victims(make):
     assert e.value.kind == "full"
 
 
+def test_a_named_key_later_in_the_call_is_not_a_victim(make):
+    t = make(2)
+    t.reserve([A, B])
+    t.commit([0, 1])                                    # A older than B
+    assert t.reserve([C, A]) == ([1, -1], [B])          # A is the oldest but named
+
+
+def test_commit_counts_as_a_use(make):
+    t = make(2)
+    assert t.reserve([A, B]) == ([0, 1], [])            # A 1, B 2
+    t.commit([1])                                       # B 3
+    t.commit([0])                                       # A 4: now the newer one
+    assert t.reserve([C]) == ([1], [B])
+
+
 def test_writing_entries_miss_until_committed(make):
     t = make(4)
     assert t.reserve([A, A, B]) == ([0, -1, 1], [])     # the repeat is present by then
