@@ -382,6 +382,7 @@ void set_publish(const Publish* pub, PublishArgs* p)
     p->ready = pub->ready;
     p->layer_target = pub->layer_target;
     p->publish_value = pub->value;
+    p->block = 1;
 }
 
 int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, int32_t lb,
@@ -455,6 +456,23 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
             int64_t grid = std::max<int64_t>(1, std::min<int64_t>(a.s.total_units, gmax));
             if ((order & 1u) && grid > 8) grid &= ~int64_t(7);   // whole rounds of 8 XCDs
             cfg.grid = static_cast<int>(grid);
+            // publishing kernels draw blocks of units: one per draw over the
+            // host link (a slow read holds back one unit); in device memory,
+            // where each count's L2 write-back is what costs, blocks of about
+            // 2 MiB that tile each layer, at least one per workgroup.
+            // Measured on the device path, restore with publish: llama8b
+            // 5.37 TB/s, trtllm_hnd 6.00, mla_fp8 4.94 (16, 32 and 16 units),
+            // against 4.15, 3.28 and 2.11 one unit per draw; blocks that
+            // straddle layers (mla_fp8, 14 or 15 units) lose about 12%.
+            if (pub && !tg.host) {
+                int64_t b = t.publish_block;
+                if (b <= 0) {
+                    b = std::max<int64_t>(1, kPublishBlockBytes / a.g.chunk_bytes);
+                    b = std::min<int64_t>(b, std::max<int64_t>(1, a.s.total_units / grid));
+                    while (b > 1 && per_layer % b != 0) b--;
+                }
+                a.p.block = static_cast<uint32_t>(b);
+            }
             hipError_t e = launch_move(dir, cfg, a, s);
             if (e != hipSuccess) return hip_fail(e, "kernel launch");
         }
@@ -1554,6 +1572,10 @@ int kvx_set_option(int32_t option, int64_t value)
         if (value != 0 && value != 1) break;
         g_tune.ring_pairing = value;
         return KVX_OK;
+    case KVX_OPT_PUBLISH_BLOCK:
+        if (value < 0 || value > 4096) break;
+        g_tune.publish_block = value;
+        return KVX_OK;
     default:
         return fail(KVX_E_INVAL, "set_option: unknown option " + std::to_string(option));
     }
@@ -1581,6 +1603,7 @@ int kvx_get_option(int32_t option, int64_t* value)
     case KVX_OPT_HND_LDS: *value = g_tune.hnd_lds; return KVX_OK;
     case KVX_OPT_FAIL_ALLOCS: *value = g_tune.fail_allocs; return KVX_OK;
     case KVX_OPT_RING_PAIRING: *value = g_tune.ring_pairing; return KVX_OK;
+    case KVX_OPT_PUBLISH_BLOCK: *value = g_tune.publish_block; return KVX_OK;
     default: return fail(KVX_E_INVAL, "get_option: unknown option " + std::to_string(option));
     }
 }

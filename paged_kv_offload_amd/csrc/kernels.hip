@@ -146,18 +146,29 @@ __device__ __forceinline__ void move_unit(const UnitGeom& a, const uint8_t* src_
     for (int u = 0; u < U; u++) store16<CP>(dst, lane_off + u * (64u * kVecBytes), v[u]);
 }
 
-// Counts `units` finished units of layer l. Every lane first makes its own
-// stores visible at agent scope (release fence), the barrier gathers the
-// workgroup, and one lane adds to the layer's counter; the add that completes
-// the layer acquires the other workgroups' releases, clears the counter for
-// the next call and publishes the page count with a system-scope release.
+// s_waitcnt with vmcnt 0 and the other counters at their maximum (gfx9
+// encoding: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8): waits until
+// every vector memory access of this wave has completed.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Counts `units` finished units of layer l. Every wave first waits until its
+// own stores have completed, the barrier gathers the workgroup, and thread 0
+// releases at agent scope: one L2 write-back then covers the stores of the
+// whole workgroup (a release fence in every wave, plus a release on the add,
+// cost five write-backs per count; measured on the device path, publishing
+// restores ran 2.3-3x slower with them). Thread 0 waits for the write-back
+// and adds to the layer's counter; the add that completes the layer acquires
+// the other workgroups' releases, clears the counter for the next call and
+// publishes the page count with a system-scope release.
 __device__ __forceinline__ void count_units(const PublishArgs& a, int32_t l, uint32_t units,
                                             uint32_t tid)
 {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
     if (tid == 0) {
-        const uint32_t done = __hip_atomic_fetch_add(&a.layer_done[l], units, __ATOMIC_RELEASE,
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        const uint32_t done = __hip_atomic_fetch_add(&a.layer_done[l], units, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT) + units;
         if (done == a.layer_target) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
@@ -324,11 +335,18 @@ __global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
     };
 
     if constexpr (PUBLISH) {
-        // Units come from the queue in number order, so every unit of layer
-        // l is handed out before any of layer l + 1 and a workgroup that
-        // runs slowly (measured: reads of pinned host memory are not served
-        // evenly across workgroups) holds back at most the unit it is on.
-        for_queued_units(a.p.queue, a.s.total_units, tid, do_unit);
+        // Blocks of a.p.block consecutive units come from the queue in
+        // number order, so every unit of layer l is handed out before any of
+        // layer l + 1 and a workgroup that runs slowly (measured: reads of
+        // pinned host memory are not served evenly across workgroups) holds
+        // back at most the block it is on. A workgroup counts once per layer
+        // it leaves, so larger blocks mean fewer counts.
+        const uint32_t B = a.p.block;
+        const uint32_t total = a.s.total_units;
+        for_queued_units(a.p.queue, (total + B - 1) / B, tid, [&](uint32_t b) {
+            const uint32_t q1 = (b + 1) * B < total ? (b + 1) * B : total;
+            for (uint32_t q = b * B; q < q1; q++) do_unit(q);
+        });
         if (pend) count_units(a.p, pend_layer, pend, tid);
     } else {
         // Workgroups are dispatched round-robin over the 8 XCDs (block b runs

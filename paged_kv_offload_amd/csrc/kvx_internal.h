@@ -80,6 +80,7 @@ struct Tuning {
     int64_t hnd_lds = -1;                 // HND<->NHD through LDS: 1 both, 0 never, -1 scatter only
     int64_t fail_allocs = 0;              // test hook: internal device allocations left to fail
     int64_t ring_pairing = 1;             // ring executor runs BACKUP + RESTORE as one exchange
+    int64_t publish_block = 0;            // units per queue draw of device-memory publishing kernels (0 = auto)
 };
 Tuning tuning();
 
@@ -90,6 +91,7 @@ constexpr int kThreads = 256;        // 4 wave64 per workgroup
 constexpr int kMaxPairs = 448;       // (page, slot) pairs carried in the kernel arguments
 constexpr int kHostGridAuto = 32;    // default workgroups of a kernel streaming over the host link
 constexpr int64_t kRestoreChunkMin = 32ll << 20;   // default minimum staged restore chunk
+constexpr int64_t kPublishBlockBytes = 2ll << 20;  // auto publish block: about this many bytes
 
 enum Dir : int32_t { GATHER = 0, SCATTER = 1 };
 
@@ -127,6 +129,7 @@ struct PublishArgs {
     uint32_t* ready;         // device view of counts + slot_base, indexed by layer
     uint32_t layer_target;   // work units of one layer over the whole call
     uint32_t publish_value;  // n
+    uint32_t block;          // move kernels: consecutive units per queue draw (>= 1)
 };
 
 // One direction: pairs[2j] is the page and pairs[2j + 1] its slot.

@@ -232,6 +232,15 @@ def test_options_roundtrip():
         with pytest.raises(kvx.KvxError):
             K.kvx_set_option(dma, v)
     assert K.kvx_get_option(dma) == -1
+    # publish block: 0 auto (the default), else 1..4096 units per draw
+    pb = K.KVX_OPT_PUBLISH_BLOCK
+    assert K.kvx_get_option(pb) == 0
+    for v in (1, 4096, 0):
+        K.kvx_set_option(pb, v)
+        assert K.kvx_get_option(pb) == v
+    for v in (-1, 4097):
+        with pytest.raises(kvx.KvxError):
+            K.kvx_set_option(pb, v)
 
 
 def test_ipc_handle_layout_matches_the_header(tmp_path):

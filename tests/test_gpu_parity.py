@@ -417,17 +417,25 @@ def test_ready_generation_range_and_lifetime(stream):
     pool.close()
 
 
-def test_gpu_consumer_waits_for_published_layer(stream):
+@pytest.mark.parametrize("path,policy,block", [("zerocopy", -1, 0), ("device", -1, 0),
+                                               ("device", 0, 0), ("device", 0, 1),
+                                               ("zerocopy", 0, 0), ("device", 3, 5)])
+def test_gpu_consumer_waits_for_published_layer(path, policy, block, stream):
     """A consumer stream waits (bounded) for the last layer's count, then
-    reads that layer back; the bytes must be the restored ones."""
+    reads that layer back; the bytes must be the restored ones. Also with
+    plain stores that stay in L2 until written back (cache policy 0 or 3)
+    and with other publish blocks."""
     t = torch()
     w, n = SMALL["llama_small"]
     L = oracle_layout(w)
+    old = {o: K.kvx_get_option(o) for o in (K.KVX_OPT_CACHE_POLICY, K.KVX_OPT_PUBLISH_BLOCK)}
+    K.kvx_set_option(K.KVX_OPT_CACHE_POLICY, policy)
+    K.kvx_set_option(K.KVX_OPT_PUBLISH_BLOCK, block)
     pool = DevicePool(w, seed=305, generation=2)
     img = pool.host_image()
     _, dst = pages(w, n)
     nb = w.host_bytes(n)
-    pk = Packed(w, n, "zerocopy", fill_seed=11)
+    pk = Packed(w, n, path, fill_seed=11)
     hbytes = synth.gen_bytes(11, 0, nb)
     ready = K.kvx_ready_create(w.num_layers, 2)
     consumer = t.cuda.Stream()
@@ -436,8 +444,7 @@ def test_gpu_consumer_waits_for_published_layer(stream):
     t.cuda.synchronize()
     last = w.num_layers - 1
     try:
-        K.kvx_restore(pool.handle, pk.ptr, nb, dst, 0, w.num_layers, ready, 0, stream,
-                      K.KVX_PATH_ZEROCOPY)
+        K.kvx_restore(pool.handle, pk.ptr, nb, dst, 0, w.num_layers, ready, 0, stream, PATHS[path])
         # everything the producer needs is enqueued before the consumer waits
         K.kvx_ready_wait_gpu(ready, last, n, consumer, 2_000_000, status)
         K.kvx_backup(pool.handle, dst, out.ptr, nb, last, w.num_layers, consumer,
@@ -458,6 +465,8 @@ def test_gpu_consumer_waits_for_published_layer(stream):
         K.kvx_sync(consumer)
         assert int(status.item()) == 0
     finally:
+        for o, v in old.items():
+            K.kvx_set_option(o, v)
         K.kvx_ready_destroy(ready)
         pk.close()
         pool.close()

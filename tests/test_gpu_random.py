@@ -79,6 +79,7 @@ TUNING = {
     "STAGE_SLOTS": [3, 2, 8],
     "RESTORE_CHUNK_LAYERS": [0, 0, 1, 2],
     "STAGED_DMA_ON_CALLER": [-1, 0, 1],
+    "PUBLISH_BLOCK": [0, 0, 1, 3, 16, 4096],
 }
 NUM_TUNED = 60
 
