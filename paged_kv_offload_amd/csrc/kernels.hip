@@ -423,7 +423,13 @@ __global__ __launch_bounds__(kThreads) void kvx_exchange_kernel(A a)
             if constexpr (PUBLISH) pend++;
         }
     };
-    for_queued_units(a.p.queue, tb + tr, tid, do_unit);
+    // blocks of a.p.block consecutive unit numbers per draw (both sides
+    // alternating inside a block), as in the move kernel
+    const uint32_t B = a.p.block, total = tb + tr;
+    for_queued_units(a.p.queue, (total + B - 1) / B, tid, [&](uint32_t blk) {
+        const uint32_t q1 = (blk + 1) * B < total ? (blk + 1) * B : total;
+        for (uint32_t q = blk * B; q < q1; q++) do_unit(q);
+    });
     if constexpr (PUBLISH) {
         if (pend) count_units(a.p, pend_layer, pend, tid);
     }
