@@ -472,6 +472,56 @@ def test_gpu_consumer_waits_for_published_layer(path, policy, block, stream):
         pool.close()
 
 
+@pytest.mark.parametrize("path,policy", [("device", -1), ("device", 0), ("zerocopy", -1),
+                                         ("zerocopy", 0)])
+@pytest.mark.parametrize("case", ["mla_small", "llama_small"])
+def test_consumer_reads_every_layer_as_it_is_published(case, path, policy, stream):
+    """Eight rounds, each restoring fresh bytes into the same pages: a
+    consumer stream waits (bounded) for each layer's count in turn and
+    copies that layer out at once, while the producer still writes later
+    layers. Every copy holds the round's bytes, never an earlier round's:
+    the producer's stores reach the consumer's reads through the count
+    alone. Also with plain stores that stay in L2 until written back
+    (cache policy 0)."""
+    t = torch()
+    w, n = SMALL[case]
+    L = oracle_layout(w)
+    NL = w.num_layers
+    old = K.kvx_get_option(K.KVX_OPT_CACHE_POLICY)
+    K.kvx_set_option(K.KVX_OPT_CACHE_POLICY, policy)
+    pool = DevicePool(w, seed=306, generation=2)
+    img = pool.host_image()
+    _, dst = pages(w, n)
+    nb = w.host_bytes(n)
+    ready = K.kvx_ready_create(NL, 2)
+    consumer = t.cuda.Stream()
+    status = t.zeros(NL, dtype=t.int32, device="cuda")
+    out = Packed(w, n, "device")
+    print(f"\n[consumer] case={case} path={path} policy={policy} n={n} layers={NL}", flush=True)
+    try:
+        for r in range(8):
+            pk = Packed(w, n, path, fill_seed=500 + r)
+            status.zero_()
+            K.kvx_ready_reset(ready)
+            t.cuda.synchronize()
+            K.kvx_restore(pool.handle, pk.ptr, nb, dst, 0, NL, ready, 0, stream, PATHS[path])
+            for l in range(NL):
+                K.kvx_ready_wait_gpu(ready, l, n, consumer, 2_000_000, status[l:l + 1])
+                K.kvx_backup(pool.handle, dst, out.ptr, nb, l, l + 1, consumer, K.KVX_PATH_DEVICE)
+            K.kvx_sync(consumer)
+            K.kvx_sync(stream)
+            assert status.tolist() == [1] * NL, f"round {r}: a wait gave up"
+            want = oracle.backup(L, oracle.restore(L, img, synth.gen_bytes(500 + r, 0, nb), dst, 0, NL),
+                                 dst, 0, NL)
+            got = out.numpy()
+            assert np.array_equal(got, want), f"round {r}: " + diff_report(got, want)
+            pk.close()
+    finally:
+        K.kvx_set_option(K.KVX_OPT_CACHE_POLICY, old)
+        K.kvx_ready_destroy(ready)
+        pool.close()
+
+
 @pytest.mark.parametrize("path", ["zerocopy", "staged"])
 def test_gpu_consumer_reads_layer0_while_later_layers_are_held_back(path, stream):
     """The producer restores layer 0; the later layers are held back on the
