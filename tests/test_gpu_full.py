@@ -114,6 +114,51 @@ def test_full_size_backup_restore(name, path):
         pool.close()
 
 
+@pytest.mark.parametrize("name", ["llama8b", "mla_fp8"])
+def test_full_size_device_path_as_benchmarked(name):
+    """The benchmark's roofline calls at full size: the request packed into
+    a device buffer in one call (the whole packed buffer checked against
+    the closed form of BACKUP), unpacked into the destination pages without
+    publish, then - after the pool is refilled - unpacked again publishing
+    every layer (the queue-driven kernel drawing blocks of units); each time
+    the whole allocation is checked against the closed form of the round
+    trip."""
+    t = torch()
+    w = WORKLOADS[name]
+    n = w.pages_per_request
+    print(f"\n[full] {name} device path: pool {w.pool_bytes / 2**30:.1f} GiB, n={n}", flush=True)
+    L = oracle_layout(w)
+    src, dst = request_pair(w)
+    pool = DevicePool(w, generation=5)
+    P = w.payload_bytes(n)
+    dev = t.empty(P, dtype=t.uint8, device="cuda")
+    stream = t.cuda.Stream()
+    ready = K.kvx_ready_create(w.num_layers, 5)
+    D = K.KVX_PATH_DEVICE
+    try:
+        K.kvx_backup(pool.handle, src, dev.data_ptr(), P, 0, w.num_layers, stream, D)
+        K.kvx_sync(stream)
+        bad, first = check_packed(w, L, w.seed, src, 0, w.num_layers, dev.cpu().numpy())
+        assert bad == 0, f"pack: {bad} bytes differ, first at packed offset {first}"
+        for publish in (False, True):
+            if publish:
+                synth.fill_alloc_gpu(pool.alloc.data_ptr(), w, w.seed)
+                t.cuda.synchronize()
+            K.kvx_restore(pool.handle, dev.data_ptr(), P, dst, 0, w.num_layers,
+                          ready if publish else None, 0, stream, D)
+            K.kvx_sync(stream)
+            if publish:
+                assert [K.kvx_layer_ready(ready, l) for l in range(w.num_layers)] == [n] * w.num_layers
+            t0 = time.time()
+            bad, first = check_alloc(w, L, w.seed, src, dst, 0, w.num_layers, pool.alloc)
+            print(f"[full] allocation (publish={publish}) checked in {time.time() - t0:.1f} s", flush=True)
+            assert bad == 0, f"unpack (publish={publish}): {bad} bytes differ, first at allocation byte {first}"
+    finally:
+        K.kvx_ready_destroy(ready)
+        del dev
+        pool.close()
+
+
 def test_full_size_mla_layerwise_ready():
     """The MLA fp8 pool: four 64-page requests, each backed up and restored
     layer by layer into its own pages; a CPU thread samples the published
