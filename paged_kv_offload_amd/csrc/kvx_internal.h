@@ -61,6 +61,7 @@ namespace kvx {
 
 bool pool_known(const kvx_pool* p);
 bool ready_known(const kvx_ready* r);
+void register_ready(const kvx_ready* r);   // enters a new ready handle in the registry
 
 // ---------------------------------------------------------------------------
 // tuning
