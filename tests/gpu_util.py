@@ -44,10 +44,21 @@ class DevicePool:
         synth.fill_alloc_gpu(self.alloc.data_ptr(), w, self.seed,
                              stream=0 if stream is None else stream.cuda_stream)
         t.cuda.synchronize()
-        dt = {1: t.uint8, 2: t.bfloat16, 4: t.float32}[w.dtype_bytes]
-        view = self.alloc[w.byte_offset:w.byte_offset + w.pool_bytes].view(dt)
-        self.tensor = view.view(*w.tensor_shape())
-        self.handle = K.register_tensor(self.tensor, kvx_layout(w), generation)
+        dt = {1: t.uint8, 2: t.bfloat16, 4: t.float32}.get(w.dtype_bytes)
+        if dt is not None:
+            view = self.alloc[w.byte_offset:w.byte_offset + w.pool_bytes].view(dt)
+            self.tensor = view.view(*w.tensor_shape())
+            self.handle = K.register_tensor(self.tensor, kvx_layout(w), generation)
+        else:
+            # an element size torch has no dtype for: the C ABI takes the
+            # allocation base, the byte offset and element shape and strides
+            self.tensor = None
+            shape = w.tensor_shape()
+            stride = [int(np.prod(shape[i + 1:])) for i in range(len(shape))]
+            base, _ = K.kvx_alloc_range(self.alloc.data_ptr())
+            self.handle = K.kvx_register_pool(kvx_layout(w), base,
+                                              self.alloc.data_ptr() + w.byte_offset - base,
+                                              w.dtype_bytes, shape, stride, generation)
 
     def host_image(self) -> np.ndarray:
         torch().cuda.synchronize()

@@ -24,12 +24,18 @@ NUM_GEOMS = 160
 POOL_CAP = 12 << 20   # pool bytes at most (about), so the oracle stays fast
 
 
-def random_workload(k: int) -> Workload:
+def random_workload(k: int, exotic: bool = False) -> Workload:
     rng = np.random.default_rng(9000 + k)
     outer = tuple(str(a) for a in rng.permutation(["page", "layer", "kv"]))
     inner = str(rng.choice(["NHD", "HND"]))
-    eb = int(rng.choice([1, 2, 4]))
-    row = 16 * int(rng.integers(1, 40))
+    if not exotic:
+        eb = int(rng.choice([1, 2, 4]))
+        row = 16 * int(rng.integers(1, 40))
+    else:
+        # element sizes no torch dtype has: rows stay 16-byte multiples
+        eb = int(rng.choice([3, 6, 8, 12, 16, 64]))
+        unit = int(np.lcm(16, eb))
+        row = unit * int(rng.integers(1, max(2, 640 // unit + 1)))
     T = int(rng.integers(1, 70))
     H = int(rng.integers(1, 10))
     KV = int(rng.integers(1, 3))
@@ -45,6 +51,8 @@ def random_workload(k: int) -> Workload:
 
 
 GEOMS = [random_workload(k) for k in range(NUM_GEOMS)]
+NUM_EXOTIC = 24
+EXOTIC = [random_workload(NUM_GEOMS + k, exotic=True) for k in range(NUM_EXOTIC)]
 
 
 def layer_range(rng, NL):
@@ -109,8 +117,16 @@ def test_random_geometry_with_random_tuning(k, stream):
             K.kvx_set_option(getattr(K, "KVX_OPT_" + name), v)
 
 
-def run_geometry(k, rng, stream):
-    w = GEOMS[k]
+@pytest.mark.gpu
+@pytest.mark.parametrize("k", range(NUM_EXOTIC))
+def test_random_geometry_with_other_element_sizes(k, stream):
+    """Element sizes of 3, 6, 8, 12, 16 and 64 bytes: the library only sizes
+    rows with them, so the bytes must come out as for any other size."""
+    run_geometry(k, np.random.default_rng(9900 + k), stream, EXOTIC[k])
+
+
+def run_geometry(k, rng, stream, w=None):
+    w = GEOMS[k] if w is None else w
     NB, NL = w.num_pages, w.num_layers
     print(f"\n[random] k={k} outer={w.outer} inner={w.inner} NB={NB} NL={NL} KV={w.num_kv} "
           f"T={w.page_size} H={w.num_heads} row={w.row_bytes} eb={w.dtype_bytes} "
@@ -244,7 +260,7 @@ def test_random_geometries_are_valid_pools():
     alone and K and V, merged and split views, pieces above one 128 KiB
     unit, and pieces that are not a multiple of 4 KiB."""
     fake = 0x7F0000000000   # never dereferenced: registration reads no memory
-    for w in GEOMS:
+    for w in GEOMS + EXOTIC:
         assert w.row_bytes % 16 == 0 and w.byte_offset % 16 == 0
         shape = w.tensor_shape()
         stride = [int(np.prod(shape[i + 1:])) for i in range(len(shape))]
@@ -262,6 +278,7 @@ def test_random_geometries_are_valid_pools():
     assert any(w.piece_bytes > 128 * 1024 for w in GEOMS)
     assert any(w.piece_bytes % 4096 for w in GEOMS)
     assert any(w.inner == "HND" and w.num_heads > 1 and w.page_size > 1 for w in GEOMS)
+    assert {w.dtype_bytes for w in EXOTIC} == {3, 6, 8, 12, 16, 64}
 
 
 def test_random_tuning_values_are_accepted():
