@@ -522,6 +522,52 @@ def test_consumer_reads_every_layer_as_it_is_published(case, path, policy, strea
         pool.close()
 
 
+@pytest.mark.parametrize("path", list(PATHS))
+@pytest.mark.parametrize("case", ["trtllm_small", "ragged_nhd"])
+def test_byte_offset_moves_the_pool_and_nothing_else(case, path, stream):
+    """The same pool bytes placed at byte offset 0 and at offsets of 16 B,
+    4 KiB and 12 KiB + 16 B of their allocations: every BACKUP gives the
+    same packed bytes (the oracle's), every RESTORE of the same host bytes
+    leaves the same pool bytes, and the padding before and after the pool
+    keeps its bytes."""
+    t = torch()
+    w0, n = SMALL[case]
+    src, dst = pages(w0, n)
+    nb = w0.host_bytes(n)
+    packed, pools = [], []
+    for off in (0, 16, 4096, 12304):
+        w = w0.scaled(byte_offset=off, alloc_tail=4096 + 48)
+        L = oracle_layout(w)
+        pool = DevicePool(w, seed=311, generation=3)
+        # the pool region holds stream 311 from its own first byte, whatever the offset
+        synth.fill_gpu(pool.alloc.data_ptr() + off, w.pool_bytes, 311, 0)
+        t.cuda.synchronize()
+        img = pool.host_image()
+        pk = Packed(w, n, path, fill_seed=21)
+        K.kvx_backup(pool.handle, src, pk.ptr, nb, 0, w.num_layers, stream, PATHS[path])
+        K.kvx_sync(stream)
+        got = pk.numpy()
+        want = oracle.backup(L, img, src, 0, w.num_layers, host=synth.gen_bytes(21, 0, nb))
+        assert np.array_equal(got, want), f"offset {off}: backup " + diff_report(got, want)
+        packed.append(got)
+        pk.fill(22)
+        K.kvx_restore(pool.handle, pk.ptr, nb, dst, 0, w.num_layers, None, 0, stream, PATHS[path])
+        K.kvx_sync(stream)
+        after = pool.host_image()
+        want_alloc = oracle.restore(L, img, synth.gen_bytes(22, 0, nb), dst, 0, w.num_layers)
+        assert np.array_equal(after, want_alloc), f"offset {off}: restore " + diff_report(after, want_alloc)
+        pad = np.concatenate([after[:off], after[off + w.pool_bytes:]])
+        pad_want = np.concatenate([synth.gen_bytes(312, 0, off),
+                                   synth.gen_bytes(312, off + w.pool_bytes, w.alloc_bytes - off - w.pool_bytes)])
+        assert np.array_equal(pad, pad_want), f"offset {off}: padding changed"
+        pools.append(after[off:off + w.pool_bytes].copy())
+        pk.close()
+        pool.close()
+    for k in range(1, len(packed)):
+        assert np.array_equal(packed[k], packed[0])
+        assert np.array_equal(pools[k], pools[0])
+
+
 @pytest.mark.parametrize("path", ["zerocopy", "staged"])
 def test_gpu_consumer_reads_layer0_while_later_layers_are_held_back(path, stream):
     """The producer restores layer 0; the later layers are held back on the
