@@ -51,7 +51,8 @@ def build(verbose: bool = False, out_dir: str = None) -> str:
     rpaths = [d for d in (torch_lib_dir(), "/opt/rocm/lib") if d]
     lib = os.path.join(out_dir, "libkvx.so")
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", lib + ".tmp"] + objs + \
-          [f"-Wl,-rpath,{d}" for d in rpaths] + ["-Wl,--no-undefined", "-Wl,-soname,libkvx.so"]
+          [f"-Wl,-rpath,{d}" for d in rpaths] + ["-L/opt/rocm/lib", "-lrocprofiler-sdk-roctx",
+                                                 "-Wl,--no-undefined", "-Wl,-soname,libkvx.so"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)

@@ -19,6 +19,8 @@
 #include <iterator>
 #include <set>
 
+#include <rocprofiler-sdk-roctx/roctx.h>
+
 #include "kvx_internal.h"
 
 namespace kvx {
@@ -47,6 +49,28 @@ int fail(int code, const std::string& msg)
 }
 
 void clear_error() { t_error.clear(); }
+
+// KVX_TRACE=1: every data-moving call is a roctx range named after it, so a
+// marker trace (rocprofv3 --marker-trace) shows the calls around their
+// kernels and copies. Read once; off by default.
+bool trace_on()
+{
+    static const bool on = [] {
+        const char* e = std::getenv("KVX_TRACE");
+        return e && std::atoi(e) > 0;
+    }();
+    return on;
+}
+
+TraceRange::TraceRange(const char* name) : on(trace_on())
+{
+    if (on) roctxRangePushA(name);
+}
+
+TraceRange::~TraceRange()
+{
+    if (on) roctxRangePop();
+}
 
 void log_warn(const std::string& msg)
 {
@@ -1013,6 +1037,7 @@ int kvx_packed_bytes(const kvx_pool* pool, int32_t n, uint64_t* bytes)
 int kvx_backup(kvx_pool* pool, const int32_t* page_ids, int32_t n, void* dst, uint64_t dst_bytes,
                int32_t layer_begin, int32_t layer_end, void* stream, int32_t path)
 {
+    const TraceRange tr("kvx_backup");
     return run_op(pool, GATHER, page_ids, n, dst, dst_bytes, layer_begin, layer_end, nullptr, 0,
                 stream, path);
 }
@@ -1021,6 +1046,7 @@ int kvx_restore(kvx_pool* pool, const void* src, uint64_t src_bytes, const int32
                 int32_t n, int32_t layer_begin, int32_t layer_end, kvx_ready* ready,
                 int32_t slot_base, void* stream, int32_t path)
 {
+    const TraceRange tr("kvx_restore");
     return run_op(pool, SCATTER, page_ids, n, const_cast<void*>(src), src_bytes, layer_begin,
                 layer_end, ready, slot_base, stream, path);
 }
@@ -1029,6 +1055,7 @@ int kvx_backup_slots(kvx_pool* pool, const int32_t* page_ids, const int32_t* hos
                      void* host_pool, uint64_t host_pool_bytes, int32_t num_host_slots,
                      int32_t layer_begin, int32_t layer_end, void* stream, int32_t path)
 {
+    const TraceRange tr("kvx_backup_slots");
     const HostSlots hs{host_slots, num_host_slots};
     return run_op(pool, GATHER, page_ids, n, host_pool, host_pool_bytes, layer_begin, layer_end,
                   nullptr, 0, stream, path, &hs);
@@ -1039,6 +1066,7 @@ int kvx_restore_slots(kvx_pool* pool, const void* host_pool, uint64_t host_pool_
                       int32_t n, int32_t layer_begin, int32_t layer_end, kvx_ready* ready,
                       int32_t slot_base, void* stream, int32_t path)
 {
+    const TraceRange tr("kvx_restore_slots");
     const HostSlots hs{host_slots, num_host_slots};
     return run_op(pool, SCATTER, page_ids, n, const_cast<void*>(host_pool), host_pool_bytes,
                   layer_begin, layer_end, ready, slot_base, stream, path, &hs);
@@ -1047,6 +1075,7 @@ int kvx_restore_slots(kvx_pool* pool, const void* host_pool, uint64_t host_pool_
 int kvx_exchange(kvx_pool* pool, const kvx_xfer* backup, const kvx_xfer* restore, kvx_ready* ready,
                  int32_t slot_base, void* stream, int32_t path)
 {
+    const TraceRange tr("kvx_exchange");
     clear_error();
     if (!backup || !restore) return fail(KVX_E_INVAL, "exchange: NULL transfer description");
     if (!pool_known(pool)) return fail(KVX_E_INVAL, "exchange: unknown pool handle");
@@ -1106,6 +1135,7 @@ int kvx_exchange(kvx_pool* pool, const kvx_xfer* backup, const kvx_xfer* restore
 int kvx_exchange_slots(kvx_pool* pool, const kvx_xfer_slots* backup, const kvx_xfer_slots* restore,
                        kvx_ready* ready, int32_t slot_base, void* stream, int32_t path)
 {
+    const TraceRange tr("kvx_exchange_slots");
     clear_error();
     if (!backup || !restore) return fail(KVX_E_INVAL, "exchange_slots: NULL transfer description");
     if (!pool_known(pool)) return fail(KVX_E_INVAL, "exchange_slots: unknown pool handle");

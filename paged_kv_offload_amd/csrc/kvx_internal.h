@@ -18,6 +18,15 @@ namespace kvx {
 
 int hip_fail(hipError_t e, const char* what);  // KVX_E_HIP with the runtime's message
 
+// A roctx range around a data-moving call while KVX_TRACE is set.
+struct TraceRange {
+    explicit TraceRange(const char* name);
+    ~TraceRange();
+    TraceRange(const TraceRange&) = delete;
+    TraceRange& operator=(const TraceRange&) = delete;
+    bool on;
+};
+
 #define KVX_HIP(call)                                   \
     do {                                                \
         hipError_t e_ = (call);                         \

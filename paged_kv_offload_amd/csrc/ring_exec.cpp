@@ -236,6 +236,7 @@ int kvx_ring_serve(kvx_ring* r, kvx_pool* const* pools, int32_t num_pools, void*
                    const uint64_t* buffer_bytes, int32_t num_buffers, kvx_ready* ready, void* stream,
                    int32_t max_ops, int32_t* taken, int32_t* completed)
 {
+    const TraceRange tr("kvx_ring_serve");
     int rc = open_server(r, "ring_serve");
     if (rc != KVX_OK) return rc;
     if (!taken || !completed) return fail(KVX_E_INVAL, "ring_serve: NULL output");
@@ -292,6 +293,7 @@ int kvx_ring_serve(kvx_ring* r, kvx_pool* const* pools, int32_t num_pools, void*
 
 int kvx_ring_drain(kvx_ring* r, int32_t* completed)
 {
+    const TraceRange tr("kvx_ring_drain");
     int rc = open_server(r, "ring_drain");
     if (rc != KVX_OK) return rc;
     if (!completed) return fail(KVX_E_INVAL, "ring_drain: completed is NULL");

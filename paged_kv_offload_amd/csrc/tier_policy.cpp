@@ -38,6 +38,7 @@ int kvx_tier_backup(kvx_tier* tier, kvx_pool* pool, const uint64_t* keys, const 
                     int32_t n, void* host_pool, uint64_t host_pool_bytes, void* stream,
                     int32_t path, int32_t* slots, uint64_t* evicted, int32_t* num_evicted)
 {
+    const TraceRange tr("kvx_tier_backup");
     clear_error();
     int rc = tier_for_pool(tier, pool, "tier_backup");
     if (rc != KVX_OK) return rc;
@@ -86,6 +87,7 @@ int kvx_tier_restore(kvx_tier* tier, kvx_pool* pool, const uint64_t* keys, const
                      kvx_ready* ready, int32_t slot_base, void* stream, int32_t path,
                      int32_t* slots, int32_t* hits)
 {
+    const TraceRange tr("kvx_tier_restore");
     clear_error();
     int rc = tier_for_pool(tier, pool, "tier_restore");
     if (rc != KVX_OK) return rc;
@@ -126,6 +128,7 @@ int kvx_tier_exchange(kvx_tier* tier, kvx_pool* pool, const uint64_t* backup_key
                       int32_t path, int32_t* backup_slots, uint64_t* evicted, int32_t* num_evicted,
                       int32_t* restore_slots, int32_t* hits)
 {
+    const TraceRange tr("kvx_tier_exchange");
     clear_error();
     int rc = tier_for_pool(tier, pool, "tier_exchange");
     if (rc != KVX_OK) return rc;

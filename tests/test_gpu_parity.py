@@ -976,3 +976,19 @@ def test_empty_work_is_a_noop_on_the_gpu(path, stream):
         K.kvx_ready_destroy(ready)
         pk.close()
         pool.close()
+
+
+def test_trace_ranges_leave_results_unchanged():
+    """With KVX_TRACE=1 every data-moving call opens and closes a roctx
+    range; the smoke round trip (staged path and kvx_exchange, checked
+    against the oracle) still passes. A process of its own, since the
+    setting is read once."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, KVX_TRACE="1")
+    r = subprocess.run([sys.executable, "-c", "import __graft_entry__ as g; g.smoke()"], cwd=root,
+                       env=env, capture_output=True, text=True, timeout=240)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    assert "smoke ok" in r.stdout
