@@ -5,6 +5,7 @@ that, inside a process that already imported torch, it binds to the same
 HIP runtime instance as torch (both sonames are libamdhip64.so.7; the rpath
 puts torch's copy first when kvx is loaded on its own).
 """
+import concurrent.futures
 import os
 import subprocess
 import sys
@@ -38,16 +39,20 @@ def build(verbose: bool = False, out_dir: str = None) -> str:
     out_dir = out_dir or HERE
     obj_dir = os.path.join(out_dir, "_build")
     os.makedirs(obj_dir, exist_ok=True)
-    objs = []
+    objs, cmds = [], []
     for src in SOURCES:
         obj = os.path.join(obj_dir, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC] + lang + \
-              ["-c", os.path.join(CSRC, src), "-o", obj]
-        if verbose:
-            print(" ".join(cmd), flush=True)
-        subprocess.run(cmd, check=True)
+        cmds.append([hipcc()] + HIPCC_FLAGS + ["-I", INCLUDE, "-I", CSRC] + lang +
+                    ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
+    # the sources compile independently: a few at a time
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, os.cpu_count() or 1)) as ex:
+        for cmd in cmds:
+            if verbose:
+                print(" ".join(cmd), flush=True)
+        for r in ex.map(lambda c: subprocess.run(c, check=True), cmds):
+            pass
     rpaths = [d for d in (torch_lib_dir(), "/opt/rocm/lib") if d]
     lib = os.path.join(out_dir, "libkvx.so")
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", lib + ".tmp"] + objs + \

@@ -288,6 +288,18 @@ __device__ __forceinline__ void move_at(const UnitGeom& g, const Side& s, const 
 // workgroup stops at its first draw past the end, so draw number
 // total + gridDim.x - 1 is the launch's last: whoever makes it resets the
 // queue for the next launch on the stream.
+//
+// Every lane reads the same LDS word after the barrier; readfirstlane tells
+// the compiler so. Without it the unit number, and every buffer resource
+// derived from it, counts as divergent, and each buffer access is wrapped in
+// a readfirstlane loop (measured on MI355X, device-path restore publishing
+// every layer: 5.36 TB/s with the loops on llama8b against 5.69 without,
+// 181 VGPRs against 164).
+__device__ __forceinline__ uint32_t uniform_u32(uint32_t v)
+{
+    return static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v)));
+}
+
 template <class F>
 __device__ __forceinline__ void for_queued_units(uint32_t* queue, uint32_t total, uint32_t tid, F&& f)
 {
@@ -299,7 +311,7 @@ __device__ __forceinline__ void for_queued_units(uint32_t* queue, uint32_t total
         next[0] = d;
     }
     __syncthreads();
-    uint32_t q = next[0];
+    uint32_t q = uniform_u32(next[0]);
     for (uint32_t it = 1; q < total; it++) {
         uint32_t d = 0;
         if (tid == 0) d = __hip_atomic_fetch_add(queue, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -309,7 +321,7 @@ __device__ __forceinline__ void for_queued_units(uint32_t* queue, uint32_t total
             next[it & 1u] = d;
         }
         __syncthreads();
-        q = next[it & 1u];
+        q = uniform_u32(next[it & 1u]);
     }
 }
 
