@@ -96,6 +96,7 @@ def lib() -> ctypes.CDLL:
         L.kvxo_hnd_to_nhd.argtypes = [u8p, u8p, i64, i64, i64]
         L.kvxo_ready_prefix.argtypes = [ctypes.c_void_p, i64]
         L.kvxo_ready_prefix.restype = i64
+        L.kvxo_ready_publish.argtypes = [ctypes.c_void_p, i64, i64, i64, i64, ctypes.c_uint32]
         L.kvxo_gen_word.argtypes = [u64, u64]
         L.kvxo_gen_word.restype = u64
         L.kvxo_splitmix64_next.argtypes = [_P(u64)]
@@ -216,6 +217,15 @@ def hnd_to_nhd(piece: np.ndarray, T: int, H: int, row_bytes: int) -> np.ndarray:
 def ready_prefix(counts: Sequence[int]) -> int:
     a = np.ascontiguousarray(np.asarray(counts, dtype=np.uint32))
     return lib().kvxo_ready_prefix(_ptr(a), a.size)
+
+
+def ready_publish(counts: Sequence[int], slot_base: int, l0: int, l1: int, n: int) -> list:
+    """The ready counts after a RESTORE of n pages over layers [l0, l1) that
+    publishes from slot_base has completed (a new list; `counts` is left as
+    it was)."""
+    a = np.array(np.asarray(counts, dtype=np.uint32), dtype=np.uint32, copy=True)
+    lib().kvxo_ready_publish(_ptr(a), a.size, slot_base, l0, l1, n)
+    return [int(x) for x in a]
 
 
 def splitmix64_stream(state: int, count: int) -> list:

@@ -246,6 +246,29 @@ int64_t kvxo_ready_prefix(const uint32_t* counts, int64_t num_slots)
 }
 
 /* ---------------------------------------------------------------------------
+ * Per-layer publish of one RESTORE.
+ * [TICKET, "PP Prefetch Ticket Path" diagram]: KV arrives layer by layer and
+ * each KV layer and sidecar publishes its own progress; the safe prefix is
+ * the minimum of that progress. The page leaves open what a count holds
+ * when a ready object serves one restore after another. The reading taken
+ * here: a count is the number of pages published into its slot since the
+ * object was created or reset, so a RESTORE of n pages over layers
+ * [l0, l1) from slot_base adds n to slots [slot_base + l0, slot_base + l1)
+ * once each of those layers is complete; counts only grow, and a consumer
+ * of the k-th restore waits for the sum of the n of the first k. Counts are
+ * 32-bit and wrap modulo 2^32.
+ * ------------------------------------------------------------------------- */
+void kvxo_ready_publish(uint32_t* counts, int64_t num_slots, int64_t slot_base, int64_t l0,
+                        int64_t l1, uint32_t n)
+{
+    for (int64_t l = l0; l < l1; l++) {
+        int64_t s = slot_base + l;
+        if (s >= 0 && s < num_slots)
+            counts[s] = counts[s] + n;
+    }
+}
+
+/* ---------------------------------------------------------------------------
  * The synthetic-input generator, written here independently of the input
  * module so that the closed forms below do not depend on it.
  * SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom number

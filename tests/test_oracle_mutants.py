@@ -54,6 +54,11 @@ MUTANTS = [
     ("ready_prefix_is_max", "kvxo_ready_prefix", "(int64_t)counts[s] < m",
      "(int64_t)counts[s] > m"),
     ("ready_prefix_skips_last", "kvxo_ready_prefix", "s < num_slots", "s + 1 < num_slots"),
+    ("ready_publish_overwrites", "kvxo_ready_publish", "counts[s] = counts[s] + n;", "counts[s] = n;"),
+    ("ready_publish_ignores_l0", "kvxo_ready_publish", "for (int64_t l = l0; l < l1; l++)",
+     "for (int64_t l = 0; l < l1; l++)"),
+    ("ready_publish_ignores_slot_base", "kvxo_ready_publish", "int64_t s = slot_base + l;",
+     "int64_t s = l;"),
     ("splitmix_shift_28", "kvxo_splitmix64_next", "(z >> 27)", "(z >> 28)"),
     ("generator_word_off_by_one", "kvxo_gen_word", "seed + j * 0x9e3779b97f4a7c15ULL",
      "seed + (j + 1) * 0x9e3779b97f4a7c15ULL"),

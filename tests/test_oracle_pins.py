@@ -282,6 +282,33 @@ def test_ready_prefix_is_minimum():
     assert oracle.ready_prefix([9]) == 9
 
 
+def test_ready_publish_adds_n_to_the_call_slots():
+    """Hand-worked counts of a ready object serving several restores (the
+    reading of the ticket page's per-layer progress: a count is the pages
+    published into its slot since the object was created or reset)."""
+    # six slots; a restore of 4 pages over layers [0, 3) published from slot 2
+    c = oracle.ready_publish([0] * 6, 2, 0, 3, 4)
+    assert c == [0, 0, 4, 4, 4, 0]
+    # a second restore into layers [1, 3) of the same slots adds, never overwrites
+    c = oracle.ready_publish(c, 2, 1, 3, 4)
+    assert c == [0, 0, 4, 8, 8, 0]
+    # an empty layer range or n = 0 changes nothing
+    assert oracle.ready_publish(c, 2, 2, 2, 4) == c
+    assert oracle.ready_publish(c, 0, 0, 6, 0) == c
+    # main pool in slots 0-2, a sidecar in slot 3: the prefix waits for both
+    c = oracle.ready_publish([0] * 4, 0, 0, 3, 16)
+    assert oracle.ready_prefix(c) == 0
+    c = oracle.ready_publish(c, 3, 0, 1, 16)
+    assert c == [16, 16, 16, 16] and oracle.ready_prefix(c) == 16
+    # the next request's main restore alone does not move the prefix
+    c = oracle.ready_publish(c, 0, 0, 3, 16)
+    assert c == [32, 32, 32, 16] and oracle.ready_prefix(c) == 16
+    c = oracle.ready_publish(c, 3, 0, 1, 16)
+    assert oracle.ready_prefix(c) == 32
+    # 32-bit counts wrap
+    assert oracle.ready_publish([2 ** 32 - 1, 7], 0, 0, 1, 2) == [1, 7]
+
+
 # ---------------------------------------------------------------------------
 # slot-addressed host pool
 # ---------------------------------------------------------------------------
