@@ -86,10 +86,10 @@ extern "C" int kvx_ipc_export(const void* device_ptr, kvx_ipc_handle* out)
     hipDeviceptr_t base = nullptr;
     size_t bytes = 0;
     KVX_HIP(hipMemGetAddressRange(&base, &bytes, const_cast<void*>(device_ptr)));
-    if (bytes > KVX_IPC_MAX_BYTES)
+    if (bytes >= KVX_IPC_MAX_BYTES)
         return fail(KVX_E_RANGE, "ipc_export: the allocation holds " + std::to_string(bytes) +
-                                     " bytes; at most " + std::to_string(KVX_IPC_MAX_BYTES) +
-                                     " are shared");
+                                     " bytes; only allocations below " +
+                                     std::to_string(KVX_IPC_MAX_BYTES) + " bytes are shared");
     hipIpcMemHandle_t mh;
     KVX_HIP(hipIpcGetMemHandle(&mh, base));
     hipDevice_t dev;
@@ -115,10 +115,10 @@ extern "C" int kvx_ipc_import(const kvx_ipc_handle* handle, void** base_out, int
     if (handle->version != KVX_IPC_HANDLE_VERSION || handle->reserved != 0 || handle->alloc_bytes == 0 ||
         handle->offset >= handle->alloc_bytes)
         return fail(KVX_E_INVAL, "ipc_import: malformed handle");
-    if (handle->alloc_bytes > KVX_IPC_MAX_BYTES)
+    if (handle->alloc_bytes >= KVX_IPC_MAX_BYTES)
         return fail(KVX_E_RANGE, "ipc_import: the allocation holds " +
-                                     std::to_string(handle->alloc_bytes) + " bytes; at most " +
-                                     std::to_string(KVX_IPC_MAX_BYTES) + " are shared");
+                                     std::to_string(handle->alloc_bytes) + " bytes; only allocations below " +
+                                     std::to_string(KVX_IPC_MAX_BYTES) + " bytes are shared");
     const std::string key(reinterpret_cast<const char*>(handle->mem_handle), sizeof handle->mem_handle);
     std::lock_guard<std::mutex> lk(g_ipc_mu);
     auto it = g_by_handle.find(key);

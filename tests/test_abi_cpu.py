@@ -267,15 +267,17 @@ def test_ipc_handle_layout_matches_the_header(tmp_path):
 
 
 def test_ipc_import_and_close_validate_before_any_gpu_call():
-    """Malformed or oversized handles and unknown bases are refused by
-    validation alone (no HIP call is reached)."""
+    """Malformed or oversized handles (2 GiB, exactly, and more) and unknown
+    bases are refused by validation alone (no HIP call is reached)."""
     h = K.kvx_ipc_handle()
     h.version, h.alloc_bytes, h.offset = 1, 1 << 20, 0
     good = bytes(h)
     for field, value, code in (("version", 0, K.KVX_E_INVAL), ("reserved", 1, K.KVX_E_INVAL),
                                ("alloc_bytes", 0, K.KVX_E_INVAL),
                                ("offset", 1 << 20, K.KVX_E_INVAL),
-                               ("alloc_bytes", (2 << 30) + 4096, K.KVX_E_RANGE)):
+                               ("alloc_bytes", (2 << 30) + 4096, K.KVX_E_RANGE),
+                               ("alloc_bytes", 2 << 30, K.KVX_E_RANGE),
+                               ("alloc_bytes", 1 << 31, K.KVX_E_RANGE)):
         bad = K.kvx_ipc_handle.from_buffer_copy(good)
         setattr(bad, field, value)
         with pytest.raises(K.KvxError) as e:

@@ -165,3 +165,30 @@ def test_export_refuses_non_device_memory_and_large_allocations():
         K.kvx_ipc_export(big.data_ptr() + 4096)
     assert e.value.code == K.KVX_E_RANGE
     del big
+
+
+def test_export_refuses_an_allocation_of_exactly_two_gib():
+    """The IPC size bound is exclusive: an allocation of exactly
+    KVX_IPC_MAX_BYTES (2 GiB) is refused with KVX_E_RANGE by the size check,
+    before the runtime is asked for a handle, and one just below it is
+    exported. The allocations come from hipMalloc itself (torch's caching
+    allocator may hand out part of a larger segment)."""
+    torch().cuda.init()
+    hip = ctypes.CDLL(K.hip_runtimes_mapped()[0])
+    hip.hipMalloc.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t]
+    hip.hipFree.argtypes = [ctypes.c_void_p]
+    for size, ok in ((2 << 30, False), ((2 << 30) - (2 << 20), True)):
+        p = ctypes.c_void_p()
+        assert hip.hipMalloc(ctypes.byref(p), size) == 0
+        try:
+            base, got = K.kvx_alloc_range(p.value + 4096)
+            assert (base, got) == (p.value, size)
+            if ok:
+                h = K.ipc_handle_from_bytes(K.kvx_ipc_export(p.value + 4096))
+                assert (h.alloc_bytes, h.offset) == (size, 4096)
+            else:
+                with pytest.raises(K.KvxError) as e:
+                    K.kvx_ipc_export(p.value + 4096)
+                assert e.value.code == K.KVX_E_RANGE, e.value.message
+        finally:
+            assert hip.hipFree(p) == 0
