@@ -32,9 +32,11 @@
 // published safe prefix): a workgroup counts the units it finished of layer
 // l into layer_done[l] when it moves on to the next layer (one release fence
 // per workgroup and layer, not per unit); the add that completes the layer
-// stores n into the ready slot with a system-scope release, so no reader can
-// see the count before every byte of the layer. That add also resets the
-// counter, leaving it zero for the next call on the same stream.
+// adds n to the ready slot with a system-scope release, so no reader can see
+// the new count before every byte of the layer, and a count only grows: a
+// consumer of the k-th restore into a slot waits for the pages of the first
+// k. That add also resets the counter, leaving it zero for the next call on
+// the same stream.
 #include "kvx_internal.h"
 
 namespace kvx {
@@ -159,7 +161,7 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // restores ran 2.3-3x slower with them). Thread 0 waits for the write-back
 // and adds to the layer's counter; the add that completes the layer acquires
 // the other workgroups' releases, clears the counter for the next call and
-// publishes the page count with a system-scope release.
+// adds the page count to the ready slot with a system-scope release.
 __device__ __forceinline__ void count_units(const PublishArgs& a, int32_t l, uint32_t units,
                                             uint32_t tid)
 {
@@ -173,7 +175,12 @@ __device__ __forceinline__ void count_units(const PublishArgs& a, int32_t l, uin
         if (done == a.layer_target) {
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
             __hip_atomic_store(&a.layer_done[l], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(&a.ready[l], a.publish_value, __ATOMIC_RELEASE,
+            // this add is the call's only write of the slot, and calls that
+            // publish into one slot run one after the other (stream order),
+            // so a read and a store add n without an atomic read-modify-write
+            // on host memory
+            const uint32_t prev = __hip_atomic_load(&a.ready[l], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+            __hip_atomic_store(&a.ready[l], prev + a.publish_value, __ATOMIC_RELEASE,
                                __HIP_MEMORY_SCOPE_SYSTEM);
         }
     }

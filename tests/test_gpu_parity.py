@@ -182,6 +182,7 @@ def test_exchange_parity(case, nb, nr, lb, lr, path, stream):
     try:
         want_alloc = img
         wants = []
+        want_counts = [0] * w.num_layers
         for r in range(2):
             off = r * (nb + nr)
             src = perm[off:off + nb].copy()
@@ -194,6 +195,7 @@ def test_exchange_parity(case, nb, nr, lb, lr, path, stream):
                                        host=synth.gen_bytes(w.seed + 20 + r, 0, w.host_bytes(nb))))
             want_alloc = oracle.restore(L, want_alloc, synth.gen_bytes(w.seed + 30 + r, 0, w.host_bytes(nr)),
                                         dst, *lr)
+            want_counts = oracle.ready_publish(want_counts, 0, *lr, nr)
             K.kvx_exchange(pool.handle, src, pk_b.ptr, w.host_bytes(nb), lb, pk_r.ptr, w.host_bytes(nr),
                            dst, lr, ready, 0, stream, PATHS[path])
         K.kvx_sync(stream)
@@ -202,8 +204,8 @@ def test_exchange_parity(case, nb, nr, lb, lr, path, stream):
             assert np.array_equal(got, wants[r]), f"exchange {r} backup: " + diff_report(got, wants[r])
         after = pool.host_image()
         assert np.array_equal(after, want_alloc), "exchange restore: " + diff_report(after, want_alloc)
-        counts = [K.kvx_layer_ready(ready, l) for l in range(w.num_layers)]
-        assert counts == [nr if lr[0] <= l < lr[1] else 0 for l in range(w.num_layers)]
+        # each exchange's restore adds nr to every layer it publishes
+        assert [K.kvx_layer_ready(ready, l) for l in range(w.num_layers)] == want_counts
     finally:
         K.kvx_ready_destroy(ready)
         for b in bufs:
@@ -334,7 +336,11 @@ def test_publishing_restore_parity(case, path, stream):
             K.kvx_restore(pool.handle, pk.ptr, nb, dst, 0, w.num_layers, ready, 0, stream,
                           PATHS[path])
         K.kvx_sync(stream)
-        assert [K.kvx_layer_ready(ready, s) for s in range(w.num_layers)] == [n] * w.num_layers
+        # each restore adds its n to every layer's count (no reset between)
+        counts = [0] * w.num_layers
+        for _ in range(2):
+            counts = oracle.ready_publish(counts, 0, 0, w.num_layers, n)
+        assert [K.kvx_layer_ready(ready, s) for s in range(w.num_layers)] == counts
         after = pool.host_image()
         assert np.array_equal(after, want), diff_report(after, want)
     finally:
@@ -744,33 +750,6 @@ def test_injected_allocation_failures_fail_closed_and_recover():
         pk2.close()
         pool.close()
         pool2.close()
-
-
-def test_sidecar_prefix_is_min_over_pools(stream):
-    """Two pools restored with the same page IDs publish into one ready
-    object; the prefix is the minimum over all their slots."""
-    w, n = SMALL["mla_small"]
-    side_w = SMALL["tiny"][0].scaled(num_pages=w.num_pages, num_layers=w.num_layers)
-    main, side = DevicePool(w, seed=306, generation=3), DevicePool(side_w, seed=307, generation=3)
-    _, dst = pages(w, n)
-    pk_main = Packed(w, n, "zerocopy", fill_seed=1)
-    pk_side = Packed(side_w, n, "zerocopy", fill_seed=2)
-    ready = K.kvx_ready_create(2 * w.num_layers, 3)
-    try:
-        K.kvx_restore(main.handle, pk_main.ptr, pk_main.nbytes, dst, 0, w.num_layers, ready, 0,
-                      stream, K.KVX_PATH_ZEROCOPY)
-        K.kvx_sync(stream)
-        assert K.kvx_ready_prefix(ready) == 0       # sidecar slots not yet published
-        K.kvx_restore(side.handle, pk_side.ptr, pk_side.nbytes, dst, 0, w.num_layers, ready,
-                      w.num_layers, stream, K.KVX_PATH_ZEROCOPY)
-        K.kvx_sync(stream)
-        assert K.kvx_ready_prefix(ready) == n
-    finally:
-        K.kvx_ready_destroy(ready)
-        pk_main.close()
-        pk_side.close()
-        main.close()
-        side.close()
 
 
 def test_memory_kind_checks(stream):
