@@ -2,36 +2,35 @@
 and restore (pinned host -> other GPU pages, with per-layer publish) on one
 MI355X.
 
-One step = the whole hot path over one request of the Llama-3-8B-shaped bf16
-pool (32 layers, K+V, 8 KV heads, head_dim 128, page size 64, 2048 pages):
-BACKUP of 256 fragmented pages (16,384 tokens, 2 GiB) to pinned host memory
-(validation + run planning, then the gather kernel writing the packed buffer
-over the host link), RESTORE of that buffer into 256 other pages with
-per-layer publish, and the ready-prefix query, which the host polls until
-the whole request is published.
+Default workload: the mixed hit/miss stream over a bf16 pool of 32 layers,
+K+V, 8 KV heads, head_dim 128, page size 64 and 8192 pages (64 GiB). It
+stands in for the alternating storage-hit / storage-miss benchmark of the
+PP-prefetch-ticket PR (128 requests, concurrency 4, 16,384-token inputs;
+[TICKET] "Benchmark / Setup"). One step = that whole stream: 128 requests of
+256 fragmented pages (16,384 tokens, 2 GiB each), alternating BACKUP (a
+miss: gather the request's pages into a pinned host buffer) and RESTORE (a
+hit: scatter a primed host copy into 256 other pages, publishing every
+layer into a ready object), then the host polls the ready prefix until every
+restore of the step is published. Each call runs validation and run planning
+on the host and then the zero-copy gather or scatter kernel over the host
+link.
 
-The default schedule is layer-pipelined on the zero-copy path: the backup of
-layer 0, then 31 kvx_exchange launches that each back up layer l + 1 while
-they restore layer l (the restore reads what the previous launch wrote),
-then the restore of layer 31. It moves the same bytes, with the same
-results, as the serial schedule (--schedule serial: backup of every layer,
-then restore of every layer, on --path), but keeps both directions of the
-host link busy at once.
+Headline schedule: each backup paired with the restore after it in one
+kvx_exchange launch, pairs alternating over two streams, so four requests
+are in flight and both directions of the host link carry data together.
+Also reported: the same stream as separate calls on four streams (the
+config's literal reading: zero-copy and staged), through the submission
+ring's executor, the device pack/unpack kernels against the HBM roofline,
+the pinned memcpy peaks, the Llama-3-8B-shaped one-request step and the CPU
+oracle on a bounded sample (a baseline only).
 
-value = 2 x 2 GiB x steps / wall time of the steps (GB = 1e9 B). The pool is
-resident in HBM when the timed region starts; crossing the host link is
+value = 128 x 2 GiB x steps / wall time of the steps (GB = 1e9 B). The pool
+is resident in HBM when the timed region starts; crossing the host link is
 part of the method (the host tier is where BACKUP writes and RESTORE reads).
 
-Also reported: the device pack/unpack kernels alone against the HBM peak
-(the roofline), the step's kernels against the host link (link_roofline,
-with the pinned hipMemcpyAsync peaks measured in the same run), the other
-schedule, both host paths per direction, layer-pipelined schedules on two
-streams, the layer-0-ready latency, and the CPU oracle on a bounded sample
-(a baseline only).
-
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--schedule exchange|serial]
-       [--path staged|zerocopy] [--no-cpu-baseline] [--kernel-only] [--no-extras]
-       [--all-workloads]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--schedule exchange|streams]
+       [--workload mixed|llama8b|mla_fp8|trtllm_hnd|tiny] [--no-cpu-baseline] [--kernel-only]
+       [--no-extras] [--all-workloads] [--set OPTION=VALUE]
 """
 import argparse
 import json
@@ -69,11 +68,12 @@ def pcie_protocol_bound(payload=256, write_overhead=24, completion_overhead=20, 
 
 
 # HBM bytes per launch of the roofline kernel from the two rocprofv3 --pmc runs
-# (FETCH_SIZE, WRITE_SIZE, scaled by a plain 2 GiB device copy in the same
-# run; see profiles/pack_kernel_llama8b.txt). Valid only for the kernel source
-# they were taken on: reported as null once kernels.hip changes.
-MEASURED_TRAFFIC = {"workload": "llama8b", "kernels_hip_sha256": "164fbcb2bd67b348945947576205716d4e5aa6b50254fa098284582380e27001",
-                    "bytes_per_launch": 4295172094}
+# (FETCH_SIZE, WRITE_SIZE, scaled by a plain device copy in the same run; see
+# profiles/pack_kernel_<workload>.txt). Valid only for the kernel source they
+# were taken on: reported as null once kernels.hip changes.
+MEASURED_TRAFFIC = {
+    "mixed": {"kernels_hip_sha256": None, "bytes_per_launch": None},
+}
 
 
 def log(msg):
@@ -84,97 +84,38 @@ def median(xs):
     return statistics.median(xs) if xs else float("nan")
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--schedule", choices=["exchange", "serial"], default="exchange",
-                    help="exchange: layer-pipelined kvx_exchange launches (zero-copy); serial: "
-                         "backup then restore on --path")
-    ap.add_argument("--path", choices=["staged", "zerocopy"], default="zerocopy",
-                    help="host path of the serial schedule")
-    ap.add_argument("--workload", default="llama8b")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-extras", action="store_true",
-                    help="skip the per-path, pipelined and latency measurements")
-    ap.add_argument("--kernel-only", action="store_true",
-                    help="time only the device pack/unpack kernels (for counter runs)")
-    ap.add_argument("--set", action="append", default=[], metavar="OPTION=VALUE",
-                    help="kvx_set_option before timing, e.g. --set hnd_lds=0 (names of the "
-                         "KVX_OPT_* constants, lower case); recorded in config.options")
-    ap.add_argument("--all-workloads", action="store_true",
-                    help="instead of the headline step, print one line per workload with its own "
-                         "figures (tiny: latency; mla: layer-0-ready; trtllm: HND rates; mixed: "
-                         "4 streams in flight)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(json.dumps({"error": "kvx moves KV between one GPU and its host tier; this benchmark "
-                                   "measures one GPU (run with --gpus 1)"}), flush=True)
-        sys.exit(2)
+def measured_traffic(workload):
+    """Counter traffic of the roofline kernel for this workload, if it was
+    taken on the kernel source in the tree."""
+    m = MEASURED_TRAFFIC.get(workload)
+    if not m or not m["kernels_hip_sha256"]:
+        return None
+    import hashlib
+    try:
+        with open(os.path.join(ROOT, "paged_kv_offload_amd", "csrc", "kernels.hip"), "rb") as f:
+            if hashlib.sha256(f.read()).hexdigest() == m["kernels_hip_sha256"]:
+                return m["bytes_per_launch"]
+    except OSError:
+        pass
+    return None
 
-    if args.all_workloads:
-        # The mixed leg keeps four requests in flight on four streams. HIP
-        # gives a process 4 hardware queues by default and streams share
-        # them round-robin; with the default stream that is five streams, so
-        # two requests would share a queue and run one after the other.
-        try:
-            queues = int(os.environ.get("GPU_MAX_HW_QUEUES", "4"))
-        except ValueError:
-            queues = 4
-        if queues < 8:
-            os.environ["GPU_MAX_HW_QUEUES"] = "8"   # read by the HIP runtime when torch loads it
 
-    import numpy as np
-    import torch
+class Timer:
+    """HIP events on one stream (torch.cuda.Event records on the stream it is
+    given, the stream the kernels run on)."""
 
-    import synth
-    from paged_kv_offload_amd import kvx as K
-    from synth.workloads import WORKLOADS
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    torch.cuda.set_device(0)
-    K.lib()
-    options = {}
-    for item in args.set:
-        name, _, value = item.partition("=")
-        const = getattr(K, "KVX_OPT_" + name.upper(), None)
-        if const is None or not value.lstrip("-").isdigit():
-            print(json.dumps({"error": f"--set {item}: unknown option or non-integer value"}), flush=True)
-            sys.exit(2)
-        K.kvx_set_option(const, int(value))
-        options[name.lower()] = int(value)
-    if args.all_workloads:
-        all_workloads()
-        return
-    w = WORKLOADS[args.workload]
-    n = w.pages_per_request
-    P = w.payload_bytes(n)
-    perm = synth.page_perm(w.seed, w.num_pages)
-    src = np.ascontiguousarray(perm[:n])
-    dst = np.ascontiguousarray(perm[n:2 * n])
-    stream = torch.cuda.Stream()
-    log(f"workload {w.name}: pool {w.pool_bytes / 2**30:.1f} GiB, payload {P / 2**30:.2f} GiB/op")
+    def ev(self):
+        return self.torch.cuda.Event(enable_timing=True)
 
-    # ---- pool in HBM, filled from the seeded generator ----
-    alloc = torch.empty(w.alloc_bytes, dtype=torch.uint8, device="cuda")
-    synth.fill_alloc_gpu(alloc.data_ptr(), w, w.seed)
-    dt = {1: torch.uint8, 2: torch.bfloat16}[w.dtype_bytes]
-    pool_t = alloc[w.byte_offset:w.byte_offset + w.pool_bytes].view(dt).view(*w.tensor_shape())
-    layout = K.make_layout(w.outer, w.inner, w.num_pages, w.num_layers, w.num_kv, w.page_size,
-                           w.num_heads, w.head_dim)
-    pool = K.register_tensor(pool_t, layout, 1)
-    dev_packed = torch.empty(P, dtype=torch.uint8, device="cuda")
-    torch.cuda.synchronize()
-
-    def ev():
-        return torch.cuda.Event(enable_timing=True)
-
-    def timed(fn, reps, s=stream):
-        """Per-repetition durations (s) from HIP events on stream s."""
+    def timed(self, fn, reps, s=None):
+        """Per-repetition durations (s) of fn, each between two events."""
+        s = s or self.stream
         out = []
         for _ in range(reps):
-            a, b = ev(), ev()
+            a, b = self.ev(), self.ev()
             a.record(s)
             fn()
             b.record(s)
@@ -182,12 +123,14 @@ def main():
             out.append(a.elapsed_time(b) / 1e3)
         return out
 
-    def batched(fn, reps, per=10, s=stream):
-        """Per-launch durations (s): HIP events on stream s around `per`
-        back-to-back calls, `reps` times."""
+    def batched(self, fn, reps, per=10, s=None):
+        """Per-launch durations (s): events around `per` back-to-back calls,
+        `reps` times. The host work of each call overlaps the previous
+        kernel, so the average is the kernel's own duration."""
+        s = s or self.stream
         out = []
         for _ in range(reps):
-            a, b = ev(), ev()
+            a, b = self.ev(), self.ev()
             a.record(s)
             for _ in range(per):
                 fn()
@@ -196,112 +139,353 @@ def main():
             out.append(a.elapsed_time(b) / 1e3 / per)
         return out
 
-    # ---- device pack / unpack kernels alone (HBM roofline) ----
-    # one launch packs the whole request: 32 layers x 2 x 256 pieces of 128 KiB
+    def stats(self, fn, warm=2, reps=10):
+        """(median, best) of `reps` timed calls after `warm` untimed ones."""
+        self.timed(fn, warm)
+        t = self.timed(fn, reps)
+        return median(t), min(t)
+
+
+def make_pool(K, synth, torch, w):
+    """The workload's allocation on cuda:0, filled from the seeded generator,
+    and the pool registered on it."""
+    alloc = torch.empty(w.alloc_bytes, dtype=torch.uint8, device="cuda")
+    synth.fill_alloc_gpu(alloc.data_ptr(), w, w.seed)
+    dt = {1: torch.uint8, 2: torch.bfloat16}[w.dtype_bytes]
+    t = alloc[w.byte_offset:w.byte_offset + w.pool_bytes].view(dt).view(*w.tensor_shape())
+    lay = K.make_layout(w.outer, w.inner, w.num_pages, w.num_layers, w.num_kv, w.page_size,
+                        w.num_heads, w.head_dim)
+    torch.cuda.synchronize()
+    return alloc, K.register_tensor(t, lay, 1)
+
+
+def device_kernels(T, K, torch, w, pool, src, dst, reps):
+    """The device pack and unpack kernels on one request (device path), the
+    unpack publishing every layer, and torch's D2D copy of the same bytes;
+    read + write bytes over the per-launch duration (HIP events around
+    back-to-back launches on the kernels' stream)."""
+    P = w.payload_bytes(len(src))
+    dev = torch.empty(P, dtype=torch.uint8, device="cuda")
+    ready = K.kvx_ready_create(w.num_layers, 1)
+
     def pack():
-        K.kvx_backup(pool, src, dev_packed, P, 0, w.num_layers, stream, K.KVX_PATH_DEVICE)
+        K.kvx_backup(pool, src, dev, P, 0, w.num_layers, T.stream, K.KVX_PATH_DEVICE)
 
     def unpack():
-        K.kvx_restore(pool, dev_packed, P, dst, 0, w.num_layers, None, 0, stream,
-                      K.KVX_PATH_DEVICE)
-
-    # events bracket a batch of back-to-back launches, so the host work of
-    # each call overlaps the previous kernel and the per-launch average is
-    # the kernel's own duration (what the kernel trace reports)
-    kreps = max(args.steps, 10)
-    timed(pack, 3)
-    t_pack = batched(pack, kreps)
-    timed(unpack, 3)
-    t_unpack = batched(unpack, kreps)
-    pack_gbs = 2 * P / median(t_pack) / GB
-    unpack_gbs = 2 * P / median(t_unpack) / GB
-    # the same unpack publishing every layer into a ready object (the
-    # queue-driven kernel: one count per layer and block of units)
-    ready_k = K.kvx_ready_create(w.num_layers, 1)
+        K.kvx_restore(pool, dev, P, dst, 0, w.num_layers, None, 0, T.stream, K.KVX_PATH_DEVICE)
 
     def unpack_publish():
-        K.kvx_restore(pool, dev_packed, P, dst, 0, w.num_layers, ready_k, 0, stream,
-                      K.KVX_PATH_DEVICE)
+        K.kvx_restore(pool, dev, P, dst, 0, w.num_layers, ready, 0, T.stream, K.KVX_PATH_DEVICE)
 
-    timed(unpack_publish, 3)
-    t_unpack_pub = batched(unpack_publish, kreps)
-    K.kvx_ready_destroy(ready_k)
-    unpack_pub_gbs = 2 * P / median(t_unpack_pub) / GB
-    log(f"device pack {median(t_pack) * 1e3:.3f} ms = {pack_gbs:.0f} GB/s (read+write); "
-        f"unpack {median(t_unpack) * 1e3:.3f} ms = {unpack_gbs:.0f} GB/s; "
-        f"unpack with per-layer publish {unpack_pub_gbs:.0f} GB/s")
+    out = {}
+    for name, fn in (("pack", pack), ("unpack", unpack), ("unpack_publish", unpack_publish)):
+        T.timed(fn, 3)
+        t = T.batched(fn, reps)
+        out[name] = {"gbs": round(2 * P / median(t) / GB, 1), "best_gbs": round(2 * P / min(t) / GB, 1),
+                     "frac": round(2 * P / median(t) / GB / HBM_PEAK_GBS, 4),
+                     "avg_launch_ms": round(median(t) * 1e3, 4)}
+    K.kvx_ready_destroy(ready)
+    copy = torch.empty(P, dtype=torch.uint8, device="cuda")
+    with torch.cuda.stream(T.stream):
+        T.timed(lambda: copy.copy_(dev), 2)
+        t = T.timed(lambda: copy.copy_(dev), 5)
+    out["d2d_copy_gbs"] = round(2 * P / median(t) / GB, 1)
+    del dev, copy
+    log(f"device kernels, {w.name}: " + ", ".join(
+        f"{k} {v['gbs'] if isinstance(v, dict) else v} GB/s" for k, v in out.items()))
+    return out
 
-    # a plain device-to-device copy of the same byte count (the in-run
-    # achievable line, and the calibration kernel for the traffic counters)
-    d2d_a = torch.empty(P, dtype=torch.uint8, device="cuda")
-    with torch.cuda.stream(stream):
-        timed(lambda: d2d_a.copy_(dev_packed), 2)
-        t_d2d = timed(lambda: d2d_a.copy_(dev_packed), 5)
-    d2d_gbs = 2 * P / median(t_d2d) / GB
-    del d2d_a
-    log(f"D2D copy {d2d_gbs:.0f} GB/s (read+write)")
-    traffic = None
-    try:
-        import hashlib
-        with open(os.path.join(ROOT, "paged_kv_offload_amd", "csrc", "kernels.hip"), "rb") as f:
-            if (hashlib.sha256(f.read()).hexdigest() == MEASURED_TRAFFIC["kernels_hip_sha256"]
-                    and w.name == MEASURED_TRAFFIC["workload"]):
-                traffic = MEASURED_TRAFFIC["bytes_per_launch"]
-    except OSError:
-        pass
-    roofline = {"bound": "hbm",
-                "kernel": f"kvx_move_kernel<GATHER> (pack of one {P / 2**30:.2f} GiB {w.name} request, "
-                          f"device path)",
-                "achieved": round(pack_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(pack_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                "algorithmic_bytes_per_launch": 2 * P,
-                "avg_launch_ms": round(median(t_pack) * 1e3, 4)}
-    if args.kernel_only:
-        print(json.dumps({"roofline": roofline, "unpack_gbs": round(unpack_gbs, 1),
-                          "unpack_publish_gbs": round(unpack_pub_gbs, 1),
-                          "d2d_copy_gbs": round(d2d_gbs, 1), "options": options}), flush=True)
-        return
 
-    # ---- pinned host-link peaks: 1 GiB hipMemcpyAsync, median of 10 ----
-    peak_bytes = 1 << 30
-    pin = torch.empty(peak_bytes, dtype=torch.uint8, pin_memory=True)
-    pin2 = torch.empty(peak_bytes, dtype=torch.uint8, pin_memory=True)
-    dev1 = torch.empty(peak_bytes, dtype=torch.uint8, device="cuda")
-    dev2 = torch.empty(peak_bytes, dtype=torch.uint8, device="cuda")
-    sb = torch.cuda.Stream()
-    with torch.cuda.stream(stream):
-        timed(lambda: pin.copy_(dev1, non_blocking=True), 2)
-        t_d2h = timed(lambda: pin.copy_(dev1, non_blocking=True), 10)
-        t_h2d = timed(lambda: dev1.copy_(pin, non_blocking=True), 10)
-    bidir = []
+def memcpy_peaks(T, torch, s2):
+    """Pinned hipMemcpyAsync peaks, 1 GiB: D2H and H2D (median of 10 each)
+    and both directions at once on two streams (median of 5)."""
+    n = 1 << 30
+    pin, pin2 = (torch.empty(n, dtype=torch.uint8, pin_memory=True) for _ in range(2))
+    dev1, dev2 = (torch.empty(n, dtype=torch.uint8, device="cuda") for _ in range(2))
+    with torch.cuda.stream(T.stream):
+        T.timed(lambda: pin.copy_(dev1, non_blocking=True), 2)
+        t_d2h = T.timed(lambda: pin.copy_(dev1, non_blocking=True), 10)
+        t_h2d = T.timed(lambda: dev1.copy_(pin, non_blocking=True), 10)
+    both = []
     for _ in range(5):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        with torch.cuda.stream(stream):
+        with torch.cuda.stream(T.stream):
             pin.copy_(dev1, non_blocking=True)
-        with torch.cuda.stream(sb):
+        with torch.cuda.stream(s2):
             dev2.copy_(pin2, non_blocking=True)
         torch.cuda.synchronize()
-        bidir.append(time.perf_counter() - t0)
-    d2h_peak = peak_bytes / median(t_d2h) / GB
-    h2d_peak = peak_bytes / median(t_h2d) / GB
-    bidir_peak = 2 * peak_bytes / median(bidir) / GB
+        both.append(time.perf_counter() - t0)
     del pin, pin2, dev1, dev2
-    log(f"pinned memcpy peak: D2H {d2h_peak:.1f} GB/s, H2D {h2d_peak:.1f} GB/s, "
-        f"both directions at once {bidir_peak:.1f} GB/s")
+    peaks = {"d2h": round(n / median(t_d2h) / GB, 2), "h2d": round(n / median(t_h2d) / GB, 2),
+             "both_directions": round(2 * n / median(both) / GB, 2)}
+    log(f"pinned memcpy peaks: {peaks}")
+    return peaks
 
-    # ---- the step ----
+
+# ---------------------------------------------------------------------------
+# the mixed hit/miss stream (default)
+# ---------------------------------------------------------------------------
+def mixed_main(args, options):
+    import numpy as np
+    import torch
+
+    import synth
+    from paged_kv_offload_amd import kvx as K
+    from synth.workloads import WORKLOADS, mixed_schedule
+
+    w = WORKLOADS["mixed"]
+    NL, n = w.num_layers, w.pages_per_request
+    P = w.payload_bytes()
+    R = 128
+    ZC = K.KVX_PATH_ZEROCOPY
+    sched = mixed_schedule(w, R)
+    perm = synth.page_perm(w.seed, w.num_pages)
+    stream = torch.cuda.Stream()
+    T = Timer(torch, stream)
+    log(f"workload {w.name}: pool {w.pool_bytes / 2**30:.0f} GiB, {R} requests of "
+        f"{P / 2**30:.2f} GiB per step")
+    alloc, pool = make_pool(K, synth, torch, w)
+
+    # ---- HBM roofline: the pack kernel on the stream's first request ----
+    kern = device_kernels(T, K, torch, w, pool, sched[0][1], sched[1][1], max(args.steps, 10))
+    roofline = {"bound": "hbm",
+                "kernel": f"kvx_move_kernel<GATHER> (device pack of one {P / 2**30:.0f} GiB request "
+                          f"of the mixed stream: 32 layers x K,V x 256 fragmented 128 KiB pieces)",
+                "achieved": kern["pack"]["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": kern["pack"]["frac"], "traffic": measured_traffic(w.name),
+                "algorithmic_bytes_per_launch": 2 * P,
+                "avg_launch_ms": kern["pack"]["avg_launch_ms"]}
+    if args.kernel_only:
+        print(json.dumps({"roofline": roofline, "device_kernels": kern, "options": options}), flush=True)
+        return
+
+    # ---- host buffers: four primed restore sources, four rotating backup targets ----
+    bufs = [K.HostBuffer(P) for _ in range(8)]
+    for r in range(4):
+        K.kvx_backup(pool, np.ascontiguousarray(perm[n * r:n * (r + 1)]), bufs[r].ptr, P, 0, NL,
+                     stream, ZC)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    peaks = memcpy_peaks(T, torch, streams[1])
+    proto = pcie_protocol_bound()
+
+    # ---- the headline schedule: backup k + restore k+1 in one kvx_exchange ----
+    pairs = [(sched[k][1], sched[k + 1][1]) for k in range(0, R, 2)]
+    assert all(sched[k][0] == "backup" and sched[k + 1][0] == "restore" for k in range(0, R, 2))
+    ready_x = K.kvx_ready_create(2 * NL, 1)     # slots [0, NL): stream 0's restores; [NL, 2NL): stream 1's
+    published = {"x": 0, "s": 0, "r": 0}        # pages published so far into each slot of each object
+
+    def exchange_pass(marks=None):
+        for i, (ib, ir) in enumerate(pairs):
+            s = streams[i % 2]
+            if marks is not None:
+                e0 = T.ev()
+                e0.record(s)
+            K.kvx_exchange(pool, ib, bufs[4 + i % 4].ptr, P, (0, NL), bufs[i % 4].ptr, P, ir, (0, NL),
+                           ready_x, NL * (i % 2), s, ZC)
+            if marks is not None:
+                e1 = T.ev()
+                e1.record(s)
+                marks.append((e0, e1))
+        published["x"] += len(pairs) // 2 * n
+        while K.kvx_ready_prefix(ready_x) < published["x"]:    # the consumers' view of completion
+            pass
+
+    # ---- the literal schedule: every request its own call, four streams ----
+    ready_s = K.kvx_ready_create(2 * NL, 1)     # restores run on streams 1 and 3
+
+    def streams_pass(bpath, rpath):
+        nb = nr = 0
+        for k, (kind, ids) in enumerate(sched):
+            s = streams[k % 4]
+            if kind == "backup":
+                K.kvx_backup(pool, ids, bufs[4 + nb % 4].ptr, P, 0, NL, s, bpath)
+                nb += 1
+            else:
+                K.kvx_restore(pool, bufs[nr % 4].ptr, P, ids, 0, NL, ready_s, NL * ((k % 4) // 2), s,
+                              rpath)
+                nr += 1
+        published["s"] += R // 4 * n
+        while K.kvx_ready_prefix(ready_s) < published["s"]:
+            pass
+
+    def run(pass_fn, steps, warmup):
+        for _ in range(warmup):
+            pass_fn()
+        torch.cuda.synchronize()
+        marks = []
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            pass_fn(marks) if pass_fn is exchange_pass else pass_fn()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, marks
+
+    if args.schedule == "exchange":
+        head_fn = exchange_pass
+        schedule = ("each backup paired with the restore after it in one kvx_exchange launch, pairs "
+                    "alternating over two streams (4 requests in flight); zero-copy; restores publish "
+                    "every layer; the host polls the ready prefix until the step's restores are published")
+    else:
+        head_fn = lambda marks=None: streams_pass(ZC, ZC)  # noqa: E731
+        schedule = ("every request its own zero-copy call, round-robin over four streams (4 in flight); "
+                    "restores publish every layer; the host polls the ready prefix")
+    wall, marks = run(head_fn, args.steps, args.warmup)
+    value = R * P * args.steps / wall / GB
+    ms_per_step = wall / args.steps * 1e3
+    log(f"mixed stream ({args.schedule}): {ms_per_step:.1f} ms per step -> {value:.2f} GB/s")
+
+    link = {"bound": "host link (PCIe 5.0 x16, both directions at once)",
+            "achieved": round(value, 2), "unit": "GB/s", "peak": 2 * PCIE_PEAK_GBS,
+            "frac": round(value / (2 * PCIE_PEAK_GBS), 4),
+            "protocol_bound": proto,
+            "frac_of_protocol_bound": round(value / proto["both_directions"], 4),
+            "measured_memcpy_peak": peaks,
+            "frac_of_measured_memcpy_both_directions": round(value / peaks["both_directions"], 4)}
+    if marks:
+        per = [a.elapsed_time(b) / 1e3 for a, b in marks]
+        link["exchange_launch_ms"] = {"median": round(median(per) * 1e3, 3),
+                                      "best": round(min(per) * 1e3, 3),
+                                      "two_launches_in_flight": True,
+                                      "bytes_per_launch": 2 * P}
+    result = {
+        "metric": "KV GB/s moved (backup D2H, restore H2D) + % of HBM / host-link roofline",
+        "value": round(value, 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "u8",
+        "data": "synthetic",
+        "config": {"workload": w.description, "requests_per_step": R, "in_flight": 4,
+                   "pages_per_request": n, "layers": NL, "payload_bytes_per_request": P,
+                   "bytes_per_step": R * P, "path": "zerocopy", "schedule": schedule,
+                   "hw_queues": os.environ.get("GPU_MAX_HW_QUEUES", "runtime default"),
+                   "options": options},
+        "roofline": roofline,
+        "device_kernels": kern,
+        "link_roofline": link,
+    }
+
+    if not args.no_extras:
+        other = {}
+        # the other way of running the same stream, one warm-up pass and two timed
+        for name, fn in ((("streams_zerocopy", lambda m=None: streams_pass(ZC, ZC))
+                          if args.schedule == "exchange" else ("exchange_paired", exchange_pass)),
+                         ("streams_staged", lambda m=None: streams_pass(K.KVX_PATH_STAGED,
+                                                                        K.KVX_PATH_STAGED))):
+            wl, _ = run(fn, 2, 1)
+            other[name] = round(R * P * 2 / wl / GB, 2)
+            log(f"mixed stream, {name}: {other[name]} GB/s")
+        # the same stream as descriptors through a submission ring, served on
+        # one stream by the library's executor (it pairs a backup with the
+        # restore after it by itself)
+        ready_r = K.kvx_ready_create(NL, 1)
+        rname = f"/kvx-bench-{os.getpid()}"
+        ring = K.kvx_ring_create(rname, 256, 1)
+        srv = K.kvx_ring_open(rname)
+        rbufs, rsizes = [b.ptr for b in bufs], [P] * len(bufs)
+
+        def ring_pass(m=None):
+            nb = nr = 0
+            for k, (kind, ids) in enumerate(sched):
+                if kind == "backup":
+                    q = K.make_sqe(K.KVX_OP_BACKUP, k, 1, 0, 4 + nb % 4, ids, 0, NL, ZC)
+                    nb += 1
+                else:
+                    q = K.make_sqe(K.KVX_OP_RESTORE, k, 1, 0, nr % 4, ids, 0, NL, ZC, ready_slot_base=0)
+                    nr += 1
+                K.kvx_ring_submit(ring, q)
+            done = []
+            while len(done) < len(sched):
+                K.kvx_ring_serve(srv, [pool], rbufs, rsizes, ready_r, streams[0], 256)
+                done += K.kvx_ring_reap(ring, 256)
+                time.sleep(0.0002)
+            assert all(c[2] == 0 for c in done), [c for c in done if c[2] != 0][:3]
+            published["r"] += R // 2 * n
+            assert K.kvx_ready_prefix(ready_r) == published["r"]
+
+        wl, _ = run(ring_pass, 2, 1)
+        other["ring_executor_paired"] = round(R * P * 2 / wl / GB, 2)
+        log(f"mixed stream, ring executor: {other['ring_executor_paired']} GB/s")
+        K.kvx_ring_close(srv)
+        K.kvx_ring_close(ring)
+        K.kvx_ready_destroy(ready_r)
+        result["other_schedules_gbs"] = other
+
+    K.kvx_ready_destroy(ready_x)
+    K.kvx_ready_destroy(ready_s)
+    for b in bufs:
+        b.free()
+    K.kvx_unregister_pool(pool)
+    del alloc
+    torch.cuda.empty_cache()
+
+    if not args.no_extras:
+        # the Llama-3-8B-shaped one-request step (layer-pipelined exchange)
+        sub = argparse.Namespace(**vars(args))
+        sub.steps, sub.warmup, sub.schedule, sub.no_extras = min(args.steps, 10), 2, "exchange", True
+        result["llama8b_request_step"] = single_main(sub, options, WORKLOADS["llama8b"], quiet=True)
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w)
+        log(f"cpu baseline: {result['cpu_baseline']}")
+        result["cpu_baseline_all_cores"] = cpu_baseline_all_cores(w)
+        log(f"cpu baseline, all cores: {result['cpu_baseline_all_cores']}")
+    print(json.dumps(result), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# one request of a single-request workload (llama8b, mla_fp8, trtllm_hnd, tiny)
+# ---------------------------------------------------------------------------
+def single_main(args, options, w, quiet=False):
+    """One step = BACKUP of one request to pinned host memory and its RESTORE
+    into other pages with per-layer publish, then the ready-prefix poll.
+    Schedule "exchange": the backup of layer 0, then one kvx_exchange per
+    layer that backs up layer l + 1 while it restores layer l (the restore
+    reads what the previous launch wrote), then the restore of the last
+    layer; zero-copy. Schedule "streams" runs the serial form: backup of
+    every layer, then restore of every layer. Returns the result (quiet) or
+    prints it."""
+    import numpy as np
+    import torch
+
+    import synth
+    from paged_kv_offload_amd import kvx as K
+
+    n = w.pages_per_request
+    P = w.payload_bytes(n)
+    perm = synth.page_perm(w.seed, w.num_pages)
+    src = np.ascontiguousarray(perm[:n])
+    dst = np.ascontiguousarray(perm[n:2 * n])
+    stream = torch.cuda.Stream()
+    T = Timer(torch, stream)
+    log(f"workload {w.name}: pool {w.pool_bytes / 2**30:.1f} GiB, payload {P / 2**30:.2f} GiB/op")
+    alloc, pool = make_pool(K, synth, torch, w)
+    kern = device_kernels(T, K, torch, w, pool, src, dst, max(args.steps, 10))
+    roofline = {"bound": "hbm",
+                "kernel": f"kvx_move_kernel<GATHER> (pack of one {P / 2**30:.2f} GiB {w.name} request, "
+                          f"device path)",
+                "achieved": kern["pack"]["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": kern["pack"]["frac"], "traffic": measured_traffic(w.name),
+                "algorithmic_bytes_per_launch": 2 * P, "avg_launch_ms": kern["pack"]["avg_launch_ms"]}
+    if args.kernel_only:
+        print(json.dumps({"roofline": roofline, "device_kernels": kern, "options": options}), flush=True)
+        return None
+
+    sb = torch.cuda.Stream()
+    peaks = memcpy_peaks(T, torch, sb)
     host = K.HostBuffer(P)
     ready = K.kvx_ready_create(w.num_layers, 1)
-    path = {"staged": K.KVX_PATH_STAGED, "zerocopy": K.KVX_PATH_ZEROCOPY}[args.path]
     layer_bytes = P // w.num_layers
+    published = [0]
 
-    # Serial schedule: BACKUP of every layer, then RESTORE of every layer.
-    # HIP events on the stream the kernels run on bracket the backup and the
-    # restore (on the zero-copy path each call is one kernel launch).
-    def serial_step(marks=None, path=path):
-        K.kvx_ready_reset(ready)
-        e = [ev() for _ in range(3)] if marks is not None else None
+    def serial_step(marks=None, path=K.KVX_PATH_ZEROCOPY):
+        e = [T.ev() for _ in range(3)] if marks is not None else None
         if e:
             e[0].record(stream)
         K.kvx_backup(pool, src, host.ptr, P, 0, w.num_layers, stream, path)
@@ -311,17 +495,12 @@ def main():
         if e:
             e[2].record(stream)
             marks.append(e)
-        while K.kvx_ready_prefix(ready) < n:    # the consumer's view of completion
+        published[0] += n
+        while K.kvx_ready_prefix(ready) < published[0]:    # the consumer's view of completion
             pass
 
-    # Layer-pipelined schedule on the zero-copy path: BACKUP of layer 0, then
-    # one kvx_exchange per layer that backs up layer l + 1 while it restores
-    # layer l (the restore reads what the previous launch wrote), then the
-    # RESTORE of the last layer. Same bytes, same results, per-layer publish;
-    # both directions of the host link carry data at once.
     def exchange_step(marks=None):
-        K.kvx_ready_reset(ready)
-        e = [ev() for _ in range(4)] if marks is not None else None
+        e = [T.ev() for _ in range(4)] if marks is not None else None
         if e:
             e[0].record(stream)
         K.kvx_backup(pool, src, host.ptr, P, 0, 1, stream, K.KVX_PATH_ZEROCOPY)
@@ -337,7 +516,8 @@ def main():
         if e:
             e[3].record(stream)
             marks.append(e)
-        while K.kvx_ready_prefix(ready) < n:
+        published[0] += n
+        while K.kvx_ready_prefix(ready) < published[0]:
             pass
 
     def run(step_fn, steps, warmup):
@@ -351,190 +531,67 @@ def main():
         torch.cuda.synchronize()
         return time.perf_counter() - t0, marks
 
-    serial_peak = 2 / (1 / d2h_peak + 1 / h2d_peak)
-
-    def serial_report(wall, marks, steps):
-        t_bk = median([m[0].elapsed_time(m[1]) / 1e3 for m in marks])
-        t_rs = median([m[1].elapsed_time(m[2]) / 1e3 for m in marks])
-        t_bk_best = min(m[0].elapsed_time(m[1]) / 1e3 for m in marks)
-        t_rs_best = min(m[1].elapsed_time(m[2]) / 1e3 for m in marks)
-        gbs = 2 * P * steps / wall / GB
-        return gbs, {
-            "gbs": round(gbs, 3), "ms_per_step": round(wall / steps * 1e3, 3),
-            "backup_achieved": round(P / t_bk / GB, 2), "restore_achieved": round(P / t_rs / GB, 2),
-            "backup_best": round(P / t_bk_best / GB, 2), "restore_best": round(P / t_rs_best / GB, 2),
-            "backup_frac_of_pcie": round(P / t_bk / GB / PCIE_PEAK_GBS, 4),
-            "restore_frac_of_pcie": round(P / t_rs / GB / PCIE_PEAK_GBS, 4),
-            "backup_frac_of_measured": round(P / t_bk / GB / d2h_peak, 4),
-            "restore_frac_of_measured": round(P / t_rs / GB / h2d_peak, 4),
-            "frac_of_serial_measured_peak": round(gbs / serial_peak, 4)}
-
-    def exchange_report(wall, marks, steps):
-        per = [m[1].elapsed_time(m[2]) / 1e3 / (w.num_layers - 1) for m in marks]
-        t_x, t_x_best = median(per), min(per)
-        t_b0 = median([m[0].elapsed_time(m[1]) / 1e3 for m in marks])
-        t_rl = median([m[2].elapsed_time(m[3]) / 1e3 for m in marks])
-        gbs = 2 * P * steps / wall / GB
-        both = 2 * PCIE_PEAK_GBS
-        return gbs, {
-            "gbs": round(gbs, 3), "ms_per_step": round(wall / steps * 1e3, 3),
-            "exchange_launch_ms": round(t_x * 1e3, 4),
-            "exchange_achieved": round(2 * layer_bytes / t_x / GB, 2),
-            "exchange_best": round(2 * layer_bytes / t_x_best / GB, 2),
-            "exchange_frac_of_pcie_both_directions": round(2 * layer_bytes / t_x / GB / both, 4),
-            "exchange_frac_of_measured_both_directions": round(2 * layer_bytes / t_x / GB / bidir_peak, 4),
-            "first_backup_gbs": round(layer_bytes / t_b0 / GB, 2),
-            "last_restore_gbs": round(layer_bytes / t_rl / GB, 2)}
-
-    if args.schedule == "exchange":
+    if args.schedule == "exchange" and w.num_layers > 1:
         wall, marks = run(exchange_step, args.steps, args.warmup)
-        value, main_rep = exchange_report(wall, marks, args.steps)
+        per = [m[1].elapsed_time(m[2]) / 1e3 / (w.num_layers - 1) for m in marks]
+        step = {"exchange_launch_ms": round(median(per) * 1e3, 4),
+                "exchange_achieved": round(2 * layer_bytes / median(per) / GB, 2),
+                "exchange_best": round(2 * layer_bytes / min(per) / GB, 2)}
         schedule = ("layer-pipelined: backup of layer 0, then one kvx_exchange per layer (backup of "
-                    "layer l+1 and restore of layer l in one launch), then restore of the last "
-                    "layer; zero-copy; the host waits for the ready prefix")
-        path_name = "zerocopy"
+                    "layer l+1 and restore of layer l in one launch), then restore of the last layer; "
+                    "zero-copy; the host waits for the ready prefix")
     else:
         wall, marks = run(serial_step, args.steps, args.warmup)
-        value, main_rep = serial_report(wall, marks, args.steps)
-        schedule = "backup then restore, host waits for the ready prefix"
-        path_name = args.path
-    ms_per_step = wall / args.steps * 1e3
-    log(f"step ({args.schedule}, {path_name}): {ms_per_step:.2f} ms -> {value:.2f} GB/s")
-
-    if args.schedule == "exchange":
-        link = {"bound": "host link (PCIe 5.0 x16, both directions at once)",
-                "kernels": "the step's kvx_exchange launches (zero-copy backup of one layer and restore "
-                           "of another in each), HIP events in the timed region",
-                "achieved": main_rep["exchange_achieved"], "best": main_rep["exchange_best"],
-                "unit": "GB/s", "peak": 2 * PCIE_PEAK_GBS,
-                "frac": main_rep["exchange_frac_of_pcie_both_directions"],
-                "frac_of_measured_both_directions": main_rep["exchange_frac_of_measured_both_directions"],
-                "step": main_rep}
-    else:
-        link = {"bound": "host link (PCIe 5.0 x16)",
-                "kernels": f"the step's {path_name} backup and restore, HIP events in the timed region",
-                "unit": "GB/s", "peak": PCIE_PEAK_GBS, "step": main_rep}
-    link["measured_memcpy_peak"] = {"d2h": round(d2h_peak, 2), "h2d": round(h2d_peak, 2),
-                                    "both_directions": round(bidir_peak, 2)}
-    proto = pcie_protocol_bound()
-    link["protocol_bound"] = proto
-    if args.schedule == "exchange":
-        link["frac_of_protocol_bound"] = round(main_rep["exchange_achieved"] / proto["both_directions"], 4)
-
+        t_bk = [m[0].elapsed_time(m[1]) / 1e3 for m in marks]
+        t_rs = [m[1].elapsed_time(m[2]) / 1e3 for m in marks]
+        step = {"backup_gbs": round(P / median(t_bk) / GB, 2), "backup_best": round(P / min(t_bk) / GB, 2),
+                "restore_gbs": round(P / median(t_rs) / GB, 2), "restore_best": round(P / min(t_rs) / GB, 2)}
+        schedule = "backup then restore (zero-copy), the host waits for the ready prefix"
+    value = 2 * P * args.steps / wall / GB
+    ms = wall / args.steps * 1e3
+    log(f"{w.name} step: {ms:.2f} ms -> {value:.2f} GB/s")
     result = {
         "metric": "KV GB/s moved (backup D2H, restore H2D) + % of HBM / host-link roofline",
-        "value": round(value, 3),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 3),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "u8",
-        "data": "synthetic",
+        "value": round(value, 3), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "u8", "data": "synthetic",
         "config": {"workload": w.description, "pages_per_request": n, "layers": w.num_layers,
-                   "payload_bytes_per_op": P, "path": path_name, "schedule": schedule,
+                   "payload_bytes_per_op": P, "path": "zerocopy", "schedule": schedule,
                    "options": options},
         "roofline": roofline,
-        "unpack_roofline": {"achieved": round(unpack_gbs, 1), "peak": HBM_PEAK_GBS,
-                            "unit": "GB/s", "frac": round(unpack_gbs / HBM_PEAK_GBS, 4),
-                            "with_per_layer_publish": {
-                                "achieved": round(unpack_pub_gbs, 1),
-                                "frac": round(unpack_pub_gbs / HBM_PEAK_GBS, 4)}},
-        "d2d_copy_gbs": round(d2d_gbs, 1),
-        "link_roofline": link,
+        "device_kernels": kern,
+        "link_roofline": {"bound": "host link (PCIe 5.0 x16)", "unit": "GB/s",
+                          "peak_both_directions": 2 * PCIE_PEAK_GBS, "step": step,
+                          "measured_memcpy_peak": peaks, "protocol_bound": pcie_protocol_bound()},
     }
 
     if not args.no_extras:
-        # the other schedule, same number of steps
-        if args.schedule == "exchange":
-            wall2, marks2 = run(lambda m=None: serial_step(m, K.KVX_PATH_ZEROCOPY), args.steps, 1)
-            _, rep2 = serial_report(wall2, marks2, args.steps)
-            result["link_roofline"]["serial_step_zerocopy"] = rep2
-        else:
-            wall2, marks2 = run(exchange_step, args.steps, 1)
-            _, rep2 = exchange_report(wall2, marks2, args.steps)
-            result["link_roofline"]["exchange_step"] = rep2
-        log(f"other schedule: {rep2['gbs']} GB/s")
-
-    if not args.no_extras:
-        extras = {}
+        # each host path per direction: 2 warm-up and 10 timed calls, median and best
+        per_path = {}
         for name, pth in (("staged", K.KVX_PATH_STAGED), ("zerocopy", K.KVX_PATH_ZEROCOPY)):
             b = lambda: K.kvx_backup(pool, src, host.ptr, P, 0, w.num_layers, stream, pth)  # noqa
-            r = lambda: K.kvx_restore(pool, host.ptr, P, dst, 0, w.num_layers, ready, 0,  # noqa
+            r = lambda: K.kvx_restore(pool, host.ptr, P, dst, 0, w.num_layers, None, 0,  # noqa
                                       stream, pth)
-            timed(b, 1)
-            tb = timed(b, 3)
-            timed(r, 1)
-            tr = timed(r, 3)
-            extras[name] = {"backup_gbs": round(P / median(tb) / GB, 2),
-                            "backup_frac_d2h_peak": round(P / median(tb) / GB / d2h_peak, 4),
-                            "restore_gbs": round(P / median(tr) / GB, 2),
-                            "restore_frac_h2d_peak": round(P / median(tr) / GB / h2d_peak, 4)}
-            log(f"{name}: backup {extras[name]['backup_gbs']} GB/s, "
-                f"restore {extras[name]['restore_gbs']} GB/s")
-        result["link_roofline"]["per_path"] = extras
-
-        # layer-pipelined: restore of layer group g runs on a second stream
-        # while group g+1 is backed up, so both link directions carry data
-        def pipelined(pth, group=2):
-            K.kvx_ready_reset(ready)
-            for l0 in range(0, w.num_layers, group):
-                l1 = min(w.num_layers, l0 + group)
-                K.kvx_backup(pool, src, host.ptr, P, l0, l1, stream, pth)
-                e = torch.cuda.Event()
-                e.record(stream)
-                sb.wait_event(e)
-                K.kvx_restore(pool, host.ptr, P, dst, l0, l1, ready, 0, sb, pth)
-            while K.kvx_ready_prefix(ready) < n:
-                pass
-        pipe = {}
-        for name, pth in (("staged", K.KVX_PATH_STAGED), ("zerocopy", K.KVX_PATH_ZEROCOPY)):
-            pipelined(pth)
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(3):
-                pipelined(pth)
-            torch.cuda.synchronize()
-            pipe[name] = round(2 * P * 3 / (time.perf_counter() - t0) / GB, 2)
-        # the same schedule in one stream with kvx_exchange: each launch
-        # backs up layer group g + 1 while it restores group g
-        def exchanged(group):
-            K.kvx_ready_reset(ready)
-            G = (w.num_layers + group - 1) // group
-            rng = lambda g: (g * group, min(w.num_layers, (g + 1) * group))  # noqa: E731
-            K.kvx_backup(pool, src, host.ptr, P, *rng(0), stream, K.KVX_PATH_ZEROCOPY)
-            for g in range(1, G):
-                K.kvx_exchange(pool, src, host.ptr, P, rng(g), host.ptr, P, dst, rng(g - 1),
-                               ready, 0, stream, K.KVX_PATH_ZEROCOPY)
-            K.kvx_restore(pool, host.ptr, P, dst, *rng(G - 1), ready, 0, stream,
-                          K.KVX_PATH_ZEROCOPY)
-            while K.kvx_ready_prefix(ready) < n:
-                pass
-        for group in (1, 2, 4):
-            exchanged(group)
-            torch.cuda.synchronize()
-            t0 = time.perf_counter()
-            for _ in range(3):
-                exchanged(group)
-            torch.cuda.synchronize()
-            pipe[f"zerocopy_exchange_group{group}"] = round(2 * P * 3 / (time.perf_counter() - t0) / GB, 2)
-        result["layer_pipelined_gbs"] = pipe
-        log(f"layer-pipelined step: {pipe}")
-
+            tb, tb_best = T.stats(b)
+            tr, tr_best = T.stats(r)
+            per_path[name] = {"backup_gbs": round(P / tb / GB, 2), "backup_best": round(P / tb_best / GB, 2),
+                              "backup_frac_d2h_peak": round(P / tb / GB / peaks["d2h"], 4),
+                              "restore_gbs": round(P / tr / GB, 2), "restore_best": round(P / tr_best / GB, 2),
+                              "restore_frac_h2d_peak": round(P / tr / GB / peaks["h2d"], 4)}
+            log(f"{name}: {per_path[name]}")
+        result["link_roofline"]["per_path"] = per_path
         # layer-0-ready latency of a restore: the CPU polls layer 0's count
         lat = {}
         for name, pth in (("staged", K.KVX_PATH_STAGED), ("zerocopy", K.KVX_PATH_ZEROCOPY)):
-            K.kvx_ready_reset(ready)
             torch.cuda.synchronize()
+            base = K.kvx_layer_ready(ready, 0)
             t0 = time.perf_counter()
             K.kvx_restore(pool, host.ptr, P, dst, 0, w.num_layers, ready, 0, stream, pth)
-            while K.kvx_layer_ready(ready, 0) < n:
+            while K.kvx_layer_ready(ready, 0) < base + n:
                 pass
             t_l0 = time.perf_counter() - t0
-            while K.kvx_ready_prefix(ready) < n:
+            published[0] += n
+            while K.kvx_ready_prefix(ready) < published[0]:
                 pass
             t_all = time.perf_counter() - t0
             stream.synchronize()
@@ -542,18 +599,23 @@ def main():
         result["restore_ready_latency"] = lat
         log(f"restore ready latency: {lat}")
 
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w)
-        log(f"cpu baseline: {result['cpu_baseline']}")
-        result["cpu_baseline_all_cores"] = cpu_baseline_all_cores(w)
-        log(f"cpu baseline, all cores: {result['cpu_baseline_all_cores']}")
-    print(json.dumps(result), flush=True)
-
     K.kvx_ready_destroy(ready)
     K.kvx_unregister_pool(pool)
     host.free()
+    del alloc
+    torch.cuda.empty_cache()
+    if quiet:
+        return result
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w)
+        result["cpu_baseline_all_cores"] = cpu_baseline_all_cores(w)
+    print(json.dumps(result), flush=True)
+    return None
 
 
+# ---------------------------------------------------------------------------
+# --all-workloads: one line per other workload
+# ---------------------------------------------------------------------------
 def all_workloads():
     """One JSON line per workload with the figures that workload is measured
     by (latency for the tiny pool, layer-0-ready latency for the layer-wise
@@ -853,126 +915,6 @@ def all_workloads():
     del alloc
     torch.cuda.empty_cache()
 
-    # ---- mixed: 128 alternating requests, four in flight on four streams ----
-    w = WORKLOADS["mixed"]
-    P = w.payload_bytes()
-    alloc, pool = make_pool(w)
-    perm = synth.page_perm(w.seed, w.num_pages)
-    prime = [np.ascontiguousarray(perm[256 * r:256 * (r + 1)]) for r in range(4)]
-    slots = [K.HostBuffer(P) for _ in range(8)]
-    streams = [torch.cuda.Stream() for _ in range(4)]
-    for r in range(4):
-        K.kvx_backup(pool, prime[r], slots[r].ptr, P, 0, w.num_layers, streams[0],
-                     K.KVX_PATH_ZEROCOPY)
-    torch.cuda.synchronize()
-    sched = mixed_schedule(w, 128)
-    res = {"workload": w.description, "requests": 128, "in_flight": 4,
-           "bytes_total": 128 * P, "unit": "GB/s",
-           "hw_queues": os.environ.get("GPU_MAX_HW_QUEUES", "runtime default")}
-    # both directions at once with plain copies: the peak the mixed stream is
-    # measured against
-    GiB = 1 << 30
-    pin_a = torch.empty(GiB, dtype=torch.uint8, pin_memory=True)
-    pin_b = torch.empty(GiB, dtype=torch.uint8, pin_memory=True)
-    dev_a = torch.empty(GiB, dtype=torch.uint8, device="cuda")
-    dev_b = torch.empty(GiB, dtype=torch.uint8, device="cuda")
-    bid = []
-    for _ in range(4):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        with torch.cuda.stream(streams[0]):
-            pin_a.copy_(dev_a, non_blocking=True)
-        with torch.cuda.stream(streams[1]):
-            dev_b.copy_(pin_b, non_blocking=True)
-        torch.cuda.synchronize()
-        bid.append(2 * GiB / (time.perf_counter() - t0) / GB)
-    del pin_a, pin_b, dev_a, dev_b
-    res["memcpy_both_directions_gbs"] = round(statistics.median(bid[1:]), 2)
-    # backup k and restore k + 1 of the schedule as one kvx_exchange, the
-    # pairs round-robin on two streams (four requests in flight)
-    def run_exchange():
-        nb = nr = 0
-        pairs = [(sched[k], sched[k + 1]) for k in range(0, len(sched), 2)]
-        for i, ((kb, ib), (kr, ir)) in enumerate(pairs):
-            assert kb == "backup" and kr == "restore"
-            K.kvx_exchange(pool, ib, slots[4 + nb % 4].ptr, P, (0, w.num_layers), slots[nr % 4].ptr,
-                           P, ir, (0, w.num_layers), None, 0, streams[i % 2], K.KVX_PATH_ZEROCOPY)
-            nb += 1
-            nr += 1
-        torch.cuda.synchronize()
-    run_exchange()
-    t0 = time.perf_counter()
-    run_exchange()
-    res["zerocopy_exchange"] = round(128 * P / (time.perf_counter() - t0) / GB, 2)
-    res["zerocopy_exchange_frac_of_memcpy_both_directions"] = round(
-        res["zerocopy_exchange"] / res["memcpy_both_directions_gbs"], 4)
-    log(f"mixed zerocopy_exchange: {res['zerocopy_exchange']} GB/s")
-    # the same schedule as descriptors through a submission ring, served on
-    # one stream by the library's executor; with pairing on it runs each
-    # backup and the restore after it as one exchange by itself
-    rname = f"/kvx-bench-mixed-{os.getpid()}"
-    ring = K.kvx_ring_create(rname, 256, 1)
-    srv = K.kvx_ring_open(rname)
-    rbufs, rsizes = [h.ptr for h in slots], [P] * len(slots)
-
-    def run_ring():
-        nb = nr = 0
-        for k, (kind, ids) in enumerate(sched):
-            if kind == "backup":
-                q = K.make_sqe(K.KVX_OP_BACKUP, k, 1, 0, 4 + nb % 4, ids, 0, w.num_layers,
-                               K.KVX_PATH_ZEROCOPY)
-                nb += 1
-            else:
-                q = K.make_sqe(K.KVX_OP_RESTORE, k, 1, 0, nr % 4, ids, 0, w.num_layers,
-                               K.KVX_PATH_ZEROCOPY)
-                nr += 1
-            K.kvx_ring_submit(ring, q)
-        done = []
-        while len(done) < len(sched):
-            K.kvx_ring_serve(srv, [pool], rbufs, rsizes, None, streams[0], 256)
-            done += K.kvx_ring_reap(ring, 256)
-            time.sleep(0.0002)
-        assert all(c[2] == 0 for c in done), [c for c in done if c[2] != 0][:3]
-
-    for pairing in (1, 0):
-        K.kvx_set_option(K.KVX_OPT_RING_PAIRING, pairing)
-        run_ring()
-        t0 = time.perf_counter()
-        run_ring()
-        key = "ring_zerocopy_paired" if pairing else "ring_zerocopy_one_by_one"
-        res[key] = round(128 * P / (time.perf_counter() - t0) / GB, 2)
-        log(f"mixed {key}: {res[key]} GB/s")
-    K.kvx_set_option(K.KVX_OPT_RING_PAIRING, 1)
-    K.kvx_ring_close(srv)
-    K.kvx_ring_close(ring)
-    for name, bpath, rpath in (("zerocopy", K.KVX_PATH_ZEROCOPY, K.KVX_PATH_ZEROCOPY),
-                               ("staged", K.KVX_PATH_STAGED, K.KVX_PATH_STAGED),
-                               ("zerocopy_backup_staged_restore", K.KVX_PATH_ZEROCOPY,
-                                K.KVX_PATH_STAGED)):
-        def run():
-            nb = nr = 0
-            for k, (kind, ids) in enumerate(sched):
-                s = streams[k % 4]
-                if kind == "backup":
-                    K.kvx_backup(pool, ids, slots[4 + nb % 4].ptr, P, 0, w.num_layers, s, bpath)
-                    nb += 1
-                else:
-                    K.kvx_restore(pool, slots[nr % 4].ptr, P, ids, 0, w.num_layers, None, 0, s,
-                                  rpath)
-                    nr += 1
-            torch.cuda.synchronize()
-        run()
-        t0 = time.perf_counter()
-        run()
-        res[name] = round(128 * P / (time.perf_counter() - t0) / GB, 2)
-        res[name + "_frac_of_memcpy_both_directions"] = round(
-            res[name] / res["memcpy_both_directions_gbs"], 4)
-        log(f"mixed {name}: {res[name]} GB/s")
-    print(json.dumps({"mixed": res}), flush=True)
-    for h in slots:
-        h.free()
-    K.kvx_unregister_pool(pool)
-
 
 def cpu_baseline(w, budget_s: float = 12.0):
     """The oracle's backup + restore byte loops, single-threaded, on a host
@@ -987,12 +929,7 @@ def cpu_baseline(w, budget_s: float = 12.0):
     n = w.pages_per_request
     nl = min(w.num_layers, 4)
     sample = w.scaled(num_pages=2 * n, num_layers=nl)
-    L = oracle.Layout(outer=tuple({"page": oracle.PAGE, "layer": oracle.LAYER,
-                                   "kv": oracle.KV}[a] for a in sample.outer),
-                      inner=oracle.NHD if sample.inner == "NHD" else oracle.HND,
-                      num_pages=sample.num_pages, num_layers=nl, num_kv=sample.num_kv,
-                      page_size=sample.page_size, num_heads=sample.num_heads,
-                      head_dim=sample.head_dim, dtype_bytes=sample.dtype_bytes)
+    L = oracle_layout_of(oracle, sample)
     # only the shape matters for the timing; the bytes are a constant pattern
     alloc = np.full(sample.pool_bytes, 0x5A, dtype=np.uint8)
     perm = synth.page_perm(w.seed, 2 * n)
@@ -1015,6 +952,15 @@ def cpu_baseline(w, budget_s: float = 12.0):
             "cpu_model": cpu_model()}
 
 
+def oracle_layout_of(oracle, w):
+    return oracle.Layout(outer=tuple({"page": oracle.PAGE, "layer": oracle.LAYER,
+                                      "kv": oracle.KV}[a] for a in w.outer),
+                         inner=oracle.NHD if w.inner == "NHD" else oracle.HND,
+                         num_pages=w.num_pages, num_layers=w.num_layers, num_kv=w.num_kv,
+                         page_size=w.page_size, num_heads=w.num_heads, head_dim=w.head_dim,
+                         dtype_bytes=w.dtype_bytes)
+
+
 def cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -1027,11 +973,13 @@ def cpu_model():
 
 def cpu_baseline_all_cores(w, budget_s: float = 8.0, max_threads: int = 16):
     """The same oracle calls from one host thread per core (the process's
-    affinity set, at most max_threads): each thread owns a one-layer host
-    pool and packed buffer of the workload's piece shape and runs
-    backup + restore passes for about budget_s seconds. The oracle's C
-    functions run without the interpreter lock, so the threads run in
-    parallel; the oracle itself is unchanged."""
+    affinity set, at most max_threads) over the pieces of ONE host pool:
+    the pool and its packed buffer have one layer per thread, and thread k
+    runs backup + restore passes of layer k (its own pieces of the pool and
+    its own slice of the packed buffer, so no two threads touch the same
+    bytes) for about budget_s seconds. The oracle's C functions run without
+    the interpreter lock, so the threads run in parallel; the oracle itself
+    is unchanged."""
     import threading
 
     import numpy as np
@@ -1041,13 +989,10 @@ def cpu_baseline_all_cores(w, budget_s: float = 8.0, max_threads: int = 16):
 
     threads = max(1, min(max_threads, len(os.sched_getaffinity(0))))
     n = w.pages_per_request
-    sample = w.scaled(num_pages=2 * n, num_layers=1)
-    L = oracle.Layout(outer=tuple({"page": oracle.PAGE, "layer": oracle.LAYER,
-                                   "kv": oracle.KV}[a] for a in sample.outer),
-                      inner=oracle.NHD if sample.inner == "NHD" else oracle.HND,
-                      num_pages=sample.num_pages, num_layers=1, num_kv=sample.num_kv,
-                      page_size=sample.page_size, num_heads=sample.num_heads,
-                      head_dim=sample.head_dim, dtype_bytes=sample.dtype_bytes)
+    sample = w.scaled(num_pages=2 * n, num_layers=threads)
+    L = oracle_layout_of(oracle, sample)
+    alloc = np.full(sample.pool_bytes, 0x5A, dtype=np.uint8)
+    host = np.zeros(sample.host_bytes(n), dtype=np.uint8)
     perm = synth.page_perm(w.seed, 2 * n)
     src, dst = perm[:n].copy(), perm[n:].copy()
     per_pass = 2 * sample.num_kv * n * sample.piece_bytes
@@ -1056,12 +1001,10 @@ def cpu_baseline_all_cores(w, budget_s: float = 8.0, max_threads: int = 16):
     stop = threading.Event()
 
     def worker(k):
-        alloc = np.full(sample.pool_bytes, 0x5A, dtype=np.uint8)
-        host = np.zeros(sample.host_bytes(n), dtype=np.uint8)
         start.wait()
         while not stop.is_set():
-            oracle.backup(L, alloc, src, 0, 1, host=host)
-            oracle.restore(L, alloc, host, dst, 0, 1, out=alloc)
+            oracle.backup(L, alloc, src, k, k + 1, host=host)
+            oracle.restore(L, alloc, host, dst, k, k + 1, out=alloc)
             passes[k] += 1
 
     ths = [threading.Thread(target=worker, args=(k,)) for k in range(threads)]
@@ -1077,9 +1020,75 @@ def cpu_baseline_all_cores(w, budget_s: float = 8.0, max_threads: int = 16):
     moved = sum(passes) * per_pass
     return {"value": round(moved / t / GB, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{sum(passes)} single-layer backup+restore passes of {n} fragmented pages x "
-                      f"{sample.num_kv} x {sample.piece_bytes} B pieces, one {2 * n}-page host pool "
-                      f"per thread ({moved / GB:.2f} GB moved in {t:.1f} s)",
+                      f"{sample.num_kv} x {sample.piece_bytes} B pieces over one {2 * n}-page, "
+                      f"{threads}-layer host pool, one layer per thread ({moved / GB:.2f} GB moved "
+                      f"in {t:.1f} s)",
             "cpu_model": cpu_model()}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="mixed",
+                    help="mixed (the 128-request hit/miss stream, default) or a single-request "
+                         "workload: llama8b, mla_fp8, trtllm_hnd, tiny")
+    ap.add_argument("--schedule", choices=["exchange", "streams"], default="exchange",
+                    help="mixed: exchange = backup + next restore in one kvx_exchange on two streams, "
+                         "streams = one call per request on four streams; single-request workloads: "
+                         "exchange = layer-pipelined, streams = serial backup then restore")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the other schedules, the per-path rates and the latency legs")
+    ap.add_argument("--kernel-only", action="store_true",
+                    help="time only the device pack/unpack kernels (for counter runs)")
+    ap.add_argument("--set", action="append", default=[], metavar="OPTION=VALUE",
+                    help="kvx_set_option before timing, e.g. --set hnd_lds=0 (names of the "
+                         "KVX_OPT_* constants, lower case); recorded in config.options")
+    ap.add_argument("--all-workloads", action="store_true",
+                    help="instead of the headline, print one line per other workload with its own "
+                         "figures (tiny: latency; mla: layer-0-ready; trtllm: HND rates; host tier)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "kvx moves KV between one GPU and its host tier; this benchmark "
+                                   "measures one GPU (run with --gpus 1)"}), flush=True)
+        sys.exit(2)
+
+    # The mixed stream keeps requests in flight on several streams. HIP gives
+    # a process 4 hardware queues by default and streams share them
+    # round-robin; with the default stream, five streams would put two
+    # requests on one queue, and those run one after the other.
+    try:
+        queues = int(os.environ.get("GPU_MAX_HW_QUEUES", "4"))
+    except ValueError:
+        queues = 4
+    if queues < 8:
+        os.environ["GPU_MAX_HW_QUEUES"] = "8"   # read by the HIP runtime when torch loads it
+
+    import torch
+
+    from paged_kv_offload_amd import kvx as K
+    from synth.workloads import WORKLOADS
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    K.lib()
+    options = {}
+    for item in args.set:
+        name, _, value = item.partition("=")
+        const = getattr(K, "KVX_OPT_" + name.upper(), None)
+        if const is None or not value.lstrip("-").isdigit():
+            print(json.dumps({"error": f"--set {item}: unknown option or non-integer value"}), flush=True)
+            sys.exit(2)
+        K.kvx_set_option(const, int(value))
+        options[name.lower()] = int(value)
+    if args.all_workloads:
+        all_workloads()
+    elif args.workload == "mixed":
+        mixed_main(args, options)
+    else:
+        single_main(args, options, WORKLOADS[args.workload])
 
 
 if __name__ == "__main__":
