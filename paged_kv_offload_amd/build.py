@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libkvx.so")
-SOURCES = ["api.cpp", "geometry.cpp", "pages.cpp", "ipc.cpp", "ready.cpp", "tier.cpp", "ring.cpp", "tier_policy.cpp", "ring_exec.cpp", "kernels.hip"]
+SOURCES = ["api.cpp", "geometry.cpp", "pages.cpp", "ipc.cpp", "ready.cpp", "tier.cpp", "ring.cpp", "tier_policy.cpp", "ring_exec.cpp", "kernels.hip", "noalloc.hip"]
 ARCH = "gfx950"
 # packed-fp32 instructions are disabled for all device code
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wextra",

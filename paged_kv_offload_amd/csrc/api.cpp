@@ -415,9 +415,10 @@ void set_publish(const Publish* pub, PublishArgs* p)
     p->block = 1;
 }
 
+// pairs: (page, slot) in visiting order; NULL: ids[i] in slot i, caller order.
 int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, int32_t lb,
                  const PageSlot* pairs, size_t npairs, const Publish* pub, const Tuning& t,
-                 int cu_count, hipStream_t s)
+                 int cu_count, hipStream_t s, const int32_t* ids = nullptr)
 {
     const PoolGeom& g = pool->geom;
     MoveArgs a;
@@ -446,8 +447,8 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
     for (size_t p0 = 0; p0 < npairs; p0 += per_launch) {
         const size_t np = std::min<size_t>(per_launch, npairs - p0);
         for (size_t j = 0; j < np; j++) {
-            a.pairs[2 * j] = pairs[p0 + j].page;
-            a.pairs[2 * j + 1] = pairs[p0 + j].slot;
+            a.pairs[2 * j] = pairs ? pairs[p0 + j].page : ids[p0 + j];
+            a.pairs[2 * j + 1] = pairs ? pairs[p0 + j].slot : static_cast<int32_t>(p0 + j);
         }
         a.s.npairs = static_cast<uint32_t>(np);
         const int64_t per_layer = g.num_kv * static_cast<int64_t>(np) * a.g.chunks_per_piece;
@@ -1049,6 +1050,66 @@ int kvx_restore(kvx_pool* pool, const void* src, uint64_t src_bytes, const int32
     const TraceRange tr("kvx_restore");
     return run_op(pool, SCATTER, page_ids, n, const_cast<void*>(src), src_bytes, layer_begin,
                 layer_end, ready, slot_base, stream, path);
+}
+
+int kvx_restore_noalloc(kvx_pool* pool, const void* src, uint64_t src_bytes, const int32_t* page_ids,
+                        int32_t n, int32_t layer_begin, int32_t layer_end, kvx_ready* ready,
+                        int32_t slot_base, void* stream, int32_t path)
+{
+    const TraceRange tr("kvx_restore_noalloc");
+    clear_error();
+    if (!pool_known(pool)) return fail(KVX_E_INVAL, "restore_noalloc: unknown pool handle");
+    if (!pool->live.load()) return fail(KVX_E_STALE, "restore_noalloc: pool handle was unregistered");
+    if (path != KVX_PATH_ZEROCOPY && path != KVX_PATH_DEVICE)
+        return fail(KVX_E_INVAL, "restore_noalloc: runs on the zero-copy or device path (the staged "
+                                 "path needs the library's staging ring)");
+    if (pool->geom.num_layers > kNoAllocMaxLayers)
+        return fail(KVX_E_RANGE, "restore_noalloc: the pool has " + std::to_string(pool->geom.num_layers) +
+                                     " layers; its scratch serves at most " +
+                                     std::to_string(kNoAllocMaxLayers));
+    bool active = false;
+    int rc = validate_side(pool, SCATTER, page_ids, n, src, src_bytes, layer_begin, layer_end, ready,
+                           slot_base, "restore_noalloc", &active);
+    if (rc != KVX_OK || !active) return rc;
+
+    // ---- HIP from here on; nothing has been enqueued yet ----
+    rc = resolve_device(pool);
+    if (rc != KVX_OK) return rc;
+    if (ready && ready->device >= 0 && ready->device != pool->device)
+        return fail(KVX_E_INVAL, "restore_noalloc: the ready object's counts are on GPU " +
+                                     std::to_string(ready->device) + ", the pool on GPU " +
+                                     std::to_string(pool->device));
+    DeviceGuard dg(pool->device);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* view = nullptr;
+    rc = check_packed_kind(pool, const_cast<void*>(src), path, "restore_noalloc", &view);
+    if (rc != KVX_OK) return rc;
+    int cu_count = 0;
+    KVX_HIP(hipDeviceGetAttribute(&cu_count, hipDeviceAttributeMultiprocessorCount, pool->device));
+    const Tuning t = tuning();
+    const PoolGeom& g = pool->geom;
+    Publish pub;
+    const Publish* pubp = nullptr;
+    if (ready) {
+        uint32_t* scratch = nullptr;
+        rc = noalloc_scratch(pool->device, &scratch);
+        if (rc != KVX_OK) return rc;
+        // the counters and the queue start at zero in stream order (a kernel,
+        // not a memset node, for callers that capture the stream)
+        KVX_HIP(launch_clear_u32(scratch, static_cast<uint32_t>(g.num_layers), s));
+        KVX_HIP(launch_clear_u32(scratch + kNoAllocMaxLayers, 1, s));
+        const int64_t chunk = int64_t(kThreads) * kVecBytes * unroll_for(g, t, path == KVX_PATH_ZEROCOPY);
+        pub.layer_done = scratch;
+        pub.queue = scratch + kNoAllocMaxLayers;
+        pub.ready = ready->counts_dev + slot_base;
+        pub.layer_target = static_cast<uint32_t>(g.num_kv * int64_t(n) * ((g.piece_bytes + chunk - 1) / chunk));
+        pub.value = static_cast<uint32_t>(n);
+        pubp = &pub;
+    }
+    // pages in the caller's order, page_ids[i] from packed slot i
+    const Target tg{view, 0, 0, int64_t(n), path == KVX_PATH_ZEROCOPY};
+    return launch_range(SCATTER, pool, tg, layer_begin, layer_end, nullptr, static_cast<size_t>(n), pubp,
+                        t, cu_count, s, page_ids);
 }
 
 int kvx_backup_slots(kvx_pool* pool, const int32_t* page_ids, const int32_t* host_slots, int32_t n,

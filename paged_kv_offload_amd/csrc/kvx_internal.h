@@ -102,6 +102,10 @@ constexpr int kMaxPairs = 448;       // (page, slot) pairs carried in the kernel
 constexpr int kHostGridAuto = 32;    // default workgroups of a kernel streaming over the host link
 constexpr int64_t kRestoreChunkMin = 32ll << 20;   // default minimum staged restore chunk
 constexpr int64_t kPublishBlockBytes = 2ll << 20;  // auto publish block: about this many bytes
+// kvx_restore_noalloc: layers of a pool it serves, and the words of its device
+// scratch (one counter per layer, the unit queue, padding)
+constexpr int64_t kNoAllocMaxLayers = KVX_NOALLOC_MAX_LAYERS;
+constexpr int64_t kNoAllocScratchWords = kNoAllocMaxLayers + 64;
 
 enum Dir : int32_t { GATHER = 0, SCATTER = 1 };
 
@@ -211,6 +215,9 @@ hipError_t launch_move(Dir dir, const LaunchCfg& cfg, const MoveArgs& a, hipStre
 hipError_t launch_exchange(const LaunchCfg& cfg, const ExchangeArgs& a, hipStream_t s);
 hipError_t launch_exchange(const LaunchCfg& cfg, const ExchangeSlotArgs& a, hipStream_t s);
 hipError_t launch_clear_u32(uint32_t* p, uint32_t count, hipStream_t s);
+// Device address of this GPU's copy of the no-alloc scratch (looked up once
+// per device, with the device current).
+int noalloc_scratch(int device, uint32_t** out);
 hipError_t launch_ready_wait(const uint32_t* slot, uint32_t min_count, uint32_t spin_limit,
                              int32_t* status, hipStream_t s);
 

@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvx.so")
 KVX_OK = 0
 KVX_E_INVAL, KVX_E_NONCONTIG, KVX_E_ALIGN, KVX_E_RANGE, KVX_E_DUP = -1, -2, -3, -4, -5
 KVX_E_STALE, KVX_E_NOTPINNED, KVX_E_NOMEM, KVX_E_HIP, KVX_E_FULL = -6, -7, -8, -9, -10
+KVX_NOALLOC_MAX_LAYERS = 4096      # layers kvx_restore_noalloc serves (its scratch)
 TIER_FREE, TIER_WRITING, TIER_RESIDENT = 0, 1, 2
 KVX_RING_MAX_PAGES = 1024
 KVX_OP_BACKUP, KVX_OP_RESTORE, KVX_OP_BACKUP_SLOTS, KVX_OP_RESTORE_SLOTS = 1, 2, 3, 4
@@ -111,6 +112,8 @@ SIGNATURES = [
     ("kvx_backup", ctypes.c_int, [_vp, _P(_i32), _i32, _vp, _u64, _i32, _i32, _vp, _i32]),
     ("kvx_restore", ctypes.c_int, [_vp, _vp, _u64, _P(_i32), _i32, _i32, _i32, _vp, _i32, _vp,
                                    _i32]),
+    ("kvx_restore_noalloc", ctypes.c_int, [_vp, _vp, _u64, _P(_i32), _i32, _i32, _i32, _vp, _i32,
+                                           _vp, _i32]),
     ("kvx_plan_runs", ctypes.c_int, [_vp, _P(_i32), _i32, _P(_i32), _i32, _P(_i32)]),
     ("kvx_ready_create", ctypes.c_int, [_i32, _u64, _P(_vp)]),
     ("kvx_ready_create_device", ctypes.c_int, [_i32, _i32, _u64, _P(_vp)]),
@@ -390,6 +393,14 @@ def kvx_restore(pool: int, src, src_bytes: int, page_ids: Iterable[int], layer_b
     ids = _ids(page_ids)
     _check(lib().kvx_restore(pool, _ptr(src), src_bytes, _ids_ptr(ids), ids.size, layer_begin,
                              layer_end, ready or 0, slot_base, _stream(stream), path))
+
+
+def kvx_restore_noalloc(pool: int, src, src_bytes: int, page_ids: Iterable[int], layer_begin: int,
+                        layer_end: int, ready: int = None, slot_base: int = 0, stream=None,
+                        path: int = KVX_PATH_ZEROCOPY) -> None:
+    ids = _ids(page_ids)
+    _check(lib().kvx_restore_noalloc(pool, _ptr(src), src_bytes, _ids_ptr(ids), ids.size, layer_begin,
+                                     layer_end, ready or 0, slot_base, _stream(stream), path))
 
 
 def kvx_backup_slots(pool: int, page_ids: Iterable[int], host_slots: Iterable[int], host_pool,
@@ -765,6 +776,7 @@ def kvx_host_alloc(nbytes: int) -> int:
 
 def kvx_host_free(ptr: int) -> None:
     _check(lib().kvx_host_free(ptr))
+
 
 
 def kvx_sync(stream=None) -> None:
