@@ -171,12 +171,17 @@ int lane_init(Lane* L)
     return KVX_OK;
 }
 
-int get_lane(int device, hipStream_t caller, Lane** out)
+// The lane of (device, caller stream), created on first use, returned with
+// its mutex held by *held. The mutex is taken while the registry's is held,
+// so kvx_release_stream (which takes both in the same order) never frees a
+// lane that a call has found.
+int get_lane(int device, hipStream_t caller, Lane** out, std::unique_lock<std::mutex>* held)
 {
     std::lock_guard<std::mutex> lk(g_lanes_mu);
     auto key = std::make_pair(device, caller);
     auto it = g_lanes.find(key);
     if (it != g_lanes.end()) {
+        *held = std::unique_lock<std::mutex>(it->second->mu);
         *out = it->second;
         return KVX_OK;
     }
@@ -187,8 +192,34 @@ int get_lane(int device, hipStream_t caller, Lane** out)
     int rc = lane_init(L);
     if (rc != KVX_OK) return rc;   // a half-built lane is leaked on purpose: never reused
     g_lanes[key] = L;
+    *held = std::unique_lock<std::mutex>(L->mu);
     *out = L;
     return KVX_OK;
+}
+
+// Waits for everything a lane enqueued and frees what it holds: the staging
+// ring, the per-layer counters, the side stream and the events. Failures are
+// logged; the lane is not used again either way.
+void lane_free(Lane* L)
+{
+    DeviceGuard dg(L->device);
+    auto check = [](hipError_t e, const char* what) {
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            log_warn(std::string("release_stream: ") + what + " failed: " + hipGetErrorString(e));
+        }
+    };
+    check(hipStreamSynchronize(L->caller), "waiting for the caller's stream");
+    if (L->side) {
+        check(hipStreamSynchronize(L->side), "waiting for the side stream");
+        check(hipStreamDestroy(L->side), "hipStreamDestroy");
+    }
+    for (hipEvent_t e : L->slot_free) check(hipEventDestroy(e), "hipEventDestroy");
+    for (hipEvent_t e : L->slot_ready) check(hipEventDestroy(e), "hipEventDestroy");
+    if (L->ev_start) check(hipEventDestroy(L->ev_start), "hipEventDestroy");
+    if (L->ev_done) check(hipEventDestroy(L->ev_done), "hipEventDestroy");
+    if (L->ring) check(hipFree(L->ring), "hipFree of the staging ring");
+    if (L->layer_done) check(hipFree(L->layer_done), "hipFree of the per-layer counters");
 }
 
 // waits until no earlier operation of this lane still reads or writes the
@@ -627,9 +658,9 @@ int run_op(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, void* buf, ui
     if (rc != KVX_OK) return rc;
     const Tuning t = tuning();
     Lane* L = nullptr;
-    rc = get_lane(pool->device, s, &L);
+    std::unique_lock<std::mutex> lk;
+    rc = get_lane(pool->device, s, &L, &lk);
     if (rc != KVX_OK) return rc;
-    std::lock_guard<std::mutex> lk(L->mu);
     rc = enqueue(pool, dir, ids, n, static_cast<uint8_t*>(buf), view, l0, l1, ready, slot_base, s,
                  path, t, L, hs);
     if (rc != KVX_OK) {
@@ -919,9 +950,9 @@ int run_exchange(kvx_pool* pool, XSide bk, XSide rs, kvx_ready* ready, int32_t s
     if (rc != KVX_OK) return rc;
     const Tuning t = tuning();
     Lane* L = nullptr;
-    rc = get_lane(pool->device, s, &L);
+    std::unique_lock<std::mutex> lk;
+    rc = get_lane(pool->device, s, &L, &lk);
     if (rc != KVX_OK) return rc;
-    std::lock_guard<std::mutex> lk(L->mu);
     rc = lane_counters(L, g.num_layers);   // the unit queue, and the publish counters
     if (rc != KVX_OK) return rc;
     rc = bk.slots ? exchange_launches<ExchangeSlotArgs>(pool, bk, rs, ready, slot_base, s, host, t, L,
@@ -1334,6 +1365,54 @@ int kvx_alloc_range(const void* ptr, void** base, uint64_t* size)
     }
     *base = b;
     *size = sz;
+    return KVX_OK;
+}
+
+int kvx_release_stream(void* stream)
+{
+    const TraceRange tr("kvx_release_stream");
+    clear_error();
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    // take the stream's lanes out of the registry, each with its mutex held
+    // (a call still enqueueing on one finishes first)
+    std::vector<Lane*> gone;
+    {
+        std::lock_guard<std::mutex> lk(g_lanes_mu);
+        for (auto it = g_lanes.begin(); it != g_lanes.end();) {
+            if (it->first.second == s) {
+                it->second->mu.lock();
+                gone.push_back(it->second);
+                it = g_lanes.erase(it);
+            } else {
+                ++it;
+            }
+        }
+    }
+    for (Lane* L : gone) {
+        lane_free(L);
+        L->mu.unlock();
+        delete L;
+    }
+    // the pools' records of their last operation on this stream
+    std::vector<kvx_pool*> pools;
+    {
+        std::lock_guard<std::mutex> lk(g_reg_mu);
+        for (const kvx_pool* p : g_pools) pools.push_back(const_cast<kvx_pool*>(p));
+    }
+    for (kvx_pool* p : pools) {
+        std::lock_guard<std::mutex> lk(p->mu);
+        auto it = p->last_op.find(s);
+        if (it == p->last_op.end()) continue;
+        DeviceGuard dg(p->device);
+        hipError_t e = hipEventSynchronize(it->second);
+        if (e == hipSuccess) e = hipEventDestroy(it->second);
+        if (e != hipSuccess) {
+            (void)hipGetLastError();
+            log_warn(std::string("release_stream: an end-of-operation event failed: ") +
+                     hipGetErrorString(e));
+        }
+        p->last_op.erase(it);
+    }
     return KVX_OK;
 }
 

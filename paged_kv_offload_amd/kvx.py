@@ -128,6 +128,7 @@ SIGNATURES = [
     ("kvx_host_free", ctypes.c_int, [_vp]),
     ("kvx_alloc_range", ctypes.c_int, [_vp, _P(_vp), _P(_u64)]),
     ("kvx_sync", ctypes.c_int, [_vp]),
+    ("kvx_release_stream", ctypes.c_int, [_vp]),
     ("kvx_last_error", ctypes.c_char_p, []),
     ("kvx_version", ctypes.c_int, []),
     ("kvx_set_option", ctypes.c_int, [_i32, _i64]),
@@ -777,6 +778,10 @@ def kvx_host_alloc(nbytes: int) -> int:
 def kvx_host_free(ptr: int) -> None:
     _check(lib().kvx_host_free(ptr))
 
+
+def kvx_release_stream(stream) -> None:
+    """Frees the library's per-stream state (see include/kvx.h)."""
+    _check(lib().kvx_release_stream(_stream(stream)))
 
 
 def kvx_sync(stream=None) -> None:
