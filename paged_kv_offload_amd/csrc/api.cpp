@@ -446,10 +446,55 @@ void set_publish(const Publish* pub, PublishArgs* p)
     p->block = 1;
 }
 
+// Runs of adjacent pages for a launch sequence over `pairs` (in visiting
+// order): consecutive pages that land in consecutive slots, in a pool whose
+// pages are adjacent in memory (the page is the innermost outer axis). On
+// both sides a run is one span of count x piece_bytes, cut into units like
+// a piece. Used when rows are not reordered (a span is moved as it is) and
+// the runs need fewer units than the pieces do: small pieces get fewer,
+// fuller units, and pieces that a unit does not tile lose their partial
+// unit.
+struct RunPlan {
+    std::vector<Run> runs;
+    int unroll = 0;          // vector rounds of a unit
+    int64_t units_lc = 0;    // units of one (layer, kv) over all runs
+};
+
+bool plan_run_units(const PoolGeom& g, const Tuning& t, bool host, const std::vector<PageSlot>& pairs,
+                    RunPlan* rp)
+{
+    const bool permute = (g.inner == KVX_HND) && g.num_heads > 1 && g.page_size > 1;
+    if (t.coalesce_runs == 0 || permute || !g.pages_adjacent || pairs.size() < 2) return false;
+    plan_runs(g, pairs, &rp->runs);
+    if (rp->runs.size() == pairs.size()) return false;
+    const int64_t round = int64_t(kThreads) * kVecBytes;
+    const int64_t piece_chunk = round * unroll_for(g, t, host);
+    const int64_t piece_units = int64_t(pairs.size()) * ((g.piece_bytes + piece_chunk - 1) / piece_chunk);
+    int64_t span = 0;
+    for (const Run& r : rp->runs) {
+        const int64_t b = int64_t(r.count) * g.piece_bytes;
+        if (b >= (int64_t(1) << 31)) return false;   // a buffer resource spans < 2 GiB
+        span += b;
+    }
+    // the unit of a piece of the runs' average span
+    int max_unroll = static_cast<int>(t.max_unroll);
+    if (host) max_unroll = std::min(max_unroll, 2);
+    rp->unroll = pick_unroll(span / int64_t(rp->runs.size()), max_unroll, static_cast<int>(t.unit_rounds));
+    const int64_t chunk = round * rp->unroll;
+    int64_t units = 0;
+    for (const Run& r : rp->runs) units += (int64_t(r.count) * g.piece_bytes + chunk - 1) / chunk;
+    // only for a clear gain: a few accidental runs in a fragmented list
+    // would mostly add launches (fewer runs than pairs fit one)
+    if (4 * units > 3 * piece_units) return false;
+    rp->units_lc = units;
+    return true;
+}
+
 // pairs: (page, slot) in visiting order; NULL: ids[i] in slot i, caller order.
+// rp: launch over the plan's runs instead (pairs then unused).
 int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, int32_t lb,
                  const PageSlot* pairs, size_t npairs, const Publish* pub, const Tuning& t,
-                 int cu_count, hipStream_t s, const int32_t* ids = nullptr)
+                 int cu_count, hipStream_t s, const int32_t* ids = nullptr, const RunPlan* rp = nullptr)
 {
     const PoolGeom& g = pool->geom;
     MoveArgs a;
@@ -457,6 +502,13 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
     LaunchCfg cfg;
     cfg.host_link = tg.host;
     setup_geom(pool, tg.host, t, &a.g, &cfg);
+    if (rp) {
+        // whole runs, never reordered rows (the plan requires the same inner layout)
+        cfg.unroll = rp->unroll;
+        cfg.permute = 0;
+        a.g.chunk_bytes = static_cast<uint32_t>(kThreads * kVecBytes * rp->unroll);
+        a.g.runs = 1;
+    }
     cfg.publish = pub != nullptr;
     // cache policy (measured on MI355X): HBM to HBM, non-temporal loads and
     // non-temporal device-scope stores; into pinned host memory, non-temporal
@@ -470,19 +522,11 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
     a.s.pk_slot0 = tg.pk_slot0;
     set_publish(pub, &a.p);
     const int64_t limit = (int64_t(1) << 31) - 1;
-    // pairs per launch: at most kMaxPairs, spread evenly over the launches
-    // (512 pages as 256 + 256, not 448 + 64)
-    const size_t per_launch = npairs ? (npairs + (npairs + kMaxPairs - 1) / kMaxPairs - 1) /
-                                           ((npairs + kMaxPairs - 1) / kMaxPairs)
-                                     : 1;
-    for (size_t p0 = 0; p0 < npairs; p0 += per_launch) {
-        const size_t np = std::min<size_t>(per_launch, npairs - p0);
-        for (size_t j = 0; j < np; j++) {
-            a.pairs[2 * j] = pairs ? pairs[p0 + j].page : ids[p0 + j];
-            a.pairs[2 * j + 1] = pairs ? pairs[p0 + j].slot : static_cast<int32_t>(p0 + j);
-        }
-        a.s.npairs = static_cast<uint32_t>(np);
-        const int64_t per_layer = g.num_kv * static_cast<int64_t>(np) * a.g.chunks_per_piece;
+
+    // launches over layers [la, lb) of the pairs or runs now in `a`, each
+    // (layer, kv) holding per_lc work units
+    auto launch_layers = [&](int64_t per_lc) -> int {
+        const int64_t per_layer = g.num_kv * per_lc;
         if (per_layer > limit) return fail(KVX_E_INVAL, "one layer of this call has too many work units");
         const int32_t step = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(lb - la, limit / per_layer)));
         for (int32_t l = la; l < lb; l += step) {
@@ -509,11 +553,12 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
                 gmax = std::min<int64_t>(int64_t(cu_count) * 8, std::max<int64_t>(cu_count, per_layer / 4));
             } else if (a.g.chunk_bytes >= (32u << 10)) {
                 gmax = a.s.total_units;
-                order = 3;
+                order = a.g.runs ? 1 : 3;   // chunk rotation is per piece
             } else {
                 gmax = int64_t(cu_count) * 32;
             }
             if (t.unit_order >= 0) order = static_cast<uint32_t>(t.unit_order);
+            if (a.g.runs) order &= 1u;
             a.g.unit_order = order;
             int64_t grid = std::max<int64_t>(1, std::min<int64_t>(a.s.total_units, gmax));
             if ((order & 1u) && grid > 8) grid &= ~int64_t(7);   // whole rounds of 8 XCDs
@@ -526,18 +571,82 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
             // 5.37 TB/s, trtllm_hnd 6.00, mla_fp8 4.94 (16, 32 and 16 units),
             // against 4.15, 3.28 and 2.11 one unit per draw; blocks that
             // straddle layers (mla_fp8, 14 or 15 units) lose about 12%.
+            // Among the block sizes that tile a layer, from that size down
+            // to half of it (smaller blocks mean more counts: one unit per
+            // draw ran the MLA pool at 2.1 TB/s), the one whose last round of
+            // draws is fullest: the fewest units a workgroup may have to move
+            // (rounds x block), ties to the larger block. Measured on the MLA
+            // pool's 144 KiB pieces as 9 MiB runs (72 units of 128 KiB a
+            // layer): 12-unit blocks left the second round 43% full
+            // (4.46 TB/s).
             if (pub && !tg.host) {
                 int64_t b = t.publish_block;
                 if (b <= 0) {
-                    b = std::max<int64_t>(1, kPublishBlockBytes / a.g.chunk_bytes);
-                    b = std::min<int64_t>(b, std::max<int64_t>(1, a.s.total_units / grid));
-                    while (b > 1 && per_layer % b != 0) b--;
+                    const int64_t bmax = std::max<int64_t>(1, std::min<int64_t>(
+                        kPublishBlockBytes / a.g.chunk_bytes, std::max<int64_t>(1, a.s.total_units / grid)));
+                    int64_t best = 1, best_cost = INT64_MAX;
+                    for (int64_t c = bmax; c >= std::max<int64_t>(1, bmax / 2); c--) {
+                        if (per_layer % c != 0) continue;
+                        const int64_t blocks = (a.s.total_units + c - 1) / c;
+                        const int64_t cost = (blocks + grid - 1) / grid * c;
+                        if (cost < best_cost) {
+                            best = c;
+                            best_cost = cost;
+                        }
+                    }
+                    if (best_cost == INT64_MAX) {   // no size in the range tiles a layer
+                        best = bmax;
+                        while (best > 1 && per_layer % best != 0) best--;
+                    }
+                    b = best;
                 }
                 a.p.block = static_cast<uint32_t>(b);
             }
             hipError_t e = launch_move(dir, cfg, a, s);
             if (e != hipSuccess) return hip_fail(e, "kernel launch");
         }
+        return KVX_OK;
+    };
+
+    if (rp) {
+        // runs per launch: at most kMaxRuns, spread evenly over the launches
+        const size_t nr = rp->runs.size();
+        const size_t nl = (nr + kMaxRuns - 1) / kMaxRuns;
+        const size_t per_launch = (nr + nl - 1) / nl;
+        const int64_t chunk = a.g.chunk_bytes;
+        for (size_t r0 = 0; r0 < nr; r0 += per_launch) {
+            const size_t k = std::min(per_launch, nr - r0);
+            int64_t units = 0;
+            for (size_t j = 0; j < k; j++) {
+                const Run& r = rp->runs[r0 + j];
+                a.pairs[4 * j] = r.page;
+                a.pairs[4 * j + 1] = r.slot;
+                a.pairs[4 * j + 2] = r.count;
+                a.pairs[4 * j + 3] = static_cast<int32_t>(units);
+                units += (int64_t(r.count) * g.piece_bytes + chunk - 1) / chunk;
+            }
+            if (units > limit) return fail(KVX_E_INVAL, "one layer of this call has too many work units");
+            a.s.npairs = static_cast<uint32_t>(k);
+            a.g.units_lc = static_cast<uint32_t>(units);
+            const int rc = launch_layers(units);
+            if (rc != KVX_OK) return rc;
+        }
+        return KVX_OK;
+    }
+    // pairs per launch: at most kMaxPairs, spread evenly over the launches
+    // (512 pages as 256 + 256, not 448 + 64)
+    const size_t per_launch = npairs ? (npairs + (npairs + kMaxPairs - 1) / kMaxPairs - 1) /
+                                           ((npairs + kMaxPairs - 1) / kMaxPairs)
+                                     : 1;
+    for (size_t p0 = 0; p0 < npairs; p0 += per_launch) {
+        const size_t np = std::min<size_t>(per_launch, npairs - p0);
+        for (size_t j = 0; j < np; j++) {
+            a.pairs[2 * j] = pairs ? pairs[p0 + j].page : ids[p0 + j];
+            a.pairs[2 * j + 1] = pairs ? pairs[p0 + j].slot : static_cast<int32_t>(p0 + j);
+        }
+        a.s.npairs = static_cast<uint32_t>(np);
+        const int rc = launch_layers(static_cast<int64_t>(np) * a.g.chunks_per_piece);
+        if (rc != KVX_OK) return rc;
     }
     return KVX_OK;
 }
@@ -687,6 +796,11 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
     std::vector<PageSlot> pairs;
     order_pairs(ids, hs ? hs->slots : nullptr, n, t.sort_pages != 0, &pairs);
 
+    // runs of adjacent pages (zero-copy and device paths: the staged path
+    // cuts layers into slot ranges of its ring)
+    RunPlan runs;
+    const bool use_runs = path != KVX_PATH_STAGED &&
+                          plan_run_units(g, t, path == KVX_PATH_ZEROCOPY, pairs, &runs);
     Publish pub;
     const Publish* pubp = nullptr;
     if (ready) {
@@ -696,13 +810,15 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
         pub.layer_done = L->layer_done;
         pub.queue = L->layer_done + L->layer_cap;
         pub.ready = ready->counts_dev + slot_base;
-        pub.layer_target = static_cast<uint32_t>(g.num_kv * int64_t(n) * ((g.piece_bytes + chunk - 1) / chunk));
+        pub.layer_target = static_cast<uint32_t>(
+            use_runs ? g.num_kv * runs.units_lc : g.num_kv * int64_t(n) * ((g.piece_bytes + chunk - 1) / chunk));
         pub.value = static_cast<uint32_t>(n);
         pubp = &pub;
     }
     if (path != KVX_PATH_STAGED) {
         Target tg{view, 0, 0, hs ? hs->num : int64_t(n), path == KVX_PATH_ZEROCOPY};
-        rc = launch_range(dir, pool, tg, l0, l1, pairs.data(), pairs.size(), pubp, t, L->cu_count, s);
+        rc = launch_range(dir, pool, tg, l0, l1, pairs.data(), pairs.size(), pubp, t, L->cu_count, s,
+                          nullptr, use_runs ? &runs : nullptr);
     } else {
         // chunks of whole layers when one layer fits a ring slot, else slot
         // ranges of one layer
@@ -1491,6 +1607,10 @@ int kvx_set_option(int32_t option, int64_t value)
         if (value < 0 || value > 4096) break;
         g_tune.publish_block = value;
         return KVX_OK;
+    case KVX_OPT_COALESCE_RUNS:
+        if (value != 0 && value != 1) break;
+        g_tune.coalesce_runs = value;
+        return KVX_OK;
     default:
         return fail(KVX_E_INVAL, "set_option: unknown option " + std::to_string(option));
     }
@@ -1519,6 +1639,7 @@ int kvx_get_option(int32_t option, int64_t* value)
     case KVX_OPT_FAIL_ALLOCS: *value = g_tune.fail_allocs; return KVX_OK;
     case KVX_OPT_RING_PAIRING: *value = g_tune.ring_pairing; return KVX_OK;
     case KVX_OPT_PUBLISH_BLOCK: *value = g_tune.publish_block; return KVX_OK;
+    case KVX_OPT_COALESCE_RUNS: *value = g_tune.coalesce_runs; return KVX_OK;
     default: return fail(KVX_E_INVAL, "get_option: unknown option " + std::to_string(option));
     }
 }

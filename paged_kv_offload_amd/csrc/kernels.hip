@@ -117,7 +117,9 @@ __device__ __forceinline__ uint32_t source_offset(const UnitGeom& a, uint32_t of
     }
 }
 
-// Moves one unit: the bytes [unit_base, unit_base + U * 4 KiB) of one piece,
+// Moves one unit: the bytes [unit_base, unit_base + U * 4 KiB) of one piece
+// (or of a run of adjacent pieces, `span` bytes; for a piece span is
+// piece_bytes),
 // without per-access predicates, so that all U loads are in flight before
 // the first store and the stores issue back to back. The destination
 // resource (and the source one, when the layouts match) starts at the unit
@@ -131,9 +133,10 @@ __device__ __forceinline__ uint32_t source_offset(const UnitGeom& a, uint32_t of
 // any in-range load.
 template <Dir D, int U, bool PERMUTE, int CP>
 __device__ __forceinline__ void move_unit(const UnitGeom& a, const uint8_t* src_piece,
-                                          uint8_t* dst_piece, uint32_t unit_base, uint32_t tid)
+                                          uint8_t* dst_piece, uint32_t span, uint32_t unit_base,
+                                          uint32_t tid)
 {
-    const uint32_t rest = a.piece_bytes - unit_base;
+    const uint32_t rest = span - unit_base;
     const rsrc_t dst = piece_rsrc(dst_piece + unit_base, rest);
     const rsrc_t src = PERMUTE ? piece_rsrc(src_piece, a.piece_bytes)
                                : piece_rsrc(src_piece + unit_base, rest);
@@ -268,11 +271,13 @@ __device__ __forceinline__ UnitPos decode_unit(const UnitGeom& g, const Side& s,
 }
 
 // Moves the unit at `u` of a side between pool page `page` and packed slot
-// `slot`. PERM: 0 = same inner layout, 1 = HND<->NHD row by row, 2 = HND<->NHD
+// `slot`; `span` is the bytes the unit's piece or run covers from there.
+// PERM: 0 = same inner layout, 1 = HND<->NHD row by row, 2 = HND<->NHD
 // through LDS token blocks (`lds` holds U * kThreads vectors).
 template <Dir D, int U, int PERM, int CP>
 __device__ __forceinline__ void move_at(const UnitGeom& g, const Side& s, const UnitPos& u,
-                                        int32_t page, int32_t slot, uint32_t tid, v4u* lds)
+                                        int32_t page, int32_t slot, uint32_t span, uint32_t tid,
+                                        v4u* lds)
 {
     uint8_t* pool_piece = g.pool + static_cast<int64_t>(page) * g.page_stride +
                           static_cast<int64_t>(u.l) * g.layer_stride +
@@ -286,7 +291,29 @@ __device__ __forceinline__ void move_at(const UnitGeom& g, const Side& s, const 
         move_unit_lds<D, U, CP>(g, piece_rsrc(src, g.piece_bytes), piece_rsrc(dst, g.piece_bytes), u.k,
                                 tid, lds);
     else
-        move_unit<D, U, PERM == 1, CP>(g, src, dst, u.k * g.chunk_bytes, tid);
+        move_unit<D, U, PERM == 1, CP>(g, src, dst, span, u.k * g.chunk_bytes, tid);
+}
+
+// Position of unit q of a move launch over runs of adjacent pages: run r of
+// the launch starts at pairs[4r] (page) and pairs[4r + 1] (slot), spans
+// pairs[4r + 2] pieces and holds the units [pairs[4r + 3], pairs[4r + 3] +
+// its units) of each (layer, kv); j is the run, k the unit inside it.
+__device__ __forceinline__ UnitPos decode_run_unit(const MoveArgs& a, uint32_t q)
+{
+    const uint32_t per = a.g.units_lc;
+    const uint32_t lc = q / per;
+    const uint32_t rem = q - lc * per;
+    uint32_t lo = 0, hi = a.s.npairs - 1;   // the last run whose first unit is <= rem
+    while (lo < hi) {
+        const uint32_t mid = (lo + hi + 1) >> 1;
+        if (static_cast<uint32_t>(a.pairs[4 * mid + 3]) <= rem)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    const uint32_t lrel = lc / a.g.num_kv;
+    return UnitPos{a.s.layer_begin + static_cast<int32_t>(lrel), lc - lrel * a.g.num_kv, lo,
+                   rem - static_cast<uint32_t>(a.pairs[4 * lo + 3])};
 }
 
 // Runs f(q) for the unit numbers [0, total) drawn from `queue` in number
@@ -340,7 +367,20 @@ __global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
     uint32_t pend = 0;
     __shared__ v4u lds[PERM == 2 ? U * kThreads : 1];
     auto do_unit = [&](uint32_t q) {
-        const UnitPos u = decode_unit(a.g, a.s, q);
+        UnitPos u;
+        int32_t page, slot;
+        uint32_t span;
+        if (a.g.runs) {
+            u = decode_run_unit(a, q);
+            page = a.pairs[4 * u.j];
+            slot = a.pairs[4 * u.j + 1];
+            span = static_cast<uint32_t>(a.pairs[4 * u.j + 2]) * a.g.piece_bytes;
+        } else {
+            u = decode_unit(a.g, a.s, q);
+            page = a.pairs[2 * u.j];
+            slot = a.pairs[2 * u.j + 1];
+            span = a.g.piece_bytes;
+        }
         if constexpr (PUBLISH) {
             // units arrive layer by layer: count a layer once this workgroup leaves it
             if (u.l != pend_layer) {
@@ -349,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
                 pend = 0;
             }
         }
-        move_at<D, U, PERM, CP>(a.g, a.s, u, a.pairs[2 * u.j], a.pairs[2 * u.j + 1], tid, lds);
+        move_at<D, U, PERM, CP>(a.g, a.s, u, page, slot, span, tid, lds);
         if constexpr (PUBLISH) pend++;
     };
 
@@ -428,7 +468,8 @@ __global__ __launch_bounds__(kThreads) void kvx_exchange_kernel(A a)
         }
         if (gather) {
             const UnitPos u = decode_unit(a.g, a.b, idx);
-            move_at<GATHER, U, PERM, CPG>(a.g, a.b, u, page_b(a, u.j), slot_b(a, u.j), tid, lds);
+            move_at<GATHER, U, PERM, CPG>(a.g, a.b, u, page_b(a, u.j), slot_b(a, u.j), a.g.piece_bytes, tid,
+                                          lds);
         } else {
             const UnitPos u = decode_unit(a.g, a.r, idx);
             if constexpr (PUBLISH) {
@@ -438,7 +479,8 @@ __global__ __launch_bounds__(kThreads) void kvx_exchange_kernel(A a)
                     pend = 0;
                 }
             }
-            move_at<SCATTER, U, PERM, CPS>(a.g, a.r, u, page_r(a, u.j), slot_r(a, u.j), tid, lds);
+            move_at<SCATTER, U, PERM, CPS>(a.g, a.r, u, page_r(a, u.j), slot_r(a, u.j), a.g.piece_bytes,
+                                           tid, lds);
             if constexpr (PUBLISH) pend++;
         }
     };

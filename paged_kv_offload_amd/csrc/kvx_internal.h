@@ -91,6 +91,7 @@ struct Tuning {
     int64_t fail_allocs = 0;              // test hook: internal device allocations left to fail
     int64_t ring_pairing = 1;             // ring executor runs BACKUP + RESTORE as one exchange
     int64_t publish_block = 0;            // units per queue draw of device-memory publishing kernels (0 = auto)
+    int64_t coalesce_runs = 1;            // move runs of adjacent pages as spans when that takes fewer units
 };
 Tuning tuning();
 
@@ -122,6 +123,8 @@ struct UnitGeom {
     uint32_t mg_row_vec, mg_H, mg_T;     // magic multipliers (0 means divisor 1)
     uint32_t TU, seg, mg_seg;            // LDS token blocks: tokens per unit, TU * row_vec
     uint32_t unit_order;     // bit 0: XCD-contiguous unit numbering; bit 1: rotate chunks
+    uint32_t runs;           // move launches: 1 = the pair list holds runs of adjacent pages
+    uint32_t units_lc;       // runs: work units of one (layer, kv) over the launch's runs
 };
 
 // One direction's share of a launch: the pieces (page, layer, kv) of layers
@@ -146,7 +149,12 @@ struct PublishArgs {
     uint32_t block;          // move kernels: consecutive units per queue draw (>= 1)
 };
 
-// One direction: pairs[2j] is the page and pairs[2j + 1] its slot.
+// Runs of adjacent pages per move launch: (first page, first slot, pages,
+// units before the run in its (layer, kv)) in the pair array.
+constexpr int kMaxRuns = kMaxPairs / 2;
+
+// One direction: pairs[2j] is the page and pairs[2j + 1] its slot; in a
+// launch over runs (g.runs), pairs[4r .. 4r + 3] describe run r.
 struct MoveArgs {
     UnitGeom g;
     Side s;
