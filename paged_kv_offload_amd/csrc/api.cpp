@@ -375,8 +375,9 @@ struct Publish {
     uint32_t* layer_done = nullptr;
     uint32_t* queue = nullptr;   // unit queue of the publishing kernels
     uint32_t* ready = nullptr;   // device view of counts + slot_base
-    uint32_t layer_target = 0;
+    uint32_t layer_target = 0;   // units of one layer over the call (unless target_here)
     uint32_t value = 0;
+    bool target_here = false;    // the launch sequence is the whole call: it counts the target
 };
 
 // Unit size (vector rounds of 4 KiB per workgroup) of a launch; the publish
@@ -522,6 +523,30 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
     a.s.pk_slot0 = tg.pk_slot0;
     set_publish(pub, &a.p);
     const int64_t limit = (int64_t(1) << 31) - 1;
+    // Tails: with 128 KiB units, a piece that they do not tile has a partial
+    // last unit in which most waves idle (the MLA pool's 144 KiB pieces: a
+    // 16 KiB tail, one wave of four busy for half its rounds). Instead the
+    // tails of several pieces share a unit, each wave moving 1, 2, 4 or 8
+    // whole tails of up to 32, 16, 8 or 4 KiB. Not for a publishing call
+    // whose target is counted outside this launch sequence (the staged
+    // path's chunks), nor for runs or reordered rows.
+    if (!rp && cfg.unroll == 32 && cfg.permute == 0 && t.tail_units != 0 && (!pub || pub->target_here)) {
+        const int64_t main = g.piece_bytes / a.g.chunk_bytes;
+        const int64_t tail = g.piece_bytes - main * a.g.chunk_bytes;
+        const uint32_t tpw = tail <= 0 ? 0u : tail <= 4096 ? 8u : tail <= 8192 ? 4u : tail <= 16384 ? 2u
+                                                             : tail <= 32768 ? 1u : 0u;
+        if (tpw) {
+            a.g.tails_per_wave = tpw;
+            a.g.main_units = static_cast<uint32_t>(main);
+            a.g.tail_bytes = static_cast<uint32_t>(tail);
+        }
+    }
+    // work units of one (layer, kv) of a launch over np pairs
+    auto pair_units = [&](int64_t np) -> int64_t {
+        if (a.g.tails_per_wave)
+            return np * a.g.main_units + (np + 4 * a.g.tails_per_wave - 1) / (4 * a.g.tails_per_wave);
+        return np * a.g.chunks_per_piece;
+    };
 
     // launches over layers [la, lb) of the pairs or runs now in `a`, each
     // (layer, kv) holding per_lc work units
@@ -614,6 +639,13 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
         const size_t nl = (nr + kMaxRuns - 1) / kMaxRuns;
         const size_t per_launch = (nr + nl - 1) / nl;
         const int64_t chunk = a.g.chunk_bytes;
+        if (pub && pub->target_here) {
+            int64_t units = 0;
+            for (const Run& r : rp->runs) units += (int64_t(r.count) * g.piece_bytes + chunk - 1) / chunk;
+            if (g.num_kv * units >= (int64_t(1) << 32))
+                return fail(KVX_E_INVAL, "too many work units for per-layer publish");
+            a.p.layer_target = static_cast<uint32_t>(g.num_kv * units);
+        }
         for (size_t r0 = 0; r0 < nr; r0 += per_launch) {
             const size_t k = std::min(per_launch, nr - r0);
             int64_t units = 0;
@@ -638,6 +670,14 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
     const size_t per_launch = npairs ? (npairs + (npairs + kMaxPairs - 1) / kMaxPairs - 1) /
                                            ((npairs + kMaxPairs - 1) / kMaxPairs)
                                      : 1;
+    if (pub && pub->target_here) {
+        int64_t units = 0;
+        for (size_t p0 = 0; p0 < npairs; p0 += per_launch)
+            units += pair_units(static_cast<int64_t>(std::min<size_t>(per_launch, npairs - p0)));
+        if (g.num_kv * units >= (int64_t(1) << 32))
+            return fail(KVX_E_INVAL, "too many work units for per-layer publish");
+        a.p.layer_target = static_cast<uint32_t>(g.num_kv * units);
+    }
     for (size_t p0 = 0; p0 < npairs; p0 += per_launch) {
         const size_t np = std::min<size_t>(per_launch, npairs - p0);
         for (size_t j = 0; j < np; j++) {
@@ -645,7 +685,8 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
             a.pairs[2 * j + 1] = pairs ? pairs[p0 + j].slot : static_cast<int32_t>(p0 + j);
         }
         a.s.npairs = static_cast<uint32_t>(np);
-        const int rc = launch_layers(static_cast<int64_t>(np) * a.g.chunks_per_piece);
+        a.g.units_lc = static_cast<uint32_t>(pair_units(static_cast<int64_t>(np)));
+        const int rc = launch_layers(pair_units(static_cast<int64_t>(np)));
         if (rc != KVX_OK) return rc;
     }
     return KVX_OK;
@@ -810,8 +851,10 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
         pub.layer_done = L->layer_done;
         pub.queue = L->layer_done + L->layer_cap;
         pub.ready = ready->counts_dev + slot_base;
-        pub.layer_target = static_cast<uint32_t>(
-            use_runs ? g.num_kv * runs.units_lc : g.num_kv * int64_t(n) * ((g.piece_bytes + chunk - 1) / chunk));
+        // the staged path's chunks each launch part of a layer: the target is
+        // counted here; the other paths' single launch sequence counts it
+        pub.layer_target = static_cast<uint32_t>(g.num_kv * int64_t(n) * ((g.piece_bytes + chunk - 1) / chunk));
+        pub.target_here = path != KVX_PATH_STAGED;
         pub.value = static_cast<uint32_t>(n);
         pubp = &pub;
     }
@@ -1250,6 +1293,7 @@ int kvx_restore_noalloc(kvx_pool* pool, const void* src, uint64_t src_bytes, con
         pub.queue = scratch + kNoAllocMaxLayers;
         pub.ready = ready->counts_dev + slot_base;
         pub.layer_target = static_cast<uint32_t>(g.num_kv * int64_t(n) * ((g.piece_bytes + chunk - 1) / chunk));
+        pub.target_here = true;
         pub.value = static_cast<uint32_t>(n);
         pubp = &pub;
     }
@@ -1611,6 +1655,10 @@ int kvx_set_option(int32_t option, int64_t value)
         if (value != 0 && value != 1) break;
         g_tune.coalesce_runs = value;
         return KVX_OK;
+    case KVX_OPT_TAIL_UNITS:
+        if (value != 0 && value != 1) break;
+        g_tune.tail_units = value;
+        return KVX_OK;
     default:
         return fail(KVX_E_INVAL, "set_option: unknown option " + std::to_string(option));
     }
@@ -1640,6 +1688,7 @@ int kvx_get_option(int32_t option, int64_t* value)
     case KVX_OPT_RING_PAIRING: *value = g_tune.ring_pairing; return KVX_OK;
     case KVX_OPT_PUBLISH_BLOCK: *value = g_tune.publish_block; return KVX_OK;
     case KVX_OPT_COALESCE_RUNS: *value = g_tune.coalesce_runs; return KVX_OK;
+    case KVX_OPT_TAIL_UNITS: *value = g_tune.tail_units; return KVX_OK;
     default: return fail(KVX_E_INVAL, "get_option: unknown option " + std::to_string(option));
     }
 }

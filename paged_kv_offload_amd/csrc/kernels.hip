@@ -82,6 +82,22 @@ __device__ __forceinline__ void store16(rsrc_t r, uint32_t off, v4u v)
                                            ((CP & 2) ? kAuxNT : 0) | ((CP & 4) ? kAuxSC1 : 0));
 }
 
+// The same with a scalar part of the offset (soffset) next to the lane's
+// vector part: per-round offsets then need no vector registers.
+template <int CP>
+__device__ __forceinline__ v4u load16s(rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, static_cast<int>(voff), static_cast<int>(soff),
+                                                 (CP & 1) ? kAuxNT : 0);
+}
+
+template <int CP>
+__device__ __forceinline__ void store16s(rsrc_t r, uint32_t voff, uint32_t soff, v4u v)
+{
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, static_cast<int>(voff), static_cast<int>(soff),
+                                           ((CP & 2) ? kAuxNT : 0) | ((CP & 4) ? kAuxSC1 : 0));
+}
+
 // Vector index of lane `tid`'s round u inside a unit of U rounds: wave w owns
 // vectors [w * 64U, (w + 1) * 64U), one 64-vector (1 KiB) run per round.
 template <int U>
@@ -257,6 +273,23 @@ struct UnitPos {
 
 __device__ __forceinline__ UnitPos decode_unit(const UnitGeom& g, const Side& s, uint32_t q)
 {
+    if (g.tails_per_wave) {
+        // per (layer, kv): the pieces' whole units, then the tail units; a
+        // tail unit is marked k == main_units, j its first piece
+        const uint32_t lc = q / g.units_lc;
+        const uint32_t rem = q - lc * g.units_lc;
+        const uint32_t main = s.npairs * g.main_units;
+        uint32_t j, k;
+        if (rem < main) {
+            j = rem / g.main_units;
+            k = rem - j * g.main_units;
+        } else {
+            j = (rem - main) * 4u * g.tails_per_wave;
+            k = g.main_units;
+        }
+        const uint32_t lrel = lc / g.num_kv;
+        return UnitPos{s.layer_begin + static_cast<int32_t>(lrel), lc - lrel * g.num_kv, j, k};
+    }
     const uint32_t cpp = g.chunks_per_piece;
     const uint32_t pu = q / cpp;
     uint32_t k = q - pu * cpp;
@@ -292,6 +325,44 @@ __device__ __forceinline__ void move_at(const UnitGeom& g, const Side& s, const 
                                 tid, lds);
     else
         move_unit<D, U, PERM == 1, CP>(g, src, dst, span, u.k * g.chunk_bytes, tid);
+}
+
+// A tail unit: the tails of the pieces j0 .. j0 + 4 * TPW - 1 of a move
+// launch (those that exist), the last tail_bytes of each after its
+// main_units whole units. Wave w moves the tails of pieces j0 + w * TPW ..
+// j0 + (w + 1) * TPW - 1, U / TPW rounds of 1 KiB each; a tail shorter than
+// that, or a piece past the launch's last, is bounded by its buffer
+// resource (a missing piece gets a resource of length zero). Wave-uniform
+// throughout: the wave index is read through readfirstlane so that every
+// resource stays scalar.
+template <Dir D, int U, int TPW, int CP>
+__device__ __forceinline__ void move_tails(const MoveArgs& a, const UnitPos& u, uint32_t tid)
+{
+    constexpr int TR = U / TPW;   // rounds per tail
+    const uint32_t wave = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(tid >> 6)));
+    const uint32_t lane_off = (tid & 63u) * kVecBytes;
+    const uint32_t tail0 = a.g.main_units * a.g.chunk_bytes;
+    rsrc_t src[TPW], dst[TPW];
+#pragma unroll
+    for (int t = 0; t < TPW; t++) {
+        const uint32_t j = u.j + wave * TPW + t;
+        const bool live = j < a.s.npairs;
+        const uint32_t jj = live ? j : u.j;
+        uint8_t* pool_piece = a.g.pool + static_cast<int64_t>(a.pairs[2 * jj]) * a.g.page_stride +
+                              static_cast<int64_t>(u.l) * a.g.layer_stride +
+                              static_cast<int64_t>(u.c) * a.g.kv_stride;
+        uint8_t* pk_piece = a.s.packed +
+                            (static_cast<int64_t>(u.l - a.s.pk_layer0) * a.g.num_kv + u.c) * a.s.pk_lc_stride +
+                            static_cast<int64_t>(a.pairs[2 * jj + 1] - a.s.pk_slot0) * a.g.piece_bytes;
+        const uint32_t bytes = live ? a.g.tail_bytes : 0u;
+        src[t] = piece_rsrc((D == GATHER ? pool_piece : pk_piece) + tail0, bytes);
+        dst[t] = piece_rsrc((D == GATHER ? pk_piece : pool_piece) + tail0, bytes);
+    }
+    v4u v[U];
+#pragma unroll
+    for (int r = 0; r < U; r++) v[r] = load16s<CP>(src[r / TR], lane_off, (r % TR) * (64u * kVecBytes));
+#pragma unroll
+    for (int r = 0; r < U; r++) store16s<CP>(dst[r / TR], lane_off, (r % TR) * (64u * kVecBytes), v[r]);
 }
 
 // Position of unit q of a move launch over runs of adjacent pages: run r of
@@ -381,6 +452,7 @@ __global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
             slot = a.pairs[2 * u.j + 1];
             span = a.g.piece_bytes;
         }
+        const bool tail = a.g.tails_per_wave != 0 && u.k == a.g.main_units;
         if constexpr (PUBLISH) {
             // units arrive layer by layer: count a layer once this workgroup leaves it
             if (u.l != pend_layer) {
@@ -389,7 +461,21 @@ __global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
                 pend = 0;
             }
         }
-        move_at<D, U, PERM, CP>(a.g, a.s, u, page, slot, span, tid, lds);
+        if constexpr (U == 32 && PERM == 0) {
+            if (tail) {
+                switch (a.g.tails_per_wave) {
+                case 1: move_tails<D, U, 1, CP>(a, u, tid); break;
+                case 2: move_tails<D, U, 2, CP>(a, u, tid); break;
+                case 4: move_tails<D, U, 4, CP>(a, u, tid); break;
+                default: move_tails<D, U, 8, CP>(a, u, tid); break;
+                }
+            } else {
+                move_at<D, U, PERM, CP>(a.g, a.s, u, page, slot, span, tid, lds);
+            }
+        } else {
+            (void)tail;
+            move_at<D, U, PERM, CP>(a.g, a.s, u, page, slot, span, tid, lds);
+        }
         if constexpr (PUBLISH) pend++;
     };
 

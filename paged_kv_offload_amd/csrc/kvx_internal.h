@@ -92,6 +92,7 @@ struct Tuning {
     int64_t ring_pairing = 1;             // ring executor runs BACKUP + RESTORE as one exchange
     int64_t publish_block = 0;            // units per queue draw of device-memory publishing kernels (0 = auto)
     int64_t coalesce_runs = 1;            // move runs of adjacent pages as spans when that takes fewer units
+    int64_t tail_units = 1;               // the tails of pieces that 128 KiB units do not tile share units
 };
 Tuning tuning();
 
@@ -124,7 +125,13 @@ struct UnitGeom {
     uint32_t TU, seg, mg_seg;            // LDS token blocks: tokens per unit, TU * row_vec
     uint32_t unit_order;     // bit 0: XCD-contiguous unit numbering; bit 1: rotate chunks
     uint32_t runs;           // move launches: 1 = the pair list holds runs of adjacent pages
-    uint32_t units_lc;       // runs: work units of one (layer, kv) over the launch's runs
+    uint32_t units_lc;       // runs, tails: work units of one (layer, kv) in the launch
+    // tails (move launches over pairs, 32-round units): a piece is main_units
+    // whole units and a tail of tail_bytes; the tails of tails_per_wave * 4
+    // pieces share one unit, each wave moving tails_per_wave of them
+    uint32_t tails_per_wave; // 0: no tail units (a piece's last unit may be partial)
+    uint32_t main_units;
+    uint32_t tail_bytes;
 };
 
 // One direction's share of a launch: the pieces (page, layer, kv) of layers
