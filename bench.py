@@ -67,13 +67,24 @@ def pcie_protocol_bound(payload=256, write_overhead=24, completion_overhead=20, 
                        f"one {request_bytes} B read request per completion, no link-layer packets"}
 
 
+# pages one move-kernel launch carries; a call over more pages is split into
+# equal launches (the roofline figures of such a call are per call)
+PAGES_PER_LAUNCH = 448
+
 # HBM bytes per launch of the roofline kernel from the two rocprofv3 --pmc runs
 # (FETCH_SIZE, WRITE_SIZE, scaled by a plain device copy in the same run; see
 # profiles/pack_kernel_<workload>.txt). Valid only for the kernel source they
 # were taken on: reported as null once kernels.hip changes.
 MEASURED_TRAFFIC = {
-    "mixed": {"kernels_hip_sha256": "4ec5d29742f6c4cf080e817188d21c1b20f09f37a4c67cdda0e4de48b01ea4c7",
-              "bytes_per_launch": 4295170789},
+    "mixed": {"kernels_hip_sha256": "273cf3f4be5d93efe111820ec96b545f8bd228ff5440622d98922579320fb8c9",
+              "bytes_per_launch": 4295193769},
+    "llama8b": {"kernels_hip_sha256": "273cf3f4be5d93efe111820ec96b545f8bd228ff5440622d98922579320fb8c9",
+                "bytes_per_launch": 4295194428},
+    "mla_fp8": {"kernels_hip_sha256": "273cf3f4be5d93efe111820ec96b545f8bd228ff5440622d98922579320fb8c9",
+                "bytes_per_launch": 1151478773},
+    # one call = two launches of 256 pages: the bytes of both
+    "trtllm_hnd": {"kernels_hip_sha256": "273cf3f4be5d93efe111820ec96b545f8bd228ff5440622d98922579320fb8c9",
+                   "bytes_per_launch": 4295474956},
 }
 
 
@@ -473,7 +484,8 @@ def single_main(args, options, w, quiet=False):
                           f"device path)",
                 "achieved": kern["pack"]["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": kern["pack"]["frac"], "traffic": measured_traffic(w.name),
-                "algorithmic_bytes_per_launch": 2 * P, "avg_launch_ms": kern["pack"]["avg_launch_ms"]}
+                "algorithmic_bytes_per_launch": 2 * P, "avg_launch_ms": kern["pack"]["avg_launch_ms"],
+                "launches_per_call": -(-n // PAGES_PER_LAUNCH)}
     if args.kernel_only:
         print(json.dumps({"roofline": roofline, "device_kernels": kern, "options": options}), flush=True)
         return None
