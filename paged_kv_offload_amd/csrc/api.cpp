@@ -397,6 +397,80 @@ int unroll_for(const PoolGeom& g, const Tuning& t, bool host)
     return pick_unroll(g.piece_bytes, max_unroll, static_cast<int>(t.unit_rounds));
 }
 
+// Tail units of a launch over (page, slot) pairs: a piece is main_units whole
+// units and a tail, and the tails of 4 * tails_per_wave pieces share one unit,
+// each wave moving tails_per_wave whole tails (the kernels carry this form
+// for units of 32 rounds in device memory and of 2 over the host link).
+//  - Pieces that such units do not tile (the MLA pool's 144 KiB pieces: a
+//    16 KiB tail after one 128 KiB unit) lose their mostly idle partial
+//    unit.
+//  - Pieces no longer than a wave's share of such a unit (32 KiB in device
+//    memory, 2 KiB over the host link; a pool of one token per page has
+//    2 KiB pieces) are all tail: 4 * tails_per_wave of them travel in one
+//    unit instead of one piece in a unit of its own.
+// Not for reordered rows, nor where the unit size is forced.
+struct TailPlan {
+    int unroll = 0;
+    uint32_t tails_per_wave = 0, main_units = 0, tail_bytes = 0;
+};
+
+// Whether short pieces travel whole, several to a unit, rather than one to a
+// unit of their own size. Measured on MI355X, fragmented 1 GiB requests of a
+// 32-layer K+V pool (TB/s read + write, one piece a unit -> whole pieces):
+//   piece   plain pack     plain unpack   publishing unpack
+//   1 KiB   2.10 -> 3.42   1.99 -> 3.07   0.28 -> 1.57
+//   2 KiB   3.96 -> 4.40   3.82 -> 3.98   0.72 -> 2.37
+//   4 KiB   5.35 -> 4.80   4.82 -> 4.40   1.63 -> 3.23
+//   8 KiB   5.45 -> 5.39   4.97 -> 4.83   2.67 -> 3.87
+//  16 KiB   5.55 -> 5.84   5.08 -> 5.10   3.87 -> 3.54
+//  32 KiB   5.60 -> 6.05   5.23 -> 5.53   3.75 -> 3.93
+// and zero-copy restores of 1 and 2 KiB pieces at 54.5 and 55.9 GB/s
+// against 17.1 and 34.2.
+bool whole_pieces_pay(int64_t piece_bytes, bool host, bool publish)
+{
+    if (host) return true;
+    if (publish) return piece_bytes <= 8192 || piece_bytes > 16384;
+    return piece_bytes <= 2048 || piece_bytes >= 16384;
+}
+
+bool plan_tails(const PoolGeom& g, const Tuning& t, bool host, bool publish, TailPlan* tp)
+{
+    const bool permute = (g.inner == KVX_HND) && g.num_heads > 1 && g.page_size > 1;
+    if (permute || t.tail_units == 0) return false;
+    const int umax = host ? 2 : 32;
+    const int64_t wave_round = 64 * kVecBytes;   // one round of one wave
+    const int unroll = unroll_for(g, t, host);
+    int64_t main = 0, tail = 0;
+    if (unroll == umax) {
+        main = g.piece_bytes / (4 * wave_round * umax);
+        tail = g.piece_bytes - main * 4 * wave_round * umax;
+    } else if (t.unit_rounds == 0 && t.max_unroll >= umax && g.piece_bytes <= umax * wave_round &&
+               whole_pieces_pay(g.piece_bytes, host, publish)) {
+        tail = g.piece_bytes;
+    } else {
+        return false;
+    }
+    if (tail <= 0) return false;
+    for (int tpw = 8; tpw >= 1; tpw /= 2) {
+        if (tpw <= umax && tail <= (umax / tpw) * wave_round) {
+            tp->unroll = umax;
+            tp->tails_per_wave = static_cast<uint32_t>(tpw);
+            tp->main_units = static_cast<uint32_t>(main);
+            tp->tail_bytes = static_cast<uint32_t>(tail);
+            return true;
+        }
+    }
+    return false;
+}
+
+// Work units of one (layer, kv) of a launch over np pairs.
+int64_t pair_units(const TailPlan* tp, int64_t chunks_per_piece, int64_t np)
+{
+    if (tp && tp->tails_per_wave)
+        return np * tp->main_units + (np + 4 * tp->tails_per_wave - 1) / (4 * tp->tails_per_wave);
+    return np * chunks_per_piece;
+}
+
 // Unit geometry of launches on `pool`; sets cfg.unroll and cfg.permute.
 void setup_geom(const kvx_pool* pool, bool host, const Tuning& t, UnitGeom* ug, LaunchCfg* cfg)
 {
@@ -461,8 +535,8 @@ struct RunPlan {
     int64_t units_lc = 0;    // units of one (layer, kv) over all runs
 };
 
-bool plan_run_units(const PoolGeom& g, const Tuning& t, bool host, const std::vector<PageSlot>& pairs,
-                    RunPlan* rp)
+bool plan_run_units(const PoolGeom& g, const Tuning& t, bool host, bool publish,
+                    const std::vector<PageSlot>& pairs, RunPlan* rp)
 {
     const bool permute = (g.inner == KVX_HND) && g.num_heads > 1 && g.page_size > 1;
     if (t.coalesce_runs == 0 || permute || !g.pages_adjacent || pairs.size() < 2) return false;
@@ -470,7 +544,11 @@ bool plan_run_units(const PoolGeom& g, const Tuning& t, bool host, const std::ve
     if (rp->runs.size() == pairs.size()) return false;
     const int64_t round = int64_t(kThreads) * kVecBytes;
     const int64_t piece_chunk = round * unroll_for(g, t, host);
-    const int64_t piece_units = int64_t(pairs.size()) * ((g.piece_bytes + piece_chunk - 1) / piece_chunk);
+    // what the pairs would take (tail units where they apply)
+    TailPlan tp;
+    const int64_t piece_units = pair_units(plan_tails(g, t, host, publish, &tp) ? &tp : nullptr,
+                                           (g.piece_bytes + piece_chunk - 1) / piece_chunk,
+                                           static_cast<int64_t>(pairs.size()));
     int64_t span = 0;
     for (const Run& r : rp->runs) {
         const int64_t b = int64_t(r.count) * g.piece_bytes;
@@ -523,29 +601,21 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
     a.s.pk_slot0 = tg.pk_slot0;
     set_publish(pub, &a.p);
     const int64_t limit = (int64_t(1) << 31) - 1;
-    // Tails: with 128 KiB units, a piece that they do not tile has a partial
-    // last unit in which most waves idle (the MLA pool's 144 KiB pieces: a
-    // 16 KiB tail, one wave of four busy for half its rounds). Instead the
-    // tails of several pieces share a unit, each wave moving 1, 2, 4 or 8
-    // whole tails of up to 32, 16, 8 or 4 KiB. Not for a publishing call
-    // whose target is counted outside this launch sequence (the staged
-    // path's chunks), nor for runs or reordered rows.
-    if (!rp && cfg.unroll == 32 && cfg.permute == 0 && t.tail_units != 0 && (!pub || pub->target_here)) {
-        const int64_t main = g.piece_bytes / a.g.chunk_bytes;
-        const int64_t tail = g.piece_bytes - main * a.g.chunk_bytes;
-        const uint32_t tpw = tail <= 0 ? 0u : tail <= 4096 ? 8u : tail <= 8192 ? 4u : tail <= 16384 ? 2u
-                                                             : tail <= 32768 ? 1u : 0u;
-        if (tpw) {
-            a.g.tails_per_wave = tpw;
-            a.g.main_units = static_cast<uint32_t>(main);
-            a.g.tail_bytes = static_cast<uint32_t>(tail);
-        }
+    // tail units (not for a publishing call whose target is counted outside
+    // this launch sequence: the staged path's chunks)
+    TailPlan tp;
+    const bool tails = !rp && (!pub || pub->target_here) && plan_tails(g, t, tg.host, pub != nullptr, &tp);
+    if (tails) {
+        cfg.unroll = tp.unroll;
+        a.g.chunk_bytes = static_cast<uint32_t>(kThreads * kVecBytes * tp.unroll);
+        a.g.chunks_per_piece = static_cast<uint32_t>((g.piece_bytes + a.g.chunk_bytes - 1) / a.g.chunk_bytes);
+        a.g.tails_per_wave = tp.tails_per_wave;
+        a.g.main_units = tp.main_units;
+        a.g.tail_bytes = tp.tail_bytes;
     }
     // work units of one (layer, kv) of a launch over np pairs
-    auto pair_units = [&](int64_t np) -> int64_t {
-        if (a.g.tails_per_wave)
-            return np * a.g.main_units + (np + 4 * a.g.tails_per_wave - 1) / (4 * a.g.tails_per_wave);
-        return np * a.g.chunks_per_piece;
+    auto units_of = [&](int64_t np) -> int64_t {
+        return pair_units(tails ? &tp : nullptr, a.g.chunks_per_piece, np);
     };
 
     // launches over layers [la, lb) of the pairs or runs now in `a`, each
@@ -673,7 +743,7 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
     if (pub && pub->target_here) {
         int64_t units = 0;
         for (size_t p0 = 0; p0 < npairs; p0 += per_launch)
-            units += pair_units(static_cast<int64_t>(std::min<size_t>(per_launch, npairs - p0)));
+            units += units_of(static_cast<int64_t>(std::min<size_t>(per_launch, npairs - p0)));
         if (g.num_kv * units >= (int64_t(1) << 32))
             return fail(KVX_E_INVAL, "too many work units for per-layer publish");
         a.p.layer_target = static_cast<uint32_t>(g.num_kv * units);
@@ -685,8 +755,8 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
             a.pairs[2 * j + 1] = pairs ? pairs[p0 + j].slot : static_cast<int32_t>(p0 + j);
         }
         a.s.npairs = static_cast<uint32_t>(np);
-        a.g.units_lc = static_cast<uint32_t>(pair_units(static_cast<int64_t>(np)));
-        const int rc = launch_layers(pair_units(static_cast<int64_t>(np)));
+        a.g.units_lc = static_cast<uint32_t>(units_of(static_cast<int64_t>(np)));
+        const int rc = launch_layers(units_of(static_cast<int64_t>(np)));
         if (rc != KVX_OK) return rc;
     }
     return KVX_OK;
@@ -841,7 +911,7 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
     // cuts layers into slot ranges of its ring)
     RunPlan runs;
     const bool use_runs = path != KVX_PATH_STAGED &&
-                          plan_run_units(g, t, path == KVX_PATH_ZEROCOPY, pairs, &runs);
+                          plan_run_units(g, t, path == KVX_PATH_ZEROCOPY, ready != nullptr, pairs, &runs);
     Publish pub;
     const Publish* pubp = nullptr;
     if (ready) {

@@ -329,7 +329,9 @@ __device__ __forceinline__ void move_at(const UnitGeom& g, const Side& s, const 
 
 // A tail unit: the tails of the pieces j0 .. j0 + 4 * TPW - 1 of a move
 // launch (those that exist), the last tail_bytes of each after its
-// main_units whole units. Wave w moves the tails of pieces j0 + w * TPW ..
+// main_units whole units; with main_units 0 the tail is the whole piece, so
+// pieces shorter than a wave's share of a unit travel 4 * TPW to a unit
+// instead of one. Wave w moves the tails of pieces j0 + w * TPW ..
 // j0 + (w + 1) * TPW - 1, U / TPW rounds of 1 KiB each; a tail shorter than
 // that, or a piece past the launch's last, is bounded by its buffer
 // resource (a missing piece gets a resource of length zero). Wave-uniform
@@ -469,6 +471,16 @@ __global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
                 case 4: move_tails<D, U, 4, CP>(a, u, tid); break;
                 default: move_tails<D, U, 8, CP>(a, u, tid); break;
                 }
+            } else {
+                move_at<D, U, PERM, CP>(a.g, a.s, u, page, slot, span, tid, lds);
+            }
+        } else if constexpr (U == 2 && PERM == 0) {
+            // the host link's 8 KiB units: one or two short pieces a wave
+            if (tail) {
+                if (a.g.tails_per_wave == 1)
+                    move_tails<D, U, 1, CP>(a, u, tid);
+                else
+                    move_tails<D, U, 2, CP>(a, u, tid);
             } else {
                 move_at<D, U, PERM, CP>(a.g, a.s, u, page, slot, span, tid, lds);
             }

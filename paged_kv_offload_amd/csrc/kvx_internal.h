@@ -126,9 +126,10 @@ struct UnitGeom {
     uint32_t unit_order;     // bit 0: XCD-contiguous unit numbering; bit 1: rotate chunks
     uint32_t runs;           // move launches: 1 = the pair list holds runs of adjacent pages
     uint32_t units_lc;       // runs, tails: work units of one (layer, kv) in the launch
-    // tails (move launches over pairs, 32-round units): a piece is main_units
-    // whole units and a tail of tail_bytes; the tails of tails_per_wave * 4
-    // pieces share one unit, each wave moving tails_per_wave of them
+    // tails (move launches over pairs, units of 32 rounds in device memory
+    // or 2 over the host link): a piece is main_units whole units (possibly
+    // none) and a tail of tail_bytes; the tails of tails_per_wave * 4 pieces
+    // share one unit, each wave moving tails_per_wave of them
     uint32_t tails_per_wave; // 0: no tail units (a piece's last unit may be partial)
     uint32_t main_units;
     uint32_t tail_bytes;

@@ -1,7 +1,9 @@
 """Tail units: pieces that 128 KiB work units do not tile (the MLA pool's
 144 KiB pieces) end in a tail, and the tails of several pieces share a unit
 (one to eight per wave) instead of each piece ending in a mostly idle
-partial unit. Bytes and published counts must be the oracle's, and the
+partial unit; pieces no longer than a wave's share of a unit (32 KiB in
+device memory, 2 KiB over the host link's 8 KiB units) travel whole, several
+to a unit. Bytes and published counts must be the oracle's, and the
 same with tail units switched off, for every tail size class, tails that are
 not a whole number of 1 KiB rounds, more pages than one launch carries, a
 last tail unit only partly filled, and every path (the staged path's
@@ -34,6 +36,15 @@ CASES = {
     "tail24k": pool(152, 1024),      # 24 KiB (1 a wave)
     "tail1_5k": pool(224, 592),      # 132,608 B: a 1.5 KiB tail, half a round in its last
     "two_units": pool(272, 1024),    # 272 KiB: two whole units and a 16 KiB tail
+    # pieces no longer than a wave's share of a unit are all tail: device
+    # memory packs 32 KiB or less (1 to 8 a wave), the host link 2 KiB or less
+    "whole240": pool(5, 48),         # 240 B: 8 a wave; host 2 a wave, a fraction of a round each
+    "whole1k": pool(1, 1024),        # 1 KiB: 8 a wave, one round of four used; host 2 a wave
+    "whole2k": pool(2, 1024),        # 2 KiB, a one-token bf16 page of 8 heads: 8 a wave; host 1
+    "whole4k": pool(4, 1024),        # 4 KiB: 8 a wave, every round used; host: a unit each
+    "whole6k": pool(6, 1024),        # 6 KiB: 4 a wave
+    "whole20k": pool(20, 1024),      # 20 KiB: 1 a wave
+    "whole32k": pool(32, 1024),      # 32 KiB: 1 a wave, the largest
 }
 
 
@@ -84,12 +95,20 @@ def test_tail_units_move_the_oracle_bytes(case, n, path, stream):
                 counts = oracle.ready_publish(oracle.ready_publish([0] * w.num_layers, 0, 0, w.num_layers, n),
                                               0, 1, w.num_layers, n)
                 assert [K.kvx_layer_ready(ready, s) for s in range(w.num_layers)] == counts
-                results[tails] = (got, after)
+                # a plain restore too (short pieces travel whole by another
+                # rule without publish), the slots into the pages reversed
+                rdst = dst[::-1].copy()
+                want2 = oracle.restore(L, want, got, rdst, 0, w.num_layers)
+                K.kvx_restore(p.handle, pk.ptr, nb, rdst, 0, w.num_layers, None, 0, stream, PATHS[path])
+                K.kvx_sync(stream)
+                after2 = p.host_image()
+                assert np.array_equal(after2, want2), "plain restore " + diff_report(after2, want2)
+                results[tails] = (got, after, after2)
             finally:
                 K.kvx_ready_destroy(ready)
                 pk.close()
                 p.close()
     finally:
         K.kvx_set_option(K.KVX_OPT_TAIL_UNITS, old)
-    assert np.array_equal(results[0][0], results[1][0])
-    assert np.array_equal(results[0][1], results[1][1])
+    for k in range(3):
+        assert np.array_equal(results[0][k], results[1][k])
