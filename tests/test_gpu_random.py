@@ -88,6 +88,8 @@ TUNING = {
     "RESTORE_CHUNK_LAYERS": [0, 0, 1, 2],
     "STAGED_DMA_ON_CALLER": [-1, 0, 1],
     "PUBLISH_BLOCK": [0, 0, 1, 3, 16, 4096],
+    "COALESCE_RUNS": [1, 1, 0],
+    "TAIL_UNITS": [1, 1, 0],
 }
 NUM_TUNED = 60
 
