@@ -327,6 +327,18 @@ __device__ __forceinline__ void move_at(const UnitGeom& g, const Side& s, const 
         move_unit<D, U, PERM == 1, CP>(g, src, dst, span, u.k * g.chunk_bytes, tid);
 }
 
+// Word i of a move launch's pair or run list: from device memory when the
+// list is longer than the kernel arguments carry, else from the arguments.
+// The device list is read through a constant-address-space pointer: it does
+// not change during the launch, and the index is wave-uniform, so the reads
+// are scalar loads through the scalar cache.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+
+__device__ __forceinline__ int32_t pair_word(const MoveArgs& a, uint32_t i)
+{
+    return a.list ? ((const_i32_ptr)(a.list))[i] : a.pairs[i];
+}
+
 // A tail unit: the tails of the pieces j0 .. j0 + 4 * TPW - 1 of a move
 // launch (those that exist), the last tail_bytes of each after its
 // main_units whole units; with main_units 0 the tail is the whole piece, so
@@ -350,12 +362,12 @@ __device__ __forceinline__ void move_tails(const MoveArgs& a, const UnitPos& u, 
         const uint32_t j = u.j + wave * TPW + t;
         const bool live = j < a.s.npairs;
         const uint32_t jj = live ? j : u.j;
-        uint8_t* pool_piece = a.g.pool + static_cast<int64_t>(a.pairs[2 * jj]) * a.g.page_stride +
+        uint8_t* pool_piece = a.g.pool + static_cast<int64_t>(pair_word(a, 2 * jj)) * a.g.page_stride +
                               static_cast<int64_t>(u.l) * a.g.layer_stride +
                               static_cast<int64_t>(u.c) * a.g.kv_stride;
         uint8_t* pk_piece = a.s.packed +
                             (static_cast<int64_t>(u.l - a.s.pk_layer0) * a.g.num_kv + u.c) * a.s.pk_lc_stride +
-                            static_cast<int64_t>(a.pairs[2 * jj + 1] - a.s.pk_slot0) * a.g.piece_bytes;
+                            static_cast<int64_t>(pair_word(a, 2 * jj + 1) - a.s.pk_slot0) * a.g.piece_bytes;
         const uint32_t bytes = live ? a.g.tail_bytes : 0u;
         src[t] = piece_rsrc((D == GATHER ? pool_piece : pk_piece) + tail0, bytes);
         dst[t] = piece_rsrc((D == GATHER ? pk_piece : pool_piece) + tail0, bytes);
@@ -379,14 +391,14 @@ __device__ __forceinline__ UnitPos decode_run_unit(const MoveArgs& a, uint32_t q
     uint32_t lo = 0, hi = a.s.npairs - 1;   // the last run whose first unit is <= rem
     while (lo < hi) {
         const uint32_t mid = (lo + hi + 1) >> 1;
-        if (static_cast<uint32_t>(a.pairs[4 * mid + 3]) <= rem)
+        if (static_cast<uint32_t>(pair_word(a, 4 * mid + 3)) <= rem)
             lo = mid;
         else
             hi = mid - 1;
     }
     const uint32_t lrel = lc / a.g.num_kv;
     return UnitPos{a.s.layer_begin + static_cast<int32_t>(lrel), lc - lrel * a.g.num_kv, lo,
-                   rem - static_cast<uint32_t>(a.pairs[4 * lo + 3])};
+                   rem - static_cast<uint32_t>(pair_word(a, 4 * lo + 3))};
 }
 
 // Runs f(q) for the unit numbers [0, total) drawn from `queue` in number
@@ -445,13 +457,13 @@ __global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
         uint32_t span;
         if (a.g.runs) {
             u = decode_run_unit(a, q);
-            page = a.pairs[4 * u.j];
-            slot = a.pairs[4 * u.j + 1];
-            span = static_cast<uint32_t>(a.pairs[4 * u.j + 2]) * a.g.piece_bytes;
+            page = pair_word(a, 4 * u.j);
+            slot = pair_word(a, 4 * u.j + 1);
+            span = static_cast<uint32_t>(pair_word(a, 4 * u.j + 2)) * a.g.piece_bytes;
         } else {
             u = decode_unit(a.g, a.s, q);
-            page = a.pairs[2 * u.j];
-            slot = a.pairs[2 * u.j + 1];
+            page = pair_word(a, 2 * u.j);
+            slot = pair_word(a, 2 * u.j + 1);
             span = a.g.piece_bytes;
         }
         const bool tail = a.g.tails_per_wave != 0 && u.k == a.g.main_units;

@@ -93,6 +93,7 @@ struct Tuning {
     int64_t publish_block = 0;            // units per queue draw of device-memory publishing kernels (0 = auto)
     int64_t coalesce_runs = 1;            // move runs of adjacent pages as spans when that takes fewer units
     int64_t tail_units = 1;               // the tails of pieces that 128 KiB units do not tile share units
+    int64_t device_lists = 1;             // lists longer than the kernel arguments carry go to device memory
 };
 Tuning tuning();
 
@@ -101,6 +102,7 @@ Tuning tuning();
 // ---------------------------------------------------------------------------
 constexpr int kThreads = 256;        // 4 wave64 per workgroup
 constexpr int kMaxPairs = 448;       // (page, slot) pairs carried in the kernel arguments
+constexpr int kListHostSlots = 4;    // pinned host buffers a stream's long page lists rotate through
 constexpr int kHostGridAuto = 32;    // default workgroups of a kernel streaming over the host link
 constexpr int64_t kRestoreChunkMin = 32ll << 20;   // default minimum staged restore chunk
 constexpr int64_t kPublishBlockBytes = 2ll << 20;  // auto publish block: about this many bytes
@@ -167,6 +169,9 @@ struct MoveArgs {
     UnitGeom g;
     Side s;
     PublishArgs p;
+    // the launch's (page, slot) pairs or runs: in device memory when `list`
+    // is set (lists longer than the kernel arguments carry), else in `pairs`
+    const int32_t* list;
     int32_t pairs[2 * kMaxPairs];
 };
 static_assert(sizeof(MoveArgs) <= 4096, "kernel arguments are limited to 4 KiB");

@@ -90,6 +90,7 @@ TUNING = {
     "PUBLISH_BLOCK": [0, 0, 1, 3, 16, 4096],
     "COALESCE_RUNS": [1, 1, 0],
     "TAIL_UNITS": [1, 1, 0],
+    "DEVICE_LISTS": [1, 1, 0],
 }
 NUM_TUNED = 60
 
