@@ -29,7 +29,7 @@ is resident in HBM when the timed region starts; crossing the host link is
 part of the method (the host tier is where BACKUP writes and RESTORE reads).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--schedule exchange|streams]
-       [--workload mixed|llama8b|mla_fp8|trtllm_hnd|tiny] [--no-cpu-baseline] [--kernel-only]
+       [--workload mixed|llama8b|mla_fp8|trtllm_hnd|tiny|token_pages] [--no-cpu-baseline] [--kernel-only]
        [--no-extras] [--all-workloads] [--set OPTION=VALUE]
 """
 import argparse
@@ -1046,7 +1046,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="mixed",
                     help="mixed (the 128-request hit/miss stream, default) or a single-request "
-                         "workload: llama8b, mla_fp8, trtllm_hnd, tiny")
+                         "workload: llama8b, mla_fp8, trtllm_hnd, tiny, token_pages (the llama8b "
+                         "shape at one token per page)")
     ap.add_argument("--schedule", choices=["exchange", "streams"], default="exchange",
                     help="mixed: exchange = backup + next restore in one kvx_exchange on two streams, "
                          "streams = one call per request on four streams; single-request workloads: "

@@ -18,6 +18,7 @@
 #include <cstring>
 #include <iterator>
 #include <set>
+#include <type_traits>
 
 #include <rocprofiler-sdk-roctx/roctx.h>
 
@@ -1195,8 +1196,11 @@ struct XSide {
 
 // Fills side x of launch args `a` with pairs [p0, p0 + per) of `xs`;
 // returns the side's work units.
-int64_t exchange_side(const PoolGeom& g, int64_t cpp, const XSide& xs, Side* x, int64_t p0, int64_t per,
-                      ExchangeArgs& a, bool backup)
+// The side's list in the kernel arguments (fill) or, with a device list,
+// only its count; units_of(np) is the side's work units of one (layer, kv).
+template <class F>
+int64_t exchange_side(const PoolGeom& g, F units_of, const XSide& xs, Side* x, int64_t p0, int64_t per,
+                      ExchangeArgs& a, bool backup, bool fill)
 {
     const int64_t np = std::max<int64_t>(0, std::min<int64_t>(per, xs.n - p0));
     x->packed = xs.view;
@@ -1206,13 +1210,14 @@ int64_t exchange_side(const PoolGeom& g, int64_t cpp, const XSide& xs, Side* x, 
     x->layer_begin = xs.l0;
     x->npairs = static_cast<uint32_t>(np);
     int32_t* pages = backup ? a.pages_b : a.pages_r;
-    for (int64_t j = 0; j < np; j++) pages[j] = xs.pages[p0 + j];
+    for (int64_t j = 0; j < np && fill; j++) pages[j] = xs.pages[p0 + j];
     (backup ? a.first_b : a.first_r) = static_cast<int32_t>(p0);
-    return int64_t(xs.l1 - xs.l0) * g.num_kv * np * cpp;
+    return int64_t(xs.l1 - xs.l0) * g.num_kv * units_of(np);
 }
 
-int64_t exchange_side(const PoolGeom& g, int64_t cpp, const XSide& xs, Side* x, int64_t p0, int64_t per,
-                      ExchangeSlotArgs& a, bool backup)
+template <class F>
+int64_t exchange_side(const PoolGeom& g, F units_of, const XSide& xs, Side* x, int64_t p0, int64_t per,
+                      ExchangeSlotArgs& a, bool backup, bool fill)
 {
     const int64_t np = std::max<int64_t>(0, std::min<int64_t>(per, xs.n - p0));
     x->packed = xs.view;
@@ -1222,11 +1227,21 @@ int64_t exchange_side(const PoolGeom& g, int64_t cpp, const XSide& xs, Side* x, 
     x->layer_begin = xs.l0;
     x->npairs = static_cast<uint32_t>(np);
     int32_t* pairs = backup ? a.pairs_b : a.pairs_r;
-    for (int64_t j = 0; j < np; j++) {
+    for (int64_t j = 0; j < np && fill; j++) {
         pairs[2 * j] = xs.pages[p0 + j];
         pairs[2 * j + 1] = xs.slots[p0 + j];
     }
-    return int64_t(xs.l1 - xs.l0) * g.num_kv * np * cpp;
+    return int64_t(xs.l1 - xs.l0) * g.num_kv * units_of(np);
+}
+
+// The device-memory form of an exchange side's list: pages in slot order
+// (packed buffers) or (page, slot) pairs (host pools).
+void side_words(const XSide& xs, bool slot_pairs, std::vector<int32_t>* w)
+{
+    for (int32_t j = 0; j < xs.n; j++) {
+        w->push_back(xs.pages[j]);
+        if (slot_pairs) w->push_back(xs.slots[j]);
+    }
 }
 
 // The launches of one exchange: each interleaves one share of both sides'
@@ -1244,24 +1259,58 @@ int exchange_launches(kvx_pool* pool, const XSide& bk, const XSide& rs, kvx_read
     cfg.cache_policy = 0;   // fixed per side inside the exchange kernel
     setup_geom(pool, host, t, &a.g, &cfg);
     cfg.publish = ready != nullptr;
+    // tail units (tails and whole short pieces) as in one-direction launches
+    TailPlan tp;
+    const bool tails = plan_tails(g, t, host, ready != nullptr, &tp);
+    if (tails) {
+        cfg.unroll = tp.unroll;
+        a.g.chunk_bytes = static_cast<uint32_t>(kThreads * kVecBytes * tp.unroll);
+        a.g.chunks_per_piece = static_cast<uint32_t>((g.piece_bytes + a.g.chunk_bytes - 1) / a.g.chunk_bytes);
+        a.g.tails_per_wave = tp.tails_per_wave;
+        a.g.main_units = tp.main_units;
+        a.g.tail_bytes = tp.tail_bytes;
+    }
+    const int64_t cpp = a.g.chunks_per_piece;
+    auto units_of = [&](int64_t np) { return pair_units(tails ? &tp : nullptr, cpp, np); };
+    // lists longer than the kernel arguments carry: both sides in device
+    // memory and one launch
+    const int32_t* dev = nullptr;
+    if (t.device_lists != 0 && (bk.n > max_pairs || rs.n > max_pairs)) {
+        constexpr bool slot_pairs = std::is_same<A, ExchangeSlotArgs>::value;
+        std::vector<int32_t> words;
+        words.reserve((slot_pairs ? 2 : 1) * (size_t(bk.n) + size_t(rs.n)));
+        side_words(bk, slot_pairs, &words);
+        const size_t len_b = words.size();
+        side_words(rs, slot_pairs, &words);
+        const int rc = lane_upload_list(L, words, &dev);
+        if (rc != KVX_OK) return rc;
+        a.list_b = dev;
+        a.list_r = dev + len_b;
+    }
+    const int64_t launches = dev ? 1
+                                 : std::max<int64_t>((bk.n + max_pairs - 1) / max_pairs,
+                                                     (rs.n + max_pairs - 1) / max_pairs);
+    const int64_t per_b = (bk.n + launches - 1) / launches;
+    const int64_t per_r = (rs.n + launches - 1) / launches;
     Publish pub;
     pub.layer_done = L->layer_done;
     pub.queue = L->layer_done + L->layer_cap;
     if (ready) {
+        // the RESTORE side's units of one layer over all launches
+        int64_t units = 0;
+        for (int64_t k = 0; k < launches; k++)
+            units += units_of(std::max<int64_t>(0, std::min<int64_t>(per_r, rs.n - k * per_r)));
+        if (g.num_kv * units >= (int64_t(1) << 32))
+            return fail(KVX_E_INVAL, "exchange: too many work units for per-layer publish");
         pub.ready = ready->counts_dev + slot_base;
-        pub.layer_target = static_cast<uint32_t>(g.num_kv * int64_t(rs.n) * a.g.chunks_per_piece);
+        pub.layer_target = static_cast<uint32_t>(g.num_kv * units);
         pub.value = static_cast<uint32_t>(rs.n);
     }
     set_publish(&pub, &a.p);
     a.g.unit_order = 0;
-    const int64_t cpp = a.g.chunks_per_piece;
-    const int64_t launches = std::max<int64_t>((bk.n + max_pairs - 1) / max_pairs,
-                                               (rs.n + max_pairs - 1) / max_pairs);
-    const int64_t per_b = (bk.n + launches - 1) / launches;
-    const int64_t per_r = (rs.n + launches - 1) / launches;
     for (int64_t k = 0; k < launches; k++) {
-        const int64_t ub = exchange_side(g, cpp, bk, &a.b, k * per_b, per_b, a, true);
-        const int64_t ur = exchange_side(g, cpp, rs, &a.r, k * per_r, per_r, a, false);
+        const int64_t ub = exchange_side(g, units_of, bk, &a.b, k * per_b, per_b, a, true, !dev);
+        const int64_t ur = exchange_side(g, units_of, rs, &a.r, k * per_r, per_r, a, false, !dev);
         if (ub + ur >= (int64_t(1) << 31))
             return fail(KVX_E_INVAL, "exchange: one launch would have too many work units");
         a.b.total_units = static_cast<uint32_t>(ub);

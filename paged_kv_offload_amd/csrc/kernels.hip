@@ -274,17 +274,19 @@ struct UnitPos {
 __device__ __forceinline__ UnitPos decode_unit(const UnitGeom& g, const Side& s, uint32_t q)
 {
     if (g.tails_per_wave) {
-        // per (layer, kv): the pieces' whole units, then the tail units; a
-        // tail unit is marked k == main_units, j its first piece
-        const uint32_t lc = q / g.units_lc;
-        const uint32_t rem = q - lc * g.units_lc;
+        // per (layer, kv): the side's pieces' whole units, then its tail
+        // units; a tail unit is marked k == main_units, j its first piece
+        const uint32_t per_unit = 4u * g.tails_per_wave;   // pieces a tail unit holds
         const uint32_t main = s.npairs * g.main_units;
+        const uint32_t units_lc = main + (s.npairs + per_unit - 1) / per_unit;
+        const uint32_t lc = q / units_lc;
+        const uint32_t rem = q - lc * units_lc;
         uint32_t j, k;
         if (rem < main) {
             j = rem / g.main_units;
             k = rem - j * g.main_units;
         } else {
-            j = (rem - main) * 4u * g.tails_per_wave;
+            j = (rem - main) * per_unit;
             k = g.main_units;
         }
         const uint32_t lrel = lc / g.num_kv;
@@ -349,26 +351,27 @@ __device__ __forceinline__ int32_t pair_word(const MoveArgs& a, uint32_t i)
 // resource (a missing piece gets a resource of length zero). Wave-uniform
 // throughout: the wave index is read through readfirstlane so that every
 // resource stays scalar.
-template <Dir D, int U, int TPW, int CP>
-__device__ __forceinline__ void move_tails(const MoveArgs& a, const UnitPos& u, uint32_t tid)
+template <Dir D, int U, int TPW, int CP, class PS>
+__device__ __forceinline__ void move_tails(const UnitGeom& g, const Side& s, const UnitPos& u, PS page_slot,
+                                           uint32_t tid)
 {
     constexpr int TR = U / TPW;   // rounds per tail
     const uint32_t wave = static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(tid >> 6)));
     const uint32_t lane_off = (tid & 63u) * kVecBytes;
-    const uint32_t tail0 = a.g.main_units * a.g.chunk_bytes;
+    const uint32_t tail0 = g.main_units * g.chunk_bytes;
     rsrc_t src[TPW], dst[TPW];
 #pragma unroll
     for (int t = 0; t < TPW; t++) {
         const uint32_t j = u.j + wave * TPW + t;
-        const bool live = j < a.s.npairs;
+        const bool live = j < s.npairs;
         const uint32_t jj = live ? j : u.j;
-        uint8_t* pool_piece = a.g.pool + static_cast<int64_t>(pair_word(a, 2 * jj)) * a.g.page_stride +
-                              static_cast<int64_t>(u.l) * a.g.layer_stride +
-                              static_cast<int64_t>(u.c) * a.g.kv_stride;
-        uint8_t* pk_piece = a.s.packed +
-                            (static_cast<int64_t>(u.l - a.s.pk_layer0) * a.g.num_kv + u.c) * a.s.pk_lc_stride +
-                            static_cast<int64_t>(pair_word(a, 2 * jj + 1) - a.s.pk_slot0) * a.g.piece_bytes;
-        const uint32_t bytes = live ? a.g.tail_bytes : 0u;
+        const int32_t page = page_slot.page(jj), slot = page_slot.slot(jj);
+        uint8_t* pool_piece = g.pool + static_cast<int64_t>(page) * g.page_stride +
+                              static_cast<int64_t>(u.l) * g.layer_stride +
+                              static_cast<int64_t>(u.c) * g.kv_stride;
+        uint8_t* pk_piece = s.packed + (static_cast<int64_t>(u.l - s.pk_layer0) * g.num_kv + u.c) * s.pk_lc_stride +
+                            static_cast<int64_t>(slot - s.pk_slot0) * g.piece_bytes;
+        const uint32_t bytes = live ? g.tail_bytes : 0u;
         src[t] = piece_rsrc((D == GATHER ? pool_piece : pk_piece) + tail0, bytes);
         dst[t] = piece_rsrc((D == GATHER ? pk_piece : pool_piece) + tail0, bytes);
     }
@@ -378,6 +381,43 @@ __device__ __forceinline__ void move_tails(const MoveArgs& a, const UnitPos& u, 
 #pragma unroll
     for (int r = 0; r < U; r++) store16s<CP>(dst[r / TR], lane_off, (r % TR) * (64u * kVecBytes), v[r]);
 }
+
+// Moves unit `u` of a side: a tail unit (tail units are built for units of
+// 32 rounds in device memory and 2 over the host link, without reordered
+// rows) or a chunk of the piece or run at (page, slot) spanning `span`
+// bytes. page_slot(j) gives pair j of the side for tail units.
+template <Dir D, int U, int PERM, int CP, class PS>
+__device__ __forceinline__ void move_side(const UnitGeom& g, const Side& s, const UnitPos& u, int32_t page,
+                                          int32_t slot, uint32_t span, PS page_slot, uint32_t tid, v4u* lds)
+{
+    if constexpr ((U == 32 || U == 2) && PERM == 0) {
+        if (g.tails_per_wave != 0 && u.k == g.main_units) {
+            if constexpr (U == 32) {
+                switch (g.tails_per_wave) {
+                case 1: move_tails<D, U, 1, CP>(g, s, u, page_slot, tid); break;
+                case 2: move_tails<D, U, 2, CP>(g, s, u, page_slot, tid); break;
+                case 4: move_tails<D, U, 4, CP>(g, s, u, page_slot, tid); break;
+                default: move_tails<D, U, 8, CP>(g, s, u, page_slot, tid); break;
+                }
+            } else {
+                // the host link's 8 KiB units: one or two short pieces a wave
+                if (g.tails_per_wave == 1)
+                    move_tails<D, U, 1, CP>(g, s, u, page_slot, tid);
+                else
+                    move_tails<D, U, 2, CP>(g, s, u, page_slot, tid);
+            }
+            return;
+        }
+    }
+    move_at<D, U, PERM, CP>(g, s, u, page, slot, span, tid, lds);
+}
+
+// Pair j of a move launch's (page, slot) list.
+struct MovePairs {
+    const MoveArgs& a;
+    __device__ int32_t page(uint32_t j) const { return pair_word(a, 2 * j); }
+    __device__ int32_t slot(uint32_t j) const { return pair_word(a, 2 * j + 1); }
+};
 
 // Position of unit q of a move launch over runs of adjacent pages: run r of
 // the launch starts at pairs[4r] (page) and pairs[4r + 1] (slot), spans
@@ -466,7 +506,6 @@ __global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
             slot = pair_word(a, 2 * u.j + 1);
             span = a.g.piece_bytes;
         }
-        const bool tail = a.g.tails_per_wave != 0 && u.k == a.g.main_units;
         if constexpr (PUBLISH) {
             // units arrive layer by layer: count a layer once this workgroup leaves it
             if (u.l != pend_layer) {
@@ -475,31 +514,7 @@ __global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
                 pend = 0;
             }
         }
-        if constexpr (U == 32 && PERM == 0) {
-            if (tail) {
-                switch (a.g.tails_per_wave) {
-                case 1: move_tails<D, U, 1, CP>(a, u, tid); break;
-                case 2: move_tails<D, U, 2, CP>(a, u, tid); break;
-                case 4: move_tails<D, U, 4, CP>(a, u, tid); break;
-                default: move_tails<D, U, 8, CP>(a, u, tid); break;
-                }
-            } else {
-                move_at<D, U, PERM, CP>(a.g, a.s, u, page, slot, span, tid, lds);
-            }
-        } else if constexpr (U == 2 && PERM == 0) {
-            // the host link's 8 KiB units: one or two short pieces a wave
-            if (tail) {
-                if (a.g.tails_per_wave == 1)
-                    move_tails<D, U, 1, CP>(a, u, tid);
-                else
-                    move_tails<D, U, 2, CP>(a, u, tid);
-            } else {
-                move_at<D, U, PERM, CP>(a.g, a.s, u, page, slot, span, tid, lds);
-            }
-        } else {
-            (void)tail;
-            move_at<D, U, PERM, CP>(a.g, a.s, u, page, slot, span, tid, lds);
-        }
+        move_side<D, U, PERM, CP>(a.g, a.s, u, page, slot, span, MovePairs{a}, tid, lds);
         if constexpr (PUBLISH) pend++;
     };
 
@@ -537,21 +552,47 @@ __global__ __launch_bounds__(kThreads) void kvx_move_kernel(MoveArgs a)
 // the same work as two kernels on two streams drifts out of step and falls
 // to 67-76 GB/s. Only the RESTORE side publishes.
 // Page and packed slot of pair j of a side: listed in slot order from
-// first_x (packed buffers), or as explicit (page, slot) pairs (host pools).
-__device__ __forceinline__ int32_t page_b(const ExchangeArgs& a, uint32_t j) { return a.pages_b[j]; }
+// first_x (packed buffers), or as explicit (page, slot) pairs (host pools);
+// in device memory (list_x, read through scalar loads) when the list is
+// longer than the kernel arguments carry.
+__device__ __forceinline__ int32_t list_word(const int32_t* list, const int32_t* args, uint32_t i)
+{
+    return list ? ((const_i32_ptr)(list))[i] : args[i];
+}
+__device__ __forceinline__ int32_t page_b(const ExchangeArgs& a, uint32_t j) { return list_word(a.list_b, a.pages_b, j); }
 __device__ __forceinline__ int32_t slot_b(const ExchangeArgs& a, uint32_t j)
 {
     return a.first_b + static_cast<int32_t>(j);
 }
-__device__ __forceinline__ int32_t page_r(const ExchangeArgs& a, uint32_t j) { return a.pages_r[j]; }
+__device__ __forceinline__ int32_t page_r(const ExchangeArgs& a, uint32_t j) { return list_word(a.list_r, a.pages_r, j); }
 __device__ __forceinline__ int32_t slot_r(const ExchangeArgs& a, uint32_t j)
 {
     return a.first_r + static_cast<int32_t>(j);
 }
-__device__ __forceinline__ int32_t page_b(const ExchangeSlotArgs& a, uint32_t j) { return a.pairs_b[2 * j]; }
-__device__ __forceinline__ int32_t slot_b(const ExchangeSlotArgs& a, uint32_t j) { return a.pairs_b[2 * j + 1]; }
-__device__ __forceinline__ int32_t page_r(const ExchangeSlotArgs& a, uint32_t j) { return a.pairs_r[2 * j]; }
-__device__ __forceinline__ int32_t slot_r(const ExchangeSlotArgs& a, uint32_t j) { return a.pairs_r[2 * j + 1]; }
+__device__ __forceinline__ int32_t page_b(const ExchangeSlotArgs& a, uint32_t j)
+{
+    return list_word(a.list_b, a.pairs_b, 2 * j);
+}
+__device__ __forceinline__ int32_t slot_b(const ExchangeSlotArgs& a, uint32_t j)
+{
+    return list_word(a.list_b, a.pairs_b, 2 * j + 1);
+}
+__device__ __forceinline__ int32_t page_r(const ExchangeSlotArgs& a, uint32_t j)
+{
+    return list_word(a.list_r, a.pairs_r, 2 * j);
+}
+__device__ __forceinline__ int32_t slot_r(const ExchangeSlotArgs& a, uint32_t j)
+{
+    return list_word(a.list_r, a.pairs_r, 2 * j + 1);
+}
+
+// Pair j of an exchange's BACKUP (B) or RESTORE side.
+template <class A, bool B>
+struct SidePairs {
+    const A& a;
+    __device__ int32_t page(uint32_t j) const { return B ? page_b(a, j) : page_r(a, j); }
+    __device__ int32_t slot(uint32_t j) const { return B ? slot_b(a, j) : slot_r(a, j); }
+};
 
 template <int U, int PERM, bool PUBLISH, bool HOST, class A>
 __global__ __launch_bounds__(kThreads) void kvx_exchange_kernel(A a)
@@ -578,8 +619,8 @@ __global__ __launch_bounds__(kThreads) void kvx_exchange_kernel(A a)
         }
         if (gather) {
             const UnitPos u = decode_unit(a.g, a.b, idx);
-            move_at<GATHER, U, PERM, CPG>(a.g, a.b, u, page_b(a, u.j), slot_b(a, u.j), a.g.piece_bytes, tid,
-                                          lds);
+            move_side<GATHER, U, PERM, CPG>(a.g, a.b, u, page_b(a, u.j), slot_b(a, u.j), a.g.piece_bytes,
+                                            SidePairs<A, true>{a}, tid, lds);
         } else {
             const UnitPos u = decode_unit(a.g, a.r, idx);
             if constexpr (PUBLISH) {
@@ -589,8 +630,8 @@ __global__ __launch_bounds__(kThreads) void kvx_exchange_kernel(A a)
                     pend = 0;
                 }
             }
-            move_at<SCATTER, U, PERM, CPS>(a.g, a.r, u, page_r(a, u.j), slot_r(a, u.j), a.g.piece_bytes,
-                                           tid, lds);
+            move_side<SCATTER, U, PERM, CPS>(a.g, a.r, u, page_r(a, u.j), slot_r(a, u.j), a.g.piece_bytes,
+                                             SidePairs<A, false>{a}, tid, lds);
             if constexpr (PUBLISH) pend++;
         }
     };

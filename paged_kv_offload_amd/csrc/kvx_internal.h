@@ -127,11 +127,12 @@ struct UnitGeom {
     uint32_t TU, seg, mg_seg;            // LDS token blocks: tokens per unit, TU * row_vec
     uint32_t unit_order;     // bit 0: XCD-contiguous unit numbering; bit 1: rotate chunks
     uint32_t runs;           // move launches: 1 = the pair list holds runs of adjacent pages
-    uint32_t units_lc;       // runs, tails: work units of one (layer, kv) in the launch
-    // tails (move launches over pairs, units of 32 rounds in device memory
-    // or 2 over the host link): a piece is main_units whole units (possibly
-    // none) and a tail of tail_bytes; the tails of tails_per_wave * 4 pieces
-    // share one unit, each wave moving tails_per_wave of them
+    uint32_t units_lc;       // runs: work units of one (layer, kv) in the launch
+    // tails (launches over pairs, not runs; units of 32 rounds in device
+    // memory or 2 over the host link): a piece is main_units whole units
+    // (possibly none) and a tail of tail_bytes; the tails of
+    // tails_per_wave * 4 consecutive pairs of a side share one unit, each
+    // wave moving tails_per_wave of them
     uint32_t tails_per_wave; // 0: no tail units (a piece's last unit may be partial)
     uint32_t main_units;
     uint32_t tail_bytes;
@@ -183,6 +184,8 @@ struct ExchangeArgs {
     UnitGeom g;
     Side b, r;
     PublishArgs p;
+    const int32_t* list_b;   // the sides' pages in device memory (lists longer than
+    const int32_t* list_r;   // the arguments carry), else pages_b / pages_r
     int32_t first_b, first_r;
     int32_t pages_b[kMaxPairs];
     int32_t pages_r[kMaxPairs];
@@ -196,6 +199,8 @@ struct ExchangeSlotArgs {
     UnitGeom g;
     Side b, r;
     PublishArgs p;
+    const int32_t* list_b;   // the sides' (page, slot) pairs in device memory, else
+    const int32_t* list_r;   // pairs_b / pairs_r
     int32_t pairs_b[2 * kMaxSlotPairs];
     int32_t pairs_r[2 * kMaxSlotPairs];
 };

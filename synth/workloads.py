@@ -1,4 +1,5 @@
-"""The five synthetic pool workloads (shapes, seeds and page-ID schedules).
+"""The five synthetic pool workloads (shapes, seeds and page-ID schedules),
+and one more: the Llama-shaped pool at one token per page.
 
 Shapes follow the pools the source pages describe: a Llama-3-8B-shaped bf16
 pool, an MLA/latent fp8 pool with page size 256 as in the PP-ticket PR's
@@ -109,6 +110,14 @@ WORKLOADS: Dict[str, Workload] = {
                  dtype_bytes=2, pages_per_request=256, seed=105,
                  description="bf16 NHD pool [32L][2][8192 pages][64 tok][8 heads][128]; 128 "
                              "alternating backup/restore requests of 256 pages, 4 in flight"),
+    # not one of the five: the Llama-shaped pool at one token per page, whose
+    # 16,384-token request names 16,384 pages of 2 KiB pieces
+    "token_pages": _wl(name="token_pages", outer=("layer", "kv", "page"), inner="NHD",
+                       num_pages=131072, num_layers=32, num_kv=2, page_size=1, num_heads=8,
+                       head_dim=128, dtype_bytes=2, pages_per_request=16384, seed=106,
+                       description="Llama-3-8B-shaped bf16 NHD pool at one token per page "
+                                   "[32L][2][131072 pages][1 tok][8 heads][128]; one 16384-token "
+                                   "request = 16384 fragmented pages"),
 }
 
 
