@@ -1,5 +1,7 @@
 """GPU parity at full workload sizes, in the launch configuration the benchmark
-times (default tuning; staged and zero-copy paths).
+times (default tuning; staged and zero-copy paths); also the llama8b shape at
+one token per page, whose 16,384-page requests travel as device page lists
+and whole 2 KiB pieces.
 
 Pools are filled on the GPU from the seeded generator, so the oracle's
 closed forms give every expected byte without a host copy of the input:
@@ -78,7 +80,7 @@ def check_alloc(w, L, seed, src, dst, l0, l1, alloc_dev):
 
 
 @pytest.mark.parametrize("path", ["staged", "zerocopy"])
-@pytest.mark.parametrize("name", ["llama8b", "trtllm_hnd"])
+@pytest.mark.parametrize("name", ["llama8b", "trtllm_hnd", "token_pages"])
 def test_full_size_backup_restore(name, path):
     t = torch()
     w = WORKLOADS[name]
@@ -114,7 +116,7 @@ def test_full_size_backup_restore(name, path):
         pool.close()
 
 
-@pytest.mark.parametrize("name", ["llama8b", "mla_fp8"])
+@pytest.mark.parametrize("name", ["llama8b", "mla_fp8", "token_pages"])
 def test_full_size_device_path_as_benchmarked(name):
     """The benchmark's roofline calls at full size: the request packed into
     a device buffer in one call (the whole packed buffer checked against
