@@ -67,8 +67,11 @@ def pcie_protocol_bound(payload=256, write_overhead=24, completion_overhead=20, 
                        f"one {request_bytes} B read request per completion, no link-layer packets"}
 
 
-# pages one move-kernel launch carries; a call over more pages is split into
-# equal launches (the roofline figures of such a call are per call)
+# pages one move-kernel launch carries in its arguments; a longer page list
+# goes to device memory and one launch serves the call (KVX_OPT_DEVICE_LISTS;
+# the exception, plain device-memory kernels of units under 32 KiB, is no
+# workload here), else the call is split into equal launches and the roofline
+# figures of such a call are per call
 PAGES_PER_LAUNCH = 448
 
 # HBM bytes per launch of the roofline kernel from the two rocprofv3 --pmc runs
@@ -76,15 +79,16 @@ PAGES_PER_LAUNCH = 448
 # profiles/pack_kernel_<workload>.txt). Valid only for the kernel source they
 # were taken on: reported as null once kernels.hip changes.
 MEASURED_TRAFFIC = {
-    "mixed": {"kernels_hip_sha256": "273cf3f4be5d93efe111820ec96b545f8bd228ff5440622d98922579320fb8c9",
-              "bytes_per_launch": 4295193769},
-    "llama8b": {"kernels_hip_sha256": "273cf3f4be5d93efe111820ec96b545f8bd228ff5440622d98922579320fb8c9",
-                "bytes_per_launch": 4295194428},
-    "mla_fp8": {"kernels_hip_sha256": "273cf3f4be5d93efe111820ec96b545f8bd228ff5440622d98922579320fb8c9",
-                "bytes_per_launch": 1151478773},
-    # one call = two launches of 256 pages: the bytes of both
-    "trtllm_hnd": {"kernels_hip_sha256": "273cf3f4be5d93efe111820ec96b545f8bd228ff5440622d98922579320fb8c9",
-                   "bytes_per_launch": 4295474956},
+    "mixed": {"kernels_hip_sha256": "7409122c65a142f1e173debb13fb5d3717886e3b8859fdcc56f5484941b6cc35",
+            "bytes_per_launch": 4295192767},
+    "llama8b": {"kernels_hip_sha256": "7409122c65a142f1e173debb13fb5d3717886e3b8859fdcc56f5484941b6cc35",
+              "bytes_per_launch": 4295191652},
+    "mla_fp8": {"kernels_hip_sha256": "7409122c65a142f1e173debb13fb5d3717886e3b8859fdcc56f5484941b6cc35",
+              "bytes_per_launch": 1151511736},
+    "trtllm_hnd": {"kernels_hip_sha256": "7409122c65a142f1e173debb13fb5d3717886e3b8859fdcc56f5484941b6cc35",
+                 "bytes_per_launch": 4295389723},
+    "token_pages": {"kernels_hip_sha256": "7409122c65a142f1e173debb13fb5d3717886e3b8859fdcc56f5484941b6cc35",
+                  "bytes_per_launch": 4306347663},
 }
 
 
@@ -485,7 +489,7 @@ def single_main(args, options, w, quiet=False):
                 "achieved": kern["pack"]["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": kern["pack"]["frac"], "traffic": measured_traffic(w.name),
                 "algorithmic_bytes_per_launch": 2 * P, "avg_launch_ms": kern["pack"]["avg_launch_ms"],
-                "launches_per_call": -(-n // PAGES_PER_LAUNCH)}
+                "launches_per_call": 1 if K.kvx_get_option(K.KVX_OPT_DEVICE_LISTS) else -(-n // PAGES_PER_LAUNCH)}
     if args.kernel_only:
         print(json.dumps({"roofline": roofline, "device_kernels": kern, "options": options}), flush=True)
         return None
