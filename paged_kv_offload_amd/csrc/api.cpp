@@ -169,11 +169,63 @@ struct Lane {
     int64_t list_host_cap[kListHostSlots] = {};
     hipEvent_t list_sent[kListHostSlots] = {};
     int list_next = 0;
+    // recorded after each zero-copy call's launches (under g_link_mu): other
+    // streams' zero-copy calls see whether this one still uses the link
+    hipEvent_t link_ev = nullptr;
     std::mutex mu;
 };
 
 std::mutex g_lanes_mu;
 std::map<std::pair<int, hipStream_t>, Lane*> g_lanes;
+
+// Lanes that ran zero-copy calls, and every lane's link_ev. Taken inside a
+// lane's mutex (or with none held), never around one.
+std::mutex g_link_mu;
+std::vector<Lane*> g_link_lanes;
+
+// Zero-copy BACKUP and RESTORE calls of other streams whose launches have
+// not finished on L's GPU.
+int link_others(const Lane* L)
+{
+    std::lock_guard<std::mutex> lk(g_link_mu);
+    int n = 0;
+    for (const Lane* o : g_link_lanes) {
+        if (o == L || o->device != L->device || !o->link_ev) continue;
+        if (hipEventQuery(o->link_ev) == hipErrorNotReady) {
+            (void)hipGetLastError();
+            n++;
+        }
+    }
+    return n;
+}
+
+int link_record(Lane* L, hipStream_t s)
+{
+    std::lock_guard<std::mutex> lk(g_link_mu);
+    if (!L->link_ev) {
+        KVX_HIP(hipEventCreateWithFlags(&L->link_ev, hipEventDisableTiming));
+        g_link_lanes.push_back(L);
+    }
+    KVX_HIP(hipEventRecord(L->link_ev, s));
+    return KVX_OK;
+}
+
+// Workgroups of a one-direction kernel over the host link, given the other
+// streams' zero-copy calls in flight. Alone, kHostGridAuto (32 x 8 KiB units
+// in flight cover the link's round trip); beside others, a share of
+// kHostLinkBudget. Measured on MI355X, the mixed stream's 128 requests as
+// separate zero-copy calls on four streams (two writing host memory, two
+// reading it): 32 workgroups a kernel 61.6 GB/s, 16 77.2, 12 82.6, 8 82.3;
+// one call alone: 32 workgroups 57.0 / 57.6 GB/s (backup / restore), 24
+// 56.6 / 57.6, 16 55.1 / 57.5, 12 57.0 / 48.3. Workgroups that only write
+// host memory outpace those that only read it, and with many of both the
+// reads fall behind; a kernel that interleaves both (kvx_exchange) is not
+// affected.
+int link_grid(const Lane* L)
+{
+    const int others = link_others(L);
+    return std::min(kHostGridAuto, std::max(8, kHostLinkBudget / (others + 1)));
+}
 
 int lane_init(Lane* L)
 {
@@ -232,6 +284,12 @@ void lane_free(Lane* L)
     if (L->ev_done) check(hipEventDestroy(L->ev_done), "hipEventDestroy");
     if (L->ring) check(hipFree(L->ring), "hipFree of the staging ring");
     if (L->layer_done) check(hipFree(L->layer_done), "hipFree of the per-layer counters");
+    {
+        std::lock_guard<std::mutex> lk(g_link_mu);
+        g_link_lanes.erase(std::remove(g_link_lanes.begin(), g_link_lanes.end(), L), g_link_lanes.end());
+        if (L->link_ev) check(hipEventDestroy(L->link_ev), "hipEventDestroy");
+        L->link_ev = nullptr;
+    }
     if (L->list_dev) check(hipFree(L->list_dev), "hipFree of the page list");
     for (int h = 0; h < kListHostSlots; h++) {
         if (L->list_sent[h]) check(hipEventDestroy(L->list_sent[h]), "hipEventDestroy");
@@ -436,6 +494,7 @@ struct Target {
     int32_t pk_layer0, pk_slot0;
     int64_t pk_slots;      // slots stored per (layer, kv) in `packed`
     bool host;             // `packed` is pinned host memory read or written over the link
+    int host_grid = 0;     // host: workgroups per launch (0: kHostGridAuto)
 };
 
 struct Publish {
@@ -742,7 +801,7 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
             if (t.grid_max > 0) {
                 gmax = t.grid_max;
             } else if (tg.host) {
-                gmax = t.host_grid_max > 0 ? t.host_grid_max : kHostGridAuto;
+                gmax = t.host_grid_max > 0 ? t.host_grid_max : tg.host_grid > 0 ? tg.host_grid : kHostGridAuto;
             } else if (pub) {
                 gmax = std::min<int64_t>(int64_t(cu_count) * 8, std::max<int64_t>(cu_count, per_layer / 4));
             } else if (a.g.chunk_bytes >= (32u << 10)) {
@@ -1062,9 +1121,11 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
     if (path != KVX_PATH_STAGED) {
         rc = upload_list();
         if (rc != KVX_OK) return rc;
-        Target tg{view, 0, 0, hs ? hs->num : int64_t(n), path == KVX_PATH_ZEROCOPY};
+        const bool zc = path == KVX_PATH_ZEROCOPY;
+        Target tg{view, 0, 0, hs ? hs->num : int64_t(n), zc, zc ? link_grid(L) : 0};
         rc = launch_range(dir, pool, tg, l0, l1, pairs.data(), pairs.size(), pubp, t, L->cu_count, s,
                           nullptr, use_runs ? &runs : nullptr, dev_list);
+        if (rc == KVX_OK && zc) rc = link_record(L, s);
     } else {
         // chunks of whole layers when one layer fits a ring slot, else slot
         // ranges of one layer
