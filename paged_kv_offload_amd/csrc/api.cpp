@@ -169,8 +169,8 @@ struct Lane {
     int64_t list_host_cap[kListHostSlots] = {};
     hipEvent_t list_sent[kListHostSlots] = {};
     int list_next = 0;
-    // recorded after each zero-copy call's launches (under g_link_mu): other
-    // streams' zero-copy calls see whether this one still uses the link
+    // recorded after each zero-copy or staged call (under g_link_mu): other
+    // streams' calls see whether this one still uses the host link
     hipEvent_t link_ev = nullptr;
     std::mutex mu;
 };
@@ -183,8 +183,8 @@ std::map<std::pair<int, hipStream_t>, Lane*> g_lanes;
 std::mutex g_link_mu;
 std::vector<Lane*> g_link_lanes;
 
-// Zero-copy BACKUP and RESTORE calls of other streams whose launches have
-// not finished on L's GPU.
+// Zero-copy and staged BACKUP and RESTORE calls of other streams whose work
+// has not finished on L's GPU.
 int link_others(const Lane* L)
 {
     std::lock_guard<std::mutex> lk(g_link_mu);
@@ -211,7 +211,7 @@ int link_record(Lane* L, hipStream_t s)
 }
 
 // Workgroups of a one-direction kernel over the host link, given the other
-// streams' zero-copy calls in flight. Alone, kHostGridAuto (32 x 8 KiB units
+// streams' host-link calls in flight. Alone, kHostGridAuto (32 x 8 KiB units
 // in flight cover the link's round trip); beside others, a share of
 // kHostLinkBudget. Measured on MI355X, the mixed stream's 128 requests as
 // separate zero-copy calls on four streams (two writing host memory, two
@@ -1153,11 +1153,16 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
         // DMA on the library's side stream (overlaps the next chunk's kernel)
         // or on the caller's stream (stream order alone; no cross-stream
         // events). Auto: the side stream when there is a next chunk to
-        // overlap, else the caller's stream (measured on the tiny pool's
-        // 128 KiB request, call to completion: backup 62 -> 32 us, restore
-        // 52 -> 24 us).
+        // overlap and no other stream's host-link call is in flight, else
+        // the caller's stream. Measured on MI355X: the tiny pool's 128 KiB
+        // request (one chunk), call to completion: backup 62 -> 32 us,
+        // restore 52 -> 24 us on the caller's stream; a 2 GiB llama8b call
+        // alone: 56.3 / 55.9 GB/s (backup / restore) with the side stream,
+        // 55.5 / 55.3 without; the mixed stream as separate staged calls on
+        // four streams: 42.0 GB/s with side streams, 80.4 without.
         const bool one_chunk = (l1 - l0) <= layers_per_chunk && slots_per_chunk >= n;
-        const bool on_caller = t.staged_dma_on_caller > 0 || (t.staged_dma_on_caller < 0 && one_chunk);
+        const bool on_caller = t.staged_dma_on_caller > 0 ||
+                               (t.staged_dma_on_caller < 0 && (one_chunk || link_others(L) > 0));
         if (!on_caller && !L->side) KVX_HIP(hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking));
         hipStream_t dma = on_caller ? s : L->side;
         const bool split = dma != s;
@@ -1238,6 +1243,8 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
             KVX_HIP(hipEventRecord(L->ev_done, dma));
             KVX_HIP(hipStreamWaitEvent(s, L->ev_done, 0));
         }
+        // the caller's stream has passed the call once its copies are done
+        if (rc == KVX_OK) rc = link_record(L, s);
     }
     return rc;
 }
