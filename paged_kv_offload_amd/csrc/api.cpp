@@ -172,14 +172,15 @@ struct Lane {
     // recorded after each zero-copy or staged call (under g_link_mu): other
     // streams' calls see whether this one still uses the host link
     hipEvent_t link_ev = nullptr;
+    bool link_busy = false;         // link_ev recorded and not yet seen complete
     std::mutex mu;
 };
 
 std::mutex g_lanes_mu;
 std::map<std::pair<int, hipStream_t>, Lane*> g_lanes;
 
-// Lanes that ran zero-copy calls, and every lane's link_ev. Taken inside a
-// lane's mutex (or with none held), never around one.
+// Lanes that ran host-link calls, and every lane's link_ev and link_busy.
+// Taken inside a lane's mutex (or with none held), never around one.
 std::mutex g_link_mu;
 std::vector<Lane*> g_link_lanes;
 
@@ -189,11 +190,13 @@ int link_others(const Lane* L)
 {
     std::lock_guard<std::mutex> lk(g_link_mu);
     int n = 0;
-    for (const Lane* o : g_link_lanes) {
-        if (o == L || o->device != L->device || !o->link_ev) continue;
+    for (Lane* o : g_link_lanes) {
+        if (o == L || o->device != L->device || !o->link_busy) continue;
         if (hipEventQuery(o->link_ev) == hipErrorNotReady) {
             (void)hipGetLastError();
             n++;
+        } else {
+            o->link_busy = false;   // done: not queried again until its next call
         }
     }
     return n;
@@ -207,6 +210,7 @@ int link_record(Lane* L, hipStream_t s)
         g_link_lanes.push_back(L);
     }
     KVX_HIP(hipEventRecord(L->link_ev, s));
+    L->link_busy = true;
     return KVX_OK;
 }
 
