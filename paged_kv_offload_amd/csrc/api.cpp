@@ -839,8 +839,13 @@ int launch_range(Dir dir, const kvx_pool* pool, const Target& tg, int32_t la, in
             if (pub && !tg.host) {
                 int64_t b = t.publish_block;
                 if (b <= 0) {
+                    // bytes a unit moves: its capacity, or the whole short
+                    // pieces it holds
+                    int64_t unit_bytes = a.g.chunk_bytes;
+                    if (tails && tp.main_units == 0)
+                        unit_bytes = std::min<int64_t>(unit_bytes, int64_t(4) * tp.tails_per_wave * tp.tail_bytes);
                     const int64_t bmax = std::max<int64_t>(1, std::min<int64_t>(
-                        kPublishBlockBytes / a.g.chunk_bytes, std::max<int64_t>(1, a.s.total_units / grid)));
+                        kPublishBlockBytes / unit_bytes, std::max<int64_t>(1, a.s.total_units / grid)));
                     int64_t best = 1, best_cost = INT64_MAX;
                     for (int64_t c = bmax; c >= std::max<int64_t>(1, bmax / 2); c--) {
                         if (per_layer % c != 0) continue;
@@ -1406,8 +1411,12 @@ int exchange_launches(kvx_pool* pool, const XSide& bk, const XSide& rs, kvx_read
         a.p.block = 1;
         if (!host) {
             int64_t b = t.publish_block;
+            // bytes a unit moves: its capacity, or the whole short pieces it holds
+            int64_t unit_bytes = a.g.chunk_bytes;
+            if (tails && tp.main_units == 0)
+                unit_bytes = std::min<int64_t>(unit_bytes, int64_t(4) * tp.tails_per_wave * tp.tail_bytes);
             if (b <= 0)
-                b = std::min<int64_t>(std::max<int64_t>(1, kPublishBlockBytes / a.g.chunk_bytes),
+                b = std::min<int64_t>(std::max<int64_t>(1, kPublishBlockBytes / unit_bytes),
                                       std::max<int64_t>(1, (ub + ur) / cfg.grid));
             a.p.block = static_cast<uint32_t>(b);
         }
