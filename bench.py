@@ -989,14 +989,15 @@ def cpu_model():
 
 
 def cpu_baseline_all_cores(w, budget_s: float = 8.0, max_threads: int = 16):
-    """The same oracle calls from one host thread per core (the process's
-    affinity set, at most max_threads) over the pieces of ONE host pool:
-    the pool and its packed buffer have one layer per thread, and thread k
-    runs backup + restore passes of layer k (its own pieces of the pool and
-    its own slice of the packed buffer, so no two threads touch the same
-    bytes) for about budget_s seconds. The oracle's C functions run without
-    the interpreter lock, so the threads run in parallel; the oracle itself
-    is unchanged."""
+    """The oracle from one host thread per core (the process's affinity set,
+    at most max_threads) over the (layer, kv, page) pieces of ONE host pool
+    and one request: thread k takes every threads-th page of the request and
+    runs backup + restore passes of its pages' pieces in every layer and kv
+    (the slot-addressed oracle calls, each page to its own slot of the
+    request's packed buffer, so no two threads touch the same bytes) for
+    about budget_s seconds. The oracle's C functions run without the
+    interpreter lock, so the threads run in parallel; the oracle itself is
+    unchanged."""
     import threading
 
     import numpy as np
@@ -1006,22 +1007,25 @@ def cpu_baseline_all_cores(w, budget_s: float = 8.0, max_threads: int = 16):
 
     threads = max(1, min(max_threads, len(os.sched_getaffinity(0))))
     n = w.pages_per_request
-    sample = w.scaled(num_pages=2 * n, num_layers=threads)
+    sample = w.scaled(num_pages=2 * n, num_layers=4)
+    NL = sample.num_layers
     L = oracle_layout_of(oracle, sample)
     alloc = np.full(sample.pool_bytes, 0x5A, dtype=np.uint8)
     host = np.zeros(sample.host_bytes(n), dtype=np.uint8)
     perm = synth.page_perm(w.seed, 2 * n)
     src, dst = perm[:n].copy(), perm[n:].copy()
-    per_pass = 2 * sample.num_kv * n * sample.piece_bytes
+    mine = [np.arange(k, n, threads, dtype=np.int32) for k in range(threads)]
     passes = [0] * threads
     start = threading.Barrier(threads + 1)
     stop = threading.Event()
 
     def worker(k):
+        slots = mine[k]
+        s_ids, d_ids = src[slots].copy(), dst[slots].copy()
         start.wait()
         while not stop.is_set():
-            oracle.backup(L, alloc, src, k, k + 1, host=host)
-            oracle.restore(L, alloc, host, dst, k, k + 1, out=alloc)
+            oracle.backup_slots(L, alloc, s_ids, slots, n, 0, NL, host=host)
+            oracle.restore_slots(L, alloc, host, slots, d_ids, n, 0, NL, out=alloc)
             passes[k] += 1
 
     ths = [threading.Thread(target=worker, args=(k,)) for k in range(threads)]
@@ -1034,11 +1038,12 @@ def cpu_baseline_all_cores(w, budget_s: float = 8.0, max_threads: int = 16):
     for th in ths:
         th.join()
     t = time.perf_counter() - t0     # includes each thread finishing its last pass
-    moved = sum(passes) * per_pass
+    moved = sum(2 * NL * sample.num_kv * len(mine[k]) * sample.piece_bytes * passes[k] for k in range(threads))
     return {"value": round(moved / t / GB, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{sum(passes)} single-layer backup+restore passes of {n} fragmented pages x "
-                      f"{sample.num_kv} x {sample.piece_bytes} B pieces over one {2 * n}-page, "
-                      f"{threads}-layer host pool, one layer per thread ({moved / GB:.2f} GB moved "
+            "sample": f"backup+restore passes of one {n}-page request ({sample.num_kv} x "
+                      f"{sample.piece_bytes} B pieces, {NL} layers) over one {2 * n}-page host pool, "
+                      f"the request's pages dealt out to {threads} threads, each moving its pages' "
+                      f"pieces in every layer ({sum(passes)} thread passes, {moved / GB:.2f} GB moved "
                       f"in {t:.1f} s)",
             "cpu_model": cpu_model()}
 
