@@ -41,7 +41,7 @@ def random_workload(k: int, exotic: bool = False) -> Workload:
     KV = int(rng.integers(1, 3))
     NL = int(rng.integers(1, 6))
     piece = T * H * row
-    NB = int(rng.integers(4, max(5, min(600, POOL_CAP // (piece * NL * KV))) + 1))
+    NB = int(rng.integers(4, max(5, min(1400, POOL_CAP // (piece * NL * KV))) + 1))
     return Workload(name=f"random{k}", outer=outer, inner=inner, num_pages=NB, num_layers=NL,
                     num_kv=KV, page_size=T, num_heads=H, head_dim=row // eb, dtype_bytes=eb,
                     pages_per_request=max(1, NB // 3), seed=9100 + k,
