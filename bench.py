@@ -1005,8 +1005,9 @@ def cpu_baseline_all_cores(w, budget_s: float = 8.0, max_threads: int = 16):
     import oracle
     import synth
 
-    threads = max(1, min(max_threads, len(os.sched_getaffinity(0))))
     n = w.pages_per_request
+    # every thread gets at least one page of the request
+    threads = max(1, min(max_threads, len(os.sched_getaffinity(0)), n))
     sample = w.scaled(num_pages=2 * n, num_layers=4)
     NL = sample.num_layers
     L = oracle_layout_of(oracle, sample)
