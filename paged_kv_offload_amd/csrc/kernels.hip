@@ -3,10 +3,13 @@
 // (kvx_exchange), and the bounded ready-wait used by GPU-side consumers.
 //
 // Work decomposition. A launch moves the pieces (page, layer, kv) of a layer
-// range, every kv and a list of (page, slot) pairs carried in the kernel
-// arguments. Each piece (T*H*D*eb bytes, contiguous in every supported pool
-// layout and in the packed buffer) is cut into units of
-// kThreads * 16 * U bytes; one workgroup moves one unit at a time (a
+// range, every kv and a list of (page, slot) pairs (or runs of adjacent
+// pages) carried in the kernel arguments, or in device memory when the list
+// is longer than they hold. Each piece (T*H*D*eb bytes, contiguous in every
+// supported pool layout and in the packed buffer) is cut into units of
+// kThreads * 16 * U bytes, and the tails of pieces that such units do not
+// tile, or short pieces whole, share units; one workgroup moves one unit at
+// a time (a
 // grid-stride loop, or unit numbers drawn from a queue where the order of
 // completion matters), every lane issuing U independent 16-byte (dwordx4)
 // loads before its U stores. Each wave owns U KiB of the unit, contiguous,
