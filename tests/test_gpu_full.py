@@ -80,7 +80,7 @@ def check_alloc(w, L, seed, src, dst, l0, l1, alloc_dev):
 
 
 @pytest.mark.parametrize("path", ["staged", "zerocopy"])
-@pytest.mark.parametrize("name", ["llama8b", "trtllm_hnd", "token_pages"])
+@pytest.mark.parametrize("name", ["llama8b", "mla_fp8", "trtllm_hnd", "token_pages"])
 def test_full_size_backup_restore(name, path):
     t = torch()
     w = WORKLOADS[name]
