@@ -173,6 +173,7 @@ struct Lane {
     // streams' calls see whether this one still uses the host link
     hipEvent_t link_ev = nullptr;
     bool link_busy = false;         // link_ev recorded and not yet seen complete
+    int link_dir = 0;               // kLinkWrites | kLinkReads of the calls link_ev covers
     std::mutex mu;
 };
 
@@ -185,16 +186,23 @@ std::mutex g_link_mu;
 std::vector<Lane*> g_link_lanes;
 
 // Zero-copy and staged BACKUP and RESTORE calls of other streams whose work
-// has not finished on L's GPU.
-int link_others(const Lane* L)
+// has not finished on L's GPU, by direction: BACKUPs write host memory,
+// RESTOREs read it.
+struct LinkLoad {
+    int writers = 0, readers = 0;
+    bool any() const { return writers + readers > 0; }
+};
+
+LinkLoad link_others(const Lane* L)
 {
     std::lock_guard<std::mutex> lk(g_link_mu);
-    int n = 0;
+    LinkLoad n;
     for (Lane* o : g_link_lanes) {
         if (o == L || o->device != L->device || !o->link_busy) continue;
         if (hipEventQuery(o->link_ev) == hipErrorNotReady) {
             (void)hipGetLastError();
-            n++;
+            if (o->link_dir & kLinkWrites) n.writers++;
+            if (o->link_dir & kLinkReads) n.readers++;
         } else {
             o->link_busy = false;   // done: not queried again until its next call
         }
@@ -202,7 +210,9 @@ int link_others(const Lane* L)
     return n;
 }
 
-int link_record(Lane* L, hipStream_t s)
+// Records the end of L's latest host-link call (direction dir). Calls queued
+// on the stream before it and not yet seen complete keep their directions.
+int link_record(Lane* L, hipStream_t s, int dir)
 {
     std::lock_guard<std::mutex> lk(g_link_mu);
     if (!L->link_ev) {
@@ -210,25 +220,47 @@ int link_record(Lane* L, hipStream_t s)
         g_link_lanes.push_back(L);
     }
     KVX_HIP(hipEventRecord(L->link_ev, s));
+    L->link_dir = L->link_busy ? (L->link_dir | dir) : dir;
     L->link_busy = true;
     return KVX_OK;
 }
 
-// Workgroups of a one-direction kernel over the host link, given the other
-// streams' host-link calls in flight. Alone, kHostGridAuto (32 x 8 KiB units
-// in flight cover the link's round trip); beside others, a share of
-// kHostLinkBudget. Measured on MI355X, the mixed stream's 128 requests as
-// separate zero-copy calls on four streams (two writing host memory, two
-// reading it): 32 workgroups a kernel 61.6 GB/s, 16 77.2, 12 82.6, 8 82.3;
-// one call alone: 32 workgroups 57.0 / 57.6 GB/s (backup / restore), 24
-// 56.6 / 57.6, 16 55.1 / 57.5, 12 57.0 / 48.3. Workgroups that only write
-// host memory outpace those that only read it, and with many of both the
-// reads fall behind; a kernel that interleaves both (kvx_exchange) is not
-// affected.
-int link_grid(const Lane* L)
+// Workgroups of a one-direction kernel over the host link (dir), given the
+// other streams' host-link calls in flight. Alone, kHostGridAuto (32 x 8 KiB
+// units in flight cover the link's round trip). Beside calls that all move
+// the same direction, a share of kHostLinkBudget. Beside calls of the other
+// direction, a share of a per-direction total (duplex_writers or
+// duplex_readers) over the calls of this direction, itself included.
+//
+// Measured on MI355X (zero-copy, 2 GiB requests of 128 KiB pieces):
+//  - alone: backup 22.6 / 33.5 / 44.5 / 55.5 / 56.9 GB/s at 2 / 3 / 4 / 6 /
+//    32 workgroups, restore 25.6 / 36.7 / 48.4 / 57.4 / 57.5 at 6 / 9 / 12 /
+//    16 / 32: a workgroup writing host memory keeps about 11 GB/s going, one
+//    reading it about 4;
+//  - both directions at once, backups on one stream and restores on another
+//    (workgroups per backup / restore kernel: GB/s both ways): 24 / 24 83.3,
+//    8 / 8 52.2, 4 / 16 87.0, 6 / 16 87.3, 6 / 18 98.5-98.7, 7 / 18 99.4,
+//    5 / 18 97.1, 6 / 20 91.6, 7 / 21 81.5, 6 / 24 66.5, 4 / 24 59.7: the
+//    two directions share the link best when each is held just below what
+//    it reaches alone (about 50 GB/s each); a direction given more than that
+//    slows the other one far more than it gains;
+//  - the mixed stream's 128 requests as separate calls on four streams (two
+//    backups and two restores in flight): a share of 48 regardless of
+//    direction (12 each) 84.6-84.9, 3 / 9 per kernel 99.1-99.9, 4 / 9 93.7,
+//    3 / 8 87.4, 3 / 12 68.2, 2 / 9 82.5.
+// A kernel keeps the grid it was launched with: one sized beside calls that
+// then finish runs on at its share (a share of 6 writers still moves 55
+// GB/s alone, of 18 readers 57; half of either about 35).
+int link_grid(const Lane* L, int dir, const Tuning& t)
 {
-    const int others = link_others(L);
-    return std::min(kHostGridAuto, std::max(8, kHostLinkBudget / (others + 1)));
+    const LinkLoad o = link_others(L);
+    const int same = dir == kLinkWrites ? o.writers : o.readers;
+    const int opp = dir == kLinkWrites ? o.readers : o.writers;
+    const int64_t total = dir == kLinkWrites ? t.duplex_writers : t.duplex_readers;
+    if (opp == 0 || total <= 0)
+        return std::min(kHostGridAuto, std::max(8, kHostLinkBudget / (o.writers + o.readers + 1)));
+    // total / (same + 1), rounded to the nearest
+    return static_cast<int>(std::max<int64_t>(1, (2 * total + same + 1) / (2 * (same + 1))));
 }
 
 int lane_init(Lane* L)
@@ -1131,10 +1163,11 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
         rc = upload_list();
         if (rc != KVX_OK) return rc;
         const bool zc = path == KVX_PATH_ZEROCOPY;
-        Target tg{view, 0, 0, hs ? hs->num : int64_t(n), zc, zc ? link_grid(L) : 0};
+        const int link_dir = dir == GATHER ? kLinkWrites : kLinkReads;
+        Target tg{view, 0, 0, hs ? hs->num : int64_t(n), zc, zc ? link_grid(L, link_dir, t) : 0};
         rc = launch_range(dir, pool, tg, l0, l1, pairs.data(), pairs.size(), pubp, t, L->cu_count, s,
                           nullptr, use_runs ? &runs : nullptr, dev_list);
-        if (rc == KVX_OK && zc) rc = link_record(L, s);
+        if (rc == KVX_OK && zc) rc = link_record(L, s, link_dir);
     } else {
         // chunks of whole layers when one layer fits a ring slot, else slot
         // ranges of one layer
@@ -1171,7 +1204,7 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
         // four streams: 42.0 GB/s with side streams, 80.4 without.
         const bool one_chunk = (l1 - l0) <= layers_per_chunk && slots_per_chunk >= n;
         const bool on_caller = t.staged_dma_on_caller > 0 ||
-                               (t.staged_dma_on_caller < 0 && (one_chunk || link_others(L) > 0));
+                               (t.staged_dma_on_caller < 0 && (one_chunk || link_others(L).any()));
         if (!on_caller && !L->side) KVX_HIP(hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking));
         hipStream_t dma = on_caller ? s : L->side;
         const bool split = dma != s;
@@ -1262,7 +1295,7 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
             KVX_HIP(hipStreamWaitEvent(s, L->ev_done, 0));
         }
         // the caller's stream has passed the call once its copies are done
-        if (rc == KVX_OK) rc = link_record(L, s);
+        if (rc == KVX_OK) rc = link_record(L, s, dir == GATHER ? kLinkWrites : kLinkReads);
     }
     return rc;
 }
@@ -2010,6 +2043,14 @@ int kvx_set_option(int32_t option, int64_t value)
         if (value != 0 && value != 1) break;
         g_tune.device_lists = value;
         return KVX_OK;
+    case KVX_OPT_DUPLEX_WRITERS:
+        if (value < 0 || value > 1024) break;
+        g_tune.duplex_writers = value;
+        return KVX_OK;
+    case KVX_OPT_DUPLEX_READERS:
+        if (value < 0 || value > 1024) break;
+        g_tune.duplex_readers = value;
+        return KVX_OK;
     default:
         return fail(KVX_E_INVAL, "set_option: unknown option " + std::to_string(option));
     }
@@ -2041,6 +2082,8 @@ int kvx_get_option(int32_t option, int64_t* value)
     case KVX_OPT_COALESCE_RUNS: *value = g_tune.coalesce_runs; return KVX_OK;
     case KVX_OPT_TAIL_UNITS: *value = g_tune.tail_units; return KVX_OK;
     case KVX_OPT_DEVICE_LISTS: *value = g_tune.device_lists; return KVX_OK;
+    case KVX_OPT_DUPLEX_WRITERS: *value = g_tune.duplex_writers; return KVX_OK;
+    case KVX_OPT_DUPLEX_READERS: *value = g_tune.duplex_readers; return KVX_OK;
     default: return fail(KVX_E_INVAL, "get_option: unknown option " + std::to_string(option));
     }
 }

@@ -94,6 +94,8 @@ struct Tuning {
     int64_t coalesce_runs = 1;            // move runs of adjacent pages as spans when that takes fewer units
     int64_t tail_units = 1;               // the tails of pieces that 128 KiB units do not tile share units
     int64_t device_lists = 1;             // lists longer than the kernel arguments carry go to device memory
+    int64_t duplex_writers = 6;           // workgroups writing host memory while host reads are in flight (0 = share of 48)
+    int64_t duplex_readers = 18;          // workgroups reading host memory while host writes are in flight (0 = share of 48)
 };
 Tuning tuning();
 
@@ -105,6 +107,8 @@ constexpr int kMaxPairs = 448;       // (page, slot) pairs carried in the kernel
 constexpr int kListHostSlots = 4;    // pinned host buffers a stream's long page lists rotate through
 constexpr int kHostGridAuto = 32;    // default workgroups of a kernel streaming over the host link
 constexpr int kHostLinkBudget = 48;  // workgroups that concurrent one-direction host-link kernels share
+constexpr int kLinkWrites = 1;       // a call's host-link direction: writes host memory (BACKUP)
+constexpr int kLinkReads = 2;        // reads host memory (RESTORE)
 constexpr int64_t kRestoreChunkMin = 32ll << 20;   // default minimum staged restore chunk
 constexpr int64_t kPublishBlockBytes = 2ll << 20;  // auto publish block: about this many bytes
 // kvx_restore_noalloc: layers of a pool it serves, and the words of its device

@@ -32,6 +32,7 @@ KVX_OPT_HOST_GRID_MAX, KVX_OPT_UNIT_ORDER, KVX_OPT_MAX_UNROLL = 6, 7, 8
 KVX_OPT_STAGED_DMA_ON_CALLER, KVX_OPT_HND_LDS, KVX_OPT_UNIT_ROUNDS = 9, 10, 11
 KVX_OPT_FAIL_ALLOCS, KVX_OPT_RING_PAIRING, KVX_OPT_PUBLISH_BLOCK = 12, 13, 14
 KVX_OPT_COALESCE_RUNS, KVX_OPT_TAIL_UNITS, KVX_OPT_DEVICE_LISTS = 15, 16, 17
+KVX_OPT_DUPLEX_WRITERS, KVX_OPT_DUPLEX_READERS = 18, 19
 
 ERROR_NAMES = {0: "KVX_OK", -1: "KVX_E_INVAL", -2: "KVX_E_NONCONTIG", -3: "KVX_E_ALIGN",
                -4: "KVX_E_RANGE", -5: "KVX_E_DUP", -6: "KVX_E_STALE", -7: "KVX_E_NOTPINNED",

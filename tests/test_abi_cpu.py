@@ -241,6 +241,17 @@ def test_options_roundtrip():
     for v in (-1, 4097):
         with pytest.raises(kvx.KvxError):
             K.kvx_set_option(pb, v)
+    # duplex shares of the host link: 6 writers and 18 readers by default,
+    # 0 (the direction-blind share) to 1024
+    for opt, default in ((K.KVX_OPT_DUPLEX_WRITERS, 6), (K.KVX_OPT_DUPLEX_READERS, 18)):
+        assert K.kvx_get_option(opt) == default
+        for v in (0, 1, 1024, default):
+            K.kvx_set_option(opt, v)
+            assert K.kvx_get_option(opt) == v
+        for v in (-1, 1025):
+            with pytest.raises(kvx.KvxError):
+                K.kvx_set_option(opt, v)
+        assert K.kvx_get_option(opt) == default
 
 
 def test_ipc_handle_layout_matches_the_header(tmp_path):
