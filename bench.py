@@ -15,13 +15,15 @@ restore of the step is published. Each call runs validation and run planning
 on the host and then the zero-copy gather or scatter kernel over the host
 link.
 
-Headline schedule: each backup paired with the restore after it in one
-kvx_exchange launch, pairs alternating over two streams, so four requests
-are in flight and both directions of the host link carry data together.
-Also reported: the same stream as separate calls on four streams (the
-config's literal reading: zero-copy and staged), through the submission
-ring's executor, the device pack/unpack kernels against the HBM roofline,
-the pinned memcpy peaks, the Llama-3-8B-shaped one-request step and the CPU
+Headline schedule: every request its own zero-copy call, round-robin over
+four streams, so four requests are in flight (two backups and two restores)
+and both directions of the host link carry data together; the library sizes
+each kernel's grid by the other streams' host-link calls in flight and their
+direction. Also reported: the same stream with each backup paired with the
+restore after it in one kvx_exchange launch (pairs on two streams), the
+four-stream schedule on the staged path, through the submission ring's
+executor, the device pack/unpack kernels against the HBM roofline, the
+pinned memcpy peaks, the Llama-3-8B-shaped one-request step and the CPU
 oracle on a bounded sample (a baseline only).
 
 value = 128 x 2 GiB x steps / wall time of the steps (GB = 1e9 B). The pool
@@ -286,7 +288,7 @@ def mixed_main(args, options):
     peaks = memcpy_peaks(T, torch, streams[1])
     proto = pcie_protocol_bound()
 
-    # ---- the headline schedule: backup k + restore k+1 in one kvx_exchange ----
+    # ---- the paired schedule: backup k + restore k+1 in one kvx_exchange ----
     pairs = [(sched[k][1], sched[k + 1][1]) for k in range(0, R, 2)]
     assert all(sched[k][0] == "backup" and sched[k + 1][0] == "restore" for k in range(0, R, 2))
     ready_x = K.kvx_ready_create(2 * NL, 1)     # slots [0, NL): stream 0's restores; [NL, 2NL): stream 1's
@@ -308,7 +310,7 @@ def mixed_main(args, options):
         while K.kvx_ready_prefix(ready_x) < published["x"]:    # the consumers' view of completion
             pass
 
-    # ---- the literal schedule: every request its own call, four streams ----
+    # ---- the headline schedule: every request its own call, four streams ----
     ready_s = K.kvx_ready_create(2 * NL, 1)     # restores run on streams 1 and 3
 
     def streams_pass(bpath, rpath):
@@ -344,8 +346,11 @@ def mixed_main(args, options):
                     "every layer; the host polls the ready prefix until the step's restores are published")
     else:
         head_fn = lambda marks=None: streams_pass(ZC, ZC)  # noqa: E731
-        schedule = ("every request its own zero-copy call, round-robin over four streams (4 in flight); "
-                    "restores publish every layer; the host polls the ready prefix")
+        schedule = ("every request its own zero-copy call, round-robin over four streams (4 in flight: "
+                    "two backups, two restores; the library holds the kernels that write host memory "
+                    "to 6 workgroups and those that read it to 18 in total while both directions are "
+                    "in flight); restores publish every layer; the host polls the ready prefix until "
+                    "the step's restores are published")
     wall, marks = run(head_fn, args.steps, args.warmup)
     value = R * P * args.steps / wall / GB
     ms_per_step = wall / args.steps * 1e3
@@ -1058,10 +1063,11 @@ def main():
                     help="mixed (the 128-request hit/miss stream, default) or a single-request "
                          "workload: llama8b, mla_fp8, trtllm_hnd, tiny, token_pages (the llama8b "
                          "shape at one token per page)")
-    ap.add_argument("--schedule", choices=["exchange", "streams"], default="exchange",
-                    help="mixed: exchange = backup + next restore in one kvx_exchange on two streams, "
-                         "streams = one call per request on four streams; single-request workloads: "
-                         "exchange = layer-pipelined, streams = serial backup then restore")
+    ap.add_argument("--schedule", choices=["exchange", "streams"], default=None,
+                    help="mixed: streams (default) = one call per request on four streams, exchange = "
+                         "backup + next restore in one kvx_exchange on two streams; single-request "
+                         "workloads: exchange (default) = layer-pipelined, streams = serial backup then "
+                         "restore")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the other schedules, the per-path rates and the latency legs")
@@ -1074,6 +1080,8 @@ def main():
                     help="instead of the headline, print one line per other workload with its own "
                          "figures (tiny: latency; mla: layer-0-ready; trtllm: HND rates; host tier)")
     args = ap.parse_args()
+    if args.schedule is None:
+        args.schedule = "streams" if args.workload == "mixed" and not args.all_workloads else "exchange"
     if args.gpus != 1:
         print(json.dumps({"error": "kvx moves KV between one GPU and its host tier; this benchmark "
                                    "measures one GPU (run with --gpus 1)"}), flush=True)
