@@ -173,7 +173,7 @@ struct Lane {
     // streams' calls see whether this one still uses the host link
     hipEvent_t link_ev = nullptr;
     bool link_busy = false;         // link_ev recorded and not yet seen complete
-    int link_dir = 0;               // kLinkWrites | kLinkReads of the calls link_ev covers
+    int link_dir = 0;               // kLink* traffic of the calls link_ev covers
     std::mutex mu;
 };
 
@@ -186,11 +186,13 @@ std::mutex g_link_mu;
 std::vector<Lane*> g_link_lanes;
 
 // Zero-copy and staged BACKUP and RESTORE calls of other streams whose work
-// has not finished on L's GPU, by direction: BACKUPs write host memory,
-// RESTOREs read it.
+// has not finished on L's GPU, by direction (BACKUPs write host memory,
+// RESTOREs read it) and by mover (the zero-copy kernel, or the staged path's
+// copies).
 struct LinkLoad {
-    int writers = 0, readers = 0;
-    bool any() const { return writers + readers > 0; }
+    int writers = 0, readers = 0;           // zero-copy kernels
+    int dma_writers = 0, dma_readers = 0;   // staged copies
+    int all() const { return writers + readers + dma_writers + dma_readers; }
 };
 
 LinkLoad link_others(const Lane* L)
@@ -203,6 +205,8 @@ LinkLoad link_others(const Lane* L)
             (void)hipGetLastError();
             if (o->link_dir & kLinkWrites) n.writers++;
             if (o->link_dir & kLinkReads) n.readers++;
+            if (o->link_dir & kLinkDmaWrites) n.dma_writers++;
+            if (o->link_dir & kLinkDmaReads) n.dma_readers++;
         } else {
             o->link_busy = false;   // done: not queried again until its next call
         }
@@ -225,12 +229,16 @@ int link_record(Lane* L, hipStream_t s, int dir)
     return KVX_OK;
 }
 
-// Workgroups of a one-direction kernel over the host link (dir), given the
-// other streams' host-link calls in flight. Alone, kHostGridAuto (32 x 8 KiB
-// units in flight cover the link's round trip). Beside calls that all move
-// the same direction, a share of kHostLinkBudget. Beside calls of the other
-// direction, a share of a per-direction total (duplex_writers or
-// duplex_readers) over the calls of this direction, itself included.
+// Workgroups of a one-direction kernel over the host link (dir: kLinkWrites
+// or kLinkReads), given the other streams' host-link calls in flight. Alone,
+// kHostGridAuto (32 x 8 KiB units in flight cover the link's round trip).
+// A kernel that reads host memory, beside any call that writes it, and a
+// kernel that writes host memory, beside a zero-copy RESTORE kernel, take a
+// share of a per-direction total (duplex_writers or duplex_readers) over
+// the zero-copy kernels of their own direction, themselves included. A
+// kernel that writes host memory beside staged RESTOREs only (whose copies
+// read it) takes kHostGridAuto. Else a share of kHostLinkBudget over all
+// the calls in flight.
 //
 // Measured on MI355X (zero-copy, 2 GiB requests of 128 KiB pieces):
 //  - alone: backup 22.6 / 33.5 / 44.5 / 55.5 / 56.9 GB/s at 2 / 3 / 4 / 6 /
@@ -247,7 +255,15 @@ int link_record(Lane* L, hipStream_t s, int dir)
 //  - the mixed stream's 128 requests as separate calls on four streams (two
 //    backups and two restores in flight): a share of 48 regardless of
 //    direction (12 each) 84.6-84.9, 3 / 9 per kernel 99.1-99.9, 4 / 9 93.7,
-//    3 / 8 87.4, 3 / 12 68.2, 2 / 9 82.5.
+//    3 / 8 87.4, 3 / 12 68.2, 2 / 9 82.5;
+//  - the same with staged calls in one direction (their copies move that
+//    direction; GB/s both ways, the duplex shares on / a share of 48):
+//    zero-copy restores beside staged backups 98.6-98.8 / 69.6, zero-copy
+//    backups beside staged restores 66.1 / 82.1, and at 6 / 8 / 16 / 24 /
+//    32 workgroups a backup kernel 69.8 / 77.6 / 84.7 / 90.5 / 92.5: kernels
+//    that read host memory need holding back beside the copies' writes too,
+//    while kernels that write it beside the copies' reads do best with a
+//    full grid.
 // A kernel keeps the grid it was launched with: one sized beside calls that
 // then finish runs on at its share (a share of 6 writers still moves 55
 // GB/s alone, of 18 readers 57; half of either about 35).
@@ -255,10 +271,11 @@ int link_grid(const Lane* L, int dir, const Tuning& t)
 {
     const LinkLoad o = link_others(L);
     const int same = dir == kLinkWrites ? o.writers : o.readers;
-    const int opp = dir == kLinkWrites ? o.readers : o.writers;
+    const int opp = dir == kLinkWrites ? o.readers : o.writers + o.dma_writers;
     const int64_t total = dir == kLinkWrites ? t.duplex_writers : t.duplex_readers;
+    if (dir == kLinkWrites && opp == 0 && o.dma_readers > 0 && total > 0) return kHostGridAuto;
     if (opp == 0 || total <= 0)
-        return std::min(kHostGridAuto, std::max(8, kHostLinkBudget / (o.writers + o.readers + 1)));
+        return std::min(kHostGridAuto, std::max(8, kHostLinkBudget / (o.all() + 1)));
     // total / (same + 1), rounded to the nearest
     return static_cast<int>(std::max<int64_t>(1, (2 * total + same + 1) / (2 * (same + 1))));
 }
@@ -1204,7 +1221,7 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
         // four streams: 42.0 GB/s with side streams, 80.4 without.
         const bool one_chunk = (l1 - l0) <= layers_per_chunk && slots_per_chunk >= n;
         const bool on_caller = t.staged_dma_on_caller > 0 ||
-                               (t.staged_dma_on_caller < 0 && (one_chunk || link_others(L).any()));
+                               (t.staged_dma_on_caller < 0 && (one_chunk || link_others(L).all() > 0));
         if (!on_caller && !L->side) KVX_HIP(hipStreamCreateWithFlags(&L->side, hipStreamNonBlocking));
         hipStream_t dma = on_caller ? s : L->side;
         const bool split = dma != s;
@@ -1295,7 +1312,7 @@ int enqueue(kvx_pool* pool, Dir dir, const int32_t* ids, int32_t n, uint8_t* hos
             KVX_HIP(hipStreamWaitEvent(s, L->ev_done, 0));
         }
         // the caller's stream has passed the call once its copies are done
-        if (rc == KVX_OK) rc = link_record(L, s, dir == GATHER ? kLinkWrites : kLinkReads);
+        if (rc == KVX_OK) rc = link_record(L, s, dir == GATHER ? kLinkDmaWrites : kLinkDmaReads);
     }
     return rc;
 }
