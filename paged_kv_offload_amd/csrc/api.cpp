@@ -214,14 +214,20 @@ LinkLoad link_others(const Lane* L)
     return n;
 }
 
-// Records the end of L's latest host-link call (direction dir). Calls queued
-// on the stream before it and not yet seen complete keep their directions.
+// Records the end of L's latest host-link call (traffic dir). Calls queued
+// on the stream before it that have not finished keep their directions.
 int link_record(Lane* L, hipStream_t s, int dir)
 {
     std::lock_guard<std::mutex> lk(g_link_mu);
     if (!L->link_ev) {
         KVX_HIP(hipEventCreateWithFlags(&L->link_ev, hipEventDisableTiming));
         g_link_lanes.push_back(L);
+    }
+    if (L->link_busy) {   // the previous calls' event, recorded after them
+        if (hipEventQuery(L->link_ev) == hipErrorNotReady)
+            (void)hipGetLastError();
+        else
+            L->link_busy = false;
     }
     KVX_HIP(hipEventRecord(L->link_ev, s));
     L->link_dir = L->link_busy ? (L->link_dir | dir) : dir;
