@@ -186,15 +186,7 @@ std::mutex g_link_mu;
 std::vector<Lane*> g_link_lanes;
 
 // Zero-copy and staged BACKUP and RESTORE calls of other streams whose work
-// has not finished on L's GPU, by direction (BACKUPs write host memory,
-// RESTOREs read it) and by mover (the zero-copy kernel, or the staged path's
-// copies).
-struct LinkLoad {
-    int writers = 0, readers = 0;           // zero-copy kernels
-    int dma_writers = 0, dma_readers = 0;   // staged copies
-    int all() const { return writers + readers + dma_writers + dma_readers; }
-};
-
+// has not finished on L's GPU (LinkLoad).
 LinkLoad link_others(const Lane* L)
 {
     std::lock_guard<std::mutex> lk(g_link_mu);
@@ -235,55 +227,12 @@ int link_record(Lane* L, hipStream_t s, int dir)
     return KVX_OK;
 }
 
-// Workgroups of a one-direction kernel over the host link (dir: kLinkWrites
-// or kLinkReads), given the other streams' host-link calls in flight. Alone,
-// kHostGridAuto (32 x 8 KiB units in flight cover the link's round trip).
-// A kernel that reads host memory, beside any call that writes it, and a
-// kernel that writes host memory, beside a zero-copy RESTORE kernel, take a
-// share of a per-direction total (duplex_writers or duplex_readers) over
-// the zero-copy kernels of their own direction, themselves included. A
-// kernel that writes host memory beside staged RESTOREs only (whose copies
-// read it) takes kHostGridAuto. Else a share of kHostLinkBudget over all
-// the calls in flight.
-//
-// Measured on MI355X (zero-copy, 2 GiB requests of 128 KiB pieces):
-//  - alone: backup 22.6 / 33.5 / 44.5 / 55.5 / 56.9 GB/s at 2 / 3 / 4 / 6 /
-//    32 workgroups, restore 25.6 / 36.7 / 48.4 / 57.4 / 57.5 at 6 / 9 / 12 /
-//    16 / 32: a workgroup writing host memory keeps about 11 GB/s going, one
-//    reading it about 4;
-//  - both directions at once, backups on one stream and restores on another
-//    (workgroups per backup / restore kernel: GB/s both ways): 24 / 24 83.3,
-//    8 / 8 52.2, 4 / 16 87.0, 6 / 16 87.3, 6 / 18 98.5-98.7, 7 / 18 99.4,
-//    5 / 18 97.1, 6 / 20 91.6, 7 / 21 81.5, 6 / 24 66.5, 4 / 24 59.7: the
-//    two directions share the link best when each is held just below what
-//    it reaches alone (about 50 GB/s each); a direction given more than that
-//    slows the other one far more than it gains;
-//  - the mixed stream's 128 requests as separate calls on four streams (two
-//    backups and two restores in flight): a share of 48 regardless of
-//    direction (12 each) 84.6-84.9, 3 / 9 per kernel 99.1-99.9, 4 / 9 93.7,
-//    3 / 8 87.4, 3 / 12 68.2, 2 / 9 82.5;
-//  - the same with staged calls in one direction (their copies move that
-//    direction; GB/s both ways, the duplex shares on / a share of 48):
-//    zero-copy restores beside staged backups 98.6-98.8 / 69.6, zero-copy
-//    backups beside staged restores 66.1 / 82.1, and at 6 / 8 / 16 / 24 /
-//    32 workgroups a backup kernel 69.8 / 77.6 / 84.7 / 90.5 / 92.5: kernels
-//    that read host memory need holding back beside the copies' writes too,
-//    while kernels that write it beside the copies' reads do best with a
-//    full grid.
-// A kernel keeps the grid it was launched with: one sized beside calls that
-// then finish runs on at its share (a share of 6 writers still moves 55
-// GB/s alone, of 18 readers 57; half of either about 35).
+// Workgroups of a one-direction zero-copy kernel (dir: kLinkWrites or
+// kLinkReads), given the other streams' host-link calls in flight now
+// (link_grid_for states the policy and its measurements).
 int link_grid(const Lane* L, int dir, const Tuning& t)
 {
-    const LinkLoad o = link_others(L);
-    const int same = dir == kLinkWrites ? o.writers : o.readers;
-    const int opp = dir == kLinkWrites ? o.readers : o.writers + o.dma_writers;
-    const int64_t total = dir == kLinkWrites ? t.duplex_writers : t.duplex_readers;
-    if (dir == kLinkWrites && opp == 0 && o.dma_readers > 0 && total > 0) return kHostGridAuto;
-    if (opp == 0 || total <= 0)
-        return std::min(kHostGridAuto, std::max(8, kHostLinkBudget / (o.all() + 1)));
-    // total / (same + 1), rounded to the nearest
-    return static_cast<int>(std::max<int64_t>(1, (2 * total + same + 1) / (2 * (same + 1))));
+    return link_grid_for(link_others(L), dir, t.duplex_writers, t.duplex_readers);
 }
 
 int lane_init(Lane* L)

@@ -105,12 +105,6 @@ Tuning tuning();
 constexpr int kThreads = 256;        // 4 wave64 per workgroup
 constexpr int kMaxPairs = 448;       // (page, slot) pairs carried in the kernel arguments
 constexpr int kListHostSlots = 4;    // pinned host buffers a stream's long page lists rotate through
-constexpr int kHostGridAuto = 32;    // default workgroups of a kernel streaming over the host link
-constexpr int kHostLinkBudget = 48;  // workgroups that concurrent one-direction host-link kernels share
-constexpr int kLinkWrites = 1;       // a call's host-link traffic: a kernel writes host memory (zero-copy BACKUP)
-constexpr int kLinkReads = 2;        // a kernel reads host memory (zero-copy RESTORE)
-constexpr int kLinkDmaWrites = 4;    // copies write host memory (staged BACKUP)
-constexpr int kLinkDmaReads = 8;     // copies read host memory (staged RESTORE)
 constexpr int64_t kRestoreChunkMin = 32ll << 20;   // default minimum staged restore chunk
 constexpr int64_t kPublishBlockBytes = 2ll << 20;  // auto publish block: about this many bytes
 // kvx_restore_noalloc: layers of a pool it serves, and the words of its device

@@ -413,8 +413,53 @@ static void fuzz_ring(int iters)
                 iters, static_cast<unsigned long long>(total));
 }
 
+// The host-link grid policy against its rule, case by case: alone, beside
+// calls of the same direction, both directions (shares of 6 and 18 and their
+// rounding), beside staged copies, and with the duplex shares switched off.
+static void check_link_policy()
+{
+    struct Case {
+        int w, r, dw, dr, dir;
+        int64_t dup_w, dup_r;
+        int want;
+    };
+    const int W = kLinkWrites, R = kLinkReads;
+    const Case cases[] = {
+        {0, 0, 0, 0, W, 6, 18, 32},  {0, 0, 0, 0, R, 6, 18, 32},    // alone
+        {1, 0, 0, 0, W, 6, 18, 24},  {3, 0, 0, 0, W, 6, 18, 12},    // same direction only
+        {0, 2, 0, 0, R, 6, 18, 16},  {9, 0, 0, 0, W, 6, 18, 8},     // ... at least 8
+        {0, 1, 0, 0, W, 6, 18, 6},   {1, 1, 0, 0, W, 6, 18, 3},     // writers beside a reader kernel
+        {2, 1, 0, 0, W, 6, 18, 2},   {3, 2, 0, 0, W, 6, 18, 2},     // 6 / 3 = 2, 6 / 4 = 1.5 -> 2
+        {6, 1, 0, 0, W, 6, 18, 1},                                  // at least 1
+        {1, 0, 0, 0, R, 6, 18, 18},  {1, 1, 0, 0, R, 6, 18, 9},     // readers beside a writer
+        {2, 2, 0, 0, R, 6, 18, 6},   {2, 3, 0, 0, R, 6, 18, 5},     // 18 / 4 = 4.5 -> 5
+        {0, 0, 1, 0, R, 6, 18, 18},  {0, 1, 2, 0, R, 6, 18, 9},     // readers beside staged backups
+        {0, 0, 0, 2, W, 6, 18, 32},  {1, 0, 0, 2, W, 6, 18, 32},    // writers beside staged restores only
+        {0, 1, 0, 2, W, 6, 18, 6},                                  // ... and a reader kernel
+        {0, 0, 2, 0, W, 6, 18, 16},  {0, 0, 0, 2, R, 6, 18, 16},    // staged calls of its own direction
+        {1, 1, 0, 0, W, 0, 18, 16},  {1, 1, 0, 0, R, 6, 0, 16},     // duplex shares off: 48 / 3
+        {1, 1, 1, 1, R, 0, 0, 9},    {0, 1, 0, 2, W, 0, 18, 12},
+        {1, 1, 0, 0, W, 12, 18, 6},  {1, 1, 0, 0, R, 6, 30, 15},    // other totals
+    };
+    for (const Case& c : cases) {
+        LinkLoad o;
+        o.writers = c.w;
+        o.readers = c.r;
+        o.dma_writers = c.dw;
+        o.dma_readers = c.dr;
+        const int got = link_grid_for(o, c.dir, c.dup_w, c.dup_r);
+        if (got != c.want) {
+            std::printf("link policy: writers %d readers %d dma %d/%d dir %d shares %lld/%lld: %d, want %d\n",
+                        c.w, c.r, c.dw, c.dr, c.dir, static_cast<long long>(c.dup_w),
+                        static_cast<long long>(c.dup_r), got, c.want);
+            std::exit(1);
+        }
+    }
+}
+
 int main()
 {
+    check_link_policy();
     fuzz_extremes();
     fuzz_geometry(20000);
     fuzz_pages(3000);
